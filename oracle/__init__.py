@@ -1,0 +1,217 @@
+"""CPU oracle for the BitNet b1.58 BitLinear hot path — TEST INFRASTRUCTURE.
+
+The reference that the HIP library is checked against. Only the test suite,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+it; the library itself never does, and fails loudly when its own HIP build is
+missing instead of falling back to anything here.
+
+The steps live in ``bitlinear_oracle.c`` (plain C, one function per step, each
+citing the passage it follows). This module loads that library, marshals numpy
+arrays, and composes the two block-level chains:
+
+* :func:`ffn_block` — the MLP of the nnterp BitNet page, section "The block, in
+  order" (``m = relu(gate(z))**2 * up(z)``, ``out = down(ffn_sub_norm(m))``),
+  taken without pre-norm or residual (reading R13);
+* :func:`decoder_layer` — one decoder block's projections in the order of that
+  section, with the attention replaced by its exact value when every token
+  attends only to itself (reading R12): the output of query head ``h`` is the
+  value of key/value head ``h // (n_heads / n_kv_heads)`` (section "Loading":
+  20 query heads share 5 key/value heads).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run oracle/build.py (or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "orc_absmean": (ctypes.c_double, [_p, _i64]),
+            "orc_ternarize": (None, [_p, _i64, ctypes.c_double, _p]),
+            "orc_pack": (ctypes.c_int, [_p, _i64, _i64, _p]),
+            "orc_unpack": (_i64, [_p, _i64, _i64, _p]),
+            "orc_quant_absmax": (None, [_p, _i64, _i64, _p, _p]),
+            "orc_quant_rms": (None, [_p, _i64, _i64, _p, ctypes.c_float, _p, _p, _p]),
+            "orc_relu2_mul": (None, [_p, _i64, _i64, _p]),
+            "orc_contract": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p]),
+            "orc_rescale": (None, [_p, _i64, _i64, _p, _p, _p, ctypes.c_int, _p]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+# ---------------------------------------------------------------- single steps
+def absmean(w) -> float:
+    """O1: gamma = mean |W| (fp64, sequential)."""
+    w, pw = _c(w, np.float32)
+    return float(_load().orc_absmean(pw, w.size))
+
+
+def ternarize(w, gamma: float) -> np.ndarray:
+    """O2: codes in {-1, 0, 1}: sign(W) where |W| > gamma / 2."""
+    w, pw = _c(w, np.float32)
+    c = np.empty(w.shape, dtype=np.int8)
+    _load().orc_ternarize(pw, w.size, float(gamma), c.ctypes.data)
+    return c
+
+
+def pack(c) -> np.ndarray:
+    """O3: [n][k] codes -> [n][k/4] bytes (four to a byte)."""
+    c, pc = _c(c, np.int8)
+    n, k = c.shape
+    p = np.empty((n, k // 4), dtype=np.uint8)
+    if _load().orc_pack(pc, n, k, p.ctypes.data) != 0:
+        raise ValueError("pack: k must be a multiple of 16 and codes in {-1, 0, 1}")
+    return p
+
+
+def unpack(p, k: int):
+    """O3 inverse: returns (codes [n][k], number of invalid fields)."""
+    p, pp = _c(p, np.uint8)
+    n = p.shape[0]
+    c = np.empty((n, k), dtype=np.int8)
+    bad = _load().orc_unpack(pp, n, k, c.ctypes.data)
+    if bad < 0:
+        raise ValueError("unpack: k must be a multiple of 16")
+    return c, int(bad)
+
+
+def quant_absmax(x):
+    """O4: per-token codes and fp32 deq."""
+    x, px = _c(x, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), dtype=np.int8)
+    deq = np.empty(m, dtype=np.float32)
+    _load().orc_quant_absmax(px, m, k, q.ctypes.data, deq.ctypes.data)
+    return q, deq
+
+
+def quant_rms(x, gain=None, eps: float = 1e-5):
+    """O5: RMSNorm (gain, eps) folded into the per-token quantization."""
+    x, px = _c(x, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), dtype=np.int8)
+    deq = np.empty(m, dtype=np.float32)
+    v = np.empty(k, dtype=np.float32)
+    pg = None
+    if gain is not None:
+        gain, pg = _c(gain, np.float32)
+    _load().orc_quant_rms(px, m, k, pg, ctypes.c_float(eps), q.ctypes.data, deq.ctypes.data, v.ctypes.data)
+    return q, deq
+
+
+def relu2_mul(gu, inter: int) -> np.ndarray:
+    """O6: rows [gate | up] -> relu(gate)^2 * up (fp32, left to right)."""
+    gu, pg = _c(gu, np.float32)
+    m = gu.shape[0]
+    assert gu.shape[1] == 2 * inter
+    out = np.empty((m, inter), dtype=np.float32)
+    _load().orc_relu2_mul(pg, m, inter, out.ctypes.data)
+    return out
+
+
+def contract(q, c) -> np.ndarray:
+    """O7: acc = q @ c^T exactly (int32)."""
+    q, pq = _c(q, np.int8)
+    c, pc = _c(c, np.int8)
+    m, k = q.shape
+    n = c.shape[0]
+    assert c.shape[1] == k
+    acc = np.empty((m, n), dtype=np.int32)
+    if _load().orc_contract(pq, m, k, pc, n, acc.ctypes.data) != 0:
+        raise OverflowError("contraction does not fit int32")
+    return acc
+
+
+def rescale(acc, deq, gammas, seg_end) -> np.ndarray:
+    """O8: y = fl32(fl32(acc * deq) * fl32(gamma_seg)), no bias."""
+    acc, pa = _c(acc, np.int32)
+    deq, pd = _c(deq, np.float32)
+    g, pg = _c(np.atleast_1d(np.asarray(gammas, dtype=np.float64)), np.float64)
+    se, ps = _c(np.atleast_1d(np.asarray(seg_end, dtype=np.int64)), np.int64)
+    m, n = acc.shape
+    assert len(g) == len(se) and se[-1] == n
+    y = np.empty((m, n), dtype=np.float32)
+    _load().orc_rescale(pa, m, n, pd, pg, ps, len(g), y.ctypes.data)
+    return y
+
+
+# ---------------------------------------------------------------- compositions
+def forward(x, c, gammas, seg_end=None, gain=None, eps: float | None = None):
+    """One projection: O4 (or O5 when ``eps`` is given) -> O7 -> O8."""
+    n = c.shape[0]
+    if seg_end is None:
+        seg_end = [n]
+    if eps is None:
+        q, deq = quant_absmax(x)
+    else:
+        q, deq = quant_rms(x, gain, eps)
+    acc = contract(q, c)
+    return {"q": q, "deq": deq, "acc": acc, "y": rescale(acc, deq, gammas, seg_end)}
+
+
+def ffn_block(x, c_gu, gam_gu, c_down, gam_down, ffn_gain=None, eps: float = 1e-5):
+    """O9: q1 = O4(x); GU = [gate|up]; Mi = relu(G)^2 U; (q2, d2) = O5(Mi); y = down."""
+    inter = c_gu.shape[0] // 2
+    s1 = forward(x, c_gu, list(gam_gu), [inter, 2 * inter])
+    mi = relu2_mul(s1["y"], inter)
+    s2 = forward(mi, c_down, [gam_down], None, ffn_gain, eps)
+    return {"q1": s1["q"], "deq1": s1["deq"], "acc_gu": s1["acc"], "gu": s1["y"], "mi": mi,
+            "q2": s2["q"], "deq2": s2["deq"], "acc_down": s2["acc"], "y": s2["y"]}
+
+
+def gqa_broadcast(v, n_heads: int, n_kv_heads: int, head_dim: int) -> np.ndarray:
+    """Per-token attention output when each token attends only to itself: query
+    head h returns the value of key/value head h // (n_heads // n_kv_heads)."""
+    group = n_heads // n_kv_heads
+    m = v.shape[0]
+    out = np.empty((m, n_heads * head_dim), dtype=np.float32)
+    for h in range(n_heads):
+        kv = h // group
+        out[:, h * head_dim:(h + 1) * head_dim] = v[:, kv * head_dim:(kv + 1) * head_dim]
+    return out
+
+
+def decoder_layer(x, w, eps: float = 1e-5, n_heads: int = 20, n_kv_heads: int = 5, head_dim: int = 128):
+    """O10, one block's projection stack (nnterp BitNet page, "The block, in order").
+
+    ``w`` holds ternary codes and fp64 gammas: ``qkv`` [H + 2 kv][H] (q|k|v) with
+    ``g_qkv`` (3), ``o`` [H][H] with ``g_o``, ``gu`` [2I][H] (gate|up) with ``g_gu`` (2),
+    ``down`` [H][I] with ``g_down``; optional RMSNorm gains ``n_in``, ``n_attn``,
+    ``n_post``, ``n_ffn`` (None = 1)."""
+    hdim = x.shape[1]
+    kv = n_kv_heads * head_dim
+    inter = w["gu"].shape[0] // 2
+    s_qkv = forward(x, w["qkv"], w["g_qkv"], [hdim, hdim + kv, hdim + 2 * kv], w.get("n_in"), eps)
+    v = s_qkv["y"][:, hdim + kv:hdim + 2 * kv]
+    a = gqa_broadcast(v, n_heads, n_kv_heads, head_dim)
+    s_o = forward(a, w["o"], [w["g_o"]], None, w.get("n_attn"), eps)
+    h = (x.astype(np.float32) + s_o["y"]).astype(np.float32)
+    s_gu = forward(h, w["gu"], w["g_gu"], [inter, 2 * inter], w.get("n_post"), eps)
+    mi = relu2_mul(s_gu["y"], inter)
+    s_d = forward(mi, w["down"], [w["g_down"]], None, w.get("n_ffn"), eps)
+    x_next = (h + s_d["y"]).astype(np.float32)
+    return {"qkv": s_qkv, "attn": a, "o": s_o, "h": h, "gu": s_gu, "mi": mi, "down": s_d, "x": x_next}

@@ -1,0 +1,209 @@
+/* CPU oracle for the BitNet b1.58 BitLinear hot path — TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, single-threaded C11. It is the reference the HIP path is
+ * checked against, and nothing else: only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it. It shares no code, header or
+ * table with the HIP library, and never reads a value the HIP path produced.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off (no fast-math; x86-64 SSE2, so
+ * every float operation is one correctly rounded binary32 operation and every
+ * double operation one binary64 operation; rintf rounds half to even).
+ *
+ * Sources ("pages"):
+ *  [card]   "BitNet b1.58 2B4T - Scaling Native 1-bit LLM" (Azure AI model card),
+ *           section "Model Details".
+ *  [nnterp] "nnterp encyclopedia: BitNet b1.58" (family bitnet), sections
+ *           "The block, in order", "Scaling inside a sublayer is undone by the
+ *           sub-norm", "The projections quantize their inputs and weights",
+ *           "The MLP gates with a squared ReLU", "The two checkpoints", "Config".
+ *
+ * Where the pages leave a step open, the reading taken is stated at the step
+ * (R-numbers match the list of readings kept with the design notes).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---- O1: weight scale gamma = mean |W| over the whole matrix ------------------
+ * [card] "Model Details": weights are quantized with absmean quantization;
+ * [nnterp] "The projections quantize their inputs and weights": rounded to
+ * {-1, 0, 1} * mean|W|, stored with one weight_scale.
+ * R4: one gamma per matrix. Sum in fp64, sequentially in row-major order. */
+double orc_absmean(const float *w, int64_t count) {
+  if (count <= 0) return 0.0;
+  double s = 0.0;
+  for (int64_t i = 0; i < count; ++i) s += fabs((double)w[i]);
+  return s / (double)count;
+}
+
+/* ---- O2: ternary code of each weight ----------------------------------------
+ * c = round(W / gamma) clipped to [-1, 1] (same passages as O1). In exact
+ * arithmetic that is sign(W) when |W| > gamma / 2, and 0 otherwise; a tie
+ * |W| == gamma / 2 rounds half to even, to 0 (R5, R1). The comparison below
+ * is exact: (double)|W| is exact and 0.5 * gamma is an exact halving. */
+void orc_ternarize(const float *w, int64_t count, double gamma, int8_t *c) {
+  const double half = 0.5 * gamma;
+  for (int64_t i = 0; i < count; ++i) {
+    double a = fabs((double)w[i]);
+    c[i] = (int8_t)(a > half ? (w[i] > 0.0f ? 1 : -1) : 0);
+  }
+}
+
+/* ---- O3: "four to a byte" storage ([nnterp] "The projections quantize their
+ * inputs and weights"; "The two checkpoints") ----------------------------------
+ * The pages fix only the density. Our layout (R6): row n of K codes takes K/4
+ * bytes. Code k sits in group g = k / 16, slot t = k % 16; it is stored as the
+ * field u = c + 1 (0, 1 or 2) in byte 4g + (t % 4) of the row, at bits
+ * 2 * (t / 4) and 2 * (t / 4) + 1. Field value 3 is invalid. */
+static int64_t pack_byte(int64_t row, int64_t k, int64_t kdim) {
+  return row * (kdim / 4) + 4 * (k / 16) + (k % 16) % 4;
+}
+static int pack_shift(int64_t k) { return 2 * ((k % 16) / 4); }
+
+/* returns 0, or -1 when k is not a multiple of 16 or a code is outside {-1,0,1} */
+int orc_pack(const int8_t *c, int64_t n, int64_t k, uint8_t *p) {
+  if (k % 16 != 0) return -1;
+  memset(p, 0, (size_t)(n * (k / 4)));
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t j = 0; j < k; ++j) {
+      int v = c[r * k + j];
+      if (v < -1 || v > 1) return -1;
+      p[pack_byte(r, j, k)] |= (uint8_t)((v + 1) << pack_shift(j));
+    }
+  return 0;
+}
+
+/* decodes; returns the number of invalid fields (value 3), which decode as 0;
+ * -1 when k is not a multiple of 16 */
+int64_t orc_unpack(const uint8_t *p, int64_t n, int64_t k, int8_t *c) {
+  if (k % 16 != 0) return -1;
+  int64_t bad = 0;
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t j = 0; j < k; ++j) {
+      int u = (p[pack_byte(r, j, k)] >> pack_shift(j)) & 3;
+      if (u == 3) { ++bad; u = 1; }
+      c[r * k + j] = (int8_t)(u - 1);
+    }
+  return bad;
+}
+
+/* ---- codes of one row: round(v * 127 / max|v|) to 255 levels ---------------
+ * [nnterp] "The projections quantize their inputs and weights": each input is
+ * rounded per token to 255 levels as round(x * 127 / max|x|); [card] "Model
+ * Details": 8-bit absmax per token.
+ * R1: round half to even. R2: the scale s = 127 / a is one correctly rounded
+ * fp32 division per row, then one fp32 product per element, as written.
+ * Clamp to [-127, 127] (255 levels; it never binds, see the pins).
+ * R3: a == 0 gives all-zero codes. When a < 2^-64 the row is first scaled by
+ * 2^64 (exact), which keeps 127 / a finite and changes no code that the
+ * unscaled steps could compute. Returns a (unscaled). */
+static float codes_of_row(const float *v, int64_t k, int8_t *q) {
+  float a = 0.0f;
+  for (int64_t i = 0; i < k; ++i) {
+    float t = fabsf(v[i]);
+    if (t > a) a = t;
+  }
+  if (a == 0.0f) {
+    memset(q, 0, (size_t)k);
+    return a;
+  }
+  const int tiny = a < 0x1p-64f;
+  const float pre = tiny ? 0x1p64f : 1.0f;
+  const float s = 127.0f / (a * pre);
+  for (int64_t i = 0; i < k; ++i) {
+    float p = (v[i] * pre) * s;
+    float r = rintf(p);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    q[i] = (int8_t)r;
+  }
+  return a;
+}
+
+/* ---- O4: per-token absmax quantization ----------------------------------------
+ * codes as above; dequantization factor deq = a / 127 (fp32 division), 0 for
+ * an all-zero row. */
+void orc_quant_absmax(const float *x, int64_t m, int64_t k, int8_t *q, float *deq) {
+  for (int64_t r = 0; r < m; ++r) {
+    float a = codes_of_row(x + r * k, k, q + r * k);
+    deq[r] = a == 0.0f ? 0.0f : a / 127.0f;
+  }
+}
+
+/* ---- O5: RMSNorm followed by the per-token quantization -----------------------
+ * [nnterp] "The block, in order" and "Config": RMSNorms with eps 1e-5 sit
+ * before the projections (pre-norms, and attn_sub_norm / ffn_sub_norm right
+ * before o_proj / down_proj). R7: RMSNorm(x) = g * x / sqrt(mean(x^2) + eps).
+ * R8: "Scaling inside a sublayer is undone by the sub-norm": the positive
+ * per-token 1 / r cancels inside round(u * 127 / max|u|), so the codes are
+ * taken from v = g * x (fp32 product) and 1 / r goes into deq only:
+ *   ms  = (sum_k x_k^2) / K              fp64, sequential
+ *   r   = sqrt(ms + eps)                 fp64
+ *   deq = fl32((a_v / 127) / r)          fp64, rounded once
+ * gain == NULL means g = 1. */
+void orc_quant_rms(const float *x, int64_t m, int64_t k, const float *gain, float eps,
+                   int8_t *q, float *deq, float *scratch_v) {
+  for (int64_t r = 0; r < m; ++r) {
+    const float *xr = x + r * k;
+    double ss = 0.0;
+    for (int64_t i = 0; i < k; ++i) ss += (double)xr[i] * (double)xr[i];
+    const double ms = ss / (double)k;
+    const double rr = sqrt(ms + (double)eps);
+    for (int64_t i = 0; i < k; ++i) scratch_v[i] = gain ? gain[i] * xr[i] : xr[i];
+    float a = codes_of_row(scratch_v, k, q + r * k);
+    deq[r] = a == 0.0f ? 0.0f : (float)(((double)a / 127.0) / rr);
+  }
+}
+
+/* ---- O6: squared-ReLU gating ---------------------------------------------------
+ * [nnterp] "The block, in order": m = relu(gate)^2 * up; "The MLP gates with a
+ * squared ReLU": exactly zero where the gate is not positive.
+ * R9: left to right in fp32: t = max(G, 0); m = (t * t) * U.
+ * gu rows hold [gate (inter) | up (inter)]; out is [m][inter]. */
+void orc_relu2_mul(const float *gu, int64_t m, int64_t inter, float *out) {
+  for (int64_t r = 0; r < m; ++r)
+    for (int64_t i = 0; i < inter; ++i) {
+      float g = gu[r * 2 * inter + i], u = gu[r * 2 * inter + inter + i];
+      float t = g > 0.0f ? g : 0.0f;
+      float tt = t * t;
+      out[r * inter + i] = tt * u;
+    }
+}
+
+/* ---- O7: the ternary x int8 contraction ---------------------------------------
+ * [nnterp] "The projections quantize their inputs and weights": the projection
+ * multiplies the rounded input by the ternary weights, and its output equals
+ * the linear map of the rounded input by the ternarized weight.
+ * acc[r][n] = sum_k q[r][k] * c[n][k], exact in int64. R15: stored as int32;
+ * returns -1 if a sum does not fit (it cannot for |q| <= 127, K < 2^24). */
+int orc_contract(const int8_t *q, int64_t m, int64_t k, const int8_t *c, int64_t n, int32_t *acc) {
+  int rc = 0;
+  for (int64_t r = 0; r < m; ++r)
+    for (int64_t j = 0; j < n; ++j) {
+      int64_t s = 0;
+      const int8_t *qr = q + r * k, *cj = c + j * k;
+      for (int64_t i = 0; i < k; ++i) s += (int64_t)qr[i] * (int64_t)cj[i];
+      if (s > INT32_MAX || s < INT32_MIN) rc = -1;
+      acc[r * n + j] = (int32_t)s;
+    }
+  return rc;
+}
+
+/* ---- O8: rescale (no bias) ------------------------------------------------------
+ * [nnterp] "The two checkpoints": the packed checkpoint multiplies by its stored
+ * ternary weights and weight_scale; [card] "Model Details": no bias terms.
+ * R10: y = fl32(fl32((float)acc * deq) * gamma_f), gamma_f = fl32(gamma).
+ * R11: a fused projection (gate|up, q|k|v) is its matrices stacked along N with
+ * one gamma each: output column j uses gamma[s] for seg_end[s-1] <= j < seg_end[s]. */
+void orc_rescale(const int32_t *acc, int64_t m, int64_t n, const float *deq, const double *gamma,
+                 const int64_t *seg_end, int n_seg, float *y) {
+  for (int64_t r = 0; r < m; ++r) {
+    int s = 0;
+    for (int64_t j = 0; j < n; ++j) {
+      while (s < n_seg - 1 && j >= seg_end[s]) ++s;
+      const float g = (float)gamma[s];
+      const float t = (float)acc[r * n + j] * deq[r];
+      y[r * n + j] = t * g;
+    }
+  }
+}

@@ -1,0 +1,476 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage it checks. None of them re-types the oracle's own
+formula: they use hand-derived fixtures (tests/golden), exact rational
+arithmetic, closed forms, invariants, brute force on tiny inputs, library
+routines on special cases, and an independent fp64 formulation of the block
+written from the block equations.
+
+Pages: [card] = "BitNet b1.58 2B4T - Scaling Native 1-bit LLM" model card;
+[nnterp] = "nnterp encyclopedia: BitNet b1.58".
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_bitlinear_w1_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+F32_ULP = 2.0 ** -23
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ O1 / O2
+def test_golden_ternary_codes():
+    """[nnterp] "The projections quantize their inputs and weights"; [card] "Model Details"."""
+    for case in gold("ternary_codes.json")["cases"]:
+        w = np.array([case["w"]], dtype=np.float32)
+        g = oracle.absmean(w)
+        assert g == case["gamma"]
+        assert oracle.ternarize(w, g).tolist() == [case["codes"]]
+
+
+@pytest.mark.parametrize("a", [0.75, 0.02, 1e-3, 3.0])
+def test_P1_constant_magnitude_gives_exact_gamma(a):
+    """mean|W| of a matrix whose entries all have magnitude a is a, exactly."""
+    r = rng(1)
+    a32 = np.float32(a)
+    w = (np.where(r.random((37, 48)) < 0.5, -1, 1) * a32).astype(np.float32)
+    assert oracle.absmean(w) == float(a32)
+    c = oracle.ternarize(w, oracle.absmean(w))
+    assert np.array_equal(c, np.sign(w).astype(np.int8))
+
+
+def test_P1_grid_weights_exact_rational_mean():
+    """W on a 2^-10 grid: the fp64 sum is exact, so gamma is the correctly rounded
+    rational mean sum|W| / (N K)."""
+    r = rng(2)
+    wi = r.integers(-3000, 3001, size=(19, 33))
+    w = (wi / 1024.0).astype(np.float32)
+    exact = Fraction(int(np.abs(wi).sum()), 1024 * wi.size)
+    assert oracle.absmean(w) == float(exact)
+
+
+def test_P2_codes_match_exact_rational_threshold():
+    """Brute force: code = sign(W) * [ |W| > mean|W| / 2 ] in exact rationals
+    (round(W / gamma) clipped to [-1, 1], ties to even)."""
+    r = rng(3)
+    for trial in range(20):
+        n, k = r.integers(1, 9), r.integers(1, 17)
+        w = (r.standard_normal((n, k)) * r.choice([0.02, 1.0, 50.0])).astype(np.float32)
+        if trial % 4 == 0:  # quarter-grid values: exact ties with gamma / 2 become likely
+            w = (r.integers(-8, 9, size=(n, k)) / 4.0).astype(np.float32)
+        s = sum(Fraction(float(abs(v))) for v in w.ravel())
+        half = s / (2 * w.size)
+        want = np.array([[int(np.sign(v)) if Fraction(float(abs(v))) > half else 0 for v in row] for row in w])
+        got = oracle.ternarize(w, oracle.absmean(w))
+        assert set(np.unique(got)) <= {-1, 0, 1}
+        bad = np.argwhere(got != want)
+        for i, j in bad:  # only allowed within the fp64 rounding of gamma
+            dist = abs(Fraction(float(abs(w[i, j]))) - half)
+            assert dist <= half * Fraction(1, 2 ** 50), (trial, i, j)
+
+
+def test_P2_tie_rounds_to_zero():
+    """A weight exactly at gamma / 2 is a half-way case of round(W / gamma): it goes to 0."""
+    w = np.array([[0.625, -0.625, 3.75, 0.0]], dtype=np.float32)  # sum 5, mean 1.25, half 0.625
+    assert oracle.absmean(w) == 1.25
+    assert oracle.ternarize(w, 1.25).tolist() == [[0, 0, 1, 0]]
+    # one float step above the tie becomes +-1
+    up = np.nextafter(np.float32(0.625), np.float32(1))
+    assert oracle.ternarize(np.array([[up, -up]], dtype=np.float32), 1.25).tolist() == [[1, -1]]
+
+
+def test_P3_small_weight_edit_is_reternarized_away():
+    """[nnterp] "The projections quantize their inputs and weights": adding 0.1 * mean|W|
+    to one weight leaves the ternarized weight unchanged (when that weight is not
+    within 0.2 * mean|W| of the threshold)."""
+    w = synth.weights(synth.stream_seed(7, tensor=synth.T_WEIGHT), 64, 256)
+    g = oracle.absmean(w)
+    c = oracle.ternarize(w, g)
+    r = rng(4)
+    checked = 0
+    for idx in r.permutation(w.size)[:400]:
+        i, j = divmod(int(idx), 256)
+        v = float(w[i, j])
+        if abs(abs(v) - g / 2) < 0.2 * g or abs(abs(v + 0.1 * g) - g / 2) < 0.1 * g:
+            continue
+        w2 = w.copy()
+        w2[i, j] = np.float32(v + 0.1 * g)
+        c2 = oracle.ternarize(w2, oracle.absmean(w2))
+        assert np.array_equal(c, c2)
+        checked += 1
+    assert checked > 100
+
+
+# ------------------------------------------------------------------ O3
+def test_golden_pack_layout():
+    """Four to a byte ([nnterp] "The two checkpoints"); bytes derived by hand from the layout rule."""
+    for case in gold("pack_layout.json")["cases"]:
+        c = np.array([case["codes"]], dtype=np.int8)
+        p = oracle.pack(c)
+        assert p.shape == (1, c.shape[1] // 4)
+        assert p.ravel().tolist() == case["bytes"]
+        back, bad = oracle.unpack(p, c.shape[1])
+        assert bad == 0 and np.array_equal(back, c)
+
+
+def test_P4_roundtrip_every_dword_pattern():
+    """unpack(pack(c)) == c over all 3^16 patterns of one 16-code group, and
+    pack(unpack(p)) == p for every valid packed dword (pack is a bijection)."""
+    n = 3 ** 16
+    idx = np.arange(n, dtype=np.int64)
+    c = np.empty((n, 16), dtype=np.int8)
+    for d in range(16):
+        c[:, d] = (idx // (3 ** d)) % 3 - 1
+    del idx
+    p = oracle.pack(c)
+    back, bad = oracle.unpack(p, 16)
+    assert bad == 0
+    assert np.array_equal(back, c)
+    del back, c
+    words = p.view(np.uint32).ravel()
+    assert np.unique(words).size == n  # distinct codes give distinct words
+    p2 = oracle.pack(oracle.unpack(p, 16)[0])
+    assert np.array_equal(p2, p)
+
+
+def test_P4_invalid_field_detected():
+    """Field value 3 is not a ternary code: unpack counts it."""
+    r = rng(5)
+    p = r.integers(0, 256, size=(8, 16), dtype=np.uint8)
+    fields = np.stack([(p >> s) & 3 for s in (0, 2, 4, 6)])
+    _, bad = oracle.unpack(p, 64)
+    assert bad == int((fields == 3).sum()) and bad > 0
+
+
+# ------------------------------------------------------------------ O4
+def test_golden_act_codes():
+    """[nnterp] "The projections quantize their inputs and weights": round(x * 127 / max|x|)."""
+    for case in gold("act_codes.json")["cases"]:
+        x = np.array([case["x"]], dtype=np.float32)
+        q, deq = oracle.quant_absmax(x)
+        assert q.tolist() == [case["codes"]]
+        assert deq[0] == np.float32(float(Fraction(case["deq_num"], case["deq_den"])))
+
+
+def _round_half_even(fr: Fraction) -> int:
+    fl = math.floor(fr)
+    d = fr - fl
+    if d > Fraction(1, 2):
+        return fl + 1
+    if d < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def test_P5_codes_against_exact_rationals():
+    """q = round_half_even(x * 127 / a) exactly, except where x * 127 / a lies within
+    the fp32 rounding of the scale and product (2^-22 relative) of a half-integer;
+    there q is one of the two neighbours. Also |q| <= 127, max|q| = 127, q(-x) = -q(x)."""
+    r = rng(6)
+    x = synth.activations(synth.stream_seed(8, tensor=synth.T_ACT), 48, 64, n_outliers=2)
+    x[3] = 0.0
+    x[5, :] = (r.integers(-40, 41, size=64) / 8.0).astype(np.float32)  # grid values: many exact ties
+    q, deq = oracle.quant_absmax(x)
+    qn, deqn = oracle.quant_absmax(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(deqn, deq)
+    assert np.abs(q.astype(int)).max() <= 127
+    near = 0
+    for i in range(x.shape[0]):
+        a = Fraction(float(np.abs(x[i]).max()))
+        if a == 0:
+            assert not q[i].any() and deq[i] == 0
+            continue
+        assert np.abs(q[i].astype(int)).max() == 127
+        assert deq[i] == np.float32(float(a / 127))
+        for j in range(x.shape[1]):
+            t = Fraction(float(x[i, j])) * 127 / a
+            want = _round_half_even(t)
+            if int(q[i, j]) != want:
+                frac = abs(t - math.floor(t) - Fraction(1, 2))
+                assert frac <= abs(t) * Fraction(1, 2 ** 22) and abs(int(q[i, j]) - t) < 1, (i, j)
+                near += 1
+    assert near <= 4
+
+
+def test_P5_tiny_amax_rows():
+    """Rows whose max|x| is tiny (down to subnormals, where 127 / a overflows fp32) are
+    quantized like the same row scaled by a power of two: codes are scale invariant
+    (the per-token scale cancels), deq = a / 127 rounded to fp32."""
+    base = synth.activations(synth.stream_seed(9, tensor=synth.T_ACT), 6, 32)
+    for e in (-100, -120, -126, -130, -140):
+        x = (base.astype(np.float64) * 2.0 ** e).astype(np.float32)
+        # keep rows exactly representable: compare against the same fp32 values scaled up
+        up = (x.astype(np.float64) * 2.0 ** (-e)).astype(np.float32)
+        assert np.array_equal((up.astype(np.float64) * 2.0 ** e).astype(np.float32), x)
+        q, deq = oracle.quant_absmax(x)
+        qu, _ = oracle.quant_absmax(up)
+        assert np.array_equal(q, qu), e
+        a = np.abs(x).max(axis=1).astype(np.float64)
+        want = np.array([float(Fraction(float(v)) / 127) for v in a]).astype(np.float32)
+        assert np.array_equal(deq, want)
+
+
+@pytest.mark.parametrize("j", [-20, -3, 1, 7, 30])
+def test_P6_power_of_two_scaling(j):
+    """[nnterp] "Scaling inside a sublayer is undone by the sub-norm": x -> 2^j x leaves the
+    codes identical and scales deq by exactly 2^j."""
+    x = synth.activations(synth.stream_seed(10, tensor=synth.T_ACT), 16, 96, n_outliers=1)
+    q, deq = oracle.quant_absmax(x)
+    xs = (x * np.float32(2.0 ** j)).astype(np.float32)
+    q2, deq2 = oracle.quant_absmax(xs)
+    assert np.array_equal(q, q2)
+    assert np.array_equal(deq2, (deq * np.float32(2.0 ** j)).astype(np.float32))
+
+
+# ------------------------------------------------------------------ O5
+def _exact_rms_deq(a, xs, eps32, gain=None):
+    getcontext().prec = 60
+    k = len(xs)
+    ms = sum(Decimal(float(v)) ** 2 for v in xs) / k
+    r = (ms + Decimal(float(eps32))).sqrt()
+    return float(Decimal(float(a)) / 127 / r)
+
+
+@pytest.mark.parametrize("c", [2.0, -0.37, 1e-3, 150.0])
+def test_P7_constant_row_closed_form(c):
+    """RMSNorm(x) = g x / sqrt(mean(x^2) + eps) with eps 1e-5 ([nnterp] "Config",
+    "The block, in order"). A constant row c quantizes to +-127 everywhere and
+    deq = |c| / 127 / sqrt(c^2 + eps)."""
+    k = 64
+    x = np.full((1, k), c, dtype=np.float32)
+    q, deq = oracle.quant_rms(x, None, 1e-5)
+    assert np.all(q == (127 if c > 0 else -127))
+    want = _exact_rms_deq(abs(np.float32(c)), x[0], np.float32(1e-5))
+    assert abs(float(deq[0]) - want) <= 0.5 * F32_ULP * abs(want) * 1.0001
+
+
+def test_P7_random_rows_closed_form_and_doubling():
+    """deq of random rows against a 60-digit evaluation of |max g x| / 127 / sqrt(ms + eps);
+    doubling x keeps the codes and changes deq by 2 sqrt(ms + eps) / sqrt(4 ms + eps)."""
+    x = synth.activations(synth.stream_seed(11, tensor=synth.T_ACT), 12, 160, n_outliers=2)
+    gain = (1.0 + 0.1 * synth.normal_f32(synth.stream_seed(11, tensor=synth.T_GAIN), 160)).astype(np.float32)
+    for g in (None, gain):
+        q, deq = oracle.quant_rms(x, g, 1e-5)
+        q2, deq2 = oracle.quant_rms((2 * x).astype(np.float32), g, 1e-5)
+        assert np.array_equal(q, q2)
+        v = x if g is None else (g * x).astype(np.float32)
+        q_abs, _ = oracle.quant_absmax(v)
+        assert np.array_equal(q, q_abs)  # the codes are those of g * x: 1/r cancels
+        for i in range(x.shape[0]):
+            want = _exact_rms_deq(np.abs(v[i]).max(), x[i], np.float32(1e-5))
+            assert abs(float(deq[i]) - want) <= 0.5 * F32_ULP * want * 1.0001
+            want2 = _exact_rms_deq(np.abs(2 * v[i]).max(), 2 * x[i], np.float32(1e-5))
+            assert abs(float(deq2[i]) - want2) <= 0.5 * F32_ULP * want2 * 1.0001
+
+
+def test_P7_matches_literal_normalize_then_round():
+    """The scale-invariant codes equal the literal order (normalize in fp64, then
+    round(n * 127 / max|n|)) except at near-ties of the fp32 order."""
+    x = synth.activations(synth.stream_seed(12, tensor=synth.T_ACT), 64, 256, n_outliers=3)
+    q, _ = oracle.quant_rms(x, None, 1e-5)
+    x64 = x.astype(np.float64)
+    r = np.sqrt((x64 ** 2).mean(axis=1, keepdims=True) + float(np.float32(1e-5)))
+    n = x64 / r
+    t = n * 127.0 / np.abs(n).max(axis=1, keepdims=True)
+    lit = np.rint(t)
+    diff = lit != q
+    assert diff.sum() <= 4
+    assert np.all(np.abs(np.abs(t[diff] - np.floor(t[diff])) - 0.5) < 1e-4)
+
+
+# ------------------------------------------------------------------ O6
+def test_golden_relu2():
+    """[nnterp] "The MLP gates with a squared ReLU": relu(gate)^2 * up, zero where gate <= 0."""
+    cases = gold("relu2.json")["cases"]
+    gu = np.array([[c["gate"] for c in cases] + [c["up"] for c in cases]], dtype=np.float32)
+    out = oracle.relu2_mul(gu, len(cases))
+    assert out.ravel().tolist() == [c["out"] for c in cases]
+
+
+def test_P8a_nonpositive_gate_gives_zero_code():
+    """Wherever the gate is <= 0 the product and its code are exactly 0."""
+    m, inter = 16, 192
+    g = synth.activations(synth.stream_seed(13, tensor=synth.T_ACT), m, inter)
+    u = synth.activations(synth.stream_seed(13, tensor=synth.T_ACT2), m, inter)
+    g[0, :5] = -0.0
+    mi = oracle.relu2_mul(np.concatenate([g, u], axis=1), inter)
+    assert np.all(mi[g <= 0] == 0)
+    assert np.all(mi[g > 0] != 0)
+    q, _ = oracle.quant_rms(mi, None, 1e-5)
+    assert np.all(q[g <= 0] == 0)
+    assert 0.4 < (g <= 0).mean() < 0.6
+
+
+# ------------------------------------------------------------------ O7
+def test_P9_brute_force_every_ternary_row():
+    """Every ternary row of length <= 6 against random int8 codes, compared with an
+    int64 matrix product (a library routine)."""
+    r = rng(14)
+    for k in range(1, 7):
+        rows = np.array(np.meshgrid(*[[-1, 0, 1]] * k, indexing="ij")).reshape(k, -1).T.astype(np.int8)
+        q = r.integers(-127, 128, size=(5, k), dtype=np.int8)
+        acc = oracle.contract(q, rows)
+        assert np.array_equal(acc, q.astype(np.int64) @ rows.astype(np.int64).T)
+
+
+def test_P9_closed_forms():
+    """all q = 127, c = +1 -> 127 K; alternating +-1 against constant q -> 0;
+    one-hot rows copy columns of q; K = 6912 bound fits int32."""
+    k = 6912
+    q = np.full((2, k), 127, dtype=np.int8)
+    c = np.ones((3, k), dtype=np.int8)
+    c[1, 1::2] = -1
+    c[2] = -1
+    acc = oracle.contract(q, c)
+    assert acc[:, 0].tolist() == [127 * k] * 2 and acc[:, 1].tolist() == [0, 0] and acc[:, 2].tolist() == [-127 * k] * 2
+    r = rng(15)
+    q = r.integers(-127, 128, size=(7, 48), dtype=np.int8)
+    sel = r.permutation(48)[:10]
+    onehot = np.zeros((10, 48), dtype=np.int8)
+    onehot[np.arange(10), sel] = 1
+    assert np.array_equal(oracle.contract(q, onehot), q[:, sel].astype(np.int32))
+    assert np.array_equal(oracle.contract(q, -onehot), -q[:, sel].astype(np.int32))
+
+
+# ------------------------------------------------------------------ O8
+def test_P10_rescale_equals_dequantized_linear_map():
+    """[nnterp] "The projections quantize their inputs and weights": the output equals
+    the linear map of the rounded input by the ternarized weight. In fp64,
+    y64 = (q * deq) @ (c * gamma)^T; the fp32 result is within 3 * 2^-24 |y| of it."""
+    x = synth.activations(synth.stream_seed(16, tensor=synth.T_ACT), 32, 256, n_outliers=3)
+    w = synth.weights(synth.stream_seed(16, tensor=synth.T_WEIGHT), 96, 256)
+    wu = synth.weights(synth.stream_seed(17, tensor=synth.T_WEIGHT), 80, 256, sigma=0.05)
+    g1, g2 = oracle.absmean(w), oracle.absmean(wu)
+    c = np.concatenate([oracle.ternarize(w, g1), oracle.ternarize(wu, g2)])
+    out = oracle.forward(x, c, [g1, g2], [96, 176])
+    q, deq = out["q"], out["deq"]
+    gam = np.concatenate([np.full(96, float(np.float32(g1))), np.full(80, float(np.float32(g2)))])
+    y64 = (q.astype(np.float64) * deq.astype(np.float64)[:, None]) @ (c.astype(np.float64) * gam[:, None]).T
+    y = out["y"].astype(np.float64)
+    # the fp64 evaluation of y64 has its own error, at most ~K 2^-53 sum|terms|
+    mag = (np.abs(q).astype(np.float64) * deq.astype(np.float64)[:, None]) @ (np.abs(c).astype(np.float64) * gam[:, None]).T
+    assert np.all(np.abs(y - y64) <= 3 * 2.0 ** -24 * np.abs(y64) + 2 * x.shape[1] * 2.0 ** -53 * mag)
+    assert np.all((y == 0) == (out["acc"] == 0))
+    # fused == unfused, bit for bit
+    a = oracle.forward(x, c[:96], [g1])["y"]
+    b = oracle.forward(x, c[96:], [g2])["y"]
+    assert np.array_equal(out["y"], np.concatenate([a, b], axis=1))
+
+
+# ------------------------------------------------------------------ O9 / O10
+def _literal_quant(v):
+    """round(v * 127 / max|v|) in fp64 and its dequantized value (pages' formula)."""
+    a = np.abs(v).max(axis=1, keepdims=True)
+    a = np.where(a == 0, 1.0, a)
+    q = np.clip(np.rint(v * 127.0 / a), -127, 127)
+    return q * a / 127.0
+
+
+def _literal_rms(v, eps):
+    return v / np.sqrt((v ** 2).mean(axis=1, keepdims=True) + eps)
+
+
+def _literal_linear(v, c, gam):
+    return _literal_quant(v) @ (c.astype(np.float64) * gam[:, None]).T
+
+
+def test_ffn_block_against_literal_fp64_formulation():
+    """O9 against the block written straight from [nnterp] "The block, in order" in
+    fp64 (normalize, round, dequantize, matmul): equal up to fp32 rounding."""
+    m, hdim, inter = 24, 64, 96
+    x = synth.activations(synth.stream_seed(18, tensor=synth.T_ACT), m, hdim)
+    wg = synth.weights(synth.stream_seed(18, 0, 1, synth.T_WEIGHT), inter, hdim)
+    wu = synth.weights(synth.stream_seed(18, 0, 2, synth.T_WEIGHT), inter, hdim)
+    wd = synth.weights(synth.stream_seed(18, 0, 3, synth.T_WEIGHT), hdim, inter)
+    gg, gu_, gd = oracle.absmean(wg), oracle.absmean(wu), oracle.absmean(wd)
+    cg, cu, cd = oracle.ternarize(wg, gg), oracle.ternarize(wu, gu_), oracle.ternarize(wd, gd)
+    out = oracle.ffn_block(x, np.concatenate([cg, cu]), [gg, gu_], cd, gd, None, 1e-5)
+    eps = float(np.float32(1e-5))
+    x64 = x.astype(np.float64)
+    G = _literal_linear(x64, cg, np.full(inter, gg))
+    U = _literal_linear(x64, cu, np.full(inter, gu_))
+    Mi = np.maximum(G, 0) ** 2 * U
+    Y = _literal_linear(_literal_rms(Mi, eps), cd, np.full(hdim, gd))
+    scale = np.abs(Y).max()
+    assert np.abs(out["y"] - Y).max() <= 1e-4 * scale
+    assert np.array_equal(out["gu"][:, :inter] <= 0, G <= 0) or np.mean((out["gu"][:, :inter] <= 0) != (G <= 0)) < 1e-3
+
+
+def _small_decoder_weights(seed, hdim, inter, nh, nkv, hd, zero=()):
+    kvd = nkv * hd
+    shapes = {"q": (hdim, hdim), "k": (kvd, hdim), "v": (kvd, hdim), "o": (hdim, hdim),
+              "gate": (inter, hdim), "up": (inter, hdim), "down": (hdim, inter)}
+    codes, gam = {}, {}
+    for i, (name, (n, k)) in enumerate(shapes.items()):
+        w = synth.weights(synth.stream_seed(seed, 5, i, synth.T_WEIGHT), n, k)
+        if name in zero:
+            w[:] = 0
+        gam[name] = oracle.absmean(w)
+        codes[name] = oracle.ternarize(w, gam[name])
+    return {"qkv": np.concatenate([codes["q"], codes["k"], codes["v"]]), "g_qkv": [gam["q"], gam["k"], gam["v"]],
+            "o": codes["o"], "g_o": gam["o"], "gu": np.concatenate([codes["gate"], codes["up"]]),
+            "g_gu": [gam["gate"], gam["up"]], "down": codes["down"], "g_down": gam["down"]}, codes, gam
+
+
+def test_decoder_layer_against_literal_fp64_formulation():
+    """O10 against [nnterp] "The block, in order" written out in fp64: pre-norm, q/k/v,
+    self-only attention (query head h reads key/value head h // 4, section "Loading"),
+    attn_sub_norm, o, residual, pre-norm, gate/up, relu^2, ffn_sub_norm, down, residual."""
+    hdim, inter, nh, nkv, hd, m = 64, 96, 8, 2, 8, 6
+    w, codes, gam = _small_decoder_weights(19, hdim, inter, nh, nkv, hd)
+    x = synth.activations(synth.stream_seed(19, tensor=synth.T_ACT), m, hdim)
+    out = oracle.decoder_layer(x, w, 1e-5, nh, nkv, hd)
+    eps = float(np.float32(1e-5))
+    lin = lambda v, name: _literal_linear(v, codes[name], np.full(codes[name].shape[0], gam[name]))
+    x64 = x.astype(np.float64)
+    z = _literal_rms(x64, eps)
+    V = lin(z, "v")
+    A = np.concatenate([V[:, (h // (nh // nkv)) * hd:(h // (nh // nkv) + 1) * hd] for h in range(nh)], axis=1)
+    H = x64 + lin(_literal_rms(A, eps), "o")
+    z2 = _literal_rms(H, eps)
+    Mi = np.maximum(lin(z2, "gate"), 0) ** 2 * lin(z2, "up")
+    X1 = H + lin(_literal_rms(Mi, eps), "down")
+    assert np.abs(out["h"] - H).max() <= 1e-4 * np.abs(H).max()
+    assert np.abs(out["x"] - X1).max() <= 1e-4 * np.abs(X1).max()
+
+
+def test_P11_P12_residual_wiring_and_head_map():
+    """[nnterp] identity layer_input + attention_output + mlp_output == layer_output,
+    and "an edit to key/value head j reaches query heads 4j to 4j + 3"."""
+    hdim, inter, nh, nkv, hd, m = 64, 96, 8, 2, 8, 4
+    x = synth.activations(synth.stream_seed(20, tensor=synth.T_ACT), m, hdim)
+    w0, _, _ = _small_decoder_weights(20, hdim, inter, nh, nkv, hd, zero=("o", "down"))
+    out = oracle.decoder_layer(x, w0, 1e-5, nh, nkv, hd)
+    assert np.array_equal(out["h"], x) and np.array_equal(out["x"], x)
+    w1, _, _ = _small_decoder_weights(20, hdim, inter, nh, nkv, hd, zero=("v",))
+    out1 = oracle.decoder_layer(x, w1, 1e-5, nh, nkv, hd)
+    assert np.array_equal(out1["h"], x)  # zero values -> zero attention -> zero o_proj output
+    w2, _, _ = _small_decoder_weights(20, hdim, inter, nh, nkv, hd)
+    out2 = oracle.decoder_layer(x, w2, 1e-5, nh, nkv, hd)
+    h = (x + out2["o"]["y"]).astype(np.float32)
+    assert np.array_equal(out2["x"], (h + out2["down"]["y"]).astype(np.float32))
+    # head map: an edit of key/value head j changes exactly query heads 4j .. 4j+3
+    v = np.arange(m * nkv * hd, dtype=np.float32).reshape(m, nkv * hd)
+    a = oracle.gqa_broadcast(v, nh, nkv, hd)
+    for j in range(nkv):
+        v2 = v.copy()
+        v2[:, j * hd:(j + 1) * hd] += 1000
+        changed = np.any(oracle.gqa_broadcast(v2, nh, nkv, hd) != a, axis=0).reshape(nh, hd).any(axis=1)
+        grp = nh // nkv
+        assert changed.tolist() == [grp * j <= hh < grp * (j + 1) for hh in range(nh)]
