@@ -1,0 +1,240 @@
+/* bitlinear.h — C ABI of the BitNet b1.58 BitLinear hot path for AMD gfx950 (MI355X).
+ *
+ * The operation (sources: the "BitNet b1.58 2B4T" model card, section "Model
+ * Details"; the nnterp encyclopedia page "BitNet b1.58", sections "The
+ * projections quantize their inputs and weights", "The two checkpoints", "The
+ * block, in order", "The MLP gates with a squared ReLU", "Scaling inside a
+ * sublayer is undone by the sub-norm"):
+ *
+ *   weights  W [n][k] fp32 -> gamma = mean|W|, codes c = round(W / gamma) in {-1,0,1},
+ *            stored four to a byte;
+ *   inputs   x [m][k] fp32 -> per token: a = max|x|, codes q = round(x * 127 / a)
+ *            in [-127, 127], deq = a / 127;
+ *   output   y [m][n] = (sum_k q[m][k] * c[n][k]) * deq[m] * gamma, no bias.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers (memory of the current HIP device),
+ *    row-major, owned by the caller. The library never allocates, frees or
+ *    keeps tensors; scratch memory comes from a caller `workspace` whose size
+ *    the *_workspace_bytes functions give.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued on it and the call returns without synchronizing; device-side
+ *    faults surface at the caller's next synchronization.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns a status and enqueues nothing. bitlinear_last_error() then
+ *    gives a one-line reason (per thread).
+ *  - Inputs must be finite; NaN and Inf are outside the contract.
+ *  - The library is stateless between calls and reentrant on distinct buffers.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BITLINEAR_OK = 0,
+  BITLINEAR_ERR_NULL = 1,      /* a required pointer is NULL */
+  BITLINEAR_ERR_SHAPE = 2,     /* a size is negative, k % 16 != 0, bad segments, ... */
+  BITLINEAR_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  BITLINEAR_ERR_WORKSPACE = 4, /* workspace NULL or smaller than required */
+  BITLINEAR_ERR_DEVICE = 5,    /* no gfx950 device current, or a HIP launch failed */
+  BITLINEAR_ERR_ARG = 6        /* an enum or flag argument is out of range */
+} bitlinear_status;
+
+#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_MAX_SEGMENTS 4
+
+/* ---------------------------------------------------------------------------
+ * Packed weight layout ("four to a byte": the nnterp page, sections "The
+ * projections quantize their inputs and weights" and "The two checkpoints").
+ * The pages fix only the density; the layout is this library's own:
+ * row r of k codes occupies bytes [r * k/4, (r+1) * k/4). Code j of the row is
+ * stored as u = c + 1 (0, 1, 2; 3 is invalid) in byte 4*(j/16) + (j%16)%4 of
+ * the row, at bits 2*((j%16)/4) .. +1. Read as little-endian 32-bit words, word
+ * g holds codes 16g .. 16g+15 and (word >> 2t) & 0x03030303 gives codes
+ * 16g+4t .. 16g+4t+3 as bytes. k must be a multiple of 16.
+ * ------------------------------------------------------------------------- */
+
+/* bitlinear_quantize_weights — absmean ternarization and packing (offline
+ * checkpoint mode: "The two checkpoints"; absmean: "Model Details").
+ *   w          [n][k] fp32 master weights.
+ *   gamma_in   NULL, or a device pointer to one double: use this gamma and skip
+ *              the mean (e.g. a stored weight_scale).
+ *   w_packed   [n][k/4] bytes, layout above, 16-byte aligned.
+ *   gamma_out  device pointer to one double: the gamma used, mean|W| computed
+ *              in fp64 by a fixed-order (deterministic) reduction unless
+ *              gamma_in was given.
+ *   Codes: c = sign(W) where |W| > gamma/2 (compared exactly in fp64), else 0;
+ *   a tie |W| == gamma/2 gives 0 (round half to even).
+ *   workspace  >= bitlinear_quantize_weights_workspace_bytes(n, k) bytes.
+ * Errors: NULL w/w_packed/gamma_out/workspace -> ERR_NULL; n < 0, k <= 0 or
+ * k % 16 != 0 -> ERR_SHAPE; misaligned w or w_packed -> ERR_ALIGN. n == 0 is a
+ * no-op that still writes gamma_out (0). */
+bitlinear_status bitlinear_quantize_weights(const float *w, int64_t n, int64_t k, const double *gamma_in,
+                                            uint8_t *w_packed, double *gamma_out, void *workspace,
+                                            size_t workspace_bytes, void *stream);
+size_t bitlinear_quantize_weights_workspace_bytes(int64_t n, int64_t k);
+
+/* bitlinear_validate_packed — counts fields equal to 3 (not a ternary code).
+ *   n_bad  device pointer to one int64, overwritten with the count. */
+bitlinear_status bitlinear_validate_packed(const uint8_t *w_packed, int64_t n, int64_t k, int64_t *n_bad,
+                                           void *stream);
+
+/* Prologue of the per-token activation quantization. */
+typedef enum {
+  /* q = round(x * 127 / max|x|), deq = max|x| / 127 ("The projections quantize
+     their inputs and weights"). x is [m][k]. */
+  BITLINEAR_ACT_ABSMAX = 0,
+  /* RMSNorm (gain g, eps) then the same rounding ("The block, in order": the
+     pre-norms and attn_sub_norm / ffn_sub_norm; eps 1e-5 in "Config"). Because
+     a positive per-token factor cancels inside the rounding ("Scaling inside a
+     sublayer is undone by the sub-norm"), the codes are those of v = g*x and
+     deq = (max|v| / 127) / sqrt(mean(x^2) + eps), mean taken in fp64. */
+  BITLINEAR_ACT_RMSNORM = 1,
+  /* ReLU^2 gating then RMSNorm ("The MLP gates with a squared ReLU"): x is
+     [m][2k], each row [gate (k) | up (k)]; the normed tensor is
+     (max(gate, 0) * max(gate, 0)) * up in fp32, left to right. */
+  BITLINEAR_ACT_RELU2_RMSNORM = 2
+} bitlinear_act_mode;
+
+/* bitlinear_quantize_acts — per-token int8 quantization of an fp32 activation.
+ *   x          [m][k] fp32 ([m][2k] for RELU2_RMSNORM), 16-byte aligned.
+ *   mode       bitlinear_act_mode.
+ *   norm_gain  NULL (gain 1) or [k] fp32; used by the RMSNORM modes.
+ *   eps        RMSNorm epsilon (RMSNORM modes).
+ *   codes      [m][k] int8, 16-byte aligned.
+ *   deq        [m] fp32.
+ *   code_rowsum NULL or [m] int32: sum_k codes[m][k].
+ * Rounding is half to even; an all-zero token gives codes 0 and deq 0.
+ * Errors: NULL x/codes/deq -> ERR_NULL; m < 0, k <= 0, k % 16 != 0 -> ERR_SHAPE;
+ * bad mode -> ERR_ARG. m == 0 is a no-op. */
+bitlinear_status bitlinear_quantize_acts(const float *x, int64_t m, int64_t k, int32_t mode,
+                                         const float *norm_gain, float eps, int8_t *codes, float *deq,
+                                         int32_t *code_rowsum, void *stream);
+
+/* Kernel choice for bitlinear_forward. AUTO takes DECODE for m <= 16. */
+typedef enum {
+  BITLINEAR_PATH_AUTO = 0,
+  BITLINEAR_PATH_DECODE = 1,  /* weight-streaming GEMV, m <= 16 only */
+  BITLINEAR_PATH_PREFILL = 2  /* LDS-tiled int8 MFMA GEMM, any m */
+} bitlinear_path;
+
+/* bitlinear_forward — one BitLinear projection (AutoBitLinear's forward: "The
+ * projections quantize their inputs and weights"; packed checkpoint: "The two
+ * checkpoints"; no bias: "Model Details").
+ *   x          [m][k] fp32, quantized inside (ACT_ABSMAX); or NULL, and then
+ *   codes_in   [m][k] int8 and deq_in [m] fp32 are used as given, with
+ *   rowsum_in  NULL or [m] int32 = sum_k codes_in (computed when NULL).
+ *   w_packed   [n][k/4] packed codes (layout above).
+ *   gamma      HOST array of n_seg fp32 weight scales; seg_end HOST array of
+ *              n_seg ascending int64 ends, seg_end[n_seg-1] == n. Output column
+ *              j uses gamma[s] for seg_end[s-1] <= j < seg_end[s]: a fused
+ *              projection (q|k|v, gate|up) is its matrices stacked along n with
+ *              one gamma each. 1 <= n_seg <= BITLINEAR_MAX_SEGMENTS.
+ *   y          [m][n] fp32: y = fl32(fl32((float)acc * deq[m]) * gamma_seg),
+ *              acc = sum_k q[m][k] * c[n][k] computed exactly in int32.
+ *   acc_out    NULL or [m][n] int32: acc.
+ *   path       bitlinear_path.
+ *   workspace  >= bitlinear_forward_workspace_bytes(m, n, k, x != NULL) bytes
+ *              (may be NULL when that is 0).
+ * Errors: NULL w_packed/y/gamma/seg_end, or x and codes_in/deq_in both missing
+ * -> ERR_NULL; m < 0, n <= 0, k <= 0, k % 16 != 0, bad segments, DECODE with
+ * m > 16 -> ERR_SHAPE; misaligned tensors -> ERR_ALIGN; small workspace ->
+ * ERR_WORKSPACE; bad path -> ERR_ARG. m == 0 is a no-op. */
+bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const float *deq_in,
+                                   const int32_t *rowsum_in, int64_t m, int64_t k, const uint8_t *w_packed,
+                                   int64_t n, const float *gamma, const int64_t *seg_end, int32_t n_seg,
+                                   float *y, int32_t *acc_out, int32_t path, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside);
+
+/* ---------------------------------------------------------------------------
+ * Block-level chains ("The block, in order").
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  /* The MLP alone: q1 = ACT_ABSMAX(x); [gate|up] = forward; ReLU^2 + ffn_sub_norm
+     (ACT_RELU2_RMSNORM); y = down. No pre-norm and no residual. */
+  BITLINEAR_BLOCK_FFN = 0,
+  /* The projection stack of n_layers decoder blocks. Per layer:
+       x -> input_layernorm -> q|k|v -> attention -> attn_sub_norm -> o_proj,
+       h = x + o;  h -> post_attention_layernorm -> gate|up -> ReLU^2 ->
+       ffn_sub_norm -> down;  x' = h + down.
+     The attention is taken for a token that attends only to itself (a
+     one-token sequence at position 0): the output of query head i is the
+     value of key/value head i / (n_heads / n_kv_heads) ("Loading": 20 query
+     heads share 5 key/value heads). q and k are computed but not consumed. */
+  BITLINEAR_BLOCK_DECODER = 1
+} bitlinear_block_kind;
+
+typedef struct {
+  const uint8_t *qkv;        /* DECODER: packed [(H + 2*KV)][H/4]: q rows, k rows, v rows */
+  float qkv_gamma[3];
+  const uint8_t *o;          /* DECODER: packed [H][H/4] */
+  float o_gamma;
+  const uint8_t *gate_up;    /* packed [2I][H/4]: gate rows then up rows */
+  float gate_up_gamma[2];
+  const uint8_t *down;       /* packed [H][I/4] */
+  float down_gamma;
+  const float *input_norm_gain;     /* DECODER: [H] or NULL (gain 1) */
+  const float *attn_sub_norm_gain;  /* DECODER: [H] or NULL */
+  const float *post_attn_norm_gain; /* DECODER: [H] or NULL */
+  const float *ffn_sub_norm_gain;   /* [I] or NULL */
+} bitlinear_layer;
+
+typedef struct {
+  int32_t kind;          /* bitlinear_block_kind */
+  int32_t n_layers;      /* FFN: 1 */
+  int64_t hidden;        /* H (multiple of 16) */
+  int64_t intermediate;  /* I (multiple of 16) */
+  int32_t n_heads, n_kv_heads, head_dim; /* DECODER: H == n_heads * head_dim, KV = n_kv_heads * head_dim */
+  float eps;             /* RMSNorm epsilon */
+  const bitlinear_layer *layers; /* HOST array of n_layers (device pointers inside) */
+} bitlinear_block;
+
+/* Optional per-stage outputs for checking a chain stage by stage. Every pointer
+ * may be NULL. Layer l writes at element offset l * m * width. Widths: H, KV,
+ * I as in bitlinear_block; Q = H + 2*KV. FFN blocks use codes_in, gate_up,
+ * codes_ffn, deq (and acc_gate_up, acc_down). */
+typedef struct {
+  int8_t *codes_in;     /* [L][m][H]  codes of the block input (after input_layernorm) */
+  int8_t *codes_attn;   /* [L][m][H]  codes after attn_sub_norm */
+  int8_t *codes_post;   /* [L][m][H]  codes after post_attention_layernorm */
+  int8_t *codes_ffn;    /* [L][m][I]  codes after ReLU^2 and ffn_sub_norm */
+  float *deq;           /* [L][4][m]  deq of the four stages above, in that order */
+  float *qkv;           /* [L][m][Q] */
+  float *h;             /* [L][m][H]  residual after the attention add */
+  float *gate_up;       /* [L][m][2I] */
+  float *x_out;         /* [L][m][H]  layer outputs */
+  int32_t *acc_qkv;     /* [L][m][Q] */
+  int32_t *acc_o;       /* [L][m][H] */
+  int32_t *acc_gate_up; /* [L][m][2I] */
+  int32_t *acc_down;    /* [L][m][H] */
+} bitlinear_block_trace;
+
+/* bitlinear_block_forward — run a block chain on x [m][H] fp32 into y [m][H].
+ *   trace      NULL or per-stage outputs (above).
+ *   workspace  >= bitlinear_block_workspace_bytes(blk, m) bytes.
+ * Errors as bitlinear_forward, plus ERR_SHAPE for inconsistent head counts and
+ * ERR_ARG for an unknown kind. */
+bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float *x, int64_t m, float *y,
+                                         const bitlinear_block_trace *trace, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+size_t bitlinear_block_workspace_bytes(const bitlinear_block *blk, int64_t m);
+
+/* ---------------------------------------------------------------------------
+ * Misc.
+ * ------------------------------------------------------------------------- */
+const char *bitlinear_status_str(bitlinear_status s);
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *bitlinear_last_error(void);
+int32_t bitlinear_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

@@ -1,0 +1,234 @@
+"""Python binding of the gfx950 BitLinear library (``libbitlinear.so``).
+
+Argument marshalling only: every function below checks nothing the library
+does not check itself, takes torch tensors for device memory, passes their
+device pointers and the current HIP stream to the C entry point of the same
+name (``include/bitlinear.h``) and raises :class:`BitLinearError` on a non-OK
+status. All arithmetic runs in the HIP kernels; if the library is not built,
+loading fails with an error (there is no other implementation to fall back to).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DEVICE, ERR_ARG = range(7)
+ACT_ABSMAX, ACT_RMSNORM, ACT_RELU2_RMSNORM = 0, 1, 2
+PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+BLOCK_FFN, BLOCK_DECODER = 0, 1
+MAX_SEGMENTS = 4
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, func: str, status: int, detail: str):
+        super().__init__(f"{func}: {status_name(status)} ({detail})")
+        self.status = status
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("qkv", _p), ("qkv_gamma", ctypes.c_float * 3), ("o", _p), ("o_gamma", ctypes.c_float),
+                ("gate_up", _p), ("gate_up_gamma", ctypes.c_float * 2), ("down", _p), ("down_gamma", ctypes.c_float),
+                ("input_norm_gain", _p), ("attn_sub_norm_gain", _p), ("post_attn_norm_gain", _p),
+                ("ffn_sub_norm_gain", _p)]
+
+
+class Block(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("n_layers", _i32), ("hidden", _i64), ("intermediate", _i64),
+                ("n_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("eps", ctypes.c_float),
+                ("layers", ctypes.POINTER(Layer))]
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [(name, _p) for name in ("codes_in", "codes_attn", "codes_post", "codes_ffn", "deq", "qkv", "h",
+                                        "gate_up", "x_out", "acc_qkv", "acc_o", "acc_gate_up", "acc_down")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -m ternary_weight_bitlinear_w1_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "bitlinear_quantize_weights": (_i32, [_p, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
+            "bitlinear_quantize_weights_workspace_bytes": (_sz, [_i64, _i64]),
+            "bitlinear_validate_packed": (_i32, [_p, _i64, _i64, _p, _p]),
+            "bitlinear_quantize_acts": (_i32, [_p, _i64, _i64, _i32, _p, ctypes.c_float, _p, _p, _p, _p]),
+            "bitlinear_forward": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _p, _i32, _p, _sz,
+                                         _p]),
+            "bitlinear_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+            "bitlinear_block_forward": (_i32, [ctypes.POINTER(Block), _p, _i64, _p, ctypes.POINTER(Trace), _p, _sz,
+                                               _p]),
+            "bitlinear_block_workspace_bytes": (_sz, [ctypes.POINTER(Block), _i64]),
+            "bitlinear_status_str": (ctypes.c_char_p, [_i32]),
+            "bitlinear_last_error": (ctypes.c_char_p, []),
+            "bitlinear_abi_version": (_i32, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return lib().bitlinear_status_str(status).decode()
+
+
+def _check(func: str, status: int) -> None:
+    if status != OK:
+        raise BitLinearError(func, status, lib().bitlinear_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device) if nbytes else None
+
+
+# ---------------------------------------------------------------------------------------------
+def quantize_weights(w: torch.Tensor, gamma_in: Optional[torch.Tensor] = None):
+    """Absmean-ternarize and pack ``w`` [n][k] fp32 -> (packed [n][k/4] uint8, gamma [1] fp64)."""
+    n, k = w.shape
+    packed = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    gamma = torch.empty(1, dtype=torch.float64, device=w.device)
+    nb = lib().bitlinear_quantize_weights_workspace_bytes(n, k)
+    ws = _workspace(nb, w.device)
+    _check("bitlinear_quantize_weights",
+           lib().bitlinear_quantize_weights(_ptr(w), n, k, _ptr(gamma_in), _ptr(packed), _ptr(gamma), _ptr(ws),
+                                            nb, _stream(w.device)))
+    return packed, gamma
+
+
+def validate_packed(packed: torch.Tensor, k: int) -> int:
+    """Number of invalid (== 3) fields in a packed matrix (synchronizes)."""
+    out = torch.empty(1, dtype=torch.int64, device=packed.device)
+    _check("bitlinear_validate_packed",
+           lib().bitlinear_validate_packed(_ptr(packed), packed.shape[0], k, _ptr(out), _stream(packed.device)))
+    return int(out.item())
+
+
+def quantize_acts(x: torch.Tensor, mode: int = ACT_ABSMAX, gain: Optional[torch.Tensor] = None, eps: float = 1e-5):
+    """Per-token int8 codes of ``x`` -> (codes [m][k] int8, deq [m] fp32, rowsum [m] int32).
+    For ACT_RELU2_RMSNORM, ``x`` is [m][2k] ([gate | up] rows)."""
+    m, kk = x.shape
+    k = kk // 2 if mode == ACT_RELU2_RMSNORM else kk
+    codes = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    deq = torch.empty(m, dtype=torch.float32, device=x.device)
+    rowsum = torch.empty(m, dtype=torch.int32, device=x.device)
+    _check("bitlinear_quantize_acts",
+           lib().bitlinear_quantize_acts(_ptr(x), m, k, mode, _ptr(gain), ctypes.c_float(eps), _ptr(codes),
+                                         _ptr(deq), _ptr(rowsum), _stream(x.device)))
+    return codes, deq, rowsum
+
+
+def forward(packed: torch.Tensor, k: int, gamma: Sequence[float], seg_end: Optional[Sequence[int]] = None,
+            x: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+            deq: Optional[torch.Tensor] = None, rowsum: Optional[torch.Tensor] = None,
+            want_acc: bool = False, path: int = PATH_AUTO, out: Optional[torch.Tensor] = None):
+    """One projection -> y [m][n] fp32 (and the exact int32 acc when ``want_acc``)."""
+    n = packed.shape[0]
+    src = x if x is not None else codes
+    m = src.shape[0]
+    dev = packed.device
+    if seg_end is None:
+        seg_end = [n]
+    g = (ctypes.c_float * len(gamma))(*[float(v) for v in gamma])
+    se = (ctypes.c_int64 * len(seg_end))(*[int(v) for v in seg_end])
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
+    nb = lib().bitlinear_forward_workspace_bytes(m, n, k, 1 if x is not None else 0)
+    ws = _workspace(nb, dev)
+    _check("bitlinear_forward",
+           lib().bitlinear_forward(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), n, g, se,
+                                   len(gamma), _ptr(y), _ptr(acc), path, _ptr(ws), nb, _stream(dev)))
+    return (y, acc) if want_acc else y
+
+
+# ---------------------------------------------------------------------------------------------
+@dataclass
+class LayerWeights:
+    """Packed weights (device uint8 tensors) and fp32 scales of one block."""
+    gate_up: torch.Tensor
+    gate_up_gamma: Sequence[float]
+    down: torch.Tensor
+    down_gamma: float
+    qkv: Optional[torch.Tensor] = None
+    qkv_gamma: Sequence[float] = (0.0, 0.0, 0.0)
+    o: Optional[torch.Tensor] = None
+    o_gamma: float = 0.0
+    input_norm_gain: Optional[torch.Tensor] = None
+    attn_sub_norm_gain: Optional[torch.Tensor] = None
+    post_attn_norm_gain: Optional[torch.Tensor] = None
+    ffn_sub_norm_gain: Optional[torch.Tensor] = None
+
+
+@dataclass
+class BlockSpec:
+    kind: int
+    hidden: int
+    intermediate: int
+    layers: list = field(default_factory=list)
+    n_heads: int = 0
+    n_kv_heads: int = 0
+    head_dim: int = 0
+    eps: float = 1e-5
+
+    def to_c(self):
+        arr = (Layer * len(self.layers))()
+        for i, L in enumerate(self.layers):
+            arr[i] = Layer(_ptr(L.qkv), (ctypes.c_float * 3)(*[float(v) for v in L.qkv_gamma]), _ptr(L.o),
+                           float(L.o_gamma), _ptr(L.gate_up),
+                           (ctypes.c_float * 2)(*[float(v) for v in L.gate_up_gamma]), _ptr(L.down),
+                           float(L.down_gamma), _ptr(L.input_norm_gain), _ptr(L.attn_sub_norm_gain),
+                           _ptr(L.post_attn_norm_gain), _ptr(L.ffn_sub_norm_gain))
+        blk = Block(self.kind, len(self.layers), self.hidden, self.intermediate, self.n_heads, self.n_kv_heads,
+                    self.head_dim, self.eps, arr)
+        return blk, arr
+
+
+def block_workspace_bytes(spec: BlockSpec, m: int) -> int:
+    blk, _keep = spec.to_c()
+    return int(lib().bitlinear_block_workspace_bytes(ctypes.byref(blk), m))
+
+
+def block_forward(spec: BlockSpec, x: torch.Tensor, trace: Optional[dict] = None,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Run a block chain on x [m][H] -> y [m][H]. ``trace`` maps Trace field names to
+    preallocated device tensors (see include/bitlinear.h)."""
+    blk, _keep = spec.to_c()
+    m = x.shape[0]
+    y = out if out is not None else torch.empty_like(x)
+    nb = int(lib().bitlinear_block_workspace_bytes(ctypes.byref(blk), m))
+    ws = workspace if workspace is not None else _workspace(nb, x.device)
+    tr = None
+    if trace:
+        tr = Trace(**{k: _ptr(v) for k, v in trace.items()})
+    _check("bitlinear_block_forward",
+           lib().bitlinear_block_forward(ctypes.byref(blk), _ptr(x), m, _ptr(y),
+                                         ctypes.byref(tr) if tr is not None else None, _ptr(ws),
+                                         ws.numel() if ws is not None else 0, _stream(x.device)))
+    return y

@@ -1,0 +1,416 @@
+// C-ABI entry points of the BitLinear library (declared in include/bitlinear.h).
+//
+// Every entry point validates its arguments on the host first, and returns a
+// status without touching the HIP runtime when they are wrong; then it checks
+// that the current device is gfx950, and enqueues kernels on the caller's
+// stream without synchronizing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+bitlinear_status fail(bitlinear_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+bitlinear_status check_device() {
+  static std::mutex mu;
+  static int state[256];  // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BITLINEAR_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 256) return fail(BITLINEAR_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(BITLINEAR_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (state[dev] == 2) return fail(BITLINEAR_ERR_DEVICE, "device %d is %s, this library targets gfx950", dev,
+                                     prop.gcnArchName);
+  }
+  if (state[dev] != 1) return fail(BITLINEAR_ERR_DEVICE, "device %d is not gfx950", dev);
+  return BITLINEAR_OK;
+}
+
+bitlinear_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(BITLINEAR_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return BITLINEAR_OK;
+}
+
+#define BL_TRY(expr)                              \
+  do {                                            \
+    bitlinear_status st_ = (expr);                \
+    if (st_ != BITLINEAR_OK) return st_;          \
+  } while (0)
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------- forward core
+bitlinear_status check_segments(const float *gamma, const int64_t *seg_end, int32_t n_seg, int64_t n,
+                                bl::Epilogue *ep) {
+  if (!gamma || !seg_end) return fail(BITLINEAR_ERR_NULL, "gamma and seg_end are required");
+  if (n_seg < 1 || n_seg > BITLINEAR_MAX_SEGMENTS)
+    return fail(BITLINEAR_ERR_SHAPE, "n_seg = %d, must be 1..%d", n_seg, BITLINEAR_MAX_SEGMENTS);
+  int64_t prev = 0;
+  for (int s = 0; s < n_seg; ++s) {
+    if (seg_end[s] <= prev) return fail(BITLINEAR_ERR_SHAPE, "seg_end must be strictly ascending and positive");
+    prev = seg_end[s];
+  }
+  if (prev != n) return fail(BITLINEAR_ERR_SHAPE, "seg_end[n_seg-1] = %lld, must equal n = %lld", (long long)prev,
+                             (long long)n);
+  for (int s = 0; s < BITLINEAR_MAX_SEGMENTS; ++s) {
+    ep->gamma[s] = s < n_seg ? gamma[s] : 0.0f;
+    ep->seg_end[s] = s < n_seg ? (int32_t)seg_end[s] : (int32_t)n;
+  }
+  ep->n_seg = n_seg;
+  return BITLINEAR_OK;
+}
+
+// int32 indexing inside the kernels
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bitlinear_status contract(const int8_t *codes, const float *deq, const int32_t *rowsum, int64_t m, int64_t k,
+                          const uint8_t *w, int64_t n, const bl::Epilogue &ep, float *y, int32_t *acc_out,
+                          int32_t path, hipStream_t stream) {
+  const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && m <= 16);
+  if (decode) return launched(bl::launch_gemv_decode(codes, w, deq, rowsum, m, n, k, ep, y, acc_out, stream),
+                              "decode kernel");
+  return launched(bl::launch_gemm_prefill(codes, w, deq, rowsum, m, n, k, ep, y, acc_out, stream), "prefill kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bitlinear_status_str(bitlinear_status s) {
+  switch (s) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_ERR_NULL: return "null pointer";
+    case BITLINEAR_ERR_SHAPE: return "bad shape";
+    case BITLINEAR_ERR_ALIGN: return "misaligned pointer";
+    case BITLINEAR_ERR_WORKSPACE: return "workspace too small";
+    case BITLINEAR_ERR_DEVICE: return "device error";
+    case BITLINEAR_ERR_ARG: return "bad argument";
+  }
+  return "unknown status";
+}
+
+const char *bitlinear_last_error(void) { return g_err.c_str(); }
+
+int32_t bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+// ---------------------------------------------------------------- weights
+size_t bitlinear_quantize_weights_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 0 || k <= 0) return 0;
+  return align256(bl::absmean_partials(n * k) * sizeof(double));
+}
+
+bitlinear_status bitlinear_quantize_weights(const float *w, int64_t n, int64_t k, const double *gamma_in,
+                                            uint8_t *w_packed, double *gamma_out, void *workspace,
+                                            size_t workspace_bytes, void *stream) {
+  g_err.clear();
+  if (!w || !w_packed || !gamma_out) return fail(BITLINEAR_ERR_NULL, "w, w_packed and gamma_out are required");
+  if (n < 0 || k <= 0 || k % 16 != 0 || n > kMaxDim || k > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "n = %lld, k = %lld: need n >= 0, k > 0, k %% 16 == 0", (long long)n,
+                (long long)k);
+  if (!aligned16(w) || !aligned16(w_packed)) return fail(BITLINEAR_ERR_ALIGN, "w and w_packed must be 16-byte aligned");
+  const size_t need = bitlinear_quantize_weights_workspace_bytes(n, k);
+  if (!gamma_in && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  BL_TRY(check_device());
+  hipStream_t s = as_stream(stream);
+  if (gamma_in) {
+    BL_TRY(launched(bl::launch_copy_gamma(gamma_in, gamma_out, s), "copy gamma"));
+  } else {
+    BL_TRY(launched(bl::launch_absmean(w, n * k, static_cast<double *>(workspace), gamma_out, s), "absmean"));
+  }
+  return launched(bl::launch_ternarize_pack(w, n, k, gamma_out, w_packed, s), "ternarize");
+}
+
+bitlinear_status bitlinear_validate_packed(const uint8_t *w_packed, int64_t n, int64_t k, int64_t *n_bad,
+                                           void *stream) {
+  g_err.clear();
+  if (!w_packed || !n_bad) return fail(BITLINEAR_ERR_NULL, "w_packed and n_bad are required");
+  if (n < 0 || k <= 0 || k % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "need n >= 0, k > 0, k %% 16 == 0");
+  if (!aligned16(w_packed)) return fail(BITLINEAR_ERR_ALIGN, "w_packed must be 16-byte aligned");
+  BL_TRY(check_device());
+  return launched(bl::launch_validate_packed(w_packed, n, k, n_bad, as_stream(stream)), "validate");
+}
+
+// ---------------------------------------------------------------- activations
+bitlinear_status bitlinear_quantize_acts(const float *x, int64_t m, int64_t k, int32_t mode, const float *norm_gain,
+                                         float eps, int8_t *codes, float *deq, int32_t *code_rowsum, void *stream) {
+  g_err.clear();
+  if (!x || !codes || !deq) return fail(BITLINEAR_ERR_NULL, "x, codes and deq are required");
+  if (m < 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || k > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, k = %lld: need m >= 0, k > 0, k %% 16 == 0", (long long)m,
+                (long long)k);
+  if (mode != BITLINEAR_ACT_ABSMAX && mode != BITLINEAR_ACT_RMSNORM && mode != BITLINEAR_ACT_RELU2_RMSNORM)
+    return fail(BITLINEAR_ERR_ARG, "unknown mode %d", mode);
+  if (!aligned16(x) || !aligned16(codes) || (norm_gain && !aligned16(norm_gain)))
+    return fail(BITLINEAR_ERR_ALIGN, "x, codes and norm_gain must be 16-byte aligned");
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  const int64_t ld = mode == BITLINEAR_ACT_RELU2_RMSNORM ? 2 * k : k;
+  return launched(bl::launch_quant_acts(mode, x, nullptr, ld, m, k, norm_gain, eps, 0, 1, 1, nullptr, codes, deq,
+                                        code_rowsum, as_stream(stream)),
+                  "quantize_acts");
+}
+
+// ---------------------------------------------------------------- forward
+size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside) {
+  (void)n;
+  if (m < 0 || k < 0) return 0;
+  size_t b = align256((size_t)m * sizeof(int32_t));  // row sums
+  if (quantize_inside) b += align256((size_t)(m * k)) + align256((size_t)m * sizeof(float));
+  return b;
+}
+
+bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const float *deq_in,
+                                   const int32_t *rowsum_in, int64_t m, int64_t k, const uint8_t *w_packed, int64_t n,
+                                   const float *gamma, const int64_t *seg_end, int32_t n_seg, float *y,
+                                   int32_t *acc_out, int32_t path, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  g_err.clear();
+  if (!w_packed || !y) return fail(BITLINEAR_ERR_NULL, "w_packed and y are required");
+  if (!x && (!codes_in || !deq_in)) return fail(BITLINEAR_ERR_NULL, "give x, or codes_in and deq_in");
+  if (m < 0 || n <= 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, n = %lld, k = %lld: need m >= 0, n > 0, k > 0, k %% 16 == 0",
+                (long long)m, (long long)n, (long long)k);
+  bl::Epilogue ep;
+  BL_TRY(check_segments(gamma, seg_end, n_seg, n, &ep));
+  if (path != BITLINEAR_PATH_AUTO && path != BITLINEAR_PATH_DECODE && path != BITLINEAR_PATH_PREFILL)
+    return fail(BITLINEAR_ERR_ARG, "unknown path %d", path);
+  if (path == BITLINEAR_PATH_DECODE && m > 16) return fail(BITLINEAR_ERR_SHAPE, "the decode path takes m <= 16");
+  if ((x && !aligned16(x)) || (codes_in && !x && !aligned16(codes_in)) || !aligned16(w_packed) || !aligned16(y))
+    return fail(BITLINEAR_ERR_ALIGN, "x, codes_in, w_packed and y must be 16-byte aligned");
+  const size_t need = bitlinear_forward_workspace_bytes(m, n, k, x != nullptr);
+  if (m > 0 && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  hipStream_t s = as_stream(stream);
+  char *ws = static_cast<char *>(workspace);
+  int32_t *rowsum = reinterpret_cast<int32_t *>(ws);
+  ws += align256((size_t)m * sizeof(int32_t));
+  const int8_t *codes = codes_in;
+  const float *deq = deq_in;
+  if (x) {
+    int8_t *c = reinterpret_cast<int8_t *>(ws);
+    ws += align256((size_t)(m * k));
+    float *d = reinterpret_cast<float *>(ws);
+    BL_TRY(launched(bl::launch_quant_acts(BITLINEAR_ACT_ABSMAX, x, nullptr, k, m, k, nullptr, 0.0f, 0, 1, 1, nullptr,
+                                          c, d, rowsum, s),
+                    "quantize_acts"));
+    codes = c;
+    deq = d;
+  } else if (rowsum_in) {
+    rowsum = const_cast<int32_t *>(rowsum_in);
+  } else {
+    BL_TRY(launched(bl::launch_code_rowsum(codes, m, k, rowsum, s), "code row sums"));
+  }
+  return contract(codes, deq, rowsum, m, k, w_packed, n, ep, y, acc_out, path, s);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- blocks
+namespace {
+
+struct BlockBufs {
+  int8_t *codes;
+  float *deq;
+  int32_t *rowsum;
+  float *qkv, *o, *h, *x, *gu, *d;
+};
+
+size_t block_layout(const bitlinear_block *blk, int64_t m, BlockBufs *b, char *base) {
+  const int64_t H = blk->hidden, I = blk->intermediate;
+  const bool dec = blk->kind == BITLINEAR_BLOCK_DECODER;
+  const int64_t Q = dec ? H + 2 * (int64_t)blk->n_kv_heads * blk->head_dim : 0;
+  const int64_t widest = H > I ? H : I;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  BlockBufs t;
+  t.codes = reinterpret_cast<int8_t *>(take((size_t)(m * widest)));
+  t.deq = reinterpret_cast<float *>(take((size_t)m * 4));
+  t.rowsum = reinterpret_cast<int32_t *>(take((size_t)m * 4));
+  t.gu = reinterpret_cast<float *>(take((size_t)(m * 2 * I) * 4));
+  t.qkv = reinterpret_cast<float *>(take(dec ? (size_t)(m * Q) * 4 : 0));
+  t.o = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
+  t.h = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
+  t.x = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
+  t.d = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
+  if (b) *b = t;
+  return off;
+}
+
+bitlinear_status check_block(const bitlinear_block *blk) {
+  if (!blk || !blk->layers) return fail(BITLINEAR_ERR_NULL, "blk and blk->layers are required");
+  if (blk->kind != BITLINEAR_BLOCK_FFN && blk->kind != BITLINEAR_BLOCK_DECODER)
+    return fail(BITLINEAR_ERR_ARG, "unknown block kind %d", blk->kind);
+  const int64_t H = blk->hidden, I = blk->intermediate;
+  if (blk->n_layers < 1 || H <= 0 || I <= 0 || H % 16 || I % 16 || H > kMaxDim || I > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "need n_layers >= 1 and hidden, intermediate positive multiples of 16");
+  if (blk->kind == BITLINEAR_BLOCK_FFN && blk->n_layers != 1) return fail(BITLINEAR_ERR_SHAPE, "an FFN block has 1 layer");
+  if (blk->kind == BITLINEAR_BLOCK_DECODER) {
+    if (blk->n_heads <= 0 || blk->n_kv_heads <= 0 || blk->head_dim <= 0 || blk->head_dim % 4 ||
+        blk->n_heads % blk->n_kv_heads || (int64_t)blk->n_heads * blk->head_dim != H)
+      return fail(BITLINEAR_ERR_SHAPE, "need n_heads * head_dim == hidden, n_kv_heads | n_heads, head_dim %% 4 == 0");
+    if (((int64_t)blk->n_kv_heads * blk->head_dim) % 16)
+      return fail(BITLINEAR_ERR_SHAPE, "n_kv_heads * head_dim must be a multiple of 16");
+  }
+  for (int l = 0; l < blk->n_layers; ++l) {
+    const bitlinear_layer &L = blk->layers[l];
+    if (!L.gate_up || !L.down) return fail(BITLINEAR_ERR_NULL, "layer %d: gate_up and down are required", l);
+    if (!aligned16(L.gate_up) || !aligned16(L.down)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: misaligned weights", l);
+    if (L.ffn_sub_norm_gain && !aligned16(L.ffn_sub_norm_gain)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: gain", l);
+    if (blk->kind == BITLINEAR_BLOCK_DECODER) {
+      if (!L.qkv || !L.o) return fail(BITLINEAR_ERR_NULL, "layer %d: qkv and o are required", l);
+      if (!aligned16(L.qkv) || !aligned16(L.o)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: misaligned weights", l);
+      const float *g[3] = {L.input_norm_gain, L.attn_sub_norm_gain, L.post_attn_norm_gain};
+      for (const float *p : g)
+        if (p && !aligned16(p)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: misaligned gain", l);
+    }
+  }
+  return BITLINEAR_OK;
+}
+
+bitlinear_status copy_to(void *dst, const void *src, size_t bytes, hipStream_t s) {
+  if (!dst) return BITLINEAR_OK;
+  return launched(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s), "trace copy");
+}
+
+bitlinear_status proj(const BlockBufs &b, int64_t m, int64_t k, const uint8_t *w, int64_t n, const float *gam,
+                      const int64_t *seg, int n_seg, float *y, int32_t *acc, hipStream_t s) {
+  bl::Epilogue ep;
+  BL_TRY(check_segments(gam, seg, n_seg, n, &ep));
+  return contract(b.codes, b.deq, b.rowsum, m, k, w, n, ep, y, acc, BITLINEAR_PATH_AUTO, s);
+}
+
+bitlinear_status quant(const BlockBufs &b, int mode, const float *x, const float *x2, int64_t ld, int64_t m,
+                       int64_t k, const float *gain, float eps, int gqa_off, int hd, int group, float *h_out,
+                       hipStream_t s) {
+  return launched(bl::launch_quant_acts(mode, x, x2, ld, m, k, gain, eps, gqa_off, hd, group, h_out, b.codes, b.deq,
+                                        b.rowsum, s),
+                  "quantize stage");
+}
+
+template <typename T>
+T *at(T *p, int64_t off) {
+  return p ? p + off : nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_block_workspace_bytes(const bitlinear_block *blk, int64_t m) {
+  if (!blk || m < 0 || blk->hidden <= 0 || blk->intermediate <= 0) return 0;
+  return block_layout(blk, m, nullptr, nullptr);
+}
+
+bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float *x, int64_t m, float *y,
+                                         const bitlinear_block_trace *trace, void *workspace, size_t workspace_bytes,
+                                         void *stream) {
+  g_err.clear();
+  BL_TRY(check_block(blk));
+  if (!x || !y) return fail(BITLINEAR_ERR_NULL, "x and y are required");
+  if (m < 0 || m > kMaxDim) return fail(BITLINEAR_ERR_SHAPE, "m = %lld", (long long)m);
+  if (!aligned16(x) || !aligned16(y)) return fail(BITLINEAR_ERR_ALIGN, "x and y must be 16-byte aligned");
+  const size_t need = bitlinear_block_workspace_bytes(blk, m);
+  if (m > 0 && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  hipStream_t s = as_stream(stream);
+  BlockBufs b;
+  block_layout(blk, m, &b, static_cast<char *>(workspace));
+  const int64_t H = blk->hidden, I = blk->intermediate;
+  const float eps = blk->eps;
+  bitlinear_block_trace tr;
+  memset(&tr, 0, sizeof tr);
+  if (trace) tr = *trace;
+
+  const int64_t gu_seg[2] = {I, 2 * I};
+  const int64_t h_seg[1] = {H};
+
+  if (blk->kind == BITLINEAR_BLOCK_FFN) {
+    const bitlinear_layer &L = blk->layers[0];
+    BL_TRY(quant(b, BITLINEAR_ACT_ABSMAX, x, nullptr, H, m, H, nullptr, eps, 0, 1, 1, nullptr, s));
+    BL_TRY(copy_to(tr.codes_in, b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(tr.deq, b.deq, (size_t)m * 4, s));
+    BL_TRY(proj(b, m, H, L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, b.gu, tr.acc_gate_up, s));
+    BL_TRY(copy_to(tr.gate_up, b.gu, (size_t)(m * 2 * I) * 4, s));
+    BL_TRY(quant(b, BITLINEAR_ACT_RELU2_RMSNORM, b.gu, nullptr, 2 * I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1,
+                 nullptr, s));
+    BL_TRY(copy_to(tr.codes_ffn, b.codes, (size_t)(m * I), s));
+    BL_TRY(copy_to(at(tr.deq, 3 * m), b.deq, (size_t)m * 4, s));
+    return proj(b, m, I, L.down, H, &L.down_gamma, h_seg, 1, y, tr.acc_down, s);
+  }
+
+  const int hd = blk->head_dim, group = blk->n_heads / blk->n_kv_heads;
+  const int64_t KV = (int64_t)blk->n_kv_heads * hd, Q = H + 2 * KV;
+  const int64_t qkv_seg[3] = {H, H + KV, Q};
+  for (int l = 0; l < blk->n_layers; ++l) {
+    const bitlinear_layer &L = blk->layers[l];
+    const int64_t oH = (int64_t)l * m * H, oI = (int64_t)l * m * I, oQ = (int64_t)l * m * Q;
+    // input_layernorm; for l > 0 the layer input is h + down of the previous layer
+    const float *xin = x;
+    if (l == 0) {
+      BL_TRY(quant(b, BITLINEAR_ACT_RMSNORM, x, nullptr, H, m, H, L.input_norm_gain, eps, 0, 1, 1, nullptr, s));
+    } else {
+      BL_TRY(quant(b, bl::ACT_RESID_RMSNORM, b.h, b.d, H, m, H, L.input_norm_gain, eps, 0, 1, 1, b.x, s));
+      xin = b.x;
+    }
+    BL_TRY(copy_to(at(tr.codes_in, oH), b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l), b.deq, (size_t)m * 4, s));
+    BL_TRY(proj(b, m, H, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, b.qkv, at(tr.acc_qkv, oQ), s));
+    BL_TRY(copy_to(at(tr.qkv, oQ), b.qkv, (size_t)(m * Q) * 4, s));
+    // self-only attention output -> attn_sub_norm -> o_proj
+    BL_TRY(quant(b, bl::ACT_GQA_RMSNORM, b.qkv, nullptr, Q, m, H, L.attn_sub_norm_gain, eps, (int)(H + KV), hd, group,
+                 nullptr, s));
+    BL_TRY(copy_to(at(tr.codes_attn, oH), b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l + m), b.deq, (size_t)m * 4, s));
+    BL_TRY(proj(b, m, H, L.o, H, &L.o_gamma, h_seg, 1, b.o, at(tr.acc_o, oH), s));
+    // h = x + o -> post_attention_layernorm
+    BL_TRY(quant(b, bl::ACT_RESID_RMSNORM, xin, b.o, H, m, H, L.post_attn_norm_gain, eps, 0, 1, 1, b.h, s));
+    BL_TRY(copy_to(at(tr.h, oH), b.h, (size_t)(m * H) * 4, s));
+    BL_TRY(copy_to(at(tr.codes_post, oH), b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l + 2 * m), b.deq, (size_t)m * 4, s));
+    BL_TRY(proj(b, m, H, L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, b.gu, at(tr.acc_gate_up, 2 * oI), s));
+    BL_TRY(copy_to(at(tr.gate_up, 2 * oI), b.gu, (size_t)(m * 2 * I) * 4, s));
+    // relu^2 gating -> ffn_sub_norm -> down
+    BL_TRY(quant(b, BITLINEAR_ACT_RELU2_RMSNORM, b.gu, nullptr, 2 * I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1,
+                 nullptr, s));
+    BL_TRY(copy_to(at(tr.codes_ffn, oI), b.codes, (size_t)(m * I), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l + 3 * m), b.deq, (size_t)m * 4, s));
+    BL_TRY(proj(b, m, I, L.down, H, &L.down_gamma, h_seg, 1, b.d, at(tr.acc_down, oH), s));
+    if (tr.x_out) BL_TRY(launched(bl::launch_add(b.h, b.d, tr.x_out + oH, m * H, s), "trace add"));
+  }
+  return launched(bl::launch_add(b.h, b.d, y, m * H, s), "residual add");
+}
+
+}  // extern "C"

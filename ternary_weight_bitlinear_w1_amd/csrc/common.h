@@ -1,0 +1,85 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "bitlinear.h"
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- epilogue
+// Per-column weight scales of a (possibly fused) projection: column j uses
+// gamma[s] for seg_end[s-1] <= j < seg_end[s]; n_seg <= BITLINEAR_MAX_SEGMENTS.
+struct Epilogue {
+  float gamma[BITLINEAR_MAX_SEGMENTS];
+  int32_t seg_end[BITLINEAR_MAX_SEGMENTS];
+  int32_t n_seg;
+};
+
+__device__ __forceinline__ float epi_gamma(const Epilogue &ep, int n) {
+  float g = ep.gamma[0];
+#pragma unroll
+  for (int s = 1; s < BITLINEAR_MAX_SEGMENTS; ++s)
+    if (s < ep.n_seg && n >= ep.seg_end[s - 1]) g = ep.gamma[s];
+  return g;
+}
+
+// y = fl32(fl32((float)acc * deq) * gamma); acc is the exact int32 sum.
+__device__ __forceinline__ float rescale(int acc, float deq, float gamma) {
+  const float t = __fmul_rn((float)acc, deq);
+  return __fmul_rn(t, gamma);
+}
+
+// ---------------------------------------------------------------- reductions
+// Wave64 butterflies: every lane ends with the result. The order of
+// combination is fixed, so fp64 sums are reproducible run to run.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- launchers
+// Implemented next to their kernels; all enqueue on `stream` and return the
+// hipGetLastError() of the launch.
+hipError_t launch_quant_acts(int mode, const float *x, const float *x2, int64_t ld_x, int64_t m, int64_t k,
+                             const float *gain, float eps, int gqa_offset, int head_dim, int group,
+                             float *h_out, int8_t *codes, float *deq, int32_t *rowsum, hipStream_t stream);
+hipError_t launch_code_rowsum(const int8_t *codes, int64_t m, int64_t k, int32_t *rowsum, hipStream_t stream);
+hipError_t launch_add(const float *a, const float *b, float *out, int64_t count, hipStream_t stream);
+
+size_t absmean_partials(int64_t count);
+hipError_t launch_absmean(const float *w, int64_t count, double *partials, double *gamma_out,
+                          hipStream_t stream);
+hipError_t launch_ternarize_pack(const float *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
+                                 hipStream_t stream);
+hipError_t launch_copy_gamma(const double *src, double *dst, hipStream_t stream);
+hipError_t launch_validate_packed(const uint8_t *packed, int64_t n, int64_t k, int64_t *n_bad,
+                                  hipStream_t stream);
+
+hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const float *deq,
+                               const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
+                               float *y, int32_t *acc_out, hipStream_t stream);
+hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const float *deq,
+                              const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
+                              float *y, int32_t *acc_out, hipStream_t stream);
+
+// act-quant prologues beyond the public bitlinear_act_mode values
+enum { ACT_RESID_RMSNORM = 16, ACT_GQA_RMSNORM = 17 };
+
+}  // namespace bl

