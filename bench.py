@@ -1,0 +1,293 @@
+"""Benchmark of the BitLinear hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one prefill pass of a BitNet b1.58 2B4T MLP over M = 4096 tokens, all
+on the GPU through the C ABI:
+    per-token int8 quantization of x [4096][2560]
+    gate|up contraction 2560 -> 13824 (one weight scale per matrix) + rescale
+    ReLU^2 gating and ffn_sub_norm folded into the quantization of [4096][6912]
+    down contraction 6912 -> 2560 + rescale
+Weights are packed once before timing (the packed-checkpoint mode). ``value``
+is int8 TOPS of the whole step: 2 M N K of both contractions / step time.
+``roofline`` is the gate|up contraction kernel against dense int8 MFMA peak,
+timed with HIP events on the stream it runs on. ``decode`` reports the
+weight-streaming kernel (M = 1, 4, 16) in packed-weight GB/s against HBM peak,
+each launch reading a different copy of the weights from a ring larger than the
+256 MB last-level cache. ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same step's tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "BitLinear prefill int8 TOPS & decode packed-weight GB/s, % of roofline"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+M, H, I = 4096, 2560, 6912
+BASE_SEED = 1234
+RING_BYTES = 600 * 2 ** 20  # > 2 x the 256 MB last-level cache
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-reps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the data-parallel path shards tokens "
+                                   "with no exchange, so per-GPU throughput is the single-GPU figure",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from ternary_weight_bitlinear_w1_amd import bitlinear as bl
+    from ternary_weight_bitlinear_w1_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bl.lib()  # fails loudly if the HIP library is missing
+
+    def seed(layer, tensor):
+        return synth.stream_seed(BASE_SEED, 4, layer, tensor)
+
+    # ---------------------------------------------------------------- weights (offline)
+    log("generating weights")
+    w_gate = synth.weights(seed(0, 1), I, H)
+    w_up = synth.weights(seed(0, 2), I, H)
+    w_down = synth.weights(seed(0, 3), H, I)
+    packed_gu = torch.empty((2 * I, H // 4), dtype=torch.uint8, device=dev)
+    g_gate = bl.quantize_weights(torch.from_numpy(w_gate).to(dev))
+    g_up = bl.quantize_weights(torch.from_numpy(w_up).to(dev))
+    packed_gu[:I].copy_(g_gate[0])
+    packed_gu[I:].copy_(g_up[0])
+    packed_d, g_d = bl.quantize_weights(torch.from_numpy(w_down).to(dev))
+    gam_gu = [float(np.float32(g_gate[1].item())), float(np.float32(g_up[1].item()))]
+    gam_d = [float(np.float32(g_d.item()))]
+    x = torch.from_numpy(synth.activations(seed(0, 5), M, H)).to(dev)
+
+    # buffers of the step
+    codes1 = torch.empty((M, H), dtype=torch.int8, device=dev)
+    codes2 = torch.empty((M, I), dtype=torch.int8, device=dev)
+    deq1 = torch.empty(M, dtype=torch.float32, device=dev)
+    deq2 = torch.empty(M, dtype=torch.float32, device=dev)
+    rs1 = torch.empty(M, dtype=torch.int32, device=dev)
+    rs2 = torch.empty(M, dtype=torch.int32, device=dev)
+    gu = torch.empty((M, 2 * I), dtype=torch.float32, device=dev)
+    y = torch.empty((M, H), dtype=torch.float32, device=dev)
+    L = bl.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    c_float = bl.ctypes.c_float
+    g_gu_c = (c_float * 2)(*gam_gu)
+    se_gu = (bl.ctypes.c_int64 * 2)(I, 2 * I)
+    g_d_c = (c_float * 1)(*gam_d)
+    se_d = (bl.ctypes.c_int64 * 1)(H)
+    ws_n = L.bitlinear_forward_workspace_bytes(M, 2 * I, I, 0)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+
+    def ok(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {bl.status_name(st)} {L.bitlinear_last_error().decode()}")
+
+    def q1():
+        ok(L.bitlinear_quantize_acts(x.data_ptr(), M, H, bl.ACT_ABSMAX, None, c_float(1e-5), codes1.data_ptr(),
+                                     deq1.data_ptr(), rs1.data_ptr(), sp), "quantize x")
+
+    def f_gu():
+        ok(L.bitlinear_forward(None, codes1.data_ptr(), deq1.data_ptr(), rs1.data_ptr(), M, H, packed_gu.data_ptr(),
+                               2 * I, g_gu_c, se_gu, 2, gu.data_ptr(), None, bl.PATH_PREFILL, ws.data_ptr(), ws_n, sp),
+           "gate|up")
+
+    def q2():
+        ok(L.bitlinear_quantize_acts(gu.data_ptr(), M, I, bl.ACT_RELU2_RMSNORM, None, c_float(1e-5),
+                                     codes2.data_ptr(), deq2.data_ptr(), rs2.data_ptr(), sp), "relu2 + sub-norm")
+
+    def f_d():
+        ok(L.bitlinear_forward(None, codes2.data_ptr(), deq2.data_ptr(), rs2.data_ptr(), M, I, packed_d.data_ptr(),
+                               H, g_d_c, se_d, 1, y.data_ptr(), None, bl.PATH_PREFILL, ws.data_ptr(), ws_n, sp),
+           "down")
+
+    ops = [("quant_x", q1), ("gemm_gate_up", f_gu), ("quant_relu2_subnorm", q2), ("gemm_down", f_d)]
+
+    # ---------------------------------------------------------------- prefill step
+    log(f"prefill: warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        for _, f in ops:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for j, (_, f) in enumerate(ops):
+            f()
+            ev[s][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = {name: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(args.steps)]))
+              for j, (name, _) in enumerate(ops)}
+    step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)]))
+    ops_gu = 2.0 * M * (2 * I) * H
+    ops_d = 2.0 * M * H * I
+    tops = (ops_gu + ops_d) / (step_ms * 1e-3) / 1e12
+    gu_tops = ops_gu / (per_op["gemm_gate_up"] * 1e-3) / 1e12
+    d_tops = ops_d / (per_op["gemm_down"] * 1e-3) / 1e12
+    log(f"step {step_ms:.3f} ms ({tops:.0f} TOPS); per op ms {per_op}; wall/step {wall / args.steps * 1e3:.3f} ms")
+
+    # quantization kernels against HBM: bytes read + written per launch
+    q1_bytes = M * H * 4 + M * H + M * 12
+    q2_bytes = M * 2 * I * 4 + M * I + M * 12
+    kernels = {
+        "gemm_gate_up": {"ms": per_op["gemm_gate_up"], "tops": gu_tops, "frac_mfma": gu_tops / PEAK_INT8_TOPS},
+        "gemm_down": {"ms": per_op["gemm_down"], "tops": d_tops, "frac_mfma": d_tops / PEAK_INT8_TOPS},
+        "quant_x": {"ms": per_op["quant_x"], "gbs": q1_bytes / (per_op["quant_x"] * 1e-3) / 1e9},
+        "quant_relu2_subnorm": {"ms": per_op["quant_relu2_subnorm"],
+                                "gbs": q2_bytes / (per_op["quant_relu2_subnorm"] * 1e-3) / 1e9},
+    }
+    for kq in ("quant_x", "quant_relu2_subnorm"):
+        kernels[kq]["frac_hbm"] = kernels[kq]["gbs"] / PEAK_HBM_GBS
+
+    # ---------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        decode = bench_decode(torch, bl, synth, dev, args.decode_reps, packed_gu, gam_gu, packed_d, gam_d)
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w_gate, w_up, w_down, x.cpu().numpy(), args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "prefill of one BitNet b1.58 2B4T MLP: M=4096 tokens, quantize -> gate|up "
+                               "2560->13824 -> ReLU^2 + ffn_sub_norm quantize -> down 6912->2560",
+                   "tokens": M, "hidden": H, "intermediate": I, "ops_per_step": ops_gu + ops_d},
+        "roofline": {"bound": "mfma", "kernel": "gemm_prefill (gate|up, M=4096 N=13824 K=2560)",
+                     "achieved": round(gu_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tops / PEAK_INT8_TOPS, 4), "traffic": None,
+                     "algorithmic_ops_per_launch": ops_gu},
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d):
+    """Weight-streaming kernel at M = 1, 4, 16; each launch reads another copy of the
+    packed weights from a ring larger than the last-level cache."""
+    res = {}
+    L = bl.lib()
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    stream = torch.cuda.current_stream(dev)
+    for name, packed, k, gam, seg in (("gate_up", packed_gu, H, gam_gu, [I, 2 * I]),
+                                      ("down", packed_d, I, gam_d, [H])):
+        n = packed.shape[0]
+        nbytes = packed.numel()
+        copies = max(2, RING_BYTES // nbytes)
+        ring = packed.unsqueeze(0).repeat(copies, 1, 1)
+        g_c = (bl.ctypes.c_float * len(gam))(*gam)
+        se_c = (bl.ctypes.c_int64 * len(seg))(*seg)
+        for m in (1, 4, 16):
+            xm = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 3, m, 5), m, k,
+                                                    synth.outlier_count(k))).to(dev)
+            codes, deq, rs = bl.quantize_acts(xm)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            ws_n = L.bitlinear_forward_workspace_bytes(m, n, k, 0)
+            ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+            def launch(i):
+                st = L.bitlinear_forward(None, codes.data_ptr(), deq.data_ptr(), rs.data_ptr(), m, k,
+                                         ring[i % copies].data_ptr(), n, g_c, se_c, len(gam), y.data_ptr(), None,
+                                         bl.PATH_DECODE, ws.data_ptr(), ws_n, sp)
+                if st != 0:
+                    raise RuntimeError(L.bitlinear_last_error().decode())
+
+            for i in range(20):
+                launch(i)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for i in range(reps):
+                evs[i][0].record(stream)
+                launch(i)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            per = [a.elapsed_time(b) for a, b in evs]
+            us = float(np.median(per)) * 1e3
+            # back-to-back launches (includes the gaps between dispatches)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                launch(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            b2b_us = e0.elapsed_time(e1) / reps * 1e3
+            gbs = nbytes / (us * 1e-6) / 1e9
+            res[f"{name}_m{m}"] = {"us": round(us, 3), "gbs_packed": round(gbs, 1),
+                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "back_to_back_us": round(b2b_us, 3),
+                                   "packed_bytes": nbytes, "ring_copies": copies}
+            log(f"decode {name} m={m}: {us:.2f} us, {gbs:.0f} GB/s (back-to-back {b2b_us:.2f} us)")
+        del ring
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w_gate, w_up, w_down, x, seconds):
+    """The CPU oracle (single thread, as it stands) on a sample of the step's tokens;
+    tokens are independent, so TOPS scale with the sample."""
+    import oracle
+    log("cpu baseline: oracle weights")
+    gams = [oracle.absmean(w) for w in (w_gate, w_up, w_down)]
+    c_gu = np.concatenate([oracle.ternarize(w_gate, gams[0]), oracle.ternarize(w_up, gams[1])])
+    c_d = oracle.ternarize(w_down, gams[2])
+    ops_per_token = 2.0 * (2 * I * H + H * I)
+    t = time.perf_counter()
+    oracle.ffn_block(x[:2], c_gu, gams[:2], c_d, gams[2], None, 1e-5)
+    per_tok = (time.perf_counter() - t) / 2
+    n = int(max(2, min(M, seconds / max(per_tok, 1e-6))))
+    log(f"cpu baseline: {n} tokens (~{n * per_tok:.1f} s)")
+    t = time.perf_counter()
+    oracle.ffn_block(x[:n], c_gu, gams[:2], c_d, gams[2], None, 1e-5)
+    dt = time.perf_counter() - t
+    return {"value": round(ops_per_token * n / dt / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of the {M} tokens of the step (same weights and inputs), {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""Block chains on the GPU against the CPU oracle, free running from the same
+seeded inputs (the oracle never sees a GPU value).
+
+FFN block: x -> int8 codes -> gate|up -> ReLU^2 -> ffn_sub_norm -> down, at
+hidden 512 / intermediate 2048 and M = 1024 (and at decode sizes).
+Decoder stack: the projections of n_layers blocks in the order of the nnterp
+page's "The block, in order", attention taken for tokens that attend only to
+themselves; 30 layers at the 2B4T shapes (M = 1, and sampled tokens of M = 64;
+tokens are independent, so the oracle computes only the sampled rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_weight_bitlinear_w1_amd import bitlinear as bl
+from ternary_weight_bitlinear_w1_amd import synth
+
+from _cases import EPS, Matrix, assert_equal, assert_rel, note, seed
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def pack(mats):
+    parts = [bl.quantize_weights(gpu(m.w), gamma_in=gpu(np.array([m.gamma])))[0] for m in mats]
+    return torch.cat(parts) if len(parts) > 1 else parts[0]
+
+
+def f32(g):
+    return float(np.float32(g))
+
+
+# ------------------------------------------------------------------------------ FFN block
+@pytest.mark.parametrize("m", [1024, 16, 1, 37])
+def test_ffn_block(m):
+    hdim, inter = 512, 2048
+    note(f"block FFN m={m} H={hdim} I={inter}")
+    gate = Matrix(inter, hdim, seed(2, 0, 1))
+    up = Matrix(inter, hdim, seed(2, 0, 2))
+    down = Matrix(hdim, inter, seed(2, 0, 3))
+    x = synth.activations(seed(2, m, 5), m, hdim)
+    spec = bl.BlockSpec(bl.BLOCK_FFN, hdim, inter,
+                        [bl.LayerWeights(gate_up=pack([gate, up]), gate_up_gamma=[f32(gate.gamma), f32(up.gamma)],
+                                         down=pack([down]), down_gamma=f32(down.gamma))], eps=EPS)
+    tr = {"codes_in": torch.empty((m, hdim), dtype=torch.int8, device=DEV),
+          "codes_ffn": torch.empty((m, inter), dtype=torch.int8, device=DEV),
+          "deq": torch.zeros((4, m), dtype=torch.float32, device=DEV),
+          "gate_up": torch.empty((m, 2 * inter), dtype=torch.float32, device=DEV),
+          "acc_gate_up": torch.empty((m, 2 * inter), dtype=torch.int32, device=DEV),
+          "acc_down": torch.empty((m, hdim), dtype=torch.int32, device=DEV)}
+    y = bl.block_forward(spec, gpu(x), trace=tr)
+    ref = oracle.ffn_block(x, np.concatenate([gate.codes, up.codes]), [gate.gamma, up.gamma], down.codes,
+                           down.gamma, None, EPS)
+    assert_equal(host(tr["codes_in"]), ref["q1"], "input codes")
+    assert_equal(host(tr["acc_gate_up"]), ref["acc_gu"], "gate|up acc")
+    assert_equal(host(tr["gate_up"]), ref["gu"], "gate|up")
+    assert_equal(host(tr["codes_ffn"]), ref["q2"], "ffn_sub_norm codes")
+    assert_rel(host(tr["deq"])[3], ref["deq2"], what="ffn_sub_norm deq")
+    assert_equal(host(tr["acc_down"]), ref["acc_down"], "down acc")
+    assert_rel(host(y), ref["y"], what="y")
+
+
+# ------------------------------------------------------------------------------ decoder stack
+def _decoder_layer_mats(cfg, layer, hdim, inter, kvd):
+    names = [("q", hdim, hdim), ("k", kvd, hdim), ("v", kvd, hdim), ("o", hdim, hdim), ("gate", inter, hdim),
+             ("up", inter, hdim), ("down", hdim, inter)]
+    return {nm: Matrix(n, k, seed(cfg, layer, 10 + i)) for i, (nm, n, k) in enumerate(names)}
+
+
+def _oracle_weights(mt, gains):
+    w = {"qkv": np.concatenate([mt["q"].codes, mt["k"].codes, mt["v"].codes]),
+         "g_qkv": [mt["q"].gamma, mt["k"].gamma, mt["v"].gamma], "o": mt["o"].codes, "g_o": mt["o"].gamma,
+         "gu": np.concatenate([mt["gate"].codes, mt["up"].codes]), "g_gu": [mt["gate"].gamma, mt["up"].gamma],
+         "down": mt["down"].codes, "g_down": mt["down"].gamma}
+    if gains is not None:
+        w.update(gains)
+    return w
+
+
+def _gpu_layer(mt, gains):
+    lw = bl.LayerWeights(qkv=pack([mt["q"], mt["k"], mt["v"]]),
+                         qkv_gamma=[f32(mt["q"].gamma), f32(mt["k"].gamma), f32(mt["v"].gamma)],
+                         o=pack([mt["o"]]), o_gamma=f32(mt["o"].gamma), gate_up=pack([mt["gate"], mt["up"]]),
+                         gate_up_gamma=[f32(mt["gate"].gamma), f32(mt["up"].gamma)], down=pack([mt["down"]]),
+                         down_gamma=f32(mt["down"].gamma))
+    if gains is not None:
+        lw.input_norm_gain = gpu(gains["n_in"])
+        lw.attn_sub_norm_gain = gpu(gains["n_attn"])
+        lw.post_attn_norm_gain = gpu(gains["n_post"])
+        lw.ffn_sub_norm_gain = gpu(gains["n_ffn"])
+    return lw
+
+
+def _trace(L, m, hdim, inter, q):
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt, device=DEV)
+    return {"codes_in": z(L, m, hdim, dt=torch.int8), "codes_attn": z(L, m, hdim, dt=torch.int8),
+            "codes_post": z(L, m, hdim, dt=torch.int8), "codes_ffn": z(L, m, inter, dt=torch.int8),
+            "deq": z(L, 4, m), "qkv": z(L, m, q), "h": z(L, m, hdim), "gate_up": z(L, m, 2 * inter),
+            "x_out": z(L, m, hdim), "acc_qkv": z(L, m, q, dt=torch.int32), "acc_o": z(L, m, hdim, dt=torch.int32),
+            "acc_gate_up": z(L, m, 2 * inter, dt=torch.int32), "acc_down": z(L, m, hdim, dt=torch.int32)}
+
+
+def _compare_layer(tr, l, ref, rows=None):
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    g = {k: host(v[l]) for k, v in tr.items()}
+    assert_equal(sel(g["codes_in"]), ref["qkv"]["q"], f"layer {l} input codes")
+    assert_equal(sel(g["acc_qkv"]), ref["qkv"]["acc"], f"layer {l} qkv acc")
+    assert_equal(sel(g["qkv"]), ref["qkv"]["y"], f"layer {l} qkv")
+    assert_equal(sel(g["codes_attn"]), ref["o"]["q"], f"layer {l} attn_sub_norm codes")
+    assert_equal(sel(g["acc_o"]), ref["o"]["acc"], f"layer {l} o acc")
+    assert_equal(sel(g["h"]), ref["h"], f"layer {l} h")
+    assert_equal(sel(g["codes_post"]), ref["gu"]["q"], f"layer {l} post-norm codes")
+    assert_equal(sel(g["acc_gate_up"]), ref["gu"]["acc"], f"layer {l} gate|up acc")
+    assert_equal(sel(g["codes_ffn"]), ref["down"]["q"], f"layer {l} ffn_sub_norm codes")
+    assert_equal(sel(g["acc_down"]), ref["down"]["acc"], f"layer {l} down acc")
+    deq = g["deq"] if rows is None else g["deq"][:, rows]
+    for j, st in enumerate(("qkv", "o", "gu", "down")):
+        assert_rel(deq[j], ref[st]["deq"], what=f"layer {l} deq {st}")
+    assert_rel(sel(g["x_out"]), ref["x"], what=f"layer {l} output")
+
+
+@pytest.mark.parametrize("m,layers", [(5, 3), (20, 2), (1, 2)])
+def test_decoder_stack_small(m, layers):
+    """Small dims with random gains: H=64 (8 heads of 8), 2 kv heads, I=96."""
+    hdim, inter, nh, nkv, hd = 64, 96, 8, 2, 8
+    note(f"block decoder small m={m} layers={layers}")
+    kvd = nkv * hd
+    x = synth.activations(seed(6, m, 5), m, hdim, 1)
+    gpu_layers, refs = [], []
+    xo = x
+    for l in range(layers):
+        mt = _decoder_layer_mats(6, l, hdim, inter, kvd)
+        gains = {nm: (1.0 + 0.1 * synth.normal_f32(seed(6, l, 30 + i), n)).astype(np.float32)
+                 for i, (nm, n) in enumerate((("n_in", hdim), ("n_attn", hdim), ("n_post", hdim), ("n_ffn", inter)))}
+        ref = oracle.decoder_layer(xo, _oracle_weights(mt, gains), EPS, nh, nkv, hd)
+        refs.append(ref)
+        xo = ref["x"]
+        gpu_layers.append(_gpu_layer(mt, gains))
+    spec = bl.BlockSpec(bl.BLOCK_DECODER, hdim, inter, gpu_layers, nh, nkv, hd, EPS)
+    tr = _trace(layers, m, hdim, inter, hdim + 2 * kvd)
+    y = bl.block_forward(spec, gpu(x), trace=tr)
+    for l in range(layers):
+        _compare_layer(tr, l, refs[l])
+    assert_rel(host(y), xo, what="stack output")
+
+
+def test_decoder_stack_30_layers():
+    """30 layers at the 2B4T shapes (H 2560, I 6912, 20 / 5 heads of 128, gains 1):
+    M = 1 in full, and 3 sampled tokens of M = 64, all from the same weights."""
+    hdim, inter, nh, nkv, hd, layers = 2560, 6912, 20, 5, 128, 30
+    kvd = nkv * hd
+    note("block decoder 30 layers, M=1 and M=64")
+    x1 = synth.activations(seed(5, 1, 5), 1, hdim)
+    x64 = synth.activations(seed(5, 64, 5), 64, hdim)
+    samples = np.array([0, 37, 63])
+    xo = np.concatenate([x1, x64[samples]])
+    gpu_layers, refs = [], []
+    for l in range(layers):
+        mt = _decoder_layer_mats(5, l, hdim, inter, kvd)
+        gpu_layers.append(_gpu_layer(mt, None))
+        ref = oracle.decoder_layer(xo, _oracle_weights(mt, None), EPS, nh, nkv, hd)
+        refs.append(ref)
+        xo = ref["x"]
+        del mt
+    spec = bl.BlockSpec(bl.BLOCK_DECODER, hdim, inter, gpu_layers, nh, nkv, hd, EPS)
+    tr = _trace(layers, 1, hdim, inter, hdim + 2 * kvd)
+    y1 = bl.block_forward(spec, gpu(x1), trace=tr)
+    for l in range(layers):
+        _compare_layer(tr, l, {k: _rows(v, [0]) for k, v in refs[l].items()})
+    assert_rel(host(y1), xo[:1], what="M=1 output")
+    y64 = bl.block_forward(spec, gpu(x64))
+    assert_rel(host(y64)[samples], xo[1:], what="M=64 sampled outputs")
+
+
+def _rows(v, rows):
+    if isinstance(v, dict):
+        return {k: _rows(a, rows) for k, a in v.items()}
+    return v[rows]
