@@ -161,14 +161,17 @@ def test_forward_single_layer():
 
 
 RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 16), (257, 129, 2576),
-          (16, 16, 16), (2, 33, 4112), (300, 700, 1040)]
+          (16, 16, 16), (2, 33, 4112), (300, 700, 1040),
+          # shapes the pipelined kernel takes (N % 128 == 0, K % 128 == 0): every tile
+          # variant, K-chunk counts 1, 2, 3, 5, 9 and M not a multiple of the tile
+          (130, 512, 256), (65, 384, 384), (40, 768, 640), (333, 1280, 1152), (20, 256, 128), (257, 2560, 2560)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED)
 def test_forward_ragged(m, n, k):
     note(f"forward ragged m={m} n={n} k={k}")
     x = _edge_rows(synth.activations(seed(5, m, k), m, k, 1 if k >= 100 else 0))
-    n1 = n // 3 + 1
+    n1 = n // 3 + 1 if n % 128 else n // 2
     mats = [Matrix(n1, k, seed(5, n, 1)), Matrix(n - n1, k, seed(5, n, 2), sigma=0.05)]
     paths = [bl.PATH_PREFILL] + ([bl.PATH_DECODE] if m <= 16 else [])
     ys = [host(_check_forward(x, mats, p, f"path {p}")) for p in paths]
