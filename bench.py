@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device-to-device copy (outside the timed region) whose known size scales "
+                         "the HBM byte counters of a profiler run")
     return ap.parse_args()
 
 
@@ -132,6 +135,14 @@ def main():
            "down")
 
     ops = [("quant_x", q1), ("gemm_gate_up", f_gu), ("quant_relu2_subnorm", q2), ("gemm_down", f_d)]
+
+    if args.calibrate_copy:
+        src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.add(src, 1.0, out=dst)  # one elementwise kernel: reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration kernel: 268435456 bytes read, 268435456 bytes written")
 
     # ---------------------------------------------------------------- prefill step
     log(f"prefill: warmup {args.warmup}, steps {args.steps}")

@@ -81,6 +81,9 @@ bitlinear_status check_segments(const float *gamma, const int64_t *seg_end, int3
     ep->seg_end[s] = s < n_seg ? (int32_t)seg_end[s] : (int32_t)n;
   }
   ep->n_seg = n_seg;
+  ep->blocks32 = 1;
+  for (int s = 0; s < n_seg; ++s)
+    if (seg_end[s] % 32) ep->blocks32 = 0;
   return BITLINEAR_OK;
 }
 

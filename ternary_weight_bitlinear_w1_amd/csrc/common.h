@@ -19,6 +19,7 @@ struct Epilogue {
   float gamma[BITLINEAR_MAX_SEGMENTS];
   int32_t seg_end[BITLINEAR_MAX_SEGMENTS];
   int32_t n_seg;
+  int32_t blocks32;  // every segment end is a multiple of 32: gamma is constant per 32 columns
 };
 
 __device__ __forceinline__ float epi_gamma(const Epilogue &ep, int n) {

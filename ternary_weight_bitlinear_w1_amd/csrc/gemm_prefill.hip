@@ -32,6 +32,7 @@ namespace bl {
 namespace {
 
 typedef int v4i_u __attribute__((ext_vector_type(4), aligned(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 128;
 constexpr int kLda = kBK + 16;
@@ -193,6 +194,16 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
 constexpr int kStages = 3;
+
+// Tile of the large-M kernel: waves in M, waves in N, 32x32 tiles per wave in M
+// and N (tuned on MI355X; overridable when building variants to sweep).
+#ifndef BL_GEMM_SGB
+#define BL_GEMM_SGB 0
+#endif
+#ifndef BL_GEMM_BIG_CFG
+#define BL_GEMM_BIG_CFG 2, 2, 2, 4
+#define BL_GEMM_BIG_BN 256
+#endif
 constexpr int kGroupM = 4;
 
 // 16-byte global -> LDS copy: lane l's 16 bytes go to LDS byte address
@@ -219,6 +230,37 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// 4-byte global -> LDS copy (lane l's dword lands at lds_base + 4 l).
+__device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(src), "s"(lds_base)
+      : "memory", "m0");
+}
+
+// Persistent form: gridDim.x workgroups (two per CU) walk the tiles
+// t = blockIdx.x, blockIdx.x + gridDim.x, ... and the three-stage ring runs on
+// across tile boundaries, so the next tile's loads and MFMAs overlap the
+// previous tile's stores.
+//
+// The MFMA takes the unpacked weights as its A operand and the activation
+// codes as its B operand, so a lane's accumulators hold 4 consecutive output
+// features of one token and the epilogue stores them as one 16-byte store.
+// Rows past M are clamped to M - 1 for loading and storing: every lane then
+// computes and stores row M - 1's own value, which keeps the number of store
+// instructions the same on every wave.
+//
+// Waiting: vector memory operations of a wave complete in issue order, so
+// "at most X outstanding" waits exactly for everything older than the X most
+// recent. Per wave and step c the operations younger than chunk c are chunk
+// c + 1's loads, and, in the first two steps of a tile, the previous tile's
+// row-data load (one per wave) and its kStores output stores; X is set to
+// that count (or 0 when an acc_out copy doubles the stores past the counter).
+// Per-token deq / row sums go through a small double-buffered LDS area loaded
+// with the same global->LDS copy, one instruction per wave per tile.
 template <int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8_t *__restrict__ A,
                                                                       const uint8_t *__restrict__ B,
@@ -232,148 +274,234 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   constexpr int kAStage = BM * 128, kBStage = BN * 32, kStage = kAStage + kBStage;
   constexpr int LA = BM / 8 / NW;   // 1 KB activation loads per wave per chunk
   constexpr int LB = BN / 32 / NW;  // 1 KB weight loads per wave per chunk
+  constexpr int kStores = TM * TN * 4;  // 16-byte output stores per wave per tile
+  constexpr int kRowOps = BM / 32;      // 64-dword row-data loads per tile (deq, then row sums)
   static_assert(LA * NW * 8 == BM && LB * NW * 32 == BN, "tile must split into 1 KB wave loads");
-  // one array per stage, so that the compiler can tell a stage being read from
-  // the stages whose loads are still in flight
-  __shared__ __attribute__((aligned(1024))) int8_t st0[kStage];
-  __shared__ __attribute__((aligned(1024))) int8_t st1[kStage];
-  __shared__ __attribute__((aligned(1024))) int8_t st2[kStage];
+  static_assert(kRowOps <= NW && kRowOps >= 2, "one row-data load per wave");
+  constexpr int kWaitSteady = LA + LB;
+  constexpr int kWaitAfterTile = LA + LB + 1 + kStores;
+  static_assert(kWaitAfterTile < 64, "vmcnt range");
+  static_assert(NW * 32 * 32 * 4 <= kStage, "epilogue scratch must fit in one stage");
+  __shared__ __attribute__((aligned(1024))) int8_t ring[kStages * kStage];
+  __shared__ __attribute__((aligned(256))) float s_deq[2][BM];
+  __shared__ __attribute__((aligned(256))) int s_rs[2][BM];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
-  // ---- tile index: XCD-contiguous ranges, grouped along M
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   const int T = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  if ((T & 7) == 0) bid = (bid & 7) * (T >> 3) + (bid >> 3);
-  const int per_group = kGroupM * tiles_n;
-  const int group = bid / per_group, first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = bid - group * per_group;
-  const int m0 = (first_m + in_group % gsize) * BM;
-  const int n0 = (in_group / gsize) * BN;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int my_tiles = (T - b + G - 1) / G;
   const int64_t ldb = K >> 2;
   const int nk = K >> 7;
+  const int total = my_tiles * nk;
+  const bool two_stores = acc_out != nullptr;
 
-  // ---- per-lane load sources (chunk 0); chunk kc adds 128 kc (A) / 32 kc (B)
-  const int8_t *a_src[LA];
-#pragma unroll
-  for (int j = 0; j < LA; ++j) {
-    const int r = 8 * (wave * LA + j) + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int row = min(m0 + r, M - 1);
-    a_src[j] = A + (int64_t)row * K + 16 * c;
-  }
-  const uint8_t *b_src[LB];
-#pragma unroll
-  for (int j = 0; j < LB; ++j) {
-    const int r = 32 * (wave * LB + j) + (lane >> 1);
-    const int h = (lane & 1) ^ ((r >> 3) & 1);
-    b_src[j] = B + (int64_t)(n0 + r) * ldb + 16 * h;
-  }
-  auto issue = [&](int8_t *st, int kc) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st) + wave * 1024 * (LA + 0));
-#pragma unroll
-    for (int j = 0; j < LA; ++j) copy16_to_lds(a_src[j] + 128 * kc, base + j * 1024);
-    const uint32_t bbase = __builtin_amdgcn_readfirstlane(lds_addr(st + kAStage) + wave * 1024 * LB);
-#pragma unroll
-    for (int j = 0; j < LB; ++j) copy16_to_lds(b_src[j] + 32 * kc, bbase + j * 1024);
+  // tile i of this workgroup -> (m0, n0): XCD-contiguous ranges, grouped along M
+  auto coords = [&](int i, int &m0, int &n0) {
+    int t = b + i * G;
+    if ((T & 7) == 0 && (G & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+    const int per_group = kGroupM * tiles_n;
+    const int group = t / per_group, first_m = group * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    const int in_group = t - group * per_group;
+    m0 = (first_m + in_group % gsize) * BM;
+    n0 = (in_group / gsize) * BN;
   };
 
-  v16i acc[TM][TN];
+  // ---- issue side: the chunk stream (tile is_i, chunk is_kc)
+  int is_i = 0, is_kc = 0, is_m0, is_n0;
+  coords(0, is_m0, is_n0);
+  // per-lane source offsets of the current issue tile (32-bit: M K and N K / 4
+  // stay below 2^31 for every shape the host passes)
+  uint32_t a_off[LA], b_off[LB];
+  auto set_src = [&]() {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < LA; ++j) {
+      const int r = 8 * (wave * LA + j) + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int row = min(is_m0 + r, M - 1);
+      a_off[j] = (uint32_t)row * (uint32_t)K + 16u * c;
+    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < LB; ++j) {
+      const int r = 32 * (wave * LB + j) + (lane >> 1);
+      const int h = (lane & 1) ^ ((r >> 3) & 1);
+      b_off[j] = (uint32_t)(is_n0 + r) * (uint32_t)ldb + 16u * h;
+    }
+  };
+  set_src();
+  auto issue_chunk = [&](int8_t *st) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st) + wave * 1024 * LA);
+#pragma unroll
+    for (int j = 0; j < LA; ++j) copy16_to_lds(A + a_off[j] + 128 * is_kc, base + j * 1024);
+    const uint32_t bbase = __builtin_amdgcn_readfirstlane(lds_addr(st + kAStage) + wave * 1024 * LB);
+#pragma unroll
+    for (int j = 0; j < LB; ++j) copy16_to_lds(B + b_off[j] + 32 * is_kc, bbase + j * 1024);
+    if (++is_kc == nk) {
+      is_kc = 0;
+      if (++is_i < my_tiles) {
+        coords(is_i, is_m0, is_n0);
+        set_src();
+      }
+    }
+  };
+  // per-token deq and row sums of tile i into buffer i & 1: wave w loads part
+  // (w % kRowOps) of [deq (BM/64 parts) | row sums (BM/64 parts)]
+  auto issue_rows = [&](int i) {
+    int m0, n0;
+    coords(i, m0, n0);
+    const int op = wave % kRowOps, part = op % (kRowOps / 2);
+    const int row = min(m0 + part * 64 + lane, M - 1);
+    if (op < kRowOps / 2)
+      copy4_to_lds(deq + row, __builtin_amdgcn_readfirstlane(lds_addr(&s_deq[i & 1][part * 64])));
+    else
+      copy4_to_lds(rowsum + row, __builtin_amdgcn_readfirstlane(lds_addr(&s_rs[i & 1][part * 64])));
+  };
+
+  v16i acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0;
 
+  // One chunk: the packed weights of the chunk and the codes of k-step 0 are
+  // read first; the codes of k-step s + 1 are read while k-step s's MFMAs run.
   auto compute = [&](const int8_t *sa) {
     const int8_t *sb = sa + kAStage;
+    auto read_codes = [&](int s, v4i *af) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int r = (wm * TM + tm) * 32 + l32;
+        af[tm] = *reinterpret_cast<const v4i *>(sa + r * 128 + 16 * ((4 * half + s) ^ ((r >> 1) & 7)));
+      }
+    };
     v4i bp[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       const int r = (wn * TN + tn) * 32 + l32;
       bp[tn] = *reinterpret_cast<const v4i *>(sb + r * 32 + 16 * (half ^ ((r >> 3) & 1)));
     }
-    v4i af[4][TM];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int r = (wm * TM + tm) * 32 + l32;
-        af[s][tm] = *reinterpret_cast<const v4i *>(sa + r * 128 + 16 * ((4 * half + s) ^ ((r >> 1) & 7)));
-      }
+    v4i af[2][TM];
+    read_codes(0, af[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s < 3) read_codes(s + 1, af[(s + 1) & 1]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const v4i bo = unpack16((uint32_t)bp[tn][s]);
+        const v4i wo = unpack16((uint32_t)bp[tn][s]);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
-          acc[tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s][tm], bo, acc[tm][tn], 0, 0, 0);
+          acc[tn][tm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wo, af[s & 1][tm], acc[tn][tm], 0, 0, 0);
       }
+#if BL_GEMM_SGB
+      // next k-step's reads first, then unpack and MFMAs interleaved
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x0100, TM, 0);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        __builtin_amdgcn_sched_group_barrier(0x0002, 7, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0008, TM, 0);
+      }
+#endif
     }
   };
-  // One K chunk: wait for this thread's loads of chunk kc (those of kc + 1 may
-  // stay in flight), meet the other waves (their loads of kc have landed and
-  // they are done reading chunk kc - 1's stage), refill that stage with chunk
-  // kc + 2, then compute. The barrier carries no memory fence: the loads are
-  // ordered by the explicit vmcnt wait, and each wave's LDS reads have been
-  // consumed by its MFMAs before it reaches the next barrier.
-  auto step = [&](int8_t *cur, int8_t *refill, int kc) {
-    if (kc + 1 < nk)
-      wait_vm<LA + LB>();
-    else
-      wait_vm<0>();
+
+  // ---- compute side
+  int c_i = 0, c_kc = 0, c_m0, c_n0;
+  coords(0, c_m0, c_n0);
+  // Output of one tile. The stage just consumed serves as scratch: after a
+  // barrier (every wave is done reading it) each wave writes one 32 x 32 fp32
+  // block at a time in its accumulator layout and reads it back so that one
+  // store instruction covers 8 rows x 128 contiguous bytes. Row r's 16-byte
+  // piece c sits at piece c ^ ((r >> 1) & 7), so both the writes (16 rows, one
+  // piece) and the reads (2 rows, all pieces) of 16 lanes hit distinct banks.
+  auto epilogue = [&](int8_t *scratch_stage) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kc + 2 < nk) issue(refill, kc + 2);
-    compute(cur);
-  };
-
-  issue(st0, 0);
-  if (nk > 1) issue(st1, 1);
-  int kc = 0;
-  for (; kc + 3 <= nk; kc += 3) {
-    step(st0, st2, kc);
-    step(st1, st0, kc + 1);
-    step(st2, st1, kc + 2);
-  }
-  if (kc < nk) step(st0, st2, kc);
-  if (kc + 1 < nk) step(st1, st0, kc + 1);
-
-  // ---- epilogue: row data through LDS, then undo the field offset, rescale, store
-  __syncthreads();
-  float *s_deq = reinterpret_cast<float *>(st0);
-  int *s_rs = reinterpret_cast<int *>(st0 + BM * 4);
-  for (int i = threadIdx.x; i < BM; i += NW * 64) {
-    const int m = min(m0 + i, M - 1);
-    s_deq[i] = deq[m];
-    s_rs[i] = rowsum[m];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int n = n0 + (wn * TN + tn) * 32 + l32;
-    const float g = epi_gamma(ep, n);
+    float *sc = reinterpret_cast<float *>(scratch_stage) + wave * (32 * 32);
+    const float *sd = s_deq[c_i & 1];
+    const int *sr = s_rs[c_i & 1];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
+      const int mb = (wm * TM + tm) * 32;
+      const int ml = mb + l32;
+      const int rs = sr[ml];
+      const float dq = sd[ml];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int rl = (wm * TM + tm) * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
-        const int m = m0 + rl;
-        if (m < M) {
-          const int a = acc[tm][tn][q] - s_rs[rl];
-          const int64_t o = (int64_t)m * N + n;
-          if (acc_out) acc_out[o] = a;
-          __builtin_nontemporal_store(rescale(a, s_deq[rl], g), Y + o);
+      for (int tn = 0; tn < TN; ++tn) {
+        const int nb = c_n0 + (wn * TN + tn) * 32;
+        const float gb = epi_gamma(ep, nb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int nl = 8 * j + 4 * half;
+          const int a0 = acc[tn][tm][4 * j] - rs, a1 = acc[tn][tm][4 * j + 1] - rs;
+          const int a2 = acc[tn][tm][4 * j + 2] - rs, a3 = acc[tn][tm][4 * j + 3] - rs;
+          if (two_stores) {
+            const int m = min(c_m0 + ml, M - 1);
+            *reinterpret_cast<v4i *>(acc_out + (int64_t)m * N + nb + nl) = v4i{a0, a1, a2, a3};
+          }
+          const int n = nb + nl;
+          v4f v;
+          if (ep.blocks32) {
+            v = v4f{rescale(a0, dq, gb), rescale(a1, dq, gb), rescale(a2, dq, gb), rescale(a3, dq, gb)};
+          } else {
+            v = v4f{rescale(a0, dq, epi_gamma(ep, n)), rescale(a1, dq, epi_gamma(ep, n + 1)),
+                    rescale(a2, dq, epi_gamma(ep, n + 2)), rescale(a3, dq, epi_gamma(ep, n + 3))};
+          }
+          *reinterpret_cast<v4f *>(sc + l32 * 32 + 4 * ((nl >> 2) ^ ((l32 >> 1) & 7))) = v;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[tn][tm][q] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * i + (lane >> 3);
+          const v4f v = *reinterpret_cast<const v4f *>(sc + r * 32 + 4 * ((lane & 7) ^ ((r >> 1) & 7)));
+          const int m = min(c_m0 + mb + r, M - 1);
+          __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(Y + (int64_t)m * N + nb + 4 * (lane & 7)));
         }
       }
     }
+  };
+
+  auto meet = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  issue_rows(0);
+  issue_chunk(ring);
+  if (total > 1) issue_chunk(ring + kStage);
+  int stage = 0;  // ring slot of chunk c
+  int c = 0;
+  for (; c_i < my_tiles;) {
+    for (int kc = 0; kc < nk; ++kc, ++c) {
+      // wait for this wave's loads of chunk c: everything but the operations
+      // issued after them (see the note above the kernel)
+      if (c + 1 >= total || nk <= 2)
+        wait_vm<0>();
+      else if (c_i > 0 && kc <= 1)
+        two_stores ? wait_vm<0>() : wait_vm<kWaitAfterTile>();
+      else
+        wait_vm<kWaitSteady>();
+      meet();
+      if (c + 2 < total) issue_chunk(ring + (stage == 0 ? 2 : stage - 1) * kStage);
+      compute(ring + stage * kStage);
+      stage = stage == 2 ? 0 : stage + 1;
+    }
+    if (c_i + 1 < my_tiles) issue_rows(c_i + 1);
+    if (nk <= 2) {
+      // with so few chunks the row data may still be in flight
+      wait_vm<0>();
+      meet();
+    }
+    epilogue(ring + (stage == 0 ? 2 : stage - 1) * kStage);
+    if (++c_i < my_tiles) coords(c_i, c_m0, c_n0);
   }
 }
 
@@ -387,13 +515,27 @@ hipError_t launch_generic(const int8_t *codes, const uint8_t *packed, const floa
   return hipGetLastError();
 }
 
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int WM, int WN, int TM, int TN>
 hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
                             int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * (n / BN);
+  int64_t grid = 2 * (int64_t)cu_count();  // two workgroups fit per CU
+  if (grid > tiles) grid = tiles;
   gemm_prefill_kernel<WM, WN, TM, TN>
-      <<<dim3((unsigned)tiles), dim3(WM * WN * 64), 0, stream>>>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out);
+      <<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out);
   return hipGetLastError();
 }
 
@@ -405,6 +547,8 @@ hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const
   if (m == 0 || n == 0) return hipSuccess;
   const int M = (int)m, N = (int)n, K = (int)k;
   if (K % 128 == 0) {
+    if (N % BL_GEMM_BIG_BN == 0 && M > 64)
+      return launch_pipelined<BL_GEMM_BIG_CFG>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
     if (N % 256 == 0 && M > 64)
       return launch_pipelined<2, 2, 2, 4>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
     if (N % 128 == 0 && M > 64)
