@@ -1,25 +1,28 @@
 // Decode contraction (m <= 16 tokens): stream the packed ternary weights once
-// from HBM and contract them with the int8 codes on gfx950 int8 MFMA
-// (v_mfma_i32_16x16x64_i8). Same result as the prefill kernel:
-// y[m][n] = fl32(fl32((float)acc * deq[m]) * gamma(n)), acc exact in int32
-// (nnterp "BitNet b1.58" page, "The projections quantize their inputs and
+// from HBM and contract them with the int8 codes. Same result as the prefill
+// kernel: y[m][n] = fl32(fl32((float)acc * deq[m]) * gamma(n)), acc exact in
+// int32 (nnterp "BitNet b1.58" page, "The projections quantize their inputs and
 // weights" and "The two checkpoints"; no bias: model card "Model Details").
 //
 // This path is bound by HBM bandwidth on the packed weights (n * k / 4 bytes);
-// the codes (m * k bytes) stay in L2.
+// the codes (m * k bytes) stay in L2. Two kernels:
 //
-// A workgroup of NW waves owns RT tiles of 16 output rows and splits K into NW
-// contiguous slices, one per wave. A "superstep" is 256 k: lane l loads one
-// 16-byte piece of row (l % 16) of the tile, covering k-blocks 4 (l / 16) .. +3,
-// so the 4 lanes of a row read 64 contiguous bytes and a wave-wide load moves
-// 16 rows x 64 bytes. Each packed dword (16 weights) unpacks with one shift and
-// one AND per 4 weights into exactly the lane's 16-byte MFMA operand; MFMA t of
-// the superstep uses dword t. MFMA operand convention (checked on gfx950):
-// lane l supplies row l % 16 of A and column l % 16 of B, both for k-block
-// l / 16; output lane l, register r holds row 4 (l / 16) + r, column l % 16.
-// Here A rows are tokens (rows >= m are zero) and B columns are output rows.
-// The NW partial tiles are added in LDS (exact integer sums), then the field
-// offset is removed (acc = sum q u - sum q) and the rescale is fused.
+// * one token (gemv_dot4_kernel): coalesced lines, v_dot4, cross-lane sums;
+//   described above the kernel.
+// * several tokens (gemv_decode_kernel, int8 MFMA v_mfma_i32_16x16x64_i8): a
+//   workgroup of NW waves owns RT tiles of 16 output rows and splits K into NW
+//   contiguous slices, one per wave. A "superstep" is 256 k: lane l loads one
+//   16-byte piece of row (l % 16) of the tile, covering k-blocks 4 (l / 16) ..
+//   +3, so the 4 lanes of a row read 64 contiguous bytes and a wave-wide load
+//   moves 16 rows x 64 bytes. Each packed dword (16 weights) unpacks with one
+//   shift and one AND per 4 weights into exactly the lane's 16-byte MFMA
+//   operand; MFMA t of the superstep uses dword t. MFMA operand convention
+//   (checked on gfx950): lane l supplies row l % 16 of A and column l % 16 of
+//   B, both for k-block l / 16; output lane l, register r holds row
+//   4 (l / 16) + r, column l % 16. Here A rows are tokens (rows >= m are zero)
+//   and B columns are output rows. The NW partial tiles are added in LDS
+//   (exact integer sums), then the field offset is removed
+//   (acc = sum q u - sum q) and the rescale is fused.
 #include "common.h"
 
 namespace bl {
@@ -31,6 +34,12 @@ constexpr uint32_t kFieldMask = 0x03030303u;
 // Launch shape (tuned on MI355X; overridable when building variants to sweep).
 #ifndef BL_GEMV_MIN_WAVES
 #define BL_GEMV_MIN_WAVES 4
+#endif
+#ifndef BL_GEMV_DOT4_MAX_M
+#define BL_GEMV_DOT4_MAX_M 1
+#endif
+#ifndef BL_GEMV_MIN_WGS
+#define BL_GEMV_MIN_WGS 256
 #endif
 #ifndef BL_GEMV_RT1_MAX_M
 #define BL_GEMV_RT1_MAX_M 4
@@ -65,6 +74,22 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
   const int row = lane & 15, kb = lane >> 4;
   const bool has_a = row < M;
   const int64_t ldb = K >> 2;
+
+  // row data of this thread's epilogue elements, fetched with the weights
+  constexpr int kEpi = (RT * 256 + NW * 64 - 1) / (NW * 64);
+  int e_rs[kEpi];
+  float e_dq[kEpi];
+#pragma unroll
+  for (int j = 0; j < kEpi; ++j) {
+    const int e = threadIdx.x + j * NW * 64;
+    const int m = 4 * ((e >> 6) & 3) + (e & 3);
+    e_rs[j] = 0;
+    e_dq[j] = 0.0f;
+    if (e < RT * 256 && m < M) {
+      e_rs[j] = rowsum[m];
+      e_dq[j] = deq[m];
+    }
+  }
 
   v4i b[SPW][RT];
 #pragma unroll
@@ -114,17 +139,20 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][rt][lane][r] = acc[rt][r];
   __syncthreads();
-  for (int e = threadIdx.x; e < RT * 256; e += NW * 64) {
+#pragma unroll
+  for (int j = 0; j < kEpi; ++j) {
+    const int e = threadIdx.x + j * NW * 64;
+    if (e >= RT * 256) break;
     const int rt = e >> 8, l = (e >> 2) & 63, r = e & 3;
     int sum = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) sum += red[w][rt][l][r];
     const int m = 4 * (l >> 4) + r, n = n0 + rt * 16 + (l & 15);
     if (m < M && n < N) {
-      const int acc_v = sum - rowsum[m];
+      const int acc_v = sum - e_rs[j];
       const int64_t o = (int64_t)m * N + n;
       if (acc_out) acc_out[o] = acc_v;
-      Y[o] = rescale(acc_v, deq[m], epi_gamma(ep, n));
+      Y[o] = rescale(acc_v, e_dq[j], epi_gamma(ep, n));
     }
   }
 }
@@ -204,6 +232,134 @@ __global__ __launch_bounds__(NW * 64) void gemv_loop_kernel(const int8_t *__rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few-token kernel (m <= 4, K % 64 == 0, K <= kDot4MaxK): dot-product form.
+//
+// Lane l of a wave reads 16 bytes (64 weights) of row l / 8 at piece l % 8 of
+// each 128-byte line, so every wave-wide load moves 8 full lines. The token
+// codes of the workgroup's K range sit in LDS, where the 8 lanes that share a
+// piece read the same bytes (broadcast). Each packed dword d gives, with one
+// shift and one AND, the four weight bytes (d >> 2j) & 0x03030303 of codes
+// 16g + 4j .. +3, contracted against the matching code dword by v_dot4_i32_i8.
+// The 8 partial sums of a row are added with cross-lane shuffles, the KS
+// waves that split a row's K range through LDS, all in exact integers.
+constexpr int kDot4MaxK = 8192;
+
+template <int MT, int KS, int LPW>
+__global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
+                                                        const float *__restrict__ deq,
+                                                        const int32_t *__restrict__ rowsum, int N, int K, Epilogue ep,
+                                                        float *__restrict__ Y, int32_t *__restrict__ acc_out) {
+  constexpr int RG = 4 / KS;  // row groups of 8 rows per workgroup
+  __shared__ __attribute__((aligned(16))) int8_t sc[MT * kDot4MaxK];
+  __shared__ int red[KS][RG][8][MT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % KS, rg = wave / KS;
+  const int n = blockIdx.x * 8 * RG + rg * 8 + (lane >> 3);
+  const int p = lane & 7;
+  const int ldb = K >> 2;                 // bytes per weight row (multiple of 16)
+  const int L = (ldb + 127) >> 7;         // 128-byte lines per row, the last may be partial
+  const int l_lo = L * ks / KS, l_hi = L * (ks + 1) / KS;
+
+  // weights first: the long pole
+  v4i w[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int off = 128 * (l_lo + i) + 16 * p;
+    w[i] = v4i{0, 0, 0, 0};
+    if (l_lo + i < l_hi && off < ldb && n < N) w[i] = *reinterpret_cast<const v4i *>(B + (int64_t)n * ldb + off);
+  }
+  // this workgroup's token codes into LDS (all K: the waves of a row group
+  // share them, the row groups read the same bytes)
+  for (int i = threadIdx.x; i < MT * (K >> 4); i += 256) {
+    const int t = i / (K >> 4), c = i - t * (K >> 4);
+    *reinterpret_cast<v4i *>(sc + t * kDot4MaxK + 16 * c) = *reinterpret_cast<const v4i *>(A + (int64_t)t * K + 16 * c);
+  }
+  int rs[MT];
+  float dq[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    rs[t] = rowsum[t];
+    dq[t] = deq[t];
+  }
+  __syncthreads();
+
+  int acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = 0;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int k0 = 4 * (128 * (l_lo + i) + 16 * p);  // first code of this piece
+    if (l_lo + i < l_hi && k0 < K) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const v4i *cp = reinterpret_cast<const v4i *>(sc + t * kDot4MaxK + k0);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const v4i c = cp[d];  // codes k0 + 16 d .. + 15
+          const uint32_t wd = (uint32_t)w[i][d];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[t] = __builtin_amdgcn_sdot4((int)((wd >> (2 * j)) & kFieldMask), c[j], acc[t], false);
+        }
+      }
+    }
+  }
+  // 8 lanes per row
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    acc[t] += __shfl_xor(acc[t], 4, 64);
+    acc[t] += __shfl_xor(acc[t], 2, 64);
+    acc[t] += __shfl_xor(acc[t], 1, 64);
+  }
+  if (p == 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[ks][rg][lane >> 3][t] = acc[t];
+  }
+  __syncthreads();
+  if (ks == 0 && p == 0 && n < N) {
+    const float g = epi_gamma(ep, n);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      int sum = 0;
+#pragma unroll
+      for (int q = 0; q < KS; ++q) sum += red[q][rg][lane >> 3][t];
+      const int a = sum - rs[t];
+      const int64_t o = (int64_t)t * N + n;
+      if (acc_out) acc_out[o] = a;
+      Y[o] = rescale(a, dq[t], g);
+    }
+  }
+}
+
+template <int MT>
+hipError_t launch_dot4_mt(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int n,
+                          int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
+  const int lines = ((k >> 2) + 127) >> 7;
+  // split K over the waves of a workgroup until the workgroups cover the CUs
+  const int ks = n / 32 >= BL_GEMV_MIN_WGS ? 1 : (n / 16 >= BL_GEMV_MIN_WGS ? 2 : 4);
+  const int lpw = (lines + ks - 1) / ks;
+  const int rows_per_wg = 8 * (4 / ks);
+  const dim3 grid((unsigned)((n + rows_per_wg - 1) / rows_per_wg)), block(256);
+#define BL_DOT4(KS_, LPW_)                                                                                          \
+  gemv_dot4_kernel<MT, KS_, LPW_><<<grid, block, 0, stream>>>(codes, packed, deq, rowsum, n, k, ep, y, acc_out); \
+  return hipGetLastError()
+  if (ks == 1) {
+    if (lpw <= 4) { BL_DOT4(1, 4); }
+    if (lpw <= 8) { BL_DOT4(1, 8); }
+    BL_DOT4(1, 16);
+  }
+  if (ks == 2) {
+    if (lpw <= 4) { BL_DOT4(2, 4); }
+    if (lpw <= 8) { BL_DOT4(2, 8); }
+    BL_DOT4(2, 16);
+  }
+  if (lpw <= 4) { BL_DOT4(4, 4); }
+  if (lpw <= 8) { BL_DOT4(4, 8); }
+  BL_DOT4(4, 16);
+#undef BL_DOT4
+}
+
 template <int RT, int NW, int SPW>
 hipError_t launch_cfg(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
                       int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
@@ -236,6 +392,14 @@ hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const 
                               int64_t m, int64_t n, int64_t k, const Epilogue &ep, float *y, int32_t *acc_out,
                               hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
+  if (m <= BL_GEMV_DOT4_MAX_M && k % 64 == 0 && k <= kDot4MaxK) {
+    switch (m) {
+      case 1: return launch_dot4_mt<1>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
+      case 2: return launch_dot4_mt<2>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
+      case 3: return launch_dot4_mt<3>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
+      default: return launch_dot4_mt<4>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
+    }
+  }
   if (m > BL_GEMV_RT1_MAX_M)
     return launch_rt<2>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream);
   return launch_rt<1>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream);
