@@ -11,10 +11,12 @@ on the GPU through the C ABI:
 Weights are packed once before timing (the packed-checkpoint mode). ``value``
 is int8 TOPS of the whole step: 2 M N K of both contractions / step time.
 ``roofline`` is the gate|up contraction kernel against dense int8 MFMA peak,
-timed with HIP events on the stream it runs on. ``decode`` reports the
-weight-streaming kernel (M = 1, 4, 16) in packed-weight GB/s against HBM peak,
-each launch reading a different copy of the weights from a ring larger than the
-256 MB last-level cache. ``cpu_baseline`` times the CPU oracle on a bounded
+timed with HIP events on the stream it runs on; its ``traffic`` comes from the
+committed counter profile when the kernel source is unchanged since. ``decode``
+reports the weight-streaming kernel (M = 1, 4, 16) in packed-weight GB/s against
+HBM peak: the mean time per launch over back-to-back launches, each reading a
+different copy of the weights from a ring larger than the 256 MB last-level
+cache. ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same step's tokens.
 """
 from __future__ import annotations
@@ -47,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy (outside the timed region) whose known size scales "
                          "the HBM byte counters of a profiler run")
@@ -187,6 +191,11 @@ def main():
     if not args.no_decode:
         decode = bench_decode(torch, bl, synth, dev, args.decode_reps, packed_gu, gam_gu, packed_d, gam_d)
 
+    # ---------------------------------------------------------------- 30-layer stack
+    stack = None
+    if not args.no_stack:
+        stack = bench_stack(torch, bl, synth, dev, args.stack_steps, max(2, args.warmup // 2))
+
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -210,13 +219,32 @@ def main():
                    "tokens": M, "hidden": H, "intermediate": I, "ops_per_step": ops_gu + ops_d},
         "roofline": {"bound": "mfma", "kernel": "gemm_prefill (gate|up, M=4096 N=13824 K=2560)",
                      "achieved": round(gu_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tops / PEAK_INT8_TOPS, 4), "traffic": None,
-                     "algorithmic_ops_per_launch": ops_gu},
+                     "frac": round(gu_tops / PEAK_INT8_TOPS, 4), "traffic": measured_traffic(),
+                     "algorithmic_ops_per_launch": ops_gu,
+                     "algorithmic_bytes_per_launch": M * H + 2 * I * H // 4 + 4 * M * 2 * I + 8 * M},
         "kernels": kernels,
         "decode": decode,
+        "stack": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic():
+    """HBM-side bytes per gate|up GEMM launch from the committed counter profile
+    (FETCH_SIZE and WRITE_SIZE runs, scaled by a known-size kernel); None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "counters_gemm_prefill_m4096.md")
+    src = os.path.join(ROOT, "ternary_weight_bitlinear_w1_amd", "csrc", "gemm_prefill.hip")
+    try:
+        fields = dict(line.strip().split(": ", 1) for line in open(prof) if ": " in line and line.startswith("    "))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if fields.get("gemm_source_sha256_16") == digest:
+            return int(fields["traffic_bytes_gate_up"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d):
@@ -268,13 +296,78 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
             e1.record(stream)
             torch.cuda.synchronize()
             b2b_us = e0.elapsed_time(e1) / reps * 1e3
-            gbs = nbytes / (us * 1e-6) / 1e9
-            res[f"{name}_m{m}"] = {"us": round(us, 3), "gbs_packed": round(gbs, 1),
-                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "back_to_back_us": round(b2b_us, 3),
+            gbs = nbytes / (b2b_us * 1e-6) / 1e9
+            res[f"{name}_m{m}"] = {"us": round(b2b_us, 3), "gbs_packed": round(gbs, 1),
+                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "single_launch_event_us": round(us, 3),
                                    "packed_bytes": nbytes, "ring_copies": copies}
-            log(f"decode {name} m={m}: {us:.2f} us, {gbs:.0f} GB/s (back-to-back {b2b_us:.2f} us)")
+            log(f"decode {name} m={m}: {b2b_us:.2f} us/launch back-to-back, {gbs:.0f} GB/s "
+                f"(one launch between events: {us:.2f} us)")
         del ring
         torch.cuda.empty_cache()
+    return res
+
+
+STACK_LAYERS, STACK_HEADS, STACK_KV_HEADS, STACK_HEAD_DIM = 30, 20, 5, 128
+
+
+def bench_stack(torch, bl, synth, dev, steps, warmup):
+    """One step of the 30-layer decoder projection stack of the 2B4T shapes
+    (q|k|v, self-only attention, o, gate|up, ReLU^2, down, residuals; gains 1)
+    through bitlinear_block_forward at M = 1 and M = 64. Reports the step time
+    and the packed-weight bytes of the step per second."""
+    kvd = STACK_KV_HEADS * STACK_HEAD_DIM
+    shapes = [(H, H), (kvd, H), (kvd, H), (H, H), (I, H), (I, H), (H, I)]
+    log(f"stack: packing {STACK_LAYERS} layers")
+    layers, packed_bytes, weights = [], 0, 0
+    for l in range(STACK_LAYERS):
+        p, g = [], []
+        for t, (n, k) in enumerate(shapes):
+            w = torch.from_numpy(synth.weights(synth.stream_seed(BASE_SEED, 5, l, 10 + t), n, k)).to(dev)
+            pk, gm = bl.quantize_weights(w)
+            p.append(pk)
+            g.append(float(np.float32(gm.item())))
+            packed_bytes += pk.numel()
+            weights += n * k
+            del w
+        layers.append(bl.LayerWeights(qkv=torch.cat(p[0:3]), qkv_gamma=g[0:3], o=p[3], o_gamma=g[3],
+                                      gate_up=torch.cat(p[4:6]), gate_up_gamma=g[4:6], down=p[6], down_gamma=g[6]))
+        del p
+    spec = bl.BlockSpec(bl.BLOCK_DECODER, H, I, layers, STACK_HEADS, STACK_KV_HEADS, STACK_HEAD_DIM, 1e-5)
+    blk, keep = spec.to_c()
+    L = bl.lib()
+    stream = torch.cuda.current_stream(dev)
+    res = {"layers": STACK_LAYERS, "weights": weights, "packed_bytes": packed_bytes}
+    for m in (1, 64):
+        x = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 5, m, 5), m, H)).to(dev)
+        y = torch.empty_like(x)
+        nb = int(L.bitlinear_block_workspace_bytes(bl.ctypes.byref(blk), m))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            st = L.bitlinear_block_forward(bl.ctypes.byref(blk), x.data_ptr(), m, y.data_ptr(), None, ws.data_ptr(),
+                                           nb, stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"block forward: {bl.status_name(st)} {L.bitlinear_last_error().decode()}")
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        ms = float(np.median(t))
+        gbs = packed_bytes / (ms * 1e-3) / 1e9
+        ops = 2.0 * m * weights
+        res[f"m{m}"] = {"ms_per_step": round(ms, 4), "p10_ms": round(t[len(t) // 10], 4),
+                        "p90_ms": round(t[(9 * len(t)) // 10], 4), "gbs_packed": round(gbs, 1),
+                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "tops": round(ops / (ms * 1e-3) / 1e12, 2)}
+        log(f"stack m={m}: {ms:.3f} ms/step, {gbs:.0f} GB/s packed, {ops / (ms * 1e-3) / 1e12:.1f} TOPS")
+        del x, y, ws
+    del keep, layers
     return res
 
 
