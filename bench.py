@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--stack-only", action="store_true", help="run only the 30-layer stack leg (no JSON line)")
     ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy (outside the timed region) whose known size scales "
@@ -77,6 +78,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bl.lib()  # fails loudly if the HIP library is missing
+    if args.stack_only:
+        log(json.dumps(bench_stack(torch, bl, synth, dev, args.stack_steps, max(2, args.warmup // 2))))
+        return
 
     def seed(layer, tensor):
         return synth.stream_seed(BASE_SEED, 4, layer, tensor)
@@ -345,28 +349,53 @@ def bench_stack(torch, bl, synth, dev, steps, warmup):
 
         def step():
             st = L.bitlinear_block_forward(bl.ctypes.byref(blk), x.data_ptr(), m, y.data_ptr(), None, ws.data_ptr(),
-                                           nb, stream.cuda_stream)
+                                           nb, torch.cuda.current_stream(dev).cuda_stream)
             if st != 0:
                 raise RuntimeError(f"block forward: {bl.status_name(st)} {L.bitlinear_last_error().decode()}")
 
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in ev:
-            a.record(stream)
+        eager = y.clone()
+
+        def timed(run):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            t0 = time.perf_counter()
+            for a, b in ev:
+                a.record(stream)
+                run()
+                b.record(stream)
+            torch.cuda.synchronize()
+            host_ms = (time.perf_counter() - t0) * 1e3 / steps
+            return sorted(a.elapsed_time(b) for a, b in ev), host_ms
+
+        t_eager, host_eager = timed(step)
+        # the same step captured once into a HIP graph and replayed: one host
+        # call per step instead of one per kernel
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
             step()
-            b.record(stream)
         torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in ev)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, eager):
+            raise RuntimeError(f"stack m={m}: graph replay differs from the eager step")
+        t_graph, host_graph = timed(graph.replay)
+        if not torch.equal(y, eager):
+            raise RuntimeError(f"stack m={m}: graph replay differs from the eager step")
+        t = t_graph
         ms = float(np.median(t))
         gbs = packed_bytes / (ms * 1e-3) / 1e9
         ops = 2.0 * m * weights
         res[f"m{m}"] = {"ms_per_step": round(ms, 4), "p10_ms": round(t[len(t) // 10], 4),
                         "p90_ms": round(t[(9 * len(t)) // 10], 4), "gbs_packed": round(gbs, 1),
-                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "tops": round(ops / (ms * 1e-3) / 1e12, 2)}
-        log(f"stack m={m}: {ms:.3f} ms/step, {gbs:.0f} GB/s packed, {ops / (ms * 1e-3) / 1e12:.1f} TOPS")
-        del x, y, ws
+                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "tops": round(ops / (ms * 1e-3) / 1e12, 2),
+                        "eager_ms_per_step": round(float(np.median(t_eager)), 4),
+                        "eager_host_ms_per_step": round(host_eager, 4)}
+        log(f"stack m={m}: graph {ms:.3f} ms/step, {gbs:.0f} GB/s packed, {ops / (ms * 1e-3) / 1e12:.1f} TOPS; "
+            f"eager {np.median(t_eager):.3f} ms/step (host {host_eager:.3f} ms/step)")
+        del graph, x, y, ws
     del keep, layers
     return res
 

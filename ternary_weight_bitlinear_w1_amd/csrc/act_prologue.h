@@ -1,0 +1,248 @@
+// Per-token activation quantization of one row by a 256-thread workgroup:
+// the prologue transforms of a BitNet b1.58 block, the max |v|, the fp64 sum
+// of squares, the int8 codes and their row sum. Shared by the standalone
+// quantization kernel and by the decode contraction that quantizes its own
+// input, so that both produce the same codes and the same deq bit for bit.
+//
+// Codes: round(v * 127 / max|v|), half to even, in [-127, 127]; deq = max|v| / 127
+// (nnterp "BitNet b1.58" page, "The projections quantize their inputs and
+// weights"; model card "Model Details": 8-bit absmax per token).
+// RMSNorm prologues ("The block, in order"; eps from "Config") keep the codes
+// of v = g * pre and move 1 / sqrt(mean(pre^2) + eps) into deq, since a positive
+// per-token factor cancels inside the rounding ("Scaling inside a sublayer is
+// undone by the sub-norm"). The squared-ReLU prologue forms
+// (max(gate, 0)^2) * up ("The MLP gates with a squared ReLU").
+//
+// Thread t visits float4 f = t, t + 256, ... of the row: pass 1 forms the
+// normed input v (kept in registers when NV > 0), the fp32 max |v| and the fp64
+// sum of squares of the pre-gain input; both are reduced wave-wise, then across
+// the four waves in a fixed order. Pass 2 writes the codes (one 32-bit word per
+// four codes) and their row sum.
+//
+// With NV > 0 the row's loads can be issued on their own (row_load) and used
+// later (row_finish): vector memory operations of a wave complete in issue
+// order, so a caller that also streams other data (the weights of a
+// contraction) issues the row's loads first and waits for them alone. The
+// workgroup barriers here wait for LDS operations only, never for loads still
+// in flight.
+#pragma once
+
+#include "common.h"
+
+namespace bl {
+
+constexpr int kQuantThreads = 256;
+
+typedef ActSrc Src;
+
+// Workgroup barrier that orders LDS traffic only: outstanding global loads
+// keep flowing across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// The raw operands of elements 4f .. 4f+3 of one row, as loaded.
+struct RawIn {
+  float4 a;  // x (or the gate half, or the value head read)
+  float4 b;  // up half (ReLU^2) or second summand (residual)
+  float4 g;  // RMSNorm gain (1 when the gain is absent: multiplying by 1 is exact)
+};
+
+template <int MODE>
+__device__ __forceinline__ RawIn raw_load(const Src &s, int64_t r, int f) {
+  RawIn v;
+  const float *row = s.x + r * s.ld;
+  if constexpr (MODE == ACT_GQA_RMSNORM) {
+    // element e of the attention output reads value head (e / head_dim) / group
+    const int e = 4 * f;
+    const int head = e / s.head_dim, d = e - head * s.head_dim;
+    v.a = *reinterpret_cast<const float4 *>(row + s.gqa_offset + (head / s.group) * s.head_dim + d);
+  } else {
+    v.a = *reinterpret_cast<const float4 *>(row + 4 * f);
+  }
+  if constexpr (MODE == BITLINEAR_ACT_RELU2_RMSNORM) v.b = *reinterpret_cast<const float4 *>(row + s.k + 4 * f);
+  if constexpr (MODE == ACT_RESID_RMSNORM) v.b = *reinterpret_cast<const float4 *>(s.x2 + r * s.ld + 4 * f);
+  if constexpr (MODE != BITLINEAR_ACT_ABSMAX) {
+    // branch-free: without a gain, load x again and use 1
+    const bool has_gain = s.gain != nullptr;
+    const float4 g = *reinterpret_cast<const float4 *>((has_gain ? s.gain : row) + 4 * f);
+    v.g = has_gain ? g : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  }
+  return v;
+}
+
+// pre-norm input from the raw operands (the residual form also stores it)
+template <int MODE>
+__device__ __forceinline__ float4 pre_of(const Src &s, int64_t r, int f, const RawIn &v, bool write_h) {
+  if constexpr (MODE == BITLINEAR_ACT_RELU2_RMSNORM) {
+    float4 o;
+    float t;
+    t = v.a.x > 0.0f ? v.a.x : 0.0f; o.x = __fmul_rn(__fmul_rn(t, t), v.b.x);
+    t = v.a.y > 0.0f ? v.a.y : 0.0f; o.y = __fmul_rn(__fmul_rn(t, t), v.b.y);
+    t = v.a.z > 0.0f ? v.a.z : 0.0f; o.z = __fmul_rn(__fmul_rn(t, t), v.b.z);
+    t = v.a.w > 0.0f ? v.a.w : 0.0f; o.w = __fmul_rn(__fmul_rn(t, t), v.b.w);
+    return o;
+  } else if constexpr (MODE == ACT_RESID_RMSNORM) {
+    float4 o;
+    o.x = __fadd_rn(v.a.x, v.b.x); o.y = __fadd_rn(v.a.y, v.b.y);
+    o.z = __fadd_rn(v.a.z, v.b.z); o.w = __fadd_rn(v.a.w, v.b.w);
+    if (write_h) *reinterpret_cast<float4 *>(s.h_out + r * (int64_t)s.k + 4 * f) = o;
+    return o;
+  } else {
+    return v.a;
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ float4 gain_of(const RawIn &v, float4 p) {
+  if constexpr (MODE != BITLINEAR_ACT_ABSMAX) {
+    p.x = __fmul_rn(v.g.x, p.x); p.y = __fmul_rn(v.g.y, p.y);
+    p.z = __fmul_rn(v.g.z, p.z); p.w = __fmul_rn(v.g.w, p.w);
+  }
+  return p;
+}
+
+__device__ __forceinline__ int code_of(float v, float pre, float s) {
+  float p = __fmul_rn(__fmul_rn(v, pre), s);
+  float r = __builtin_rintf(p);
+  r = r > 127.0f ? 127.0f : r;
+  r = r < -127.0f ? -127.0f : r;
+  return (int)r;
+}
+
+struct RowQuant {
+  float deq;   // dequantization factor of the row's codes
+  int rowsum;  // sum of the row's codes
+};
+
+// The loads of one row held in registers (NV float4 per thread).
+template <int NV>
+struct RowStage {
+  RawIn in[NV];
+};
+
+template <int MODE, int NV>
+__device__ __forceinline__ void row_load(const Src &s, int64_t r, RowStage<NV> &st) {
+  static_assert(NV > 0, "register-resident rows only");
+  const int nf = s.k >> 2;
+  // every lane issues the same NV loads (past the row end it reloads element
+  // 0, unused), so the number of loads in flight is known where they are used
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int f = threadIdx.x + j * kQuantThreads;
+    st.in[j] = raw_load<MODE>(s, r, f < nf ? f : 0);
+  }
+}
+
+// All 256 threads of the workgroup call this for row r; `words` receives the
+// codes (word f = codes 4f .. 4f + 3, low byte first) and may point to LDS or
+// to global memory. The LDS arrays hold the cross-wave partials. Every thread
+// returns the same deq and row sum; words in LDS are visible to the whole
+// workgroup on return. NV = 0 streams the row twice instead of holding it.
+template <int MODE, int NV>
+__device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float eps, const RowStage<(NV > 0 ? NV : 1)> &st,
+                                               int *words, float *red_f, double *red_d, int *red_i) {
+  constexpr bool kRms = MODE != BITLINEAR_ACT_ABSMAX;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nf = s.k >> 2;  // float4 per row
+
+  float4 cache[NV > 0 ? NV : 1];
+  float amax = 0.0f;
+  double ss = 0.0;
+  // ---- pass 1: normed input, max |v|, sum of squares of the pre-gain input
+  auto visit1 = [&](int f, const RawIn &raw) -> float4 {
+    const float4 p = pre_of<MODE>(s, r, f, raw, true);
+    if (kRms) {
+      ss += (double)p.x * (double)p.x;
+      ss += (double)p.y * (double)p.y;
+      ss += (double)p.z * (double)p.z;
+      ss += (double)p.w * (double)p.w;
+    }
+    const float4 v = gain_of<MODE>(raw, p);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    return v;
+  };
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int f = tid + j * kQuantThreads;
+      if (f < nf) cache[j] = visit1(f, st.in[j]);
+    }
+  } else {
+    for (int f = tid; f < nf; f += kQuantThreads) (void)visit1(f, raw_load<MODE>(s, r, f));
+  }
+  amax = wave_max(amax);
+  if (kRms) ss = wave_sum(ss);
+  if (lane == 0) {
+    red_f[wave] = amax;
+    red_d[wave] = ss;
+  }
+  lds_barrier();
+  float a = red_f[0];
+  double sum_sq = red_d[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; ++w) {
+    a = fmaxf(a, red_f[w]);
+    sum_sq += red_d[w];
+  }
+
+  // ---- pass 2: codes
+  int rs = 0;
+  if (a == 0.0f) {
+    for (int f = tid; f < nf; f += kQuantThreads) words[f] = 0;
+  } else {
+    // rows whose max is below 2^-64 are scaled by 2^64 first (exact), which
+    // keeps 127 / a finite and changes no code the unscaled steps reach
+    const float pre = a < 0x1p-64f ? 0x1p64f : 1.0f;
+    const float sc = 127.0f / __fmul_rn(a, pre);
+    auto emit = [&](int f, float4 v) {
+      const int q0 = code_of(v.x, pre, sc), q1 = code_of(v.y, pre, sc);
+      const int q2 = code_of(v.z, pre, sc), q3 = code_of(v.w, pre, sc);
+      rs += q0 + q1 + q2 + q3;
+      words[f] = (q0 & 0xff) | ((q1 & 0xff) << 8) | ((q2 & 0xff) << 16) | ((int)((unsigned)(q3 & 0xff) << 24));
+    };
+    if constexpr (NV > 0) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int f = tid + j * kQuantThreads;
+        if (f < nf) emit(f, cache[j]);
+      }
+    } else {
+      for (int f = tid; f < nf; f += kQuantThreads) {
+        const RawIn raw = raw_load<MODE>(s, r, f);
+        emit(f, gain_of<MODE>(raw, pre_of<MODE>(s, r, f, raw, false)));
+      }
+    }
+  }
+  rs = wave_sum(rs);
+  if (lane == 0) red_i[wave] = rs;
+  lds_barrier();
+  RowQuant out;
+  out.rowsum = 0;
+#pragma unroll
+  for (int w = 0; w < kQuantThreads / 64; ++w) out.rowsum += red_i[w];
+  out.deq = 0.0f;
+  if (a != 0.0f) {
+    if (kRms) {
+      const double ms = sum_sq / (double)s.k;
+      const double rr = sqrt(ms + (double)eps);
+      out.deq = (float)(((double)a / 127.0) / rr);
+    } else {
+      out.deq = a / 127.0f;
+    }
+  }
+  return out;
+}
+
+template <int MODE, int NV>
+__device__ __forceinline__ RowQuant quant_row(const Src &s, int64_t r, float eps, int *words, float *red_f,
+                                              double *red_d, int *red_i) {
+  RowStage<(NV > 0 ? NV : 1)> st;
+  if constexpr (NV > 0) row_load<MODE, NV>(s, r, st);
+  return row_finish<MODE, NV>(s, r, eps, st, words, red_f, red_d, red_i);
+}
+
+}  // namespace bl

@@ -326,6 +326,97 @@ T *at(T *p, int64_t off) {
   return p ? p + off : nullptr;
 }
 
+bl::ActSrc act_src(const float *x, int64_t ld, int64_t k, const float *gain) {
+  bl::ActSrc a;
+  a.x = x;
+  a.x2 = nullptr;
+  a.ld = ld;
+  a.k = (int)k;
+  a.gain = gain;
+  a.gqa_offset = 0;
+  a.head_dim = 1;
+  a.group = 1;
+  a.h_out = nullptr;
+  return a;
+}
+
+// One fused decode projection: quantize the input rows in the prologue,
+// contract, then the plain / residual / ReLU^2 epilogue.
+bitlinear_status fused(int mode, int epi, const bl::ActSrc &src, float eps, int64_t m, const uint8_t *w, int64_t n,
+                       const float *gam, const int64_t *seg, int n_seg, float *y, int32_t *acc, const float *res,
+                       float *out2, float *mi, int8_t *codes_out, float *deq_out, hipStream_t s) {
+  bl::FusedDecode a;
+  a.src = src;
+  a.eps = eps;
+  a.m = (int)m;
+  a.w = w;
+  a.n = (int)n;
+  BL_TRY(check_segments(gam, seg, n_seg, n, &a.ep));
+  a.y = y;
+  a.acc_out = acc;
+  a.res = res;
+  a.out2 = out2;
+  a.mi = mi;
+  a.codes_out = codes_out;
+  a.deq_out = deq_out;
+  return launched(bl::launch_gemv_fused(mode, epi, a, s), "fused decode projection");
+}
+
+// The block chains for a decode step of at most bl::kFusedMaxM tokens: four
+// launches per decoder layer (two for the FFN block), each projection
+// quantizing its own input and applying the block's elementwise step.
+bitlinear_status block_forward_fused(const bitlinear_block *blk, const float *x, int64_t m, float *y,
+                                     const bitlinear_block_trace &tr, const BlockBufs &b, hipStream_t s) {
+  const int64_t H = blk->hidden, I = blk->intermediate;
+  const float eps = blk->eps;
+  const int64_t gu_seg[2] = {I, 2 * I};
+  const int64_t h_seg[1] = {H};
+  float *mi = b.gu;  // [m][I]: ReLU^2(gate) * up
+  if (blk->kind == BITLINEAR_BLOCK_FFN) {
+    const bitlinear_layer &L = blk->layers[0];
+    BL_TRY(fused(BITLINEAR_ACT_ABSMAX, bl::FUSED_EPI_RELU2, act_src(x, H, H, nullptr), eps, m, L.gate_up, 2 * I,
+                 L.gate_up_gamma, gu_seg, 2, tr.gate_up, tr.acc_gate_up, nullptr, nullptr, mi, tr.codes_in, tr.deq,
+                 s));
+    return fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_PLAIN, act_src(mi, I, I, L.ffn_sub_norm_gain), eps, m, L.down,
+                 H, &L.down_gamma, h_seg, 1, y, tr.acc_down, nullptr, nullptr, nullptr, tr.codes_ffn,
+                 at(tr.deq, 3 * m), s);
+  }
+  const int hd = blk->head_dim, group = blk->n_heads / blk->n_kv_heads;
+  const int64_t KV = (int64_t)blk->n_kv_heads * hd, Q = H + 2 * KV;
+  const int64_t qkv_seg[3] = {H, H + KV, Q};
+  const float *xin = x;
+  for (int l = 0; l < blk->n_layers; ++l) {
+    const bitlinear_layer &L = blk->layers[l];
+    const int64_t oH = (int64_t)l * m * H, oI = (int64_t)l * m * I, oQ = (int64_t)l * m * Q;
+    float *dq = at(tr.deq, 4 * m * l);
+    float *qkv = tr.qkv ? tr.qkv + oQ : b.qkv;
+    float *h = tr.h ? tr.h + oH : b.h;
+    float *xnext = tr.x_out ? tr.x_out + oH : (l + 1 == blk->n_layers ? y : b.x);
+    // input_layernorm -> q|k|v
+    BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_PLAIN, act_src(xin, H, H, L.input_norm_gain), eps, m, L.qkv, Q,
+                 L.qkv_gamma, qkv_seg, 3, qkv, at(tr.acc_qkv, oQ), nullptr, nullptr, nullptr, at(tr.codes_in, oH), dq,
+                 s));
+    // self-only attention -> attn_sub_norm -> o_proj; h = x + o
+    bl::ActSrc att = act_src(qkv, Q, H, L.attn_sub_norm_gain);
+    att.gqa_offset = (int)(H + KV);
+    att.head_dim = hd;
+    att.group = group;
+    BL_TRY(fused(bl::ACT_GQA_RMSNORM, bl::FUSED_EPI_RESID, att, eps, m, L.o, H, &L.o_gamma, h_seg, 1, nullptr,
+                 at(tr.acc_o, oH), xin, h, nullptr, at(tr.codes_attn, oH), at(dq, m), s));
+    // post_attention_layernorm -> gate|up -> ReLU^2(gate) * up
+    BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_RELU2, act_src(h, H, H, L.post_attn_norm_gain), eps, m,
+                 L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, at(tr.gate_up, 2 * oI), at(tr.acc_gate_up, 2 * oI),
+                 nullptr, nullptr, mi, at(tr.codes_post, oH), at(dq, 2 * m), s));
+    // ffn_sub_norm -> down; x' = h + down
+    BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_RESID, act_src(mi, I, I, L.ffn_sub_norm_gain), eps, m, L.down,
+                 H, &L.down_gamma, h_seg, 1, nullptr, at(tr.acc_down, oH), h, xnext, nullptr, at(tr.codes_ffn, oI),
+                 at(dq, 3 * m), s));
+    xin = xnext;
+  }
+  if (tr.x_out) return copy_to(y, xin, (size_t)(m * H) * 4, s);
+  return BITLINEAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,6 +450,9 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
 
   const int64_t gu_seg[2] = {I, 2 * I};
   const int64_t h_seg[1] = {H};
+
+  if (bl::fused_decode_supported(m, H) && bl::fused_decode_supported(m, I) && I % 16 == 0)
+    return block_forward_fused(blk, x, m, y, tr, b, s);
 
   if (blk->kind == BITLINEAR_BLOCK_FFN) {
     const bitlinear_layer &L = blk->layers[0];

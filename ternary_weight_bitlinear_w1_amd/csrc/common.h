@@ -83,4 +83,38 @@ hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const 
 // act-quant prologues beyond the public bitlinear_act_mode values
 enum { ACT_RESID_RMSNORM = 16, ACT_GQA_RMSNORM = 17 };
 
+// ---------------------------------------------------------------- fused decode
+// A decode projection that quantizes its own input (decode_fused.hip).
+enum { FUSED_EPI_PLAIN = 0, FUSED_EPI_RESID = 1, FUSED_EPI_RELU2 = 2 };
+constexpr int kFusedMaxM = 4;
+
+struct ActSrc {
+  const float *x;   // input rows, row stride ld
+  const float *x2;  // residual prologue: second operand
+  int64_t ld;
+  int k;            // input features
+  const float *gain;
+  int gqa_offset, head_dim, group;
+  float *h_out;     // residual prologue: receives x + x2 ([m][k]); the fused decode takes no residual prologue
+};
+
+struct FusedDecode {
+  ActSrc src;
+  float eps;
+  int m;               // tokens, 1 .. kFusedMaxM
+  const uint8_t *w;    // packed weights [n][k/4]
+  int n;
+  Epilogue ep;
+  float *y;            // [m][n]: required by the plain form, optional (trace) otherwise
+  int32_t *acc_out;    // [m][n] exact sums, optional
+  const float *res;    // residual form: [m][n] input added to y
+  float *out2;         // residual form: [m][n] res + y
+  float *mi;           // ReLU^2 form: [m][n/2]
+  int8_t *codes_out;   // optional [m][k] codes of the input
+  float *deq_out;      // optional [m]
+};
+
+bool fused_decode_supported(int64_t m, int64_t k);
+hipError_t launch_gemv_fused(int mode, int epi, const FusedDecode &a, hipStream_t stream);
+
 }  // namespace bl

@@ -1,0 +1,228 @@
+// Decode projection that quantizes its own input (m <= 4 tokens).
+//
+// One launch computes, for the tokens of a decode step, the per-token int8
+// codes of the projection's input (with the block's prologue: RMSNorm gain,
+// the self-only attention read of the value heads, or none) and the ternary
+// contraction with its rescale, and applies the block's elementwise epilogue:
+//   plain     y = fl32(fl32((float)acc * deq) * gamma(n))
+//   residual  out2 = fl32(res + y)                 (h = x + o, x' = h + down)
+//   ReLU^2    mi = fl32(fl32(max(g, 0)^2) * u)     (gate and up rows paired)
+// (nnterp "BitNet b1.58" page: "The projections quantize their inputs and
+// weights", "The block, in order", "The MLP gates with a squared ReLU").
+//
+// Each workgroup re-derives the codes of the whole input row with quant_row
+// (act_prologue.h), the same arithmetic as the standalone quantization kernel,
+// so codes and deq equal that kernel's bit for bit; the input is a few KB read
+// from L2, while the weights, issued first, stream from HBM.
+//
+// Contraction as the one-token kernel of gemv_decode.hip: 8 lanes share one
+// weight row and read 16-byte pieces of its 128-byte lines (a wave reads 8
+// rows x 128 contiguous bytes), the fields are expanded with
+// (w >> 2j) & 0x03030303 and fed to v_dot4_i32_i8 against the codes in LDS,
+// and the 8 lanes of a row are summed with xor shuffles. KS waves split the
+// lines of a row; their partial sums are added in LDS in a fixed order.
+// In the ReLU^2 form, workgroup b owns gate rows [b R/2, (b + 1) R/2) and the
+// up rows I + the same range, so it can form its slice of mi itself.
+#include "act_prologue.h"
+
+namespace bl {
+namespace {
+
+constexpr uint32_t kFieldMask = 0x03030303u;
+constexpr int kFusedMaxK = 8192;
+
+// NV: float4 of one input row per thread (K <= 1024 NV). A row has at most
+// 2 NV lines of 128 bytes, so each of the KS waves of a row loads LPW lines.
+template <int MODE, int EPI, int MT, int KS, int NV>
+__global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
+  constexpr int RG = 4 / KS;  // row groups of 8 rows
+  constexpr int R = 8 * RG;   // weight rows per workgroup
+  constexpr int LPW = 2 * NV / KS;
+  __shared__ __attribute__((aligned(16))) int8_t sc[MT * kFusedMaxK];
+  __shared__ int red[KS][RG][8][MT];
+  __shared__ float red_f[4];
+  __shared__ double red_d[4];
+  __shared__ int red_i[4];
+  __shared__ float ybuf[EPI == FUSED_EPI_RELU2 ? MT * R : 1];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % KS, rg = wave / KS;
+  const int r = rg * 8 + (lane >> 3);  // local row
+  const int p = lane & 7;
+  const int N = a.n, K = a.src.k;
+  int n;
+  if constexpr (EPI == FUSED_EPI_RELU2) {
+    const int half = R / 2, inter = N / 2;
+    n = r < half ? blockIdx.x * half + r : inter + blockIdx.x * half + (r - half);
+  } else {
+    n = blockIdx.x * R + r;
+  }
+  const bool valid = n < N;
+  const int ldb = K >> 2;          // bytes per weight row
+  const int L = (ldb + 127) >> 7;  // 128-byte lines per row, the last may be partial
+  const int l_lo = L * ks / KS, l_hi = L * (ks + 1) / KS;
+
+  // Loads in issue order: the first token's input row (a few KB, from L2),
+  // then the weights (from HBM). Loads complete in issue order, so the
+  // quantization of the first token waits for its own row only and runs while
+  // the weights are in flight.
+  RowStage<NV> st;
+  row_load<MODE, NV>(a.src, 0, st);
+  __builtin_amdgcn_sched_barrier(0);
+  // every lane issues LPW loads; pieces past its range reload the first piece
+  // of the matrix and are not used
+  v4i w[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int off = 128 * (l_lo + i) + 16 * p;
+    const bool use = l_lo + i < l_hi && off < ldb && valid;
+    w[i] = *reinterpret_cast<const v4i *>(use ? a.w + (int64_t)n * ldb + off : a.w);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the codes of every token of the step, into LDS
+  RowQuant q[MT];
+  q[0] = row_finish<MODE, NV>(a.src, 0, a.eps, st, reinterpret_cast<int *>(sc), red_f, red_d, red_i);
+#pragma unroll
+  for (int t = 1; t < MT; ++t) {
+    q[t].deq = 0.0f;
+    q[t].rowsum = 0;
+    if (t < a.m)
+      q[t] = quant_row<MODE, NV>(a.src, t, a.eps, reinterpret_cast<int *>(sc + t * kFusedMaxK), red_f, red_d, red_i);
+  }
+  if (blockIdx.x == 0 && a.codes_out) {
+    for (int i = threadIdx.x; i < a.m * (K >> 4); i += 256) {
+      const int t = i / (K >> 4), c = i - t * (K >> 4);
+      *reinterpret_cast<v4i *>(a.codes_out + (int64_t)t * K + 16 * c) =
+          *reinterpret_cast<const v4i *>(sc + t * kFusedMaxK + 16 * c);
+    }
+    if (threadIdx.x == 0 && a.deq_out) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        if (t < a.m) a.deq_out[t] = q[t].deq;
+    }
+  }
+
+  int acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = 0;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int k0 = 4 * (128 * (l_lo + i) + 16 * p);  // first code of this piece
+    if (l_lo + i < l_hi && k0 < K) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if (t < a.m) {
+          const v4i *cp = reinterpret_cast<const v4i *>(sc + t * kFusedMaxK + k0);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const v4i c = cp[d];  // codes k0 + 16 d .. + 15
+            const uint32_t wd = (uint32_t)w[i][d];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[t] = __builtin_amdgcn_sdot4((int)((wd >> (2 * j)) & kFieldMask), c[j], acc[t], false);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    acc[t] += __shfl_xor(acc[t], 4, 64);
+    acc[t] += __shfl_xor(acc[t], 2, 64);
+    acc[t] += __shfl_xor(acc[t], 1, 64);
+  }
+  if (p == 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[ks][rg][lane >> 3][t] = acc[t];
+  }
+  __syncthreads();
+  if (ks == 0 && p == 0 && valid) {
+    const float g = epi_gamma(a.ep, n);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t < a.m) {
+        int sum = 0;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sum += red[s][rg][lane >> 3][t];
+        const int av = sum - q[t].rowsum;
+        const float yv = rescale(av, q[t].deq, g);
+        const int64_t o = (int64_t)t * N + n;
+        if (a.acc_out) a.acc_out[o] = av;
+        if (EPI == FUSED_EPI_PLAIN || a.y) a.y[o] = yv;
+        if constexpr (EPI == FUSED_EPI_RESID) a.out2[o] = __fadd_rn(a.res[o], yv);
+        if constexpr (EPI == FUSED_EPI_RELU2) ybuf[t * R + r] = yv;
+      }
+    }
+  }
+  if constexpr (EPI == FUSED_EPI_RELU2) {
+    constexpr int half = R / 2;
+    __syncthreads();
+    const int inter = N / 2;
+    for (int i = threadIdx.x; i < MT * half; i += 256) {
+      const int t = i / half, j = i - t * half;
+      if (t < a.m) {
+        const float gt = ybuf[t * R + j], up = ybuf[t * R + half + j];
+        const float tt = gt > 0.0f ? gt : 0.0f;
+        a.mi[(int64_t)t * inter + blockIdx.x * half + j] = __fmul_rn(__fmul_rn(tt, tt), up);
+      }
+    }
+  }
+}
+
+template <int MODE, int EPI, int MT>
+hipError_t launch_mt(const FusedDecode &a, hipStream_t stream) {
+  // split K over the waves of a workgroup until the workgroups cover the CUs
+  const int rows = EPI == FUSED_EPI_RELU2 ? a.n / 2 : a.n;  // output rows that set the grid
+  const int per32 = EPI == FUSED_EPI_RELU2 ? rows / 16 : rows / 32;
+  const int ks = per32 >= 256 ? 1 : (2 * per32 >= 256 ? 2 : 4);
+  const int R = 32 / ks;
+  const int lines = ((a.src.k >> 2) + 127) >> 7;
+  const int nv = a.src.k <= 4096 ? 4 : 8;
+  if ((lines + ks - 1) / ks > 2 * nv / ks) return hipErrorInvalidValue;
+  int grid;
+  if (EPI == FUSED_EPI_RELU2) {
+    if (a.n % 2 != 0 || (a.n / 2) % (R / 2) != 0) return hipErrorInvalidValue;
+    grid = (a.n / 2) / (R / 2);
+  } else {
+    grid = (a.n + R - 1) / R;
+  }
+  const dim3 g((unsigned)grid), b(256);
+  if (nv == 4) {
+    if (ks == 1) gemv_fused_kernel<MODE, EPI, MT, 1, 4><<<g, b, 0, stream>>>(a);
+    else if (ks == 2) gemv_fused_kernel<MODE, EPI, MT, 2, 4><<<g, b, 0, stream>>>(a);
+    else gemv_fused_kernel<MODE, EPI, MT, 4, 4><<<g, b, 0, stream>>>(a);
+  } else {
+    if (ks == 1) gemv_fused_kernel<MODE, EPI, MT, 1, 8><<<g, b, 0, stream>>>(a);
+    else if (ks == 2) gemv_fused_kernel<MODE, EPI, MT, 2, 8><<<g, b, 0, stream>>>(a);
+    else gemv_fused_kernel<MODE, EPI, MT, 4, 8><<<g, b, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+template <int MODE, int EPI>
+hipError_t launch_pair(const FusedDecode &a, hipStream_t stream) {
+  return a.m == 1 ? launch_mt<MODE, EPI, 1>(a, stream) : launch_mt<MODE, EPI, 4>(a, stream);
+}
+
+}  // namespace
+
+bool fused_decode_supported(int64_t m, int64_t k) {
+  return m >= 1 && m <= kFusedMaxM && k % 64 == 0 && k <= kFusedMaxK;
+}
+
+hipError_t launch_gemv_fused(int mode, int epi, const FusedDecode &a, hipStream_t stream) {
+  if (!fused_decode_supported(a.m, a.src.k) || a.n <= 0) return hipErrorInvalidValue;
+  if (mode == BITLINEAR_ACT_RMSNORM && epi == FUSED_EPI_PLAIN)
+    return launch_pair<BITLINEAR_ACT_RMSNORM, FUSED_EPI_PLAIN>(a, stream);
+  if (mode == BITLINEAR_ACT_RMSNORM && epi == FUSED_EPI_RESID)
+    return launch_pair<BITLINEAR_ACT_RMSNORM, FUSED_EPI_RESID>(a, stream);
+  if (mode == BITLINEAR_ACT_RMSNORM && epi == FUSED_EPI_RELU2)
+    return launch_pair<BITLINEAR_ACT_RMSNORM, FUSED_EPI_RELU2>(a, stream);
+  if (mode == ACT_GQA_RMSNORM && epi == FUSED_EPI_RESID) return launch_pair<ACT_GQA_RMSNORM, FUSED_EPI_RESID>(a, stream);
+  if (mode == BITLINEAR_ACT_ABSMAX && epi == FUSED_EPI_RELU2)
+    return launch_pair<BITLINEAR_ACT_ABSMAX, FUSED_EPI_RELU2>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bl

@@ -41,7 +41,7 @@ def f32(g):
 
 
 # ------------------------------------------------------------------------------ FFN block
-@pytest.mark.parametrize("m", [1024, 16, 1, 37])
+@pytest.mark.parametrize("m", [1024, 16, 1, 37, 2, 3, 4, 5])
 def test_ffn_block(m):
     hdim, inter = 512, 2048
     note(f"block FFN m={m} H={hdim} I={inter}")
@@ -68,6 +68,7 @@ def test_ffn_block(m):
     assert_rel(host(tr["deq"])[3], ref["deq2"], what="ffn_sub_norm deq")
     assert_equal(host(tr["acc_down"]), ref["acc_down"], "down acc")
     assert_rel(host(y), ref["y"], what="y")
+    assert_equal(host(bl.block_forward(spec, gpu(x))), host(y), "untraced y")
 
 
 # ------------------------------------------------------------------------------ decoder stack
@@ -152,6 +153,35 @@ def test_decoder_stack_small(m, layers):
     for l in range(layers):
         _compare_layer(tr, l, refs[l])
     assert_rel(host(y), xo, what="stack output")
+
+
+@pytest.mark.parametrize("m,layers", [(1, 3), (2, 2), (3, 2), (4, 2), (5, 2)])
+def test_decoder_stack_fused_sizes(m, layers):
+    """Dims that the one-launch-per-projection decode form takes (every
+    projection input a multiple of 64; m <= 4), random gains: H=128 (8 heads
+    of 16), 2 kv heads, I=192. m = 5 takes the unfused chain."""
+    hdim, inter, nh, nkv, hd = 128, 192, 8, 2, 16
+    note(f"block decoder fused sizes m={m} layers={layers}")
+    kvd = nkv * hd
+    x = synth.activations(seed(7, m, 5), m, hdim, 2)
+    gpu_layers, refs = [], []
+    xo = x
+    for l in range(layers):
+        mt = _decoder_layer_mats(7, l, hdim, inter, kvd)
+        gains = {nm: (1.0 + 0.1 * synth.normal_f32(seed(7, l, 30 + i), n)).astype(np.float32)
+                 for i, (nm, n) in enumerate((("n_in", hdim), ("n_attn", hdim), ("n_post", hdim), ("n_ffn", inter)))}
+        ref = oracle.decoder_layer(xo, _oracle_weights(mt, gains), EPS, nh, nkv, hd)
+        refs.append(ref)
+        xo = ref["x"]
+        gpu_layers.append(_gpu_layer(mt, gains))
+    spec = bl.BlockSpec(bl.BLOCK_DECODER, hdim, inter, gpu_layers, nh, nkv, hd, EPS)
+    tr = _trace(layers, m, hdim, inter, hdim + 2 * kvd)
+    y = bl.block_forward(spec, gpu(x), trace=tr)
+    for l in range(layers):
+        _compare_layer(tr, l, refs[l])
+    assert_rel(host(y), xo, what="stack output")
+    y2 = bl.block_forward(spec, gpu(x))  # no trace: the scratch buffers carry the chain
+    assert_equal(host(y2), host(y), "untraced output")
 
 
 def test_decoder_stack_30_layers():
