@@ -90,13 +90,15 @@ bitlinear_status check_segments(const float *gamma, const int64_t *seg_end, int3
 // int32 indexing inside the kernels
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
+// split_ws: gemm_prefill_workspace_bytes(m, n, k) bytes, or NULL (no split K)
 bitlinear_status contract(const int8_t *codes, const float *deq, const int32_t *rowsum, int64_t m, int64_t k,
                           const uint8_t *w, int64_t n, const bl::Epilogue &ep, float *y, int32_t *acc_out,
-                          int32_t path, hipStream_t stream) {
+                          int32_t path, int32_t *split_ws, hipStream_t stream) {
   const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && m <= 16);
   if (decode) return launched(bl::launch_gemv_decode(codes, w, deq, rowsum, m, n, k, ep, y, acc_out, stream),
                               "decode kernel");
-  return launched(bl::launch_gemm_prefill(codes, w, deq, rowsum, m, n, k, ep, y, acc_out, stream), "prefill kernel");
+  return launched(bl::launch_gemm_prefill(codes, w, deq, rowsum, m, n, k, ep, y, acc_out, split_ws, stream),
+                  "prefill kernel");
 }
 
 }  // namespace
@@ -180,10 +182,10 @@ bitlinear_status bitlinear_quantize_acts(const float *x, int64_t m, int64_t k, i
 
 // ---------------------------------------------------------------- forward
 size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside) {
-  (void)n;
-  if (m < 0 || k < 0) return 0;
+  if (m < 0 || k < 0 || n < 0) return 0;
   size_t b = align256((size_t)m * sizeof(int32_t));  // row sums
   if (quantize_inside) b += align256((size_t)(m * k)) + align256((size_t)m * sizeof(float));
+  b += align256(bl::gemm_prefill_workspace_bytes(m, n, k));  // split-K partial sums
   return b;
 }
 
@@ -214,6 +216,9 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
   char *ws = static_cast<char *>(workspace);
   int32_t *rowsum = reinterpret_cast<int32_t *>(ws);
   ws += align256((size_t)m * sizeof(int32_t));
+  const size_t split_bytes = bl::gemm_prefill_workspace_bytes(m, n, k);
+  int32_t *split_ws = split_bytes ? reinterpret_cast<int32_t *>(ws) : nullptr;
+  ws += align256(split_bytes);
   const int8_t *codes = codes_in;
   const float *deq = deq_in;
   if (x) {
@@ -230,7 +235,7 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
   } else {
     BL_TRY(launched(bl::launch_code_rowsum(codes, m, k, rowsum, s), "code row sums"));
   }
-  return contract(codes, deq, rowsum, m, k, w_packed, n, ep, y, acc_out, path, s);
+  return contract(codes, deq, rowsum, m, k, w_packed, n, ep, y, acc_out, path, split_ws, s);
 }
 
 }  // extern "C"
@@ -243,6 +248,7 @@ struct BlockBufs {
   float *deq;
   int32_t *rowsum;
   float *qkv, *o, *h, *x, *gu, *d;
+  int32_t *split;  // split-K partial sums of the widest projection, or NULL
 };
 
 size_t block_layout(const bitlinear_block *blk, int64_t m, BlockBufs *b, char *base) {
@@ -266,6 +272,15 @@ size_t block_layout(const bitlinear_block *blk, int64_t m, BlockBufs *b, char *b
   t.h = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
   t.x = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
   t.d = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
+  size_t split = bl::gemm_prefill_workspace_bytes(m, 2 * I, H);
+  const size_t sd = bl::gemm_prefill_workspace_bytes(m, H, I);
+  if (sd > split) split = sd;
+  if (dec) {
+    const size_t sq = bl::gemm_prefill_workspace_bytes(m, Q, H), so = bl::gemm_prefill_workspace_bytes(m, H, H);
+    if (sq > split) split = sq;
+    if (so > split) split = so;
+  }
+  t.split = reinterpret_cast<int32_t *>(split ? take(split) : nullptr);
   if (b) *b = t;
   return off;
 }
@@ -310,7 +325,7 @@ bitlinear_status proj(const BlockBufs &b, int64_t m, int64_t k, const uint8_t *w
                       const int64_t *seg, int n_seg, float *y, int32_t *acc, hipStream_t s) {
   bl::Epilogue ep;
   BL_TRY(check_segments(gam, seg, n_seg, n, &ep));
-  return contract(b.codes, b.deq, b.rowsum, m, k, w, n, ep, y, acc, BITLINEAR_PATH_AUTO, s);
+  return contract(b.codes, b.deq, b.rowsum, m, k, w, n, ep, y, acc, BITLINEAR_PATH_AUTO, b.split, s);
 }
 
 bitlinear_status quant(const BlockBufs &b, int mode, const float *x, const float *x2, int64_t ld, int64_t m,

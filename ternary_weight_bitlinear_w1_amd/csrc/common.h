@@ -73,9 +73,23 @@ hipError_t launch_copy_gamma(const double *src, double *dst, hipStream_t stream)
 hipError_t launch_validate_packed(const uint8_t *packed, int64_t n, int64_t k, int64_t *n_bad,
                                   hipStream_t stream);
 
+// Prefill contraction. For shapes with few output tiles (small m) it splits K
+// into gemm_prefill_splits() ranges when split_ws (gemm_prefill_workspace_bytes()
+// bytes) is given, and adds the ranges' exact partial sums in a second kernel.
+#ifndef BL_SPLIT_TARGET
+#define BL_SPLIT_TARGET 256
+#endif
+#ifndef BL_SPLIT_BYTES_RATIO
+#define BL_SPLIT_BYTES_RATIO 1
+#endif
+constexpr int64_t kSplitMinTiles = 256;                         // split only below this many output tiles
+constexpr int64_t kSplitTarget = BL_SPLIT_TARGET;               // aim for about this many work items
+constexpr int64_t kSplitBytesPerWeightByte = BL_SPLIT_BYTES_RATIO;  // partial sums vs packed weight bytes
+int gemm_prefill_splits(int64_t m, int64_t n, int64_t k);
+size_t gemm_prefill_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const float *deq,
                                const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
-                               float *y, int32_t *acc_out, hipStream_t stream);
+                               float *y, int32_t *acc_out, int32_t *split_ws, hipStream_t stream);
 hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const float *deq,
                               const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
                               float *y, int32_t *acc_out, hipStream_t stream);

@@ -193,7 +193,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_generic_kernel(const int8_t 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
-constexpr int kStages = 3;
 
 // Tile of the large-M kernel: waves in M, waves in N, 32x32 tiles per wave in M
 // and N (tuned on MI355X; overridable when building variants to sweep).
@@ -203,6 +202,15 @@ constexpr int kStages = 3;
 #ifndef BL_GEMM_BIG_CFG
 #define BL_GEMM_BIG_CFG 2, 2, 2, 4
 #define BL_GEMM_BIG_BN 256
+#endif
+// tile of the few-token kernel (m <= 64): 64 rows x BL_GEMM_SMALL_BN columns,
+// with a deeper ring: its chunks are small, so more of them are kept in flight
+#ifndef BL_GEMM_SMALL_CFG
+#define BL_GEMM_SMALL_CFG 1, 2, 2, 1
+#define BL_GEMM_SMALL_BN 64
+#endif
+#ifndef BL_GEMM_SMALL_STAGES
+#define BL_GEMM_SMALL_STAGES 4
 #endif
 constexpr int kGroupM = 4;
 
@@ -242,9 +250,9 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds_base)
 }
 
 // Persistent form: gridDim.x workgroups (two per CU) walk the tiles
-// t = blockIdx.x, blockIdx.x + gridDim.x, ... and the three-stage ring runs on
-// across tile boundaries, so the next tile's loads and MFMAs overlap the
-// previous tile's stores.
+// t = blockIdx.x, blockIdx.x + gridDim.x, ... and the ring of P stages (P - 1
+// chunks in flight) runs on across tile boundaries, so the next tile's loads
+// and MFMAs overlap the previous tile's stores.
 //
 // The MFMA takes the unpacked weights as its A operand and the activation
 // codes as its B operand, so a lane's accumulators hold 4 consecutive output
@@ -255,20 +263,29 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds_base)
 //
 // Waiting: vector memory operations of a wave complete in issue order, so
 // "at most X outstanding" waits exactly for everything older than the X most
-// recent. Per wave and step c the operations younger than chunk c are chunk
-// c + 1's loads, and, in the first two steps of a tile, the previous tile's
-// row-data load (one per wave) and its kStores output stores; X is set to
-// that count (or 0 when an acc_out copy doubles the stores past the counter).
+// recent. Per wave and step c the operations younger than chunk c are the
+// loads of chunks c + 1 .. c + P - 2, and, in the first P - 1 steps of a tile,
+// the previous tile's row-data load (one per wave) and its kStores output
+// stores; X is set to that count (or 0 when an acc_out copy doubles the stores
+// past the counter, near the end of the stream, and for tiles of at most
+// P - 1 chunks).
 // Per-token deq / row sums go through a small double-buffered LDS area loaded
 // with the same global->LDS copy, one instruction per wave per tile.
-template <int WM, int WN, int TM, int TN>
+//
+// Split K (S > 1, for shapes with few tiles): work item t covers output tile
+// t mod (tiles) over the K range [s K / S, (s + 1) K / S) with s = t / tiles,
+// and stores its exact int32 sum of q * u over that range to
+// part[s][m][n]; the row sums, rescale and sum over s are left to the
+// consumer (integer sums: the total is the same in any order).
+template <int WM, int WN, int TM, int TN, int P>
 __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8_t *__restrict__ A,
                                                                       const uint8_t *__restrict__ B,
                                                                       const float *__restrict__ deq,
                                                                       const int32_t *__restrict__ rowsum, int M,
                                                                       int N, int K, Epilogue ep,
                                                                       float *__restrict__ Y,
-                                                                      int32_t *__restrict__ acc_out) {
+                                                                      int32_t *__restrict__ acc_out, int S,
+                                                                      int32_t *__restrict__ part) {
   constexpr int NW = WM * WN;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int kAStage = BM * 128, kBStage = BN * 32, kStage = kAStage + kBStage;
@@ -278,11 +295,13 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   constexpr int kRowOps = BM / 32;      // 64-dword row-data loads per tile (deq, then row sums)
   static_assert(LA * NW * 8 == BM && LB * NW * 32 == BN, "tile must split into 1 KB wave loads");
   static_assert(kRowOps <= NW && kRowOps >= 2, "one row-data load per wave");
-  constexpr int kWaitSteady = LA + LB;
-  constexpr int kWaitAfterTile = LA + LB + 1 + kStores;
+  constexpr int D = P - 1;  // chunks issued ahead of the one being computed
+  constexpr int kWaitSteady = (D - 1) * (LA + LB);
+  constexpr int kWaitAfterTile = kWaitSteady + 1 + kStores;
+  static_assert(P >= 3, "ring of at least three stages");
   static_assert(kWaitAfterTile < 64, "vmcnt range");
   static_assert(NW * 32 * 32 * 4 <= kStage, "epilogue scratch must fit in one stage");
-  __shared__ __attribute__((aligned(1024))) int8_t ring[kStages * kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t ring[P * kStage];
   __shared__ __attribute__((aligned(256))) float s_deq[2][BM];
   __shared__ __attribute__((aligned(256))) int s_rs[2][BM];
 
@@ -291,18 +310,22 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   const int half = lane >> 5, l32 = lane & 31;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
-  const int T = tiles_m * tiles_n;
+  const int Tmn = tiles_m * tiles_n;
+  const int T = Tmn * S;
   const int G = gridDim.x, b = blockIdx.x;
   const int my_tiles = (T - b + G - 1) / G;
   const int64_t ldb = K >> 2;
-  const int nk = K >> 7;
+  const int nk = (K >> 7) / S;  // chunks per work item
   const int total = my_tiles * nk;
   const bool two_stores = acc_out != nullptr;
 
-  // tile i of this workgroup -> (m0, n0): XCD-contiguous ranges, grouped along M
-  auto coords = [&](int i, int &m0, int &n0) {
+  // work item i of this workgroup -> (m0, n0, split): XCD-contiguous ranges,
+  // grouped along M; items of one split (one K range) are contiguous
+  auto coords = [&](int i, int &m0, int &n0, int &sp) {
     int t = b + i * G;
     if ((T & 7) == 0 && (G & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+    sp = t / Tmn;
+    t -= sp * Tmn;
     const int per_group = kGroupM * tiles_n;
     const int group = t / per_group, first_m = group * kGroupM;
     const int gsize = min(tiles_m - first_m, kGroupM);
@@ -312,8 +335,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   };
 
   // ---- issue side: the chunk stream (tile is_i, chunk is_kc)
-  int is_i = 0, is_kc = 0, is_m0, is_n0;
-  coords(0, is_m0, is_n0);
+  int is_i = 0, is_kc = 0, is_m0, is_n0, is_s;
+  coords(0, is_m0, is_n0, is_s);
   // per-lane source offsets of the current issue tile (32-bit: M K and N K / 4
   // stay below 2^31 for every shape the host passes)
   uint32_t a_off[LA], b_off[LB];
@@ -323,13 +346,13 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
       const int r = 8 * (wave * LA + j) + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int row = min(is_m0 + r, M - 1);
-      a_off[j] = (uint32_t)row * (uint32_t)K + 16u * c;
+      a_off[j] = (uint32_t)row * (uint32_t)K + 16u * c + 128u * (uint32_t)(is_s * nk);
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
       const int r = 32 * (wave * LB + j) + (lane >> 1);
       const int h = (lane & 1) ^ ((r >> 3) & 1);
-      b_off[j] = (uint32_t)(is_n0 + r) * (uint32_t)ldb + 16u * h;
+      b_off[j] = (uint32_t)(is_n0 + r) * (uint32_t)ldb + 16u * h + 32u * (uint32_t)(is_s * nk);
     }
   };
   set_src();
@@ -343,7 +366,7 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
     if (++is_kc == nk) {
       is_kc = 0;
       if (++is_i < my_tiles) {
-        coords(is_i, is_m0, is_n0);
+        coords(is_i, is_m0, is_n0, is_s);
         set_src();
       }
     }
@@ -351,8 +374,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   // per-token deq and row sums of tile i into buffer i & 1: wave w loads part
   // (w % kRowOps) of [deq (BM/64 parts) | row sums (BM/64 parts)]
   auto issue_rows = [&](int i) {
-    int m0, n0;
-    coords(i, m0, n0);
+    int m0, n0, sp;
+    coords(i, m0, n0, sp);
     const int op = wave % kRowOps, part = op % (kRowOps / 2);
     const int row = min(m0 + part * 64 + lane, M - 1);
     if (op < kRowOps / 2)
@@ -411,8 +434,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   };
 
   // ---- compute side
-  int c_i = 0, c_kc = 0, c_m0, c_n0;
-  coords(0, c_m0, c_n0);
+  int c_i = 0, c_m0, c_n0, c_s;
+  coords(0, c_m0, c_n0, c_s);
   // Output of one tile. The stage just consumed serves as scratch: after a
   // barrier (every wave is done reading it) each wave writes one 32 x 32 fp32
   // block at a time in its accumulator layout and reads it back so that one
@@ -439,6 +462,13 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int nl = 8 * j + 4 * half;
+          if (part) {  // split K: the raw partial sums, bit for bit through the fp32 scratch
+            const v4i raw = v4i{acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                                acc[tn][tm][4 * j + 3]};
+            *reinterpret_cast<v4f *>(sc + l32 * 32 + 4 * ((nl >> 2) ^ ((l32 >> 1) & 7))) =
+                __builtin_bit_cast(v4f, raw);
+            continue;
+          }
           const int a0 = acc[tn][tm][4 * j] - rs, a1 = acc[tn][tm][4 * j + 1] - rs;
           const int a2 = acc[tn][tm][4 * j + 2] - rs, a3 = acc[tn][tm][4 * j + 3] - rs;
           if (two_stores) {
@@ -462,7 +492,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
           const int r = 8 * i + (lane >> 3);
           const v4f v = *reinterpret_cast<const v4f *>(sc + r * 32 + 4 * ((lane & 7) ^ ((r >> 1) & 7)));
           const int m = min(c_m0 + mb + r, M - 1);
-          __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(Y + (int64_t)m * N + nb + 4 * (lane & 7)));
+          float *dst = part ? reinterpret_cast<float *>(part + ((int64_t)c_s * M + m) * N) : Y + (int64_t)m * N;
+          __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(dst + nb + 4 * (lane & 7)));
         }
       }
     }
@@ -475,33 +506,35 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   };
 
   issue_rows(0);
-  issue_chunk(ring);
-  if (total > 1) issue_chunk(ring + kStage);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < total) issue_chunk(ring + j * kStage);
   int stage = 0;  // ring slot of chunk c
   int c = 0;
   for (; c_i < my_tiles;) {
     for (int kc = 0; kc < nk; ++kc, ++c) {
       // wait for this wave's loads of chunk c: everything but the operations
       // issued after them (see the note above the kernel)
-      if (c + 1 >= total || nk <= 2)
+      if (c + D - 1 >= total || nk <= D)
         wait_vm<0>();
-      else if (c_i > 0 && kc <= 1)
+      else if (c_i > 0 && kc < D)
         two_stores ? wait_vm<0>() : wait_vm<kWaitAfterTile>();
       else
         wait_vm<kWaitSteady>();
       meet();
-      if (c + 2 < total) issue_chunk(ring + (stage == 0 ? 2 : stage - 1) * kStage);
+      const int prev = stage == 0 ? P - 1 : stage - 1;  // the slot computed in the last step
+      if (c + D < total) issue_chunk(ring + prev * kStage);
       compute(ring + stage * kStage);
-      stage = stage == 2 ? 0 : stage + 1;
+      stage = stage == P - 1 ? 0 : stage + 1;
     }
     if (c_i + 1 < my_tiles) issue_rows(c_i + 1);
-    if (nk <= 2) {
+    if (nk <= D) {
       // with so few chunks the row data may still be in flight
       wait_vm<0>();
       meet();
     }
-    epilogue(ring + (stage == 0 ? 2 : stage - 1) * kStage);
-    if (++c_i < my_tiles) coords(c_i, c_m0, c_n0);
+    epilogue(ring + (stage == 0 ? P - 1 : stage - 1) * kStage);
+    if (++c_i < my_tiles) coords(c_i, c_m0, c_n0, c_s);
   }
 }
 
@@ -527,40 +560,126 @@ int cu_count() {
   return cached[dev];
 }
 
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, int P>
 hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
-                            int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
+                            int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, int splits, int32_t *part,
+                            hipStream_t stream) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  const int64_t tiles = (int64_t)((m + BM - 1) / BM) * (n / BN);
+  const int64_t tiles = (int64_t)((m + BM - 1) / BM) * (n / BN) * splits;
   int64_t grid = 2 * (int64_t)cu_count();  // two workgroups fit per CU
   if (grid > tiles) grid = tiles;
-  gemm_prefill_kernel<WM, WN, TM, TN>
-      <<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out);
+  gemm_prefill_kernel<WM, WN, TM, TN, P><<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(
+      codes, packed, deq, rowsum, m, n, k, ep, y, part ? nullptr : acc_out, splits, part);
   return hipGetLastError();
+}
+
+// y = rescale(sum_s part[s] - rowsum, deq, gamma): the end of a split-K
+// contraction, four outputs per thread
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__restrict__ part, int S,
+                                                            const float *__restrict__ deq,
+                                                            const int32_t *__restrict__ rowsum, int M, int N,
+                                                            Epilogue ep, float *__restrict__ Y,
+                                                            int32_t *__restrict__ acc_out) {
+  const int64_t plane = (int64_t)M * N;
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (4 * i4 >= plane) return;
+  const int m = (int)(4 * i4 / N), n = (int)(4 * i4 - (int64_t)m * N);
+  v4i t = *reinterpret_cast<const v4i *>(part + 4 * i4);
+  for (int s = 1; s < S; ++s) t += *reinterpret_cast<const v4i *>(part + s * plane + 4 * i4);
+  const int rs = rowsum[m];
+  const float dq = deq[m];
+  t -= v4i{rs, rs, rs, rs};
+  if (acc_out) *reinterpret_cast<v4i *>(acc_out + 4 * i4) = t;
+  const v4f v = v4f{rescale(t[0], dq, epi_gamma(ep, n)), rescale(t[1], dq, epi_gamma(ep, n + 1)),
+                    rescale(t[2], dq, epi_gamma(ep, n + 2)), rescale(t[3], dq, epi_gamma(ep, n + 3))};
+  *reinterpret_cast<v4f *>(Y + 4 * i4) = v;
 }
 
 }  // namespace
 
+namespace {
+
+// Tile shape of the pipelined kernel for (m, n, k), or 0 for the generic one.
+enum { CFG_GENERIC = 0, CFG_BIG = 1, CFG_2224 = 2, CFG_2222 = 3, CFG_1422 = 4, CFG_SMALL = 5 };
+int pick_cfg(int64_t m, int64_t n, int64_t k, int64_t *bm, int64_t *bn) {
+  *bm = 0;
+  *bn = 0;
+  if (k % 128 != 0) return CFG_GENERIC;
+  if (n % BL_GEMM_BIG_BN == 0 && m > 64) { *bm = 128; *bn = BL_GEMM_BIG_BN; return CFG_BIG; }
+  if (n % 256 == 0 && m > 64) { *bm = 128; *bn = 256; return CFG_2224; }
+  if (n % 128 == 0 && m > 64) { *bm = 128; *bn = 128; return CFG_2222; }
+  if (m <= 64 && n % BL_GEMM_SMALL_BN == 0) { *bm = 64; *bn = BL_GEMM_SMALL_BN; return CFG_SMALL; }
+  if (n % 256 == 0) { *bm = 64; *bn = 256; return CFG_1422; }
+  return CFG_GENERIC;
+}
+
+}  // namespace
+
+int gemm_prefill_splits(int64_t m, int64_t n, int64_t k) {
+  int64_t bm, bn;
+  if (m <= 0 || n <= 0 || pick_cfg(m, n, k, &bm, &bn) == CFG_GENERIC) return 1;
+  const int64_t tiles = ((m + bm - 1) / bm) * (n / bn);
+  if (tiles >= kSplitMinTiles) return 1;
+  // the divisor of the chunk count (K / 128) that brings the work items
+  // closest to kSplitTarget, keeping at least two chunks per item and the
+  // partial sums (d m n int32) within kSplitBytesPerWeightByte x the packed
+  // weights (n k / 4 bytes): they are written and read back once more
+  const int64_t chunks = k / 128;
+  int best = 1;
+  int64_t best_gap = kSplitTarget > tiles ? kSplitTarget - tiles : tiles - kSplitTarget;
+  for (int64_t d = 2; 2 * d <= chunks; ++d) {
+    if (chunks % d) continue;
+    if (d * m * n * 4 > kSplitBytesPerWeightByte * (n * k / 4)) break;
+    const int64_t items = tiles * d, gap = items > kSplitTarget ? items - kSplitTarget : kSplitTarget - items;
+    if (gap < best_gap) {
+      best = (int)d;
+      best_gap = gap;
+    }
+  }
+  return best;
+}
+
+size_t gemm_prefill_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  const int s = gemm_prefill_splits(m, n, k);
+  return s > 1 ? (size_t)s * (size_t)m * (size_t)n * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,
                                int64_t m, int64_t n, int64_t k, const Epilogue &ep, float *y, int32_t *acc_out,
-                               hipStream_t stream) {
+                               int32_t *split_ws, hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
   const int M = (int)m, N = (int)n, K = (int)k;
-  if (K % 128 == 0) {
-    if (N % BL_GEMM_BIG_BN == 0 && M > 64)
-      return launch_pipelined<BL_GEMM_BIG_CFG>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
-    if (N % 256 == 0 && M > 64)
-      return launch_pipelined<2, 2, 2, 4>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
-    if (N % 128 == 0 && M > 64)
-      return launch_pipelined<2, 2, 2, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
-    if (N % 256 == 0)
-      return launch_pipelined<1, 4, 2, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
+  int64_t bm, bn;
+  const int cfg = pick_cfg(m, n, k, &bm, &bn);
+  const int S = split_ws ? gemm_prefill_splits(m, n, k) : 1;
+  int32_t *part = S > 1 ? split_ws : nullptr;
+  hipError_t e = hipSuccess;
+  switch (cfg) {
+    case CFG_BIG:
+      e = launch_pipelined<BL_GEMM_BIG_CFG, 3>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
+      break;
+    case CFG_2224:
+      e = launch_pipelined<2, 2, 2, 4, 3>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
+      break;
+    case CFG_2222:
+      e = launch_pipelined<2, 2, 2, 2, 3>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
+      break;
+    case CFG_1422:
+      e = launch_pipelined<1, 4, 2, 2, 3>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
+      break;
+    case CFG_SMALL:
+      e = launch_pipelined<BL_GEMM_SMALL_CFG, BL_GEMM_SMALL_STAGES>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
+      break;
+    default:
+      if (m >= 256) return launch_generic<2, 2, 4, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
+      if (m > 64) return launch_generic<2, 2, 2, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
+      return launch_generic<1, 4, 2, 1>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
   }
-  if (m >= 256)
-    return launch_generic<2, 2, 4, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
-  if (m > 64)
-    return launch_generic<2, 2, 2, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
-  return launch_generic<1, 4, 2, 1>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
+  if (e != hipSuccess || !part) return e;
+  const int64_t quads = m * n / 4;
+  splitk_finish_kernel<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream>>>(part, S, deq, rowsum, M, N,
+                                                                                        ep, y, acc_out);
+  return hipGetLastError();
 }
 
 }  // namespace bl

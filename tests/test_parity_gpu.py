@@ -167,7 +167,10 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           (130, 512, 256), (65, 384, 384), (40, 768, 640), (333, 1280, 1152), (20, 256, 128), (257, 2560, 2560),
           # few-token shapes the dot-product decode kernel takes (m <= 4, K % 64 == 0): rows not a
           # multiple of 8, K from one partial line to 8192, every split of K over waves
-          (1, 77, 64), (2, 200, 320), (3, 1000, 576), (4, 40, 8192), (1, 9000, 1024), (4, 5000, 448)]
+          (1, 77, 64), (2, 200, 320), (3, 1000, 576), (4, 40, 8192), (1, 9000, 1024), (4, 5000, 448),
+          # few output tiles, where K is split into ranges (16, 8, 4 here) whose int32 partial sums a
+          # second kernel adds, and neighbours that are not split
+          (9, 512, 4096), (5, 256, 2048), (48, 1024, 3072), (37, 512, 1024), (100, 384, 768)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED)
@@ -197,10 +200,11 @@ def test_forward_codes_in_path():
     assert_equal(y_r, y_x)
 
 
-@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("m", [1, 4, 16, 64])
 @pytest.mark.parametrize("proj", ["gate_up", "down"])
 def test_forward_decode_full_size(m, proj):
-    """Decode sweep at the 2B4T projection shapes, gate|up with one gamma each."""
+    """Decode sweep at the 2B4T projection shapes, gate|up with one gamma each; the
+    prefill kernel at these few-tile shapes splits K (and m = 64 takes only it)."""
     note(f"forward decode {proj} m={m}")
     if proj == "gate_up":
         k = 2560
@@ -209,9 +213,10 @@ def test_forward_decode_full_size(m, proj):
         k = 6912
         mats = [Matrix(2560, k, seed(3, 0, 3))]
     x = synth.activations(seed(3, m, k), m, k, synth.outlier_count(k))
-    y_dec = _check_forward(x, mats, bl.PATH_DECODE, f"decode {proj}")
     y_pre = _check_forward(x, mats, bl.PATH_PREFILL, f"prefill {proj}")
-    assert_equal(host(y_dec), host(y_pre), "decode == prefill")
+    if m <= 16:
+        y_dec = _check_forward(x, mats, bl.PATH_DECODE, f"decode {proj}")
+        assert_equal(host(y_dec), host(y_pre), "decode == prefill")
 
 
 @pytest.mark.parametrize("proj", ["gate_up", "down"])
