@@ -5,12 +5,13 @@
 A step is one prefill pass of a BitNet b1.58 2B4T MLP over M = 4096 tokens, all
 on the GPU through the C ABI:
     per-token int8 quantization of x [4096][2560]
-    gate|up contraction 2560 -> 13824 (one weight scale per matrix) + rescale
-    ReLU^2 gating and ffn_sub_norm folded into the quantization of [4096][6912]
+    gate|up contraction 2560 -> 2 x 6912 (one weight scale per matrix) + rescale,
+        with the ReLU^2 gating in the same kernel: writes [4096][6912]
+    ffn_sub_norm folded into the quantization of [4096][6912]
     down contraction 6912 -> 2560 + rescale
 Weights are packed once before timing (the packed-checkpoint mode). ``value``
 is int8 TOPS of the whole step: 2 M N K of both contractions / step time.
-``roofline`` is the gate|up contraction kernel against dense int8 MFMA peak,
+``roofline`` is the gated gate|up contraction kernel against dense int8 MFMA peak,
 timed with HIP events on the stream it runs on; its ``traffic`` comes from the
 committed counter profile when the kernel source is unchanged since. ``decode``
 reports the weight-streaming kernel (M = 1, 4, 16) in packed-weight GB/s against
@@ -107,7 +108,7 @@ def main():
     deq2 = torch.empty(M, dtype=torch.float32, device=dev)
     rs1 = torch.empty(M, dtype=torch.int32, device=dev)
     rs2 = torch.empty(M, dtype=torch.int32, device=dev)
-    gu = torch.empty((M, 2 * I), dtype=torch.float32, device=dev)
+    mi = torch.empty((M, I), dtype=torch.float32, device=dev)
     y = torch.empty((M, H), dtype=torch.float32, device=dev)
     L = bl.lib()
     stream = torch.cuda.current_stream(dev)
@@ -117,7 +118,8 @@ def main():
     se_gu = (bl.ctypes.c_int64 * 2)(I, 2 * I)
     g_d_c = (c_float * 1)(*gam_d)
     se_d = (bl.ctypes.c_int64 * 1)(H)
-    ws_n = L.bitlinear_forward_workspace_bytes(M, 2 * I, I, 0)
+    ws_n = max(L.bitlinear_forward_workspace_bytes(M, H, I, 0),
+               L.bitlinear_forward_relu2_glu_workspace_bytes(M, I, H, 0, bl.PATH_PREFILL))
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
 
     def ok(st, what):
@@ -129,20 +131,21 @@ def main():
                                      deq1.data_ptr(), rs1.data_ptr(), sp), "quantize x")
 
     def f_gu():
-        ok(L.bitlinear_forward(None, codes1.data_ptr(), deq1.data_ptr(), rs1.data_ptr(), M, H, packed_gu.data_ptr(),
-                               2 * I, g_gu_c, se_gu, 2, gu.data_ptr(), None, bl.PATH_PREFILL, ws.data_ptr(), ws_n, sp),
-           "gate|up")
+        ok(L.bitlinear_forward_relu2_glu(None, codes1.data_ptr(), deq1.data_ptr(), rs1.data_ptr(), M, H,
+                                         packed_gu.data_ptr(), I, g_gu_c, mi.data_ptr(), bl.PATH_PREFILL,
+                                         ws.data_ptr(), ws_n, sp),
+           "gate|up + relu2")
 
     def q2():
-        ok(L.bitlinear_quantize_acts(gu.data_ptr(), M, I, bl.ACT_RELU2_RMSNORM, None, c_float(1e-5),
-                                     codes2.data_ptr(), deq2.data_ptr(), rs2.data_ptr(), sp), "relu2 + sub-norm")
+        ok(L.bitlinear_quantize_acts(mi.data_ptr(), M, I, bl.ACT_RMSNORM, None, c_float(1e-5),
+                                     codes2.data_ptr(), deq2.data_ptr(), rs2.data_ptr(), sp), "sub-norm")
 
     def f_d():
         ok(L.bitlinear_forward(None, codes2.data_ptr(), deq2.data_ptr(), rs2.data_ptr(), M, I, packed_d.data_ptr(),
                                H, g_d_c, se_d, 1, y.data_ptr(), None, bl.PATH_PREFILL, ws.data_ptr(), ws_n, sp),
            "down")
 
-    ops = [("quant_x", q1), ("gemm_gate_up", f_gu), ("quant_relu2_subnorm", q2), ("gemm_down", f_d)]
+    ops = [("quant_x", q1), ("gemm_gate_up_relu2", f_gu), ("quant_subnorm", q2), ("gemm_down", f_d)]
 
     if args.calibrate_copy:
         src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
@@ -173,21 +176,21 @@ def main():
     ops_gu = 2.0 * M * (2 * I) * H
     ops_d = 2.0 * M * H * I
     tops = (ops_gu + ops_d) / (step_ms * 1e-3) / 1e12
-    gu_tops = ops_gu / (per_op["gemm_gate_up"] * 1e-3) / 1e12
+    gu_tops = ops_gu / (per_op["gemm_gate_up_relu2"] * 1e-3) / 1e12
     d_tops = ops_d / (per_op["gemm_down"] * 1e-3) / 1e12
     log(f"step {step_ms:.3f} ms ({tops:.0f} TOPS); per op ms {per_op}; wall/step {wall / args.steps * 1e3:.3f} ms")
 
     # quantization kernels against HBM: bytes read + written per launch
     q1_bytes = M * H * 4 + M * H + M * 12
-    q2_bytes = M * 2 * I * 4 + M * I + M * 12
+    q2_bytes = M * I * 4 + M * I + M * 12
     kernels = {
-        "gemm_gate_up": {"ms": per_op["gemm_gate_up"], "tops": gu_tops, "frac_mfma": gu_tops / PEAK_INT8_TOPS},
+        "gemm_gate_up_relu2": {"ms": per_op["gemm_gate_up_relu2"], "tops": gu_tops,
+                               "frac_mfma": gu_tops / PEAK_INT8_TOPS},
         "gemm_down": {"ms": per_op["gemm_down"], "tops": d_tops, "frac_mfma": d_tops / PEAK_INT8_TOPS},
         "quant_x": {"ms": per_op["quant_x"], "gbs": q1_bytes / (per_op["quant_x"] * 1e-3) / 1e9},
-        "quant_relu2_subnorm": {"ms": per_op["quant_relu2_subnorm"],
-                                "gbs": q2_bytes / (per_op["quant_relu2_subnorm"] * 1e-3) / 1e9},
+        "quant_subnorm": {"ms": per_op["quant_subnorm"], "gbs": q2_bytes / (per_op["quant_subnorm"] * 1e-3) / 1e9},
     }
-    for kq in ("quant_x", "quant_relu2_subnorm"):
+    for kq in ("quant_x", "quant_subnorm"):
         kernels[kq]["frac_hbm"] = kernels[kq]["gbs"] / PEAK_HBM_GBS
 
     # ---------------------------------------------------------------- decode
@@ -219,13 +222,13 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "prefill of one BitNet b1.58 2B4T MLP: M=4096 tokens, quantize -> gate|up "
-                               "2560->13824 -> ReLU^2 + ffn_sub_norm quantize -> down 6912->2560",
+                               "2560->2x6912 with ReLU^2 gating -> ffn_sub_norm quantize -> down 6912->2560",
                    "tokens": M, "hidden": H, "intermediate": I, "ops_per_step": ops_gu + ops_d},
-        "roofline": {"bound": "mfma", "kernel": "gemm_prefill (gate|up, M=4096 N=13824 K=2560)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_prefill gated (gate|up + ReLU^2, M=4096 N=2x6912 K=2560)",
                      "achieved": round(gu_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tops / PEAK_INT8_TOPS, 4), "traffic": measured_traffic(),
                      "algorithmic_ops_per_launch": ops_gu,
-                     "algorithmic_bytes_per_launch": M * H + 2 * I * H // 4 + 4 * M * 2 * I + 8 * M},
+                     "algorithmic_bytes_per_launch": M * H + 2 * I * H // 4 + 4 * M * I + 8 * M},
         "kernels": kernels,
         "decode": decode,
         "stack": stack,

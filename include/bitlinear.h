@@ -153,6 +153,29 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
                                    size_t workspace_bytes, void *stream);
 size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside);
 
+/* bitlinear_forward_relu2_glu — the MLP's gate and up projections with the
+ * squared-ReLU gating applied in the same pass ("The MLP gates with a squared
+ * ReLU"; "The block, in order"): with g and u the outputs of bitlinear_forward
+ * on the stacked matrix [gate; up] (segments [0, inter) and [inter, 2 inter)),
+ *   y[m][j] = fl32(fl32(max(g[m][j], 0) * max(g[m][j], 0)) * u[m][j]).
+ * Arguments as bitlinear_forward, except:
+ *   w_packed   [2 inter][k/4]: the inter gate rows, then the inter up rows.
+ *   inter      features of each matrix (> 0).
+ *   gamma      HOST array of 2 fp32 scales {gate, up}.
+ *   y          [m][inter] fp32 (half the columns of g|u).
+ *   workspace  >= bitlinear_forward_relu2_glu_workspace_bytes(m, inter, k,
+ *              x != NULL, path) bytes. When the tile shape allows (m > 64,
+ *              k % 128 == 0, inter % 128 == 0, not DECODE) g and u never
+ *              leave the chip; otherwise they pass through the workspace.
+ * The result equals bitlinear_forward followed by the same gating, bit for
+ * bit. Errors as bitlinear_forward. */
+bitlinear_status bitlinear_forward_relu2_glu(const float *x, const int8_t *codes_in, const float *deq_in,
+                                             const int32_t *rowsum_in, int64_t m, int64_t k,
+                                             const uint8_t *w_packed, int64_t inter, const float *gamma, float *y,
+                                             int32_t path, void *workspace, size_t workspace_bytes, void *stream);
+size_t bitlinear_forward_relu2_glu_workspace_bytes(int64_t m, int64_t inter, int64_t k, int32_t quantize_inside,
+                                                   int32_t path);
+
 /* ---------------------------------------------------------------------------
  * Block-level chains ("The block, in order").
  * ------------------------------------------------------------------------- */

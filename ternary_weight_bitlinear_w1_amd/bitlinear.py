@@ -74,6 +74,8 @@ def lib():
             "bitlinear_forward": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _p, _i32, _p, _sz,
                                          _p]),
             "bitlinear_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+            "bitlinear_forward_relu2_glu": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _sz, _p]),
+            "bitlinear_forward_relu2_glu_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
             "bitlinear_block_forward": (_i32, [ctypes.POINTER(Block), _p, _i64, _p, ctypes.POINTER(Trace), _p, _sz,
                                                _p]),
             "bitlinear_block_workspace_bytes": (_sz, [ctypes.POINTER(Block), _i64]),
@@ -166,6 +168,26 @@ def forward(packed: torch.Tensor, k: int, gamma: Sequence[float], seg_end: Optio
            lib().bitlinear_forward(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), n, g, se,
                                    len(gamma), _ptr(y), _ptr(acc), path, _ptr(ws), nb, _stream(dev)))
     return (y, acc) if want_acc else y
+
+
+def forward_relu2_glu(packed: torch.Tensor, k: int, gamma: Sequence[float], x: Optional[torch.Tensor] = None,
+                      codes: Optional[torch.Tensor] = None, deq: Optional[torch.Tensor] = None,
+                      rowsum: Optional[torch.Tensor] = None, path: int = PATH_AUTO,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gate and up projections with the squared-ReLU gating -> [m][inter] fp32.
+    ``packed`` is [gate; up] ([2 inter][k/4]); ``gamma`` = (gate, up)."""
+    inter = packed.shape[0] // 2
+    src = x if x is not None else codes
+    m = src.shape[0]
+    dev = packed.device
+    g = (ctypes.c_float * 2)(*[float(v) for v in gamma])
+    y = out if out is not None else torch.empty((m, inter), dtype=torch.float32, device=dev)
+    nb = lib().bitlinear_forward_relu2_glu_workspace_bytes(m, inter, k, 1 if x is not None else 0, path)
+    ws = _workspace(nb, dev)
+    _check("bitlinear_forward_relu2_glu",
+           lib().bitlinear_forward_relu2_glu(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), inter,
+                                             g, _ptr(y), path, _ptr(ws), nb, _stream(dev)))
+    return y
 
 
 # ---------------------------------------------------------------------------------------------

@@ -238,6 +238,78 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
   return contract(codes, deq, rowsum, m, k, w_packed, n, ep, y, acc_out, path, split_ws, s);
 }
 
+// ---------------------------------------------------------------- gated up-projection
+namespace {
+bool glu_fused(int64_t m, int64_t inter, int64_t k, int32_t path) {
+  const bool decode = path == BITLINEAR_PATH_DECODE || (path == BITLINEAR_PATH_AUTO && m <= 16);
+  return !decode && bl::gemm_glu_supported(m, inter, k);
+}
+}  // namespace
+
+size_t bitlinear_forward_relu2_glu_workspace_bytes(int64_t m, int64_t inter, int64_t k, int32_t quantize_inside,
+                                                   int32_t path) {
+  if (m < 0 || k < 0 || inter < 0) return 0;
+  size_t b = align256((size_t)m * sizeof(int32_t));  // row sums
+  if (quantize_inside) b += align256((size_t)(m * k)) + align256((size_t)m * sizeof(float));
+  if (!glu_fused(m, inter, k, path))
+    b += align256((size_t)(m * 2 * inter) * sizeof(float)) + align256(bl::gemm_prefill_workspace_bytes(m, 2 * inter, k));
+  return b;
+}
+
+bitlinear_status bitlinear_forward_relu2_glu(const float *x, const int8_t *codes_in, const float *deq_in,
+                                             const int32_t *rowsum_in, int64_t m, int64_t k,
+                                             const uint8_t *w_packed, int64_t inter, const float *gamma, float *y,
+                                             int32_t path, void *workspace, size_t workspace_bytes, void *stream) {
+  g_err.clear();
+  if (!w_packed || !y || !gamma) return fail(BITLINEAR_ERR_NULL, "w_packed, gamma and y are required");
+  if (!x && (!codes_in || !deq_in)) return fail(BITLINEAR_ERR_NULL, "give x, or codes_in and deq_in");
+  if (m < 0 || inter <= 0 || inter % 4 != 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || 2 * inter > kMaxDim ||
+      k > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, inter = %lld, k = %lld: need m >= 0, inter > 0, inter %% 4 == 0, "
+                "k > 0, k %% 16 == 0", (long long)m, (long long)inter, (long long)k);
+  if (path != BITLINEAR_PATH_AUTO && path != BITLINEAR_PATH_DECODE && path != BITLINEAR_PATH_PREFILL)
+    return fail(BITLINEAR_ERR_ARG, "unknown path %d", path);
+  if (path == BITLINEAR_PATH_DECODE && m > 16) return fail(BITLINEAR_ERR_SHAPE, "the decode path takes m <= 16");
+  if ((x && !aligned16(x)) || (codes_in && !x && !aligned16(codes_in)) || !aligned16(w_packed) || !aligned16(y))
+    return fail(BITLINEAR_ERR_ALIGN, "x, codes_in, w_packed and y must be 16-byte aligned");
+  const int64_t seg[2] = {inter, 2 * inter};
+  bl::Epilogue ep;
+  BL_TRY(check_segments(gamma, seg, 2, 2 * inter, &ep));
+  const size_t need = bitlinear_forward_relu2_glu_workspace_bytes(m, inter, k, x != nullptr, path);
+  if (m > 0 && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  hipStream_t s = as_stream(stream);
+  char *ws = static_cast<char *>(workspace);
+  int32_t *rowsum = reinterpret_cast<int32_t *>(ws);
+  ws += align256((size_t)m * sizeof(int32_t));
+  const int8_t *codes = codes_in;
+  const float *deq = deq_in;
+  if (x) {
+    int8_t *c = reinterpret_cast<int8_t *>(ws);
+    ws += align256((size_t)(m * k));
+    float *d = reinterpret_cast<float *>(ws);
+    ws += align256((size_t)m * sizeof(float));
+    BL_TRY(launched(bl::launch_quant_acts(BITLINEAR_ACT_ABSMAX, x, nullptr, k, m, k, nullptr, 0.0f, 0, 1, 1, nullptr,
+                                          c, d, rowsum, s),
+                    "quantize_acts"));
+    codes = c;
+    deq = d;
+  } else if (rowsum_in) {
+    rowsum = const_cast<int32_t *>(rowsum_in);
+  } else {
+    BL_TRY(launched(bl::launch_code_rowsum(codes, m, k, rowsum, s), "code row sums"));
+  }
+  if (glu_fused(m, inter, k, path))
+    return launched(bl::launch_gemm_glu(codes, w_packed, deq, rowsum, m, inter, k, ep, y, s), "gated prefill kernel");
+  float *gu = reinterpret_cast<float *>(ws);
+  ws += align256((size_t)(m * 2 * inter) * sizeof(float));
+  int32_t *split_ws = bl::gemm_prefill_workspace_bytes(m, 2 * inter, k) ? reinterpret_cast<int32_t *>(ws) : nullptr;
+  BL_TRY(contract(codes, deq, rowsum, m, k, w_packed, 2 * inter, ep, gu, nullptr, path, split_ws, s));
+  return launched(bl::launch_relu2_glu(gu, m, inter, y, s), "relu2 gating");
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- blocks
@@ -339,6 +411,26 @@ bitlinear_status quant(const BlockBufs &b, int mode, const float *x, const float
 template <typename T>
 T *at(T *p, int64_t off) {
   return p ? p + off : nullptr;
+}
+
+// gate|up -> ReLU^2 gating -> ffn_sub_norm quantization of the chain's b.codes.
+// Untraced and at shapes the gated kernel takes, gate and up never leave the
+// chip: it writes fl32(max(g, 0)^2 * u) ([m][I], in b.gu) and the quantization
+// reads that; otherwise gate|up ([m][2I]) goes through b.gu (and the trace).
+bitlinear_status gated_ffn_input(const BlockBufs &b, int64_t m, int64_t H, int64_t I, const bitlinear_layer &L,
+                                 float eps, float *tr_gate_up, int32_t *tr_acc_gate_up, hipStream_t s) {
+  const int64_t gu_seg[2] = {I, 2 * I};
+  if (!tr_gate_up && !tr_acc_gate_up && bl::gemm_glu_supported(m, I, H)) {
+    bl::Epilogue ep;
+    BL_TRY(check_segments(L.gate_up_gamma, gu_seg, 2, 2 * I, &ep));
+    BL_TRY(launched(bl::launch_gemm_glu(b.codes, L.gate_up, b.deq, b.rowsum, m, I, H, ep, b.gu, s),
+                    "gated prefill kernel"));
+    return quant(b, BITLINEAR_ACT_RMSNORM, b.gu, nullptr, I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1, nullptr, s);
+  }
+  BL_TRY(proj(b, m, H, L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, b.gu, tr_acc_gate_up, s));
+  BL_TRY(copy_to(tr_gate_up, b.gu, (size_t)(m * 2 * I) * 4, s));
+  return quant(b, BITLINEAR_ACT_RELU2_RMSNORM, b.gu, nullptr, 2 * I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1, nullptr,
+               s);
 }
 
 bl::ActSrc act_src(const float *x, int64_t ld, int64_t k, const float *gain) {
@@ -474,10 +566,7 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
     BL_TRY(quant(b, BITLINEAR_ACT_ABSMAX, x, nullptr, H, m, H, nullptr, eps, 0, 1, 1, nullptr, s));
     BL_TRY(copy_to(tr.codes_in, b.codes, (size_t)(m * H), s));
     BL_TRY(copy_to(tr.deq, b.deq, (size_t)m * 4, s));
-    BL_TRY(proj(b, m, H, L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, b.gu, tr.acc_gate_up, s));
-    BL_TRY(copy_to(tr.gate_up, b.gu, (size_t)(m * 2 * I) * 4, s));
-    BL_TRY(quant(b, BITLINEAR_ACT_RELU2_RMSNORM, b.gu, nullptr, 2 * I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1,
-                 nullptr, s));
+    BL_TRY(gated_ffn_input(b, m, H, I, L, eps, tr.gate_up, tr.acc_gate_up, s));
     BL_TRY(copy_to(tr.codes_ffn, b.codes, (size_t)(m * I), s));
     BL_TRY(copy_to(at(tr.deq, 3 * m), b.deq, (size_t)m * 4, s));
     return proj(b, m, I, L.down, H, &L.down_gamma, h_seg, 1, y, tr.acc_down, s);
@@ -512,11 +601,8 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
     BL_TRY(copy_to(at(tr.h, oH), b.h, (size_t)(m * H) * 4, s));
     BL_TRY(copy_to(at(tr.codes_post, oH), b.codes, (size_t)(m * H), s));
     BL_TRY(copy_to(at(tr.deq, 4 * m * l + 2 * m), b.deq, (size_t)m * 4, s));
-    BL_TRY(proj(b, m, H, L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, b.gu, at(tr.acc_gate_up, 2 * oI), s));
-    BL_TRY(copy_to(at(tr.gate_up, 2 * oI), b.gu, (size_t)(m * 2 * I) * 4, s));
     // relu^2 gating -> ffn_sub_norm -> down
-    BL_TRY(quant(b, BITLINEAR_ACT_RELU2_RMSNORM, b.gu, nullptr, 2 * I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1,
-                 nullptr, s));
+    BL_TRY(gated_ffn_input(b, m, H, I, L, eps, at(tr.gate_up, 2 * oI), at(tr.acc_gate_up, 2 * oI), s));
     BL_TRY(copy_to(at(tr.codes_ffn, oI), b.codes, (size_t)(m * I), s));
     BL_TRY(copy_to(at(tr.deq, 4 * m * l + 3 * m), b.deq, (size_t)m * 4, s));
     BL_TRY(proj(b, m, I, L.down, H, &L.down_gamma, h_seg, 1, b.d, at(tr.acc_down, oH), s));

@@ -63,6 +63,8 @@ hipError_t launch_quant_acts(int mode, const float *x, const float *x2, int64_t 
                              float *h_out, int8_t *codes, float *deq, int32_t *rowsum, hipStream_t stream);
 hipError_t launch_code_rowsum(const int8_t *codes, int64_t m, int64_t k, int32_t *rowsum, hipStream_t stream);
 hipError_t launch_add(const float *a, const float *b, float *out, int64_t count, hipStream_t stream);
+// y[m][inter] = fl32(fl32(max(g, 0)^2) * u), gu = [m][g | u], inter % 4 == 0
+hipError_t launch_relu2_glu(const float *gu, int64_t m, int64_t inter, float *y, hipStream_t stream);
 
 size_t absmean_partials(int64_t count);
 hipError_t launch_absmean(const float *w, int64_t count, double *partials, double *gamma_out,
@@ -90,6 +92,11 @@ size_t gemm_prefill_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const float *deq,
                                const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
                                float *y, int32_t *acc_out, int32_t *split_ws, hipStream_t stream);
+// Gated prefill contraction: packed [gate; up] (2 inter rows), gamma[0] gate,
+// gamma[1] up; y[m][j] = fl32(fl32(max(g, 0)^2) * u), [m][inter].
+bool gemm_glu_supported(int64_t m, int64_t inter, int64_t k);
+hipError_t launch_gemm_glu(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,
+                           int64_t m, int64_t inter, int64_t k, const Epilogue &ep, float *y, hipStream_t stream);
 hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const float *deq,
                               const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
                               float *y, int32_t *acc_out, hipStream_t stream);

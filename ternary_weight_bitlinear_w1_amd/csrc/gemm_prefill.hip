@@ -272,12 +272,20 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds_base)
 // Per-token deq / row sums go through a small double-buffered LDS area loaded
 // with the same global->LDS copy, one instruction per wave per tile.
 //
+// Gated form (GLU): the weights are [gate; up] (N = 2 I rows) and a tile
+// covers BN / 2 features j0 .. of both: its 32-column block cb holds gate
+// (cb even) or up (cb odd) rows of features j0 + 32 (cb / 2) .. + 31, so a
+// wave's accumulator tiles 2f and 2f + 1 are the gate and up sums of the same
+// elements and the epilogue stores fl32(fl32(max(g, 0)^2) * u) ([M][I])
+// instead of both (nnterp "BitNet b1.58" page, "The MLP gates with a squared
+// ReLU"; gamma[0] scales the gate rows, gamma[1] the up rows).
+//
 // Split K (S > 1, for shapes with few tiles): work item t covers output tile
 // t mod (tiles) over the K range [s K / S, (s + 1) K / S) with s = t / tiles,
 // and stores its exact int32 sum of q * u over that range to
 // part[s][m][n]; the row sums, rescale and sum over s are left to the
 // consumer (integer sums: the total is the same in any order).
-template <int WM, int WN, int TM, int TN, int P>
+template <int WM, int WN, int TM, int TN, int P, bool GLU>
 __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8_t *__restrict__ A,
                                                                       const uint8_t *__restrict__ B,
                                                                       const float *__restrict__ deq,
@@ -291,7 +299,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   constexpr int kAStage = BM * 128, kBStage = BN * 32, kStage = kAStage + kBStage;
   constexpr int LA = BM / 8 / NW;   // 1 KB activation loads per wave per chunk
   constexpr int LB = BN / 32 / NW;  // 1 KB weight loads per wave per chunk
-  constexpr int kStores = TM * TN * 4;  // 16-byte output stores per wave per tile
+  static_assert(!GLU || TN % 2 == 0, "gate and up tiles come in pairs");
+  constexpr int kStores = TM * (GLU ? TN / 2 : TN) * 4;  // 16-byte output stores per wave per tile
   constexpr int kRowOps = BM / 32;      // 64-dword row-data loads per tile (deq, then row sums)
   static_assert(LA * NW * 8 == BM && LB * NW * 32 == BN, "tile must split into 1 KB wave loads");
   static_assert(kRowOps <= NW && kRowOps >= 2, "one row-data load per wave");
@@ -309,7 +318,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;  // GLU: (N / 2) / (BN / 2)
+  const int I = N / 2;                                       // GLU: features
   const int Tmn = tiles_m * tiles_n;
   const int T = Tmn * S;
   const int G = gridDim.x, b = blockIdx.x;
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
     const int gsize = min(tiles_m - first_m, kGroupM);
     const int in_group = t - group * per_group;
     m0 = (first_m + in_group % gsize) * BM;
-    n0 = (in_group / gsize) * BN;
+    n0 = (in_group / gsize) * (GLU ? BN / 2 : BN);
   };
 
   // ---- issue side: the chunk stream (tile is_i, chunk is_kc)
@@ -352,7 +362,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
     for (int j = 0; j < LB; ++j) {
       const int r = 32 * (wave * LB + j) + (lane >> 1);
       const int h = (lane & 1) ^ ((r >> 3) & 1);
-      b_off[j] = (uint32_t)(is_n0 + r) * (uint32_t)ldb + 16u * h + 32u * (uint32_t)(is_s * nk);
+      const int wrow = GLU ? ((r >> 5) & 1) * I + is_n0 + 32 * (r >> 6) + (r & 31) : is_n0 + r;
+      b_off[j] = (uint32_t)wrow * (uint32_t)ldb + 16u * h + 32u * (uint32_t)(is_s * nk);
     }
   };
   set_src();
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
         for (int tm = 0; tm < TM; ++tm)
           acc[tn][tm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wo, af[s & 1][tm], acc[tn][tm], 0, 0, 0);
       }
-#if BL_GEMM_SGB
+#if BL_GEMM_SGB == 1
       // next k-step's reads first, then unpack and MFMAs interleaved
       if (s < 3) __builtin_amdgcn_sched_group_barrier(0x0100, TM, 0);
 #pragma unroll
@@ -429,6 +440,15 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
         __builtin_amdgcn_sched_group_barrier(0x0002, 7, 0);
         __builtin_amdgcn_sched_group_barrier(0x0008, TM, 0);
       }
+#elif BL_GEMM_SGB == 2
+      // next k-step's reads first, then this step's MFMAs
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x0100, TM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, TM * TN, 0);
+#elif BL_GEMM_SGB == 3
+      // one MFMA, the next k-step's reads, then the rest of this step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x0100, TM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, TM * TN - 1, 0);
 #endif
     }
   };
@@ -449,6 +469,46 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
     float *sc = reinterpret_cast<float *>(scratch_stage) + wave * (32 * 32);
     const float *sd = s_deq[c_i & 1];
     const int *sr = s_rs[c_i & 1];
+    if constexpr (GLU) {
+      const float g_gate = ep.gamma[0], g_up = ep.gamma[1];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int mb = (wm * TM + tm) * 32;
+        const int ml = mb + l32;
+        const int rs = sr[ml];
+        const float dq = sd[ml];
+#pragma unroll
+        for (int f = 0; f < TN / 2; ++f) {
+          const int nb = c_n0 + 32 * ((wn * TN) / 2 + f);  // first feature of this block
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int nl = 8 * j + 4 * half;
+            v4f v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float g = rescale(acc[2 * f][tm][4 * j + e] - rs, dq, g_gate);
+              const float u = rescale(acc[2 * f + 1][tm][4 * j + e] - rs, dq, g_up);
+              const float t = g > 0.0f ? g : 0.0f;
+              v[e] = __fmul_rn(__fmul_rn(t, t), u);
+            }
+            *reinterpret_cast<v4f *>(sc + l32 * 32 + 4 * ((nl >> 2) ^ ((l32 >> 1) & 7))) = v;
+          }
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            acc[2 * f][tm][q] = 0;
+            acc[2 * f + 1][tm][q] = 0;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const v4f v = *reinterpret_cast<const v4f *>(sc + r * 32 + 4 * ((lane & 7) ^ ((r >> 1) & 7)));
+            const int m = min(c_m0 + mb + r, M - 1);
+            __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(Y + (int64_t)m * I + nb + 4 * (lane & 7)));
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       const int mb = (wm * TM + tm) * 32;
@@ -560,7 +620,7 @@ int cu_count() {
   return cached[dev];
 }
 
-template <int WM, int WN, int TM, int TN, int P>
+template <int WM, int WN, int TM, int TN, int P, bool GLU = false>
 hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
                             int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, int splits, int32_t *part,
                             hipStream_t stream) {
@@ -568,7 +628,7 @@ hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const fl
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * (n / BN) * splits;
   int64_t grid = 2 * (int64_t)cu_count();  // two workgroups fit per CU
   if (grid > tiles) grid = tiles;
-  gemm_prefill_kernel<WM, WN, TM, TN, P><<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(
+  gemm_prefill_kernel<WM, WN, TM, TN, P, GLU><<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(
       codes, packed, deq, rowsum, m, n, k, ep, y, part ? nullptr : acc_out, splits, part);
   return hipGetLastError();
 }
@@ -637,6 +697,17 @@ int gemm_prefill_splits(int64_t m, int64_t n, int64_t k) {
     }
   }
   return best;
+}
+
+bool gemm_glu_supported(int64_t m, int64_t inter, int64_t k) {
+  return m > 64 && k % 128 == 0 && inter % (BL_GEMM_BIG_BN / 2) == 0 && inter > 0;
+}
+
+hipError_t launch_gemm_glu(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,
+                           int64_t m, int64_t inter, int64_t k, const Epilogue &ep, float *y, hipStream_t stream) {
+  if (!gemm_glu_supported(m, inter, k) || ep.n_seg != 2) return hipErrorInvalidValue;
+  return launch_pipelined<BL_GEMM_BIG_CFG, 3, true>(codes, packed, deq, rowsum, (int)m, (int)(2 * inter), (int)k, ep,
+                                                    y, nullptr, 1, nullptr, stream);
 }
 
 size_t gemm_prefill_workspace_bytes(int64_t m, int64_t n, int64_t k) {

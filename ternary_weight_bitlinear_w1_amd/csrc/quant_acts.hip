@@ -76,7 +76,35 @@ __global__ __launch_bounds__(kThreads) void add_kernel(const float4 *__restrict_
   }
 }
 
+// y[m][j] = fl32(fl32(max(g, 0)^2) * u) from gu = [m][g (inter) | u (inter)]
+__global__ __launch_bounds__(kThreads) void relu2_glu_kernel(const float *__restrict__ gu, int64_t m, int inter,
+                                                             float *__restrict__ y) {
+  const int q4 = inter / 4;
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < m * q4; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = i / q4;
+    const int c = (int)(i - r * q4);
+    const float4 g = *reinterpret_cast<const float4 *>(gu + r * 2 * inter + 4 * c);
+    const float4 u = *reinterpret_cast<const float4 *>(gu + r * 2 * inter + inter + 4 * c);
+    float4 o;
+    float t;
+    t = g.x > 0.0f ? g.x : 0.0f; o.x = __fmul_rn(__fmul_rn(t, t), u.x);
+    t = g.y > 0.0f ? g.y : 0.0f; o.y = __fmul_rn(__fmul_rn(t, t), u.y);
+    t = g.z > 0.0f ? g.z : 0.0f; o.z = __fmul_rn(__fmul_rn(t, t), u.z);
+    t = g.w > 0.0f ? g.w : 0.0f; o.w = __fmul_rn(__fmul_rn(t, t), u.w);
+    *reinterpret_cast<float4 *>(y + r * inter + 4 * c) = o;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_relu2_glu(const float *gu, int64_t m, int64_t inter, float *y, hipStream_t stream) {
+  const int64_t n4 = m * (inter / 4);
+  if (n4 == 0) return hipSuccess;
+  int64_t blocks = (n4 + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  relu2_glu_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(gu, m, (int)inter, y);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_acts(int mode, const float *x, const float *x2, int64_t ld_x, int64_t m, int64_t k,
                              const float *gain, float eps, int gqa_offset, int head_dim, int group,

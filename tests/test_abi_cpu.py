@@ -75,6 +75,47 @@ def test_forward_workspace_sizes():
     assert f(4096, 13824, 2560, 1) >= 4096 * 2560
 
 
+def test_forward_workspace_holds_split_partials():
+    """Few output tiles: K is split and the workspace holds the int32 partial
+    sums (at least two ranges of m x n)."""
+    f = bl.lib().bitlinear_forward_workspace_bytes
+    assert f(64, 2560, 6912, 0) >= 2 * 64 * 2560 * 4
+    assert f(4096, 2560, 6912, 0) < 4096 * 2560 * 4  # many tiles: no split
+
+
+def _glu(x=A, codes=None, deq=None, rowsum=None, m=4, k=64, w=A, inter=32, gamma=(1.0, 2.0), y=A, path=0, ws=A,
+         wsb=1 << 20):
+    g = (ctypes.c_float * 2)(*gamma)
+    return bl.lib().bitlinear_forward_relu2_glu(x, codes, deq, rowsum, m, k, w, inter, g, y, path, ws, wsb, None)
+
+
+def test_forward_relu2_glu_validation():
+    L = bl.lib()
+    assert L.bitlinear_forward_relu2_glu(A, None, None, None, 4, 64, A, 32, None, A, 0, A, 1 << 20, None) == bl.ERR_NULL
+    assert _glu(x=None) == bl.ERR_NULL
+    assert _glu(w=None) == bl.ERR_NULL
+    assert _glu(y=None) == bl.ERR_NULL
+    assert _glu(inter=0) == bl.ERR_SHAPE
+    assert _glu(inter=30) == bl.ERR_SHAPE  # inter % 4
+    assert _glu(k=24) == bl.ERR_SHAPE
+    assert _glu(m=-1) == bl.ERR_SHAPE
+    assert _glu(path=9) == bl.ERR_ARG
+    assert _glu(path=bl.PATH_DECODE, m=17) == bl.ERR_SHAPE
+    assert _glu(x=MIS) == bl.ERR_ALIGN
+    assert _glu(y=MIS) == bl.ERR_ALIGN
+    assert _glu(ws=None) == bl.ERR_WORKSPACE
+    assert _glu(m=0) == bl.OK
+
+
+def test_forward_relu2_glu_workspace_sizes():
+    f = bl.lib().bitlinear_forward_relu2_glu_workspace_bytes
+    # fused gating (m > 64, k % 128 == 0, inter % 128 == 0): no room for gate|up
+    assert f(4096, 6912, 2560, 0, bl.PATH_AUTO) < 4096 * 2 * 6912 * 4
+    # decode path: gate|up goes through the workspace
+    assert f(4, 6912, 2560, 0, bl.PATH_AUTO) >= 4 * 2 * 6912 * 4
+    assert f(4096, 6912, 2560, 0, bl.PATH_DECODE) >= 4096 * 2 * 6912 * 4
+
+
 def test_quantize_acts_validation():
     q = bl.lib().bitlinear_quantize_acts
     assert q(None, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_NULL

@@ -185,6 +185,47 @@ def test_forward_ragged(m, n, k):
         assert_equal(y, ys[0], "decode == prefill")
 
 
+# ------------------------------------------------------------------------------ gated up-projection
+GLU = [(200, 512, 1024), (130, 384, 256), (65, 256, 2560), (257, 640, 640),  # gating fused in the kernel
+       (300, 200, 1040), (40, 256, 512), (5, 512, 512), (1, 96, 320)]          # gate|up through the workspace
+
+
+@pytest.mark.parametrize("m,inter,k", GLU)
+def test_forward_relu2_glu(m, inter, k):
+    """fl32(max(g, 0)^2 * u) of the gate|up projection, against the oracle's
+    O6 of its O8 output, bit for bit, and equal to forward + gating on the GPU."""
+    note(f"forward relu2 glu m={m} inter={inter} k={k}")
+    x = synth.activations(seed(8, m, k), m, k, 1 if k >= 100 else 0)
+    mats = [Matrix(inter, k, seed(8, inter, 1)), Matrix(inter, k, seed(8, inter, 2), sigma=0.05)]
+    codes, gammas, ends = stacked(mats)
+    packed = gpu_pack(mats)
+    g = [float(np.float32(v)) for v in gammas]
+    ref = oracle.relu2_mul(oracle.forward(x, codes, gammas, ends)["y"], inter)
+    for path in [bl.PATH_AUTO, bl.PATH_PREFILL] + ([bl.PATH_DECODE] if m <= 16 else []):
+        y = host(bl.forward_relu2_glu(packed, k, g, x=gpu(x), path=path))
+        assert_equal(y, ref, f"gated y path {path}")
+    gu = bl.forward(packed, k, g, ends, x=gpu(x), path=bl.PATH_PREFILL)
+    assert_equal(host(bl.forward_relu2_glu(packed, k, g, x=gpu(x))), oracle.relu2_mul(host(gu), inter),
+                 "gated == forward + gating")
+
+
+def test_forward_relu2_glu_full_size():
+    """M=4096 gate|up 2560 -> 2 x 6912 with the gating fused: sampled rows against
+    the oracle (tokens are independent), and determinism."""
+    note("forward relu2 glu m=4096")
+    m, k, inter = 4096, 2560, 6912
+    mats = [Matrix(inter, k, seed(4, 0, 1)), Matrix(inter, k, seed(4, 0, 2))]
+    codes, gammas, ends = stacked(mats)
+    packed = gpu_pack(mats)
+    g = [float(np.float32(v)) for v in gammas]
+    x = synth.activations(seed(4, 1, 7), m, k)
+    y = host(bl.forward_relu2_glu(packed, k, g, x=gpu(x)))
+    rows = np.array([0, 1, 127, 128, 2047, 4095])
+    ref = oracle.relu2_mul(oracle.forward(x[rows], codes, gammas, ends)["y"], inter)
+    assert_equal(y[rows], ref, "sampled rows")
+    assert_equal(host(bl.forward_relu2_glu(packed, k, g, x=gpu(x))), y, "determinism")
+
+
 def test_forward_codes_in_path():
     note("forward with pre-quantized codes")
     m, k, n = 37, 512, 300
