@@ -12,7 +12,8 @@ on the GPU through the C ABI:
 Weights are packed once before timing (the packed-checkpoint mode). ``value``
 is int8 TOPS of the whole step: 2 M N K of both contractions / step time.
 ``roofline`` is the gated gate|up contraction kernel against dense int8 MFMA peak,
-timed with HIP events on the stream it runs on; its ``traffic`` comes from the
+its mean duration over back-to-back launches between two HIP events on the
+stream it runs on; its ``traffic`` comes from the
 committed counter profile when the kernel source is unchanged since. ``decode``
 reports the weight-streaming kernel (M = 1, 4, 16) in packed-weight GB/s against
 HBM peak: the mean time per launch over back-to-back launches, each reading a
@@ -176,17 +177,34 @@ def main():
     ops_gu = 2.0 * M * (2 * I) * H
     ops_d = 2.0 * M * H * I
     tops = (ops_gu + ops_d) / (step_ms * 1e-3) / 1e12
-    gu_tops = ops_gu / (per_op["gemm_gate_up_relu2"] * 1e-3) / 1e12
-    d_tops = ops_d / (per_op["gemm_down"] * 1e-3) / 1e12
+    # each contraction alone, launched back to back between two events on the
+    # stream it runs on: its mean duration per launch
+    def back_to_back(f, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f()
+        a.record(stream)
+        for _ in range(reps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    gu_ms = back_to_back(f_gu, args.steps)
+    d_ms = back_to_back(f_d, args.steps)
+    gu_tops = ops_gu / (gu_ms * 1e-3) / 1e12
+    d_tops = ops_d / (d_ms * 1e-3) / 1e12
+    log(f"gated gate|up alone {gu_ms * 1e3:.1f} us ({gu_tops:.0f} TOPS), down alone {d_ms * 1e3:.1f} us "
+        f"({d_tops:.0f} TOPS)")
     log(f"step {step_ms:.3f} ms ({tops:.0f} TOPS); per op ms {per_op}; wall/step {wall / args.steps * 1e3:.3f} ms")
 
     # quantization kernels against HBM: bytes read + written per launch
     q1_bytes = M * H * 4 + M * H + M * 12
     q2_bytes = M * I * 4 + M * I + M * 12
     kernels = {
-        "gemm_gate_up_relu2": {"ms": per_op["gemm_gate_up_relu2"], "tops": gu_tops,
+        "gemm_gate_up_relu2": {"ms": gu_ms, "ms_in_step": per_op["gemm_gate_up_relu2"], "tops": gu_tops,
                                "frac_mfma": gu_tops / PEAK_INT8_TOPS},
-        "gemm_down": {"ms": per_op["gemm_down"], "tops": d_tops, "frac_mfma": d_tops / PEAK_INT8_TOPS},
+        "gemm_down": {"ms": d_ms, "ms_in_step": per_op["gemm_down"], "tops": d_tops,
+                      "frac_mfma": d_tops / PEAK_INT8_TOPS},
         "quant_x": {"ms": per_op["quant_x"], "gbs": q1_bytes / (per_op["quant_x"] * 1e-3) / 1e9},
         "quant_subnorm": {"ms": per_op["quant_subnorm"], "gbs": q2_bytes / (per_op["quant_subnorm"] * 1e-3) / 1e9},
     }

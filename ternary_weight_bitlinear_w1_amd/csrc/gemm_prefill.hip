@@ -196,9 +196,6 @@ typedef const __attribute__((address_space(1))) void gbl_void_t;
 
 // Tile of the large-M kernel: waves in M, waves in N, 32x32 tiles per wave in M
 // and N (tuned on MI355X; overridable when building variants to sweep).
-#ifndef BL_GEMM_SGB
-#define BL_GEMM_SGB 0
-#endif
 #ifndef BL_GEMM_BIG_CFG
 #define BL_GEMM_BIG_CFG 2, 2, 2, 4
 #define BL_GEMM_BIG_BN 256
@@ -432,24 +429,6 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
         for (int tm = 0; tm < TM; ++tm)
           acc[tn][tm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wo, af[s & 1][tm], acc[tn][tm], 0, 0, 0);
       }
-#if BL_GEMM_SGB == 1
-      // next k-step's reads first, then unpack and MFMAs interleaved
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x0100, TM, 0);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        __builtin_amdgcn_sched_group_barrier(0x0002, 7, 0);
-        __builtin_amdgcn_sched_group_barrier(0x0008, TM, 0);
-      }
-#elif BL_GEMM_SGB == 2
-      // next k-step's reads first, then this step's MFMAs
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x0100, TM, 0);
-      __builtin_amdgcn_sched_group_barrier(0x0008, TM * TN, 0);
-#elif BL_GEMM_SGB == 3
-      // one MFMA, the next k-step's reads, then the rest of this step's MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x0100, TM, 0);
-      __builtin_amdgcn_sched_group_barrier(0x0008, TM * TN - 1, 0);
-#endif
     }
   };
 
