@@ -261,20 +261,42 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict
   const int L = (ldb + 127) >> 7;         // 128-byte lines per row, the last may be partial
   const int l_lo = L * ks / KS, l_hi = L * (ks + 1) / KS;
 
-  // weights first: the long pole
+  // Loads in issue order: this workgroup's token codes (a few KB from L2; the
+  // waves of a row group share them through LDS), then the weights (from
+  // HBM). Loads complete in issue order, so the codes are in LDS while the
+  // weights stream, and each weight piece is used as soon as it arrives: the
+  // barrier below waits for LDS traffic only. Every lane issues the same
+  // number of loads (out-of-range pieces reload a valid address, unused).
+  constexpr int kCodeLoads = (MT * kDot4MaxK / 16 + 255) / 256;
+  const int n_pieces = MT * (K >> 4);
+  v4i cw[kCodeLoads];
+#pragma unroll
+  for (int j = 0; j < kCodeLoads; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int t = i / (K >> 4), c = i - t * (K >> 4);
+    cw[j] = *reinterpret_cast<const v4i *>(i < n_pieces ? A + (int64_t)t * K + 16 * c : A);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   v4i w[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int off = 128 * (l_lo + i) + 16 * p;
-    w[i] = v4i{0, 0, 0, 0};
-    if (l_lo + i < l_hi && off < ldb && n < N) w[i] = *reinterpret_cast<const v4i *>(B + (int64_t)n * ldb + off);
+    const bool use = l_lo + i < l_hi && off < ldb && n < N;
+    w[i] = *reinterpret_cast<const v4i *>(use ? B + (int64_t)n * ldb + off : B);
   }
-  // this workgroup's token codes into LDS (all K: the waves of a row group
-  // share them, the row groups read the same bytes)
-  for (int i = threadIdx.x; i < MT * (K >> 4); i += 256) {
-    const int t = i / (K >> 4), c = i - t * (K >> 4);
-    *reinterpret_cast<v4i *>(sc + t * kDot4MaxK + 16 * c) = *reinterpret_cast<const v4i *>(A + (int64_t)t * K + 16 * c);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < kCodeLoads; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (i < n_pieces) {
+      const int t = i / (K >> 4), c = i - t * (K >> 4);
+      *reinterpret_cast<v4i *>(sc + t * kDot4MaxK + 16 * c) = cw[j];
+    }
   }
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's code stores are in LDS
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
   int rs[MT];
   float dq[MT];
 #pragma unroll
@@ -282,7 +304,6 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict
     rs[t] = rowsum[t];
     dq[t] = deq[t];
   }
-  __syncthreads();
 
   int acc[MT];
 #pragma unroll
