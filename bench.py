@@ -216,6 +216,11 @@ def main():
     if not args.no_decode:
         decode = bench_decode(torch, bl, synth, dev, args.decode_reps, packed_gu, gam_gu, packed_d, gam_d)
 
+    # ---------------------------------------------------------------- online mode
+    online = None
+    if not args.no_decode:
+        online = bench_online(torch, bl, synth, dev, args.decode_reps // 4, w_gate, w_up)
+
     # ---------------------------------------------------------------- 30-layer stack
     stack = None
     if not args.no_stack:
@@ -249,6 +254,7 @@ def main():
                      "algorithmic_bytes_per_launch": M * H + 2 * I * H // 4 + 4 * M * I + 8 * M},
         "kernels": kernels,
         "decode": decode,
+        "online": online,
         "stack": stack,
         "cpu_baseline": cpu,
     }
@@ -330,6 +336,46 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
         del ring
         torch.cuda.empty_cache()
     return res
+
+
+def bench_online(torch, bl, synth, dev, reps, w_gate, w_up):
+    """The online checkpoint mode at one decode token: the fp32 gate and up masters
+    (2 x 6912 x 2560) are ternarized inside every forward (a mean|W| pass and a
+    ternarize pass per matrix, each reading the masters), then projected."""
+    w = torch.from_numpy(np.concatenate([w_gate, w_up])).to(dev)
+    n, k = w.shape
+    x = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 3, 1, 5), 1, k, synth.outlier_count(k))).to(dev)
+    seg = (bl.ctypes.c_int64 * 2)(n // 2, n)
+    L = bl.lib()
+    nb = int(L.bitlinear_forward_online_workspace_bytes(1, n, k, 1, seg, 2))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        st = L.bitlinear_forward_online(x.data_ptr(), None, None, None, 1, k, w.data_ptr(), n, seg, 2, None,
+                                        y.data_ptr(), None, bl.PATH_AUTO, ws.data_ptr(), nb, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"online forward: {bl.status_name(st)} {L.bitlinear_last_error().decode()}")
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    master = 4 * n * k
+    read = 2 * master  # the mean|W| pass and the ternarize pass each read the masters
+    gbs = read / (us * 1e-6) / 1e9
+    log(f"online gate|up m=1: {us:.1f} us per forward, masters {master / 1e6:.1f} MB read twice: {gbs:.0f} GB/s")
+    del w, ws
+    return {"workload": "online mode, gate|up 2560 -> 2 x 6912 fp32 masters, one token", "us": round(us, 2),
+            "master_bytes": master, "master_bytes_read": read, "gbs_masters_read": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 STACK_LAYERS, STACK_HEADS, STACK_KV_HEADS, STACK_HEAD_DIM = 30, 20, 5, 128

@@ -142,8 +142,8 @@ typedef enum {
  *   path       bitlinear_path.
  *   workspace  >= bitlinear_forward_workspace_bytes(m, n, k, x != NULL) bytes
  *              (may be NULL when that is 0).
- * Errors: NULL w_packed/y/gamma/seg_end, or x and codes_in/deq_in both missing
- * -> ERR_NULL; m < 0, n <= 0, k <= 0, k % 16 != 0, bad segments, DECODE with
+ * Errors: NULL w_packed/y/gamma/seg_end, or (m > 0 and) x and codes_in/deq_in
+ * both missing -> ERR_NULL; m < 0, n <= 0, k <= 0, k % 16 != 0, bad segments, DECODE with
  * m > 16 -> ERR_SHAPE; misaligned tensors -> ERR_ALIGN; small workspace ->
  * ERR_WORKSPACE; bad path -> ERR_ARG. m == 0 is a no-op. */
 bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const float *deq_in,
@@ -152,6 +152,30 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
                                    float *y, int32_t *acc_out, int32_t path, void *workspace,
                                    size_t workspace_bytes, void *stream);
 size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside);
+
+/* bitlinear_forward_online — the projection in the checkpoint mode that keeps
+ * the full-precision weights and ternarizes them in every forward ("The two
+ * checkpoints": the online mode; "The projections quantize their inputs and
+ * weights"): per segment, gamma = mean|W| (fp64), codes = sign(W) [|W| >
+ * gamma / 2], packed into the workspace, then bitlinear_forward with the
+ * segments' gammas rounded to fp32.
+ *   w_master   [n][k] fp32 master weights, 16-byte aligned; segment j is rows
+ *              [seg_end[j-1], seg_end[j]) and gets its own gamma.
+ *   seg_end    HOST array of n_seg ascending int64 ends, seg_end[n_seg-1] == n.
+ *   gamma_out  NULL or device [n_seg] fp64: the gammas used.
+ * Other arguments as bitlinear_forward. The result equals
+ * bitlinear_quantize_weights on each segment followed by bitlinear_forward
+ * with those gammas, bit for bit.
+ *   workspace  >= bitlinear_forward_online_workspace_bytes(m, n, k, x != NULL,
+ *              seg_end, n_seg) bytes.
+ * Errors as bitlinear_forward; m == 0 still computes the gammas. */
+bitlinear_status bitlinear_forward_online(const float *x, const int8_t *codes_in, const float *deq_in,
+                                          const int32_t *rowsum_in, int64_t m, int64_t k, const float *w_master,
+                                          int64_t n, const int64_t *seg_end, int32_t n_seg, double *gamma_out,
+                                          float *y, int32_t *acc_out, int32_t path, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+size_t bitlinear_forward_online_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside,
+                                                const int64_t *seg_end, int32_t n_seg);
 
 /* bitlinear_forward_relu2_glu — the MLP's gate and up projections with the
  * squared-ReLU gating applied in the same pass ("The MLP gates with a squared

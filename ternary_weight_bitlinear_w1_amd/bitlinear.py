@@ -75,6 +75,9 @@ def lib():
                                          _p]),
             "bitlinear_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
             "bitlinear_forward_relu2_glu": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _sz, _p]),
+            "bitlinear_forward_online": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _i32, _p, _p, _p, _i32, _p,
+                                                _sz, _p]),
+            "bitlinear_forward_online_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _p, _i32]),
             "bitlinear_forward_relu2_glu_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
             "bitlinear_block_forward": (_i32, [ctypes.POINTER(Block), _p, _i64, _p, ctypes.POINTER(Trace), _p, _sz,
                                                _p]),
@@ -168,6 +171,31 @@ def forward(packed: torch.Tensor, k: int, gamma: Sequence[float], seg_end: Optio
            lib().bitlinear_forward(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), n, g, se,
                                    len(gamma), _ptr(y), _ptr(acc), path, _ptr(ws), nb, _stream(dev)))
     return (y, acc) if want_acc else y
+
+
+def forward_online(w_master: torch.Tensor, seg_end: Optional[Sequence[int]] = None,
+                   x: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+                   deq: Optional[torch.Tensor] = None, rowsum: Optional[torch.Tensor] = None,
+                   want_acc: bool = False, path: int = PATH_AUTO, out: Optional[torch.Tensor] = None):
+    """Online mode: ternarize the fp32 masters [n][k] (one gamma per segment) and
+    project. Returns (y, gamma) or (y, acc, gamma); gamma is a device fp64 tensor."""
+    n, k = w_master.shape
+    src = x if x is not None else codes
+    m = src.shape[0]
+    dev = w_master.device
+    if seg_end is None:
+        seg_end = [n]
+    se = (ctypes.c_int64 * len(seg_end))(*[int(v) for v in seg_end])
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
+    gamma = torch.empty(len(seg_end), dtype=torch.float64, device=dev)
+    nb = lib().bitlinear_forward_online_workspace_bytes(m, n, k, 1 if x is not None else 0, se, len(seg_end))
+    ws = _workspace(nb, dev)
+    _check("bitlinear_forward_online",
+           lib().bitlinear_forward_online(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(w_master), n, se,
+                                          len(seg_end), _ptr(gamma), _ptr(y), _ptr(acc), path, _ptr(ws), nb,
+                                          _stream(dev)))
+    return (y, acc, gamma) if want_acc else (y, gamma)
 
 
 def forward_relu2_glu(packed: torch.Tensor, k: int, gamma: Sequence[float], x: Optional[torch.Tensor] = None,

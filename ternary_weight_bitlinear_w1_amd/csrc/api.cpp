@@ -64,9 +64,19 @@ bitlinear_status launched(hipError_t e, const char *what) {
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 // ---------------------------------------------------------------- forward core
+bitlinear_status make_segments(const float *gamma, const int64_t *seg_end, int32_t n_seg, int64_t n,
+                               bl::Epilogue *ep);
+
 bitlinear_status check_segments(const float *gamma, const int64_t *seg_end, int32_t n_seg, int64_t n,
                                 bl::Epilogue *ep) {
   if (!gamma || !seg_end) return fail(BITLINEAR_ERR_NULL, "gamma and seg_end are required");
+  return make_segments(gamma, seg_end, n_seg, n, ep);
+}
+
+// gamma: host scales, or NULL when they live on the device (set gamma_dev after)
+bitlinear_status make_segments(const float *gamma, const int64_t *seg_end, int32_t n_seg, int64_t n,
+                               bl::Epilogue *ep) {
+  if (!seg_end) return fail(BITLINEAR_ERR_NULL, "seg_end is required");
   if (n_seg < 1 || n_seg > BITLINEAR_MAX_SEGMENTS)
     return fail(BITLINEAR_ERR_SHAPE, "n_seg = %d, must be 1..%d", n_seg, BITLINEAR_MAX_SEGMENTS);
   int64_t prev = 0;
@@ -77,9 +87,10 @@ bitlinear_status check_segments(const float *gamma, const int64_t *seg_end, int3
   if (prev != n) return fail(BITLINEAR_ERR_SHAPE, "seg_end[n_seg-1] = %lld, must equal n = %lld", (long long)prev,
                              (long long)n);
   for (int s = 0; s < BITLINEAR_MAX_SEGMENTS; ++s) {
-    ep->gamma[s] = s < n_seg ? gamma[s] : 0.0f;
+    ep->gamma[s] = s < n_seg && gamma ? gamma[s] : 0.0f;
     ep->seg_end[s] = s < n_seg ? (int32_t)seg_end[s] : (int32_t)n;
   }
+  ep->gamma_dev = nullptr;
   ep->n_seg = n_seg;
   ep->blocks32 = 1;
   for (int s = 0; s < n_seg; ++s)
@@ -189,31 +200,32 @@ size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_
   return b;
 }
 
-bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const float *deq_in,
-                                   const int32_t *rowsum_in, int64_t m, int64_t k, const uint8_t *w_packed, int64_t n,
-                                   const float *gamma, const int64_t *seg_end, int32_t n_seg, float *y,
-                                   int32_t *acc_out, int32_t path, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
-  g_err.clear();
-  if (!w_packed || !y) return fail(BITLINEAR_ERR_NULL, "w_packed and y are required");
-  if (!x && (!codes_in || !deq_in)) return fail(BITLINEAR_ERR_NULL, "give x, or codes_in and deq_in");
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the packed and the online forward.
+bitlinear_status check_forward_args(const float *x, const int8_t *codes_in, const float *deq_in, int64_t m,
+                                    int64_t k, const void *w, int64_t n, float *y, int32_t path) {
+  if (!w || (m != 0 && !y)) return fail(BITLINEAR_ERR_NULL, "the weights and y are required");
+  if (m != 0 && !x && (!codes_in || !deq_in)) return fail(BITLINEAR_ERR_NULL, "give x, or codes_in and deq_in");
   if (m < 0 || n <= 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
     return fail(BITLINEAR_ERR_SHAPE, "m = %lld, n = %lld, k = %lld: need m >= 0, n > 0, k > 0, k %% 16 == 0",
                 (long long)m, (long long)n, (long long)k);
-  bl::Epilogue ep;
-  BL_TRY(check_segments(gamma, seg_end, n_seg, n, &ep));
   if (path != BITLINEAR_PATH_AUTO && path != BITLINEAR_PATH_DECODE && path != BITLINEAR_PATH_PREFILL)
     return fail(BITLINEAR_ERR_ARG, "unknown path %d", path);
   if (path == BITLINEAR_PATH_DECODE && m > 16) return fail(BITLINEAR_ERR_SHAPE, "the decode path takes m <= 16");
-  if ((x && !aligned16(x)) || (codes_in && !x && !aligned16(codes_in)) || !aligned16(w_packed) || !aligned16(y))
-    return fail(BITLINEAR_ERR_ALIGN, "x, codes_in, w_packed and y must be 16-byte aligned");
-  const size_t need = bitlinear_forward_workspace_bytes(m, n, k, x != nullptr);
-  if (m > 0 && (!workspace || workspace_bytes < need))
-    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  if (m == 0) return BITLINEAR_OK;
-  BL_TRY(check_device());
-  hipStream_t s = as_stream(stream);
-  char *ws = static_cast<char *>(workspace);
+  if ((x && !aligned16(x)) || (codes_in && !x && !aligned16(codes_in)) || !aligned16(w) || !aligned16(y))
+    return fail(BITLINEAR_ERR_ALIGN, "x, codes_in, the weights and y must be 16-byte aligned");
+  return BITLINEAR_OK;
+}
+
+// The projection once the arguments are checked: quantize x (or take the
+// given codes), then contract with the packed weights. ws holds
+// bitlinear_forward_workspace_bytes(m, n, k, x != NULL) bytes.
+bitlinear_status forward_impl(const float *x, const int8_t *codes_in, const float *deq_in, const int32_t *rowsum_in,
+                              int64_t m, int64_t k, const uint8_t *w_packed, int64_t n, const bl::Epilogue &ep,
+                              float *y, int32_t *acc_out, int32_t path, char *ws, hipStream_t s) {
   int32_t *rowsum = reinterpret_cast<int32_t *>(ws);
   ws += align256((size_t)m * sizeof(int32_t));
   const size_t split_bytes = bl::gemm_prefill_workspace_bytes(m, n, k);
@@ -236,6 +248,77 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
     BL_TRY(launched(bl::launch_code_rowsum(codes, m, k, rowsum, s), "code row sums"));
   }
   return contract(codes, deq, rowsum, m, k, w_packed, n, ep, y, acc_out, path, split_ws, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const float *deq_in,
+                                   const int32_t *rowsum_in, int64_t m, int64_t k, const uint8_t *w_packed, int64_t n,
+                                   const float *gamma, const int64_t *seg_end, int32_t n_seg, float *y,
+                                   int32_t *acc_out, int32_t path, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  g_err.clear();
+  BL_TRY(check_forward_args(x, codes_in, deq_in, m, k, w_packed, n, y, path));
+  bl::Epilogue ep;
+  BL_TRY(check_segments(gamma, seg_end, n_seg, n, &ep));
+  const size_t need = bitlinear_forward_workspace_bytes(m, n, k, x != nullptr);
+  if (m > 0 && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  return forward_impl(x, codes_in, deq_in, rowsum_in, m, k, w_packed, n, ep, y, acc_out, path,
+                      static_cast<char *>(workspace), as_stream(stream));
+}
+
+// ---------------------------------------------------------------- online mode
+size_t bitlinear_forward_online_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside,
+                                                const int64_t *seg_end, int32_t n_seg) {
+  if (m < 0 || n < 0 || k < 0 || !seg_end || n_seg < 1 || n_seg > BITLINEAR_MAX_SEGMENTS) return 0;
+  size_t partials = 1;
+  int64_t lo = 0;
+  for (int s = 0; s < n_seg; ++s) {
+    const size_t p = bl::absmean_partials((seg_end[s] - lo) * k);
+    if (p > partials) partials = p;
+    lo = seg_end[s];
+  }
+  return bitlinear_forward_workspace_bytes(m, n, k, quantize_inside) + align256((size_t)(n * (k / 4))) +
+         align256(sizeof(double) * BITLINEAR_MAX_SEGMENTS) + align256(partials * sizeof(double));
+}
+
+bitlinear_status bitlinear_forward_online(const float *x, const int8_t *codes_in, const float *deq_in,
+                                          const int32_t *rowsum_in, int64_t m, int64_t k, const float *w_master,
+                                          int64_t n, const int64_t *seg_end, int32_t n_seg, double *gamma_out,
+                                          float *y, int32_t *acc_out, int32_t path, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  g_err.clear();
+  BL_TRY(check_forward_args(x, codes_in, deq_in, m, k, w_master, n, y, path));
+  bl::Epilogue ep;
+  BL_TRY(make_segments(nullptr, seg_end, n_seg, n, &ep));
+  const size_t need = bitlinear_forward_online_workspace_bytes(m, n, k, x != nullptr, seg_end, n_seg);
+  if (!workspace || workspace_bytes < need) return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  BL_TRY(check_device());
+  hipStream_t s = as_stream(stream);
+  // layout: [forward workspace][packed weights][gammas][absmean partials]
+  char *ws_fwd = static_cast<char *>(workspace);
+  char *ws = ws_fwd + bitlinear_forward_workspace_bytes(m, n, k, x != nullptr);
+  uint8_t *packed = reinterpret_cast<uint8_t *>(ws);
+  ws += align256((size_t)(n * (k / 4)));
+  double *gam = gamma_out ? gamma_out : reinterpret_cast<double *>(ws);
+  ws += align256(sizeof(double) * BITLINEAR_MAX_SEGMENTS);
+  double *partials = reinterpret_cast<double *>(ws);
+  int64_t lo = 0;
+  for (int j = 0; j < n_seg; ++j) {
+    const int64_t rows = seg_end[j] - lo;
+    BL_TRY(launched(bl::launch_absmean(w_master + lo * k, rows * k, partials, gam + j, s), "absmean"));
+    BL_TRY(launched(bl::launch_ternarize_pack(w_master + lo * k, rows, k, gam + j, packed + lo * (k / 4), s),
+                    "ternarize"));
+    lo = seg_end[j];
+  }
+  if (m == 0) return BITLINEAR_OK;
+  ep.gamma_dev = gam;
+  return forward_impl(x, codes_in, deq_in, rowsum_in, m, k, packed, n, ep, y, acc_out, path, ws_fwd, s);
 }
 
 // ---------------------------------------------------------------- gated up-projection

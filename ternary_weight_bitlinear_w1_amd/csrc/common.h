@@ -20,7 +20,21 @@ struct Epilogue {
   int32_t seg_end[BITLINEAR_MAX_SEGMENTS];
   int32_t n_seg;
   int32_t blocks32;  // every segment end is a multiple of 32: gamma is constant per 32 columns
+  // NULL, or the segments' fp64 gammas in device memory (as the weight pass
+  // writes them); they replace gamma[], rounded to fp32
+  const double *gamma_dev;
 };
+
+// A kernel's view of its epilogue: device-side gammas read and rounded once.
+__device__ __forceinline__ Epilogue resolve_gamma(const Epilogue &in) {
+  Epilogue e = in;
+  if (e.gamma_dev) {
+#pragma unroll
+    for (int s = 0; s < BITLINEAR_MAX_SEGMENTS; ++s)
+      if (s < e.n_seg) e.gamma[s] = (float)e.gamma_dev[s];
+  }
+  return e;
+}
 
 __device__ __forceinline__ float epi_gamma(const Epilogue &ep, int n) {
   float g = ep.gamma[0];

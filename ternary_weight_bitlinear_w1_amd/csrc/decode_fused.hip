@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
   const int r = rg * 8 + (lane >> 3);  // local row
   const int p = lane & 7;
   const int N = a.n, K = a.src.k;
+  const Epilogue ep = resolve_gamma(a.ep);
   int n;
   if constexpr (EPI == FUSED_EPI_RELU2) {
     const int half = R / 2, inter = N / 2;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
   }
   __syncthreads();
   if (ks == 0 && p == 0 && valid) {
-    const float g = epi_gamma(a.ep, n);
+    const float g = epi_gamma(ep, n);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       if (t < a.m) {

@@ -52,8 +52,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_generic_kernel(const int8_t 
                                                                    const uint8_t *__restrict__ B,
                                                                    const float *__restrict__ deq,
                                                                    const int32_t *__restrict__ rowsum, int M, int N,
-                                                                   int K, Epilogue ep, float *__restrict__ Y,
+                                                                   int K, Epilogue ep_in, float *__restrict__ Y,
                                                                    int32_t *__restrict__ acc_out) {
+  const Epilogue ep = resolve_gamma(ep_in);
   constexpr int kThreads = WM * WN * 64;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int kChunks = BM * (kBK / 16);  // 16-byte pieces of one A tile
@@ -287,10 +288,11 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
                                                                       const uint8_t *__restrict__ B,
                                                                       const float *__restrict__ deq,
                                                                       const int32_t *__restrict__ rowsum, int M,
-                                                                      int N, int K, Epilogue ep,
+                                                                      int N, int K, Epilogue ep_in,
                                                                       float *__restrict__ Y,
                                                                       int32_t *__restrict__ acc_out, int S,
                                                                       int32_t *__restrict__ part) {
+  const Epilogue ep = resolve_gamma(ep_in);
   constexpr int NW = WM * WN;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int kAStage = BM * 128, kBStage = BN * 32, kStage = kAStage + kBStage;
@@ -617,8 +619,9 @@ hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const fl
 __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__restrict__ part, int S,
                                                             const float *__restrict__ deq,
                                                             const int32_t *__restrict__ rowsum, int M, int N,
-                                                            Epilogue ep, float *__restrict__ Y,
+                                                            Epilogue ep_in, float *__restrict__ Y,
                                                             int32_t *__restrict__ acc_out) {
+  const Epilogue ep = resolve_gamma(ep_in);
   const int64_t plane = (int64_t)M * N;
   const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (4 * i4 >= plane) return;

@@ -63,8 +63,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
                                                               const uint8_t *__restrict__ B,
                                                               const float *__restrict__ deq,
                                                               const int32_t *__restrict__ rowsum, int M, int N, int K,
-                                                              Epilogue ep, float *__restrict__ Y,
+                                                              Epilogue ep_in, float *__restrict__ Y,
                                                               int32_t *__restrict__ acc_out) {
+  const Epilogue ep = resolve_gamma(ep_in);
   __shared__ int red[NW][RT][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16 * RT;
@@ -164,8 +165,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_loop_kernel(const int8_t *__rest
                                                             const uint8_t *__restrict__ B,
                                                             const float *__restrict__ deq,
                                                             const int32_t *__restrict__ rowsum, int M, int N, int K,
-                                                            Epilogue ep, float *__restrict__ Y,
+                                                            Epilogue ep_in, float *__restrict__ Y,
                                                             int32_t *__restrict__ acc_out) {
+  const Epilogue ep = resolve_gamma(ep_in);
   __shared__ int red[NW][RT][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16 * RT;
@@ -248,8 +250,9 @@ constexpr int kDot4MaxK = 8192;
 template <int MT, int KS, int LPW>
 __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
                                                         const float *__restrict__ deq,
-                                                        const int32_t *__restrict__ rowsum, int N, int K, Epilogue ep,
+                                                        const int32_t *__restrict__ rowsum, int N, int K, Epilogue ep_in,
                                                         float *__restrict__ Y, int32_t *__restrict__ acc_out) {
+  const Epilogue ep = resolve_gamma(ep_in);
   constexpr int RG = 4 / KS;  // row groups of 8 rows per workgroup
   __shared__ __attribute__((aligned(16))) int8_t sc[MT * kDot4MaxK];
   __shared__ int red[KS][RG][8][MT];

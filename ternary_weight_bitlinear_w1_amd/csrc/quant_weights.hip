@@ -18,7 +18,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxPartials = 2048;
-constexpr int64_t kPerBlock = 1 << 16;  // elements per partial, at least
+constexpr int64_t kPerBlock = 1 << 14;  // elements per partial, at least
+constexpr int kUnroll = 8;              // float4 loads in flight per thread
 
 __device__ __forceinline__ double block_sum(double v, double *red) {
   v = wave_sum(v);
@@ -36,13 +37,23 @@ __global__ __launch_bounds__(kThreads) void absmean_partial_kernel(const float *
   __shared__ double red[kThreads / 64];
   const int64_t lo = blockIdx.x * per;
   const int64_t hi = lo + per < count ? lo + per : count;
+  // thread t adds elements t, t + 256, ... (in float4 units) of the slice in
+  // order; kUnroll loads are issued before their sums
   double s = 0.0;
-  for (int64_t i = lo + 4 * (int64_t)threadIdx.x; i < hi; i += 4 * kThreads) {
-    const float4 v = *reinterpret_cast<const float4 *>(w + i);
-    s += fabs((double)v.x);
-    s += fabs((double)v.y);
-    s += fabs((double)v.z);
-    s += fabs((double)v.w);
+  for (int64_t i0 = lo + 4 * (int64_t)threadIdx.x; i0 < hi; i0 += 4 * kThreads * kUnroll) {
+    float4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t i = i0 + 4 * (int64_t)kThreads * j;
+      v[j] = i < hi ? *reinterpret_cast<const float4 *>(w + i) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      s += fabs((double)v[j].x);
+      s += fabs((double)v[j].y);
+      s += fabs((double)v[j].z);
+      s += fabs((double)v[j].w);
+    }
   }
   s = block_sum(s, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = s;

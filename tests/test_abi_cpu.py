@@ -116,6 +116,36 @@ def test_forward_relu2_glu_workspace_sizes():
     assert f(4096, 6912, 2560, 0, bl.PATH_DECODE) >= 4096 * 2 * 6912 * 4
 
 
+def _onl(x=A, codes=None, deq=None, rowsum=None, m=4, k=64, w=A, n=32, seg=(32,), gamma=None, y=A, acc=None, path=0,
+         ws=A, wsb=1 << 24):
+    s = (ctypes.c_int64 * max(1, len(seg)))(*seg)
+    return bl.lib().bitlinear_forward_online(x, codes, deq, rowsum, m, k, w, n, s if seg else None, len(seg), gamma,
+                                             y, acc, path, ws, wsb, None)
+
+
+def test_forward_online_validation():
+    assert _onl(w=None) == bl.ERR_NULL
+    assert _onl(x=None) == bl.ERR_NULL
+    assert _onl(y=None) == bl.ERR_NULL
+    assert _onl(seg=()) == bl.ERR_NULL     # seg_end is required
+    assert _onl(seg=(31,)) == bl.ERR_SHAPE
+    assert _onl(seg=(20, 10)) == bl.ERR_SHAPE
+    assert _onl(k=24) == bl.ERR_SHAPE
+    assert _onl(path=5) == bl.ERR_ARG
+    assert _onl(w=MIS) == bl.ERR_ALIGN
+    assert _onl(ws=None) == bl.ERR_WORKSPACE
+    assert _onl(wsb=64) == bl.ERR_WORKSPACE
+
+
+def test_forward_online_workspace_sizes():
+    f = bl.lib().bitlinear_forward_online_workspace_bytes
+    seg = (ctypes.c_int64 * 2)(6912, 13824)
+    # the packed copy of the masters and the forward's own workspace
+    assert f(1, 13824, 2560, 1, seg, 2) >= 13824 * 2560 // 4 + bl.lib().bitlinear_forward_workspace_bytes(1, 13824,
+                                                                                                           2560, 1)
+    assert f(1, 13824, 2560, 1, None, 2) == 0
+
+
 def test_quantize_acts_validation():
     q = bl.lib().bitlinear_quantize_acts
     assert q(None, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_NULL

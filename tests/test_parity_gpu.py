@@ -226,6 +226,38 @@ def test_forward_relu2_glu_full_size():
     assert_equal(host(bl.forward_relu2_glu(packed, k, g, x=gpu(x))), y, "determinism")
 
 
+# ------------------------------------------------------------------------------ online mode
+ONLINE = [(1, [512], 256), (37, [100, 300], 512), (4, [6912, 13824], 2560), (130, [2560], 6912), (0, [64], 128)]
+
+
+@pytest.mark.parametrize("m,seg,k", ONLINE)
+def test_forward_online(m, seg, k):
+    """Ternarize fp32 masters inside the forward: gamma per segment within 1e-6 of
+    the oracle's; y and acc bit-exact against the oracle run with the GPU's gamma
+    (a code can only differ within |dgamma| / 2 of its threshold); equal to
+    quantize_weights + forward on the GPU."""
+    note(f"forward online m={m} seg={seg} k={k}")
+    n = seg[-1]
+    lo = [0] + seg[:-1]
+    mats = [Matrix(hi - a, k, seed(9, n + j, k), sigma=0.02 + 0.01 * j) for j, (a, hi) in enumerate(zip(lo, seg))]
+    w = np.concatenate([mt.w for mt in mats])
+    x = synth.activations(seed(9, m, k), max(m, 1), k, 1 if k >= 100 else 0)[:m]
+    y, acc, gamma = bl.forward_online(gpu(w), seg, x=gpu(x), want_acc=True)
+    g = host(gamma)
+    for j, mt in enumerate(mats):
+        assert abs(g[j] - mt.gamma) <= GAMMA_TOL * mt.gamma, (j, g[j], mt.gamma)
+    codes = np.concatenate([oracle.ternarize(mt.w, float(g[j])) for j, mt in enumerate(mats)])
+    if m == 0:
+        assert y.shape == (0, n)
+        return
+    ref = oracle.forward(x, codes, [float(v) for v in g], seg)
+    assert_equal(host(acc), ref["acc"], "online acc")
+    assert_equal(host(y), ref["y"], "online y")
+    packed = torch.cat([bl.quantize_weights(gpu(mt.w))[0] for mt in mats])
+    y_p = bl.forward(packed, k, [float(np.float32(v)) for v in g], seg, x=gpu(x))
+    assert_equal(host(y_p), host(y), "online == quantize_weights + forward")
+
+
 def test_forward_codes_in_path():
     note("forward with pre-quantized codes")
     m, k, n = 37, 512, 300
