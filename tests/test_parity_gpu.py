@@ -170,7 +170,10 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           (1, 77, 64), (2, 200, 320), (3, 1000, 576), (4, 40, 8192), (1, 9000, 1024), (4, 5000, 448),
           # few output tiles, where K is split into ranges (16, 8, 4 here) whose int32 partial sums a
           # second kernel adds, and neighbours that are not split
-          (9, 512, 4096), (5, 256, 2048), (48, 1024, 3072), (37, 512, 1024), (100, 384, 768)]
+          (9, 512, 4096), (5, 256, 2048), (48, 1024, 3072), (37, 512, 1024), (100, 384, 768),
+          # 17..64 tokens with K % 256 == 0 (AUTO takes the skinny kernel): one and two token tiles,
+          # ragged rows, few and many supersteps per wave
+          (17, 130, 512), (32, 1000, 768), (33, 48, 2560), (64, 2600, 6912), (50, 3000, 1024)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED)
@@ -179,7 +182,7 @@ def test_forward_ragged(m, n, k):
     x = _edge_rows(synth.activations(seed(5, m, k), m, k, 1 if k >= 100 else 0))
     n1 = n // 3 + 1 if n % 128 else n // 2
     mats = [Matrix(n1, k, seed(5, n, 1)), Matrix(n - n1, k, seed(5, n, 2), sigma=0.05)]
-    paths = [bl.PATH_PREFILL] + ([bl.PATH_DECODE] if m <= 16 else [])
+    paths = [bl.PATH_PREFILL, bl.PATH_AUTO] + ([bl.PATH_DECODE] if m <= 16 else [])
     ys = [host(_check_forward(x, mats, p, f"path {p}")) for p in paths]
     for y in ys[1:]:
         assert_equal(y, ys[0], "decode == prefill")
@@ -287,6 +290,8 @@ def test_forward_decode_full_size(m, proj):
         mats = [Matrix(2560, k, seed(3, 0, 3))]
     x = synth.activations(seed(3, m, k), m, k, synth.outlier_count(k))
     y_pre = _check_forward(x, mats, bl.PATH_PREFILL, f"prefill {proj}")
+    y_auto = _check_forward(x, mats, bl.PATH_AUTO, f"auto {proj}")  # m = 64: the skinny kernel
+    assert_equal(host(y_auto), host(y_pre), "auto == prefill")
     if m <= 16:
         y_dec = _check_forward(x, mats, bl.PATH_DECODE, f"decode {proj}")
         assert_equal(host(y_dec), host(y_pre), "decode == prefill")
