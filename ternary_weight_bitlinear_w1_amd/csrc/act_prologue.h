@@ -51,24 +51,57 @@ struct RawIn {
   float4 g;  // RMSNorm gain (1 when the gain is absent: multiplying by 1 is exact)
 };
 
-template <int MODE>
+// rescale of four exact sums (less the code row sum), as the contraction does
+__device__ __forceinline__ float4 part_rescale(const Src &s, v4i t, int rs, float dq, int c) {
+  float4 y;
+  y.x = rescale(t[0] - rs, dq, epi_gamma(s.part_ep, c));
+  y.y = rescale(t[1] - rs, dq, epi_gamma(s.part_ep, c + 1));
+  y.z = rescale(t[2] - rs, dq, epi_gamma(s.part_ep, c + 2));
+  y.w = rescale(t[3] - rs, dq, epi_gamma(s.part_ep, c + 3));
+  return y;
+}
+
+// Elements c .. c+3 of row r of a projection output given as split-K partial
+// sums: the exact sums over the splits, less the row sum of the codes,
+// rescaled as the contraction's own epilogue does.
+__device__ __forceinline__ float4 part_load(const Src &s, int64_t r, int c) {
+  const int32_t *p = s.part + r * s.ld + c;
+  v4i t = *reinterpret_cast<const v4i *>(p);
+  for (int j = 1; j < s.part_splits; ++j) t += *reinterpret_cast<const v4i *>(p + j * s.part_plane);
+  return part_rescale(s, t, s.part_rowsum[r], s.part_deq[r], c);
+}
+
+// PART: the projection-output operand comes from split-K partial sums.
+template <int MODE, bool PART = false>
 __device__ __forceinline__ RawIn raw_load(const Src &s, int64_t r, int f) {
   RawIn v;
   const float *row = s.x + r * s.ld;
+  constexpr bool kPartA = PART && MODE != ACT_RESID_RMSNORM;  // the residual form's projection operand is b
   if constexpr (MODE == ACT_GQA_RMSNORM) {
     // element e of the attention output reads value head (e / head_dim) / group
     const int e = 4 * f;
     const int head = e / s.head_dim, d = e - head * s.head_dim;
-    v.a = *reinterpret_cast<const float4 *>(row + s.gqa_offset + (head / s.group) * s.head_dim + d);
+    const int col = s.gqa_offset + (head / s.group) * s.head_dim + d;
+    if constexpr (kPartA) v.a = part_load(s, r, col);
+    else v.a = *reinterpret_cast<const float4 *>(row + col);
   } else {
-    v.a = *reinterpret_cast<const float4 *>(row + 4 * f);
+    if constexpr (kPartA) v.a = part_load(s, r, 4 * f);
+    else v.a = *reinterpret_cast<const float4 *>(row + 4 * f);
   }
-  if constexpr (MODE == BITLINEAR_ACT_RELU2_RMSNORM) v.b = *reinterpret_cast<const float4 *>(row + s.k + 4 * f);
-  if constexpr (MODE == ACT_RESID_RMSNORM) v.b = *reinterpret_cast<const float4 *>(s.x2 + r * s.ld + 4 * f);
+  if constexpr (MODE == BITLINEAR_ACT_RELU2_RMSNORM) {
+    if constexpr (PART) v.b = part_load(s, r, s.k + 4 * f);
+    else v.b = *reinterpret_cast<const float4 *>(row + s.k + 4 * f);
+  }
+  if constexpr (MODE == ACT_RESID_RMSNORM) {
+    if constexpr (PART) v.b = part_load(s, r, 4 * f);
+    else v.b = *reinterpret_cast<const float4 *>(s.x2 + r * s.ld + 4 * f);
+  }
   if constexpr (MODE != BITLINEAR_ACT_ABSMAX) {
-    // branch-free: without a gain, load x again and use 1
+    // branch-free: without a gain, load a row of the input again and use 1
+    // (from the partial sums when those replace x, which is then NULL)
     const bool has_gain = s.gain != nullptr;
-    const float4 g = *reinterpret_cast<const float4 *>((has_gain ? s.gain : row) + 4 * f);
+    const float *again = kPartA ? reinterpret_cast<const float *>(s.part + r * s.ld) : row;
+    const float4 g = *reinterpret_cast<const float4 *>((has_gain ? s.gain : again) + 4 * f);
     v.g = has_gain ? g : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
   }
   return v;
@@ -124,16 +157,94 @@ struct RowStage {
   RawIn in[NV];
 };
 
+// Column of the projection output that operand p (0: a, 1: the ReLU^2 form's
+// up half) of elements 4f .. 4f+3 reads.
+template <int MODE>
+__device__ __forceinline__ int part_col(const Src &s, int f, int p) {
+  if constexpr (MODE == ACT_GQA_RMSNORM) {
+    const int e = 4 * f;
+    const int head = e / s.head_dim, d = e - head * s.head_dim;
+    return s.gqa_offset + (head / s.group) * s.head_dim + d;
+  } else {
+    return p ? s.k + 4 * f : 4 * f;
+  }
+}
+
+// A row whose projection operand is given as split-K partial sums. The plain
+// operands (residual summand, gain) are issued first; then the partial sums
+// plane by plane, two planes at a time for every slot of the thread, so a row
+// takes about S / 2 memory round trips rather than S per slot. Integer sums are
+// exact, so the order of the planes does not matter.
 template <int MODE, int NV>
-__device__ __forceinline__ void row_load(const Src &s, int64_t r, RowStage<NV> &st) {
-  static_assert(NV > 0, "register-resident rows only");
+__device__ __forceinline__ void row_load_part(const Src &s, int64_t r, RowStage<NV> &st) {
+  constexpr int NP = MODE == BITLINEAR_ACT_RELU2_RMSNORM ? 2 : 1;
   const int nf = s.k >> 2;
-  // every lane issues the same NV loads (past the row end it reloads element
-  // 0, unused), so the number of loads in flight is known where they are used
+  int col[NV][NP];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int f = threadIdx.x + j * kQuantThreads;
-    st.in[j] = raw_load<MODE>(s, r, f < nf ? f : 0);
+    int f = threadIdx.x + j * kQuantThreads;
+    f = f < nf ? f : 0;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) col[j][p] = part_col<MODE>(s, f, p);
+    if constexpr (MODE == ACT_RESID_RMSNORM)
+      st.in[j].a = *reinterpret_cast<const float4 *>(s.x + r * s.ld + 4 * f);
+    const bool has_gain = s.gain != nullptr;
+    const float *again = reinterpret_cast<const float *>(s.part + r * s.ld);
+    const float4 g = *reinterpret_cast<const float4 *>((has_gain ? s.gain : again) + 4 * f);
+    st.in[j].g = has_gain ? g : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  }
+  const int32_t *base = s.part + r * s.ld;
+  const int S = s.part_splits;
+  v4i t[NV][NP];
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) t[j][p] = *reinterpret_cast<const v4i *>(base + col[j][p]);
+  for (int sp = 1; sp < S; sp += 2) {
+    // past the last plane the second load repeats plane sp and is not added
+    const bool two = sp + 1 < S;
+    const int64_t o0 = sp * s.part_plane, o1 = (two ? sp + 1 : sp) * s.part_plane;
+    v4i u0[NV][NP], u1[NV][NP];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        u0[j][p] = *reinterpret_cast<const v4i *>(base + o0 + col[j][p]);
+        u1[j][p] = *reinterpret_cast<const v4i *>(base + o1 + col[j][p]);
+      }
+    const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) t[j][p] += u0[j][p] + (two ? u1[j][p] : zero);
+  }
+  const int rs = s.part_rowsum[r];
+  const float dq = s.part_deq[r];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    if constexpr (MODE == ACT_RESID_RMSNORM) {
+      st.in[j].b = part_rescale(s, t[j][0], rs, dq, col[j][0]);
+    } else {
+      st.in[j].a = part_rescale(s, t[j][0], rs, dq, col[j][0]);
+      if constexpr (NP == 2) st.in[j].b = part_rescale(s, t[j][1], rs, dq, col[j][1]);
+    }
+  }
+}
+
+template <int MODE, int NV, bool PART = false>
+__device__ __forceinline__ void row_load(const Src &s, int64_t r, RowStage<NV> &st) {
+  static_assert(NV > 0, "register-resident rows only");
+  if constexpr (PART) {
+    row_load_part<MODE, NV>(s, r, st);
+  } else {
+    const int nf = s.k >> 2;
+    // every lane issues the same NV loads (past the row end it reloads element
+    // 0, unused), so the number of loads in flight is known where they are used
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int f = threadIdx.x + j * kQuantThreads;
+      st.in[j] = raw_load<MODE, PART>(s, r, f < nf ? f : 0);
+    }
   }
 }
 
@@ -142,7 +253,7 @@ __device__ __forceinline__ void row_load(const Src &s, int64_t r, RowStage<NV> &
 // to global memory. The LDS arrays hold the cross-wave partials. Every thread
 // returns the same deq and row sum; words in LDS are visible to the whole
 // workgroup on return. NV = 0 streams the row twice instead of holding it.
-template <int MODE, int NV>
+template <int MODE, int NV, bool PART = false>
 __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float eps, const RowStage<(NV > 0 ? NV : 1)> &st,
                                                int *words, float *red_f, double *red_d, int *red_i) {
   constexpr bool kRms = MODE != BITLINEAR_ACT_ABSMAX;
@@ -172,7 +283,7 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
       if (f < nf) cache[j] = visit1(f, st.in[j]);
     }
   } else {
-    for (int f = tid; f < nf; f += kQuantThreads) (void)visit1(f, raw_load<MODE>(s, r, f));
+    for (int f = tid; f < nf; f += kQuantThreads) (void)visit1(f, raw_load<MODE, PART>(s, r, f));
   }
   amax = wave_max(amax);
   if (kRms) ss = wave_sum(ss);
@@ -212,7 +323,7 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
       }
     } else {
       for (int f = tid; f < nf; f += kQuantThreads) {
-        const RawIn raw = raw_load<MODE>(s, r, f);
+        const RawIn raw = raw_load<MODE, PART>(s, r, f);
         emit(f, gain_of<MODE>(raw, pre_of<MODE>(s, r, f, raw, false)));
       }
     }
@@ -237,12 +348,12 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
   return out;
 }
 
-template <int MODE, int NV>
+template <int MODE, int NV, bool PART = false>
 __device__ __forceinline__ RowQuant quant_row(const Src &s, int64_t r, float eps, int *words, float *red_f,
                                               double *red_d, int *red_i) {
   RowStage<(NV > 0 ? NV : 1)> st;
-  if constexpr (NV > 0) row_load<MODE, NV>(s, r, st);
-  return row_finish<MODE, NV>(s, r, eps, st, words, red_f, red_d, red_i);
+  if constexpr (NV > 0) row_load<MODE, NV, PART>(s, r, st);
+  return row_finish<MODE, NV, PART>(s, r, eps, st, words, red_f, red_d, red_i);
 }
 
 }  // namespace bl

@@ -402,6 +402,8 @@ struct BlockBufs {
   int8_t *codes;
   float *deq;
   int32_t *rowsum;
+  float *deq2;      // second set, so that a quantization can read the previous
+  int32_t *rowsum2; // stage's deq and row sums while it writes its own
   float *qkv, *o, *h, *x, *gu, *d;
   int32_t *split;  // split-K partial sums of the widest projection, or NULL
 };
@@ -421,6 +423,8 @@ size_t block_layout(const bitlinear_block *blk, int64_t m, BlockBufs *b, char *b
   t.codes = reinterpret_cast<int8_t *>(take((size_t)(m * widest)));
   t.deq = reinterpret_cast<float *>(take((size_t)m * 4));
   t.rowsum = reinterpret_cast<int32_t *>(take((size_t)m * 4));
+  t.deq2 = reinterpret_cast<float *>(take((size_t)m * 4));
+  t.rowsum2 = reinterpret_cast<int32_t *>(take((size_t)m * 4));
   t.gu = reinterpret_cast<float *>(take((size_t)(m * 2 * I) * 4));
   t.qkv = reinterpret_cast<float *>(take(dec ? (size_t)(m * Q) * 4 : 0));
   t.o = reinterpret_cast<float *>(take(dec ? (size_t)(m * H) * 4 : 0));
@@ -476,48 +480,13 @@ bitlinear_status copy_to(void *dst, const void *src, size_t bytes, hipStream_t s
   return launched(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s), "trace copy");
 }
 
-bitlinear_status proj(const BlockBufs &b, int64_t m, int64_t k, const uint8_t *w, int64_t n, const float *gam,
-                      const int64_t *seg, int n_seg, float *y, int32_t *acc, hipStream_t s) {
-  bl::Epilogue ep;
-  BL_TRY(check_segments(gam, seg, n_seg, n, &ep));
-  return contract(b.codes, b.deq, b.rowsum, m, k, w, n, ep, y, acc, BITLINEAR_PATH_AUTO, b.split, s);
-}
-
-bitlinear_status quant(const BlockBufs &b, int mode, const float *x, const float *x2, int64_t ld, int64_t m,
-                       int64_t k, const float *gain, float eps, int gqa_off, int hd, int group, float *h_out,
-                       hipStream_t s) {
-  return launched(bl::launch_quant_acts(mode, x, x2, ld, m, k, gain, eps, gqa_off, hd, group, h_out, b.codes, b.deq,
-                                        b.rowsum, s),
-                  "quantize stage");
-}
-
 template <typename T>
 T *at(T *p, int64_t off) {
   return p ? p + off : nullptr;
 }
 
-// gate|up -> ReLU^2 gating -> ffn_sub_norm quantization of the chain's b.codes.
-// Untraced and at shapes the gated kernel takes, gate and up never leave the
-// chip: it writes fl32(max(g, 0)^2 * u) ([m][I], in b.gu) and the quantization
-// reads that; otherwise gate|up ([m][2I]) goes through b.gu (and the trace).
-bitlinear_status gated_ffn_input(const BlockBufs &b, int64_t m, int64_t H, int64_t I, const bitlinear_layer &L,
-                                 float eps, float *tr_gate_up, int32_t *tr_acc_gate_up, hipStream_t s) {
-  const int64_t gu_seg[2] = {I, 2 * I};
-  if (!tr_gate_up && !tr_acc_gate_up && bl::gemm_glu_supported(m, I, H)) {
-    bl::Epilogue ep;
-    BL_TRY(check_segments(L.gate_up_gamma, gu_seg, 2, 2 * I, &ep));
-    BL_TRY(launched(bl::launch_gemm_glu(b.codes, L.gate_up, b.deq, b.rowsum, m, I, H, ep, b.gu, s),
-                    "gated prefill kernel"));
-    return quant(b, BITLINEAR_ACT_RMSNORM, b.gu, nullptr, I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1, nullptr, s);
-  }
-  BL_TRY(proj(b, m, H, L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, b.gu, tr_acc_gate_up, s));
-  BL_TRY(copy_to(tr_gate_up, b.gu, (size_t)(m * 2 * I) * 4, s));
-  return quant(b, BITLINEAR_ACT_RELU2_RMSNORM, b.gu, nullptr, 2 * I, m, I, L.ffn_sub_norm_gain, eps, 0, 1, 1, nullptr,
-               s);
-}
-
 bl::ActSrc act_src(const float *x, int64_t ld, int64_t k, const float *gain) {
-  bl::ActSrc a;
+  bl::ActSrc a{};
   a.x = x;
   a.x2 = nullptr;
   a.ld = ld;
@@ -607,6 +576,173 @@ bitlinear_status block_forward_fused(const bitlinear_block *blk, const float *x,
   return BITLINEAR_OK;
 }
 
+
+// A projection's output as the next stage reads it: fp32 rows, or the split-K
+// partial sums the next quantization adds itself (with the deq and row sums
+// of the codes that were contracted).
+struct ProjOut {
+  const float *y = nullptr;
+  const int32_t *part = nullptr;
+  int splits = 1;
+  int64_t plane = 0;
+  const int32_t *rowsum = nullptr;
+  const float *deq = nullptr;
+  bl::Epilogue ep{};
+};
+
+void attach(bl::ActSrc &a, const ProjOut &o) {
+  if (!o.part) return;
+  a.part = o.part;
+  a.part_splits = o.splits;
+  a.part_plane = o.plane;
+  a.part_rowsum = o.rowsum;
+  a.part_deq = o.deq;
+  a.part_ep = o.ep;
+}
+
+// The quantize -> contract chain for m > 4 tokens (and whenever the one-launch
+// decode form does not apply). Each quantization writes the deq / row-sum set
+// the previous one did not, so it can read a split-K projection's partial sums
+// with the previous set.
+struct Chain {
+  BlockBufs b;
+  int64_t m;
+  float eps;
+  hipStream_t s;
+  int set = 0;  // 0: (deq, rowsum), 1: (deq2, rowsum2) hold the current codes' scales
+  float *deq() const { return set ? b.deq2 : b.deq; }
+  int32_t *rowsum() const { return set ? b.rowsum2 : b.rowsum; }
+
+  bitlinear_status quant(int mode, const bl::ActSrc &src) {
+    set ^= 1;
+    return launched(bl::launch_quant_acts_src(mode, src, m, eps, b.codes, deq(), rowsum(), s), "quantize stage");
+  }
+  // keep: the caller takes split-K partial sums (no trace of this projection)
+  bitlinear_status proj(int64_t k, const uint8_t *w, int64_t n, const float *gam, const int64_t *seg, int n_seg,
+                        float *y, int32_t *acc, bool keep, ProjOut *out) {
+    ProjOut o;
+    BL_TRY(check_segments(gam, seg, n_seg, n, &o.ep));
+    o.y = y;
+    if (!keep || m <= 16) {
+      BL_TRY(contract(b.codes, deq(), rowsum(), m, k, w, n, o.ep, y, acc, BITLINEAR_PATH_AUTO, b.split, s));
+    } else {
+      int splits = 1;
+      BL_TRY(launched(bl::launch_gemm_prefill(b.codes, w, deq(), rowsum(), m, n, k, o.ep, y, nullptr, b.split, s,
+                                              &splits),
+                      "prefill kernel"));
+      if (splits > 1) {
+        o.y = nullptr;
+        o.part = b.split;
+        o.splits = splits;
+        o.plane = m * n;
+        o.rowsum = rowsum();
+        o.deq = deq();
+      }
+    }
+    *out = o;
+    return BITLINEAR_OK;
+  }
+  // gate|up -> ReLU^2 -> ffn_sub_norm quantization (codes of the down input)
+  bitlinear_status ffn_input(int64_t H, int64_t I, const bitlinear_layer &L, float *tr_gate_up,
+                             int32_t *tr_acc_gate_up) {
+    const int64_t gu_seg[2] = {I, 2 * I};
+    const bool traced = tr_gate_up || tr_acc_gate_up;
+    if (!traced && bl::gemm_glu_supported(m, I, H)) {
+      // the gated kernel writes fl32(max(g, 0)^2 * u) ([m][I]) and gate, up never leave the chip
+      bl::Epilogue ep;
+      BL_TRY(check_segments(L.gate_up_gamma, gu_seg, 2, 2 * I, &ep));
+      BL_TRY(launched(bl::launch_gemm_glu(b.codes, L.gate_up, deq(), rowsum(), m, I, H, ep, b.gu, s),
+                      "gated prefill kernel"));
+      return quant(BITLINEAR_ACT_RMSNORM, act_src(b.gu, I, I, L.ffn_sub_norm_gain));
+    }
+    ProjOut gu;
+    BL_TRY(proj(H, L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, b.gu, tr_acc_gate_up, !traced, &gu));
+    BL_TRY(copy_to(tr_gate_up, b.gu, (size_t)(m * 2 * I) * 4, s));
+    bl::ActSrc src = act_src(gu.y, 2 * I, I, L.ffn_sub_norm_gain);
+    attach(src, gu);
+    return quant(BITLINEAR_ACT_RELU2_RMSNORM, src);
+  }
+};
+
+bitlinear_status block_forward_chain(const bitlinear_block *blk, const float *x, int64_t m, float *y,
+                                     const bitlinear_block_trace &tr, const BlockBufs &bufs, hipStream_t s) {
+  const int64_t H = blk->hidden, I = blk->intermediate;
+  const int64_t h_seg[1] = {H};
+  Chain c{bufs, m, blk->eps, s};
+  const BlockBufs &b = bufs;
+
+  if (blk->kind == BITLINEAR_BLOCK_FFN) {
+    const bitlinear_layer &L = blk->layers[0];
+    BL_TRY(c.quant(BITLINEAR_ACT_ABSMAX, act_src(x, H, H, nullptr)));
+    BL_TRY(copy_to(tr.codes_in, b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(tr.deq, c.deq(), (size_t)m * 4, s));
+    BL_TRY(c.ffn_input(H, I, L, tr.gate_up, tr.acc_gate_up));
+    BL_TRY(copy_to(tr.codes_ffn, b.codes, (size_t)(m * I), s));
+    BL_TRY(copy_to(at(tr.deq, 3 * m), c.deq(), (size_t)m * 4, s));
+    ProjOut d;
+    return c.proj(I, L.down, H, &L.down_gamma, h_seg, 1, y, tr.acc_down, false, &d);
+  }
+
+  const int hd = blk->head_dim, group = blk->n_heads / blk->n_kv_heads;
+  const int64_t KV = (int64_t)blk->n_kv_heads * hd, Q = H + 2 * KV;
+  const int64_t qkv_seg[3] = {H, H + KV, Q};
+  ProjOut d;  // the previous layer's down projection
+  for (int l = 0; l < blk->n_layers; ++l) {
+    const bitlinear_layer &L = blk->layers[l];
+    const int64_t oH = (int64_t)l * m * H, oI = (int64_t)l * m * I, oQ = (int64_t)l * m * Q;
+    // input_layernorm; for l > 0 the layer input is h + down of the previous layer
+    const float *xin = x;
+    if (l == 0) {
+      BL_TRY(c.quant(BITLINEAR_ACT_RMSNORM, act_src(x, H, H, L.input_norm_gain)));
+    } else {
+      bl::ActSrc src = act_src(b.h, H, H, L.input_norm_gain);
+      src.x2 = d.y;
+      src.h_out = b.x;
+      attach(src, d);
+      BL_TRY(c.quant(bl::ACT_RESID_RMSNORM, src));
+      xin = b.x;
+    }
+    BL_TRY(copy_to(at(tr.codes_in, oH), b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l), c.deq(), (size_t)m * 4, s));
+    ProjOut qkv;
+    BL_TRY(c.proj(H, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, b.qkv, at(tr.acc_qkv, oQ), !tr.qkv && !tr.acc_qkv, &qkv));
+    BL_TRY(copy_to(at(tr.qkv, oQ), b.qkv, (size_t)(m * Q) * 4, s));
+    // self-only attention output -> attn_sub_norm -> o_proj
+    {
+      bl::ActSrc src = act_src(qkv.y, Q, H, L.attn_sub_norm_gain);
+      src.gqa_offset = (int)(H + KV);
+      src.head_dim = hd;
+      src.group = group;
+      attach(src, qkv);
+      BL_TRY(c.quant(bl::ACT_GQA_RMSNORM, src));
+    }
+    BL_TRY(copy_to(at(tr.codes_attn, oH), b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l + m), c.deq(), (size_t)m * 4, s));
+    ProjOut o;
+    BL_TRY(c.proj(H, L.o, H, &L.o_gamma, h_seg, 1, b.o, at(tr.acc_o, oH), !tr.acc_o, &o));
+    // h = x + o -> post_attention_layernorm
+    {
+      bl::ActSrc src = act_src(xin, H, H, L.post_attn_norm_gain);
+      src.x2 = o.y;
+      src.h_out = b.h;
+      attach(src, o);
+      BL_TRY(c.quant(bl::ACT_RESID_RMSNORM, src));
+    }
+    BL_TRY(copy_to(at(tr.h, oH), b.h, (size_t)(m * H) * 4, s));
+    BL_TRY(copy_to(at(tr.codes_post, oH), b.codes, (size_t)(m * H), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l + 2 * m), c.deq(), (size_t)m * 4, s));
+    // relu^2 gating -> ffn_sub_norm -> down
+    BL_TRY(c.ffn_input(H, I, L, at(tr.gate_up, 2 * oI), at(tr.acc_gate_up, 2 * oI)));
+    BL_TRY(copy_to(at(tr.codes_ffn, oI), b.codes, (size_t)(m * I), s));
+    BL_TRY(copy_to(at(tr.deq, 4 * m * l + 3 * m), c.deq(), (size_t)m * 4, s));
+    BL_TRY(c.proj(I, L.down, H, &L.down_gamma, h_seg, 1, b.d, at(tr.acc_down, oH), !tr.acc_down && !tr.x_out, &d));
+    if (tr.x_out) BL_TRY(launched(bl::launch_add(b.h, b.d, tr.x_out + oH, m * H, s), "trace add"));
+  }
+  if (d.part)
+    return launched(bl::launch_splitk_finish(d.part, d.splits, d.deq, d.rowsum, m, H, d.ep, y, nullptr, b.h, s),
+                    "residual add");
+  return launched(bl::launch_add(b.h, b.d, y, m * H, s), "residual add");
+}
 }  // namespace
 
 extern "C" {
@@ -633,65 +769,13 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
   BlockBufs b;
   block_layout(blk, m, &b, static_cast<char *>(workspace));
   const int64_t H = blk->hidden, I = blk->intermediate;
-  const float eps = blk->eps;
   bitlinear_block_trace tr;
   memset(&tr, 0, sizeof tr);
   if (trace) tr = *trace;
 
-  const int64_t gu_seg[2] = {I, 2 * I};
-  const int64_t h_seg[1] = {H};
-
   if (bl::fused_decode_supported(m, H) && bl::fused_decode_supported(m, I) && I % 16 == 0)
     return block_forward_fused(blk, x, m, y, tr, b, s);
-
-  if (blk->kind == BITLINEAR_BLOCK_FFN) {
-    const bitlinear_layer &L = blk->layers[0];
-    BL_TRY(quant(b, BITLINEAR_ACT_ABSMAX, x, nullptr, H, m, H, nullptr, eps, 0, 1, 1, nullptr, s));
-    BL_TRY(copy_to(tr.codes_in, b.codes, (size_t)(m * H), s));
-    BL_TRY(copy_to(tr.deq, b.deq, (size_t)m * 4, s));
-    BL_TRY(gated_ffn_input(b, m, H, I, L, eps, tr.gate_up, tr.acc_gate_up, s));
-    BL_TRY(copy_to(tr.codes_ffn, b.codes, (size_t)(m * I), s));
-    BL_TRY(copy_to(at(tr.deq, 3 * m), b.deq, (size_t)m * 4, s));
-    return proj(b, m, I, L.down, H, &L.down_gamma, h_seg, 1, y, tr.acc_down, s);
-  }
-
-  const int hd = blk->head_dim, group = blk->n_heads / blk->n_kv_heads;
-  const int64_t KV = (int64_t)blk->n_kv_heads * hd, Q = H + 2 * KV;
-  const int64_t qkv_seg[3] = {H, H + KV, Q};
-  for (int l = 0; l < blk->n_layers; ++l) {
-    const bitlinear_layer &L = blk->layers[l];
-    const int64_t oH = (int64_t)l * m * H, oI = (int64_t)l * m * I, oQ = (int64_t)l * m * Q;
-    // input_layernorm; for l > 0 the layer input is h + down of the previous layer
-    const float *xin = x;
-    if (l == 0) {
-      BL_TRY(quant(b, BITLINEAR_ACT_RMSNORM, x, nullptr, H, m, H, L.input_norm_gain, eps, 0, 1, 1, nullptr, s));
-    } else {
-      BL_TRY(quant(b, bl::ACT_RESID_RMSNORM, b.h, b.d, H, m, H, L.input_norm_gain, eps, 0, 1, 1, b.x, s));
-      xin = b.x;
-    }
-    BL_TRY(copy_to(at(tr.codes_in, oH), b.codes, (size_t)(m * H), s));
-    BL_TRY(copy_to(at(tr.deq, 4 * m * l), b.deq, (size_t)m * 4, s));
-    BL_TRY(proj(b, m, H, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, b.qkv, at(tr.acc_qkv, oQ), s));
-    BL_TRY(copy_to(at(tr.qkv, oQ), b.qkv, (size_t)(m * Q) * 4, s));
-    // self-only attention output -> attn_sub_norm -> o_proj
-    BL_TRY(quant(b, bl::ACT_GQA_RMSNORM, b.qkv, nullptr, Q, m, H, L.attn_sub_norm_gain, eps, (int)(H + KV), hd, group,
-                 nullptr, s));
-    BL_TRY(copy_to(at(tr.codes_attn, oH), b.codes, (size_t)(m * H), s));
-    BL_TRY(copy_to(at(tr.deq, 4 * m * l + m), b.deq, (size_t)m * 4, s));
-    BL_TRY(proj(b, m, H, L.o, H, &L.o_gamma, h_seg, 1, b.o, at(tr.acc_o, oH), s));
-    // h = x + o -> post_attention_layernorm
-    BL_TRY(quant(b, bl::ACT_RESID_RMSNORM, xin, b.o, H, m, H, L.post_attn_norm_gain, eps, 0, 1, 1, b.h, s));
-    BL_TRY(copy_to(at(tr.h, oH), b.h, (size_t)(m * H) * 4, s));
-    BL_TRY(copy_to(at(tr.codes_post, oH), b.codes, (size_t)(m * H), s));
-    BL_TRY(copy_to(at(tr.deq, 4 * m * l + 2 * m), b.deq, (size_t)m * 4, s));
-    // relu^2 gating -> ffn_sub_norm -> down
-    BL_TRY(gated_ffn_input(b, m, H, I, L, eps, at(tr.gate_up, 2 * oI), at(tr.acc_gate_up, 2 * oI), s));
-    BL_TRY(copy_to(at(tr.codes_ffn, oI), b.codes, (size_t)(m * I), s));
-    BL_TRY(copy_to(at(tr.deq, 4 * m * l + 3 * m), b.deq, (size_t)m * 4, s));
-    BL_TRY(proj(b, m, I, L.down, H, &L.down_gamma, h_seg, 1, b.d, at(tr.acc_down, oH), s));
-    if (tr.x_out) BL_TRY(launched(bl::launch_add(b.h, b.d, tr.x_out + oH, m * H, s), "trace add"));
-  }
-  return launched(bl::launch_add(b.h, b.d, y, m * H, s), "residual add");
+  return block_forward_chain(blk, x, m, y, tr, b, s);
 }
 
 }  // extern "C"

@@ -75,6 +75,10 @@ __device__ __forceinline__ int wave_sum(int v) {
 hipError_t launch_quant_acts(int mode, const float *x, const float *x2, int64_t ld_x, int64_t m, int64_t k,
                              const float *gain, float eps, int gqa_offset, int head_dim, int group,
                              float *h_out, int8_t *codes, float *deq, int32_t *rowsum, hipStream_t stream);
+struct ActSrc;
+// The same, with every source field given (partial-sum operands included).
+hipError_t launch_quant_acts_src(int mode, const ActSrc &src, int64_t m, float eps, int8_t *codes, float *deq,
+                                 int32_t *rowsum, hipStream_t stream);
 hipError_t launch_code_rowsum(const int8_t *codes, int64_t m, int64_t k, int32_t *rowsum, hipStream_t stream);
 hipError_t launch_add(const float *a, const float *b, float *out, int64_t count, hipStream_t stream);
 // y[m][inter] = fl32(fl32(max(g, 0)^2) * u), gu = [m][g | u], inter % 4 == 0
@@ -96,16 +100,25 @@ hipError_t launch_validate_packed(const uint8_t *packed, int64_t n, int64_t k, i
 #define BL_SPLIT_TARGET 256
 #endif
 #ifndef BL_SPLIT_BYTES_RATIO
-#define BL_SPLIT_BYTES_RATIO 1
+#define BL_SPLIT_BYTES_RATIO 2
 #endif
 constexpr int64_t kSplitMinTiles = 256;                         // split only below this many output tiles
 constexpr int64_t kSplitTarget = BL_SPLIT_TARGET;               // aim for about this many work items
 constexpr int64_t kSplitBytesPerWeightByte = BL_SPLIT_BYTES_RATIO;  // partial sums vs packed weight bytes
 int gemm_prefill_splits(int64_t m, int64_t n, int64_t k);
 size_t gemm_prefill_workspace_bytes(int64_t m, int64_t n, int64_t k);
+// splits_left: NULL, or receives the number S of K ranges whose partial sums
+// were left in split_ws (part[s][m][n], int32; 1 = y was written) for the
+// caller to add (the finish kernel is then not launched).
+// res: NULL, or [m][n] added to y by the finish kernel.
 hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const float *deq,
                                const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
-                               float *y, int32_t *acc_out, int32_t *split_ws, hipStream_t stream);
+                               float *y, int32_t *acc_out, int32_t *split_ws, hipStream_t stream,
+                               int *splits_left = nullptr, const float *res = nullptr);
+// y = [res +] rescale(sum_s part[s] - rowsum, deq, gamma), [m][n], n % 4 == 0
+hipError_t launch_splitk_finish(const int32_t *part, int splits, const float *deq, const int32_t *rowsum, int64_t m,
+                                int64_t n, const Epilogue &ep, float *y, int32_t *acc_out, const float *res,
+                                hipStream_t stream);
 // Gated prefill contraction: packed [gate; up] (2 inter rows), gamma[0] gate,
 // gamma[1] up; y[m][j] = fl32(fl32(max(g, 0)^2) * u), [m][inter].
 bool gemm_glu_supported(int64_t m, int64_t inter, int64_t k);
@@ -131,6 +144,17 @@ struct ActSrc {
   const float *gain;
   int gqa_offset, head_dim, group;
   float *h_out;     // residual prologue: receives x + x2 ([m][k]); the fused decode takes no residual prologue
+  // The projection-output operand (x2 in the residual prologue, x otherwise)
+  // given as split-K partial sums instead of fp32 rows (standalone
+  // quantization kernel only): element (r, c) is
+  //   fl32(fl32((float)(sum_s part[s][r][c] - part_rowsum[r]) * part_deq[r]) * gamma(c)),
+  // with row stride ld and part_plane elements per split; part_ep.gamma_dev is NULL.
+  const int32_t *part;
+  int part_splits;
+  int64_t part_plane;
+  const int32_t *part_rowsum;
+  const float *part_deq;
+  Epilogue part_ep;
 };
 
 struct FusedDecode {

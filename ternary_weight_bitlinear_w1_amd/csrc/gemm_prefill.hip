@@ -616,11 +616,13 @@ hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const fl
 
 // y = rescale(sum_s part[s] - rowsum, deq, gamma): the end of a split-K
 // contraction, four outputs per thread
+// (res: NULL, or [M][N] added to y: y = fl32(res + y))
 __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__restrict__ part, int S,
                                                             const float *__restrict__ deq,
                                                             const int32_t *__restrict__ rowsum, int M, int N,
                                                             Epilogue ep_in, float *__restrict__ Y,
-                                                            int32_t *__restrict__ acc_out) {
+                                                            int32_t *__restrict__ acc_out,
+                                                            const float *__restrict__ res) {
   const Epilogue ep = resolve_gamma(ep_in);
   const int64_t plane = (int64_t)M * N;
   const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -632,8 +634,12 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__res
   const float dq = deq[m];
   t -= v4i{rs, rs, rs, rs};
   if (acc_out) *reinterpret_cast<v4i *>(acc_out + 4 * i4) = t;
-  const v4f v = v4f{rescale(t[0], dq, epi_gamma(ep, n)), rescale(t[1], dq, epi_gamma(ep, n + 1)),
-                    rescale(t[2], dq, epi_gamma(ep, n + 2)), rescale(t[3], dq, epi_gamma(ep, n + 3))};
+  v4f v = v4f{rescale(t[0], dq, epi_gamma(ep, n)), rescale(t[1], dq, epi_gamma(ep, n + 1)),
+              rescale(t[2], dq, epi_gamma(ep, n + 2)), rescale(t[3], dq, epi_gamma(ep, n + 3))};
+  if (res) {
+    const v4f r = *reinterpret_cast<const v4f *>(res + 4 * i4);
+    v = v4f{__fadd_rn(r[0], v[0]), __fadd_rn(r[1], v[1]), __fadd_rn(r[2], v[2]), __fadd_rn(r[3], v[3])};
+  }
   *reinterpret_cast<v4f *>(Y + 4 * i4) = v;
 }
 
@@ -699,7 +705,7 @@ size_t gemm_prefill_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 
 hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,
                                int64_t m, int64_t n, int64_t k, const Epilogue &ep, float *y, int32_t *acc_out,
-                               int32_t *split_ws, hipStream_t stream) {
+                               int32_t *split_ws, hipStream_t stream, int *splits_left, const float *res) {
   if (m == 0 || n == 0) return hipSuccess;
   const int M = (int)m, N = (int)n, K = (int)k;
   int64_t bm, bn;
@@ -728,10 +734,21 @@ hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const
       if (m > 64) return launch_generic<2, 2, 2, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
       return launch_generic<1, 4, 2, 1>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
   }
-  if (e != hipSuccess || !part) return e;
+  if (splits_left) *splits_left = part ? S : 1;
+  if (e != hipSuccess || !part || splits_left) return e;
   const int64_t quads = m * n / 4;
   splitk_finish_kernel<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream>>>(part, S, deq, rowsum, M, N,
-                                                                                        ep, y, acc_out);
+                                                                                        ep, y, acc_out, res);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_finish(const int32_t *part, int splits, const float *deq, const int32_t *rowsum, int64_t m,
+                                int64_t n, const Epilogue &ep, float *y, int32_t *acc_out, const float *res,
+                                hipStream_t stream) {
+  const int64_t quads = m * n / 4;
+  if (quads == 0) return hipSuccess;
+  splitk_finish_kernel<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream>>>(
+      part, splits, deq, rowsum, (int)m, (int)n, ep, y, acc_out, res);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ namespace {
 
 constexpr int kThreads = kQuantThreads;
 
-template <int MODE, int NV>
+template <int MODE, int NV, bool PART>
 __global__ __launch_bounds__(kThreads) void quant_acts_kernel(Src s, int8_t *__restrict__ codes,
                                                               float *__restrict__ deq, int32_t *__restrict__ rowsum,
                                                               float eps) {
@@ -19,28 +19,28 @@ __global__ __launch_bounds__(kThreads) void quant_acts_kernel(Src s, int8_t *__r
   __shared__ int red_i[kThreads / 64];
   const int64_t r = blockIdx.x;
   int *crow = reinterpret_cast<int *>(codes + r * (int64_t)s.k);
-  const RowQuant q = quant_row<MODE, NV>(s, r, eps, crow, red_f, red_d, red_i);
+  const RowQuant q = quant_row<MODE, NV, PART>(s, r, eps, crow, red_f, red_d, red_i);
   if (threadIdx.x == 0) {
     if (rowsum) rowsum[r] = q.rowsum;
     deq[r] = q.deq;
   }
 }
 
-template <int MODE>
+template <int MODE, bool PART = false>
 hipError_t launch_mode(const Src &s, int64_t m, int8_t *codes, float *deq, int32_t *rowsum, float eps,
                        hipStream_t stream) {
   const int per_thread = (s.k / 4 + kThreads - 1) / kThreads;
   dim3 grid((unsigned)m), block(kThreads);
   if (per_thread <= 1)
-    quant_acts_kernel<MODE, 1><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
+    quant_acts_kernel<MODE, 1, PART><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
   else if (per_thread <= 2)
-    quant_acts_kernel<MODE, 2><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
+    quant_acts_kernel<MODE, 2, PART><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
   else if (per_thread <= 4)
-    quant_acts_kernel<MODE, 4><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
+    quant_acts_kernel<MODE, 4, PART><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
   else if (per_thread <= 8)
-    quant_acts_kernel<MODE, 8><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
+    quant_acts_kernel<MODE, 8, PART><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
   else
-    quant_acts_kernel<MODE, 0><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
+    quant_acts_kernel<MODE, 0, PART><<<grid, block, 0, stream>>>(s, codes, deq, rowsum, eps);
   return hipGetLastError();
 }
 
@@ -118,6 +118,21 @@ hipError_t launch_quant_acts(int mode, const float *x, const float *x2, int64_t 
       return launch_mode<BITLINEAR_ACT_RELU2_RMSNORM>(s, m, codes, deq, rowsum, eps, stream);
     case ACT_RESID_RMSNORM: return launch_mode<ACT_RESID_RMSNORM>(s, m, codes, deq, rowsum, eps, stream);
     case ACT_GQA_RMSNORM: return launch_mode<ACT_GQA_RMSNORM>(s, m, codes, deq, rowsum, eps, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_quant_acts_src(int mode, const ActSrc &src, int64_t m, float eps, int8_t *codes, float *deq,
+                                 int32_t *rowsum, hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  if (!src.part)
+    return launch_quant_acts(mode, src.x, src.x2, src.ld, m, src.k, src.gain, eps, src.gqa_offset, src.head_dim,
+                             src.group, src.h_out, codes, deq, rowsum, stream);
+  switch (mode) {
+    case BITLINEAR_ACT_RELU2_RMSNORM:
+      return launch_mode<BITLINEAR_ACT_RELU2_RMSNORM, true>(src, m, codes, deq, rowsum, eps, stream);
+    case ACT_RESID_RMSNORM: return launch_mode<ACT_RESID_RMSNORM, true>(src, m, codes, deq, rowsum, eps, stream);
+    case ACT_GQA_RMSNORM: return launch_mode<ACT_GQA_RMSNORM, true>(src, m, codes, deq, rowsum, eps, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -184,6 +184,41 @@ def test_decoder_stack_fused_sizes(m, layers):
     assert_equal(host(y2), host(y), "untraced output")
 
 
+@pytest.mark.parametrize("m,hdim,inter,nh,nkv,hd", [(24, 768, 1024, 12, 4, 64), (17, 2048, 1024, 16, 4, 128)])
+def test_decoder_stack_split_chain(m, hdim, inter, nh, nkv, hd):
+    """17 <= m <= 64 at dims where every projection splits K (2 ways at the
+    first shape; 4 ways for q|k|v, o and gate|up and 2 for down at the second):
+    without a trace the quantizations read the split partial sums themselves and
+    the last down projection is finished into the residual sum. Layer 0 has
+    random gains, layer 1 none (gain 1). Traced run against the oracle, then the
+    untraced run bit-equal to the traced one."""
+    layers = 2
+    note(f"block decoder split chain m={m} H={hdim} I={inter}")
+    kvd = nkv * hd
+    x = synth.activations(seed(8, m, 5), m, hdim, 1)
+    gpu_layers, refs = [], []
+    xo = x
+    for l in range(layers):
+        mt = _decoder_layer_mats(8, l, hdim, inter, kvd)
+        gains = None
+        if l == 0:
+            gains = {nm: (1.0 + 0.1 * synth.normal_f32(seed(8, l, 30 + i), n)).astype(np.float32)
+                     for i, (nm, n) in enumerate((("n_in", hdim), ("n_attn", hdim), ("n_post", hdim),
+                                                  ("n_ffn", inter)))}
+        ref = oracle.decoder_layer(xo, _oracle_weights(mt, gains), EPS, nh, nkv, hd)
+        refs.append(ref)
+        xo = ref["x"]
+        gpu_layers.append(_gpu_layer(mt, gains))
+    spec = bl.BlockSpec(bl.BLOCK_DECODER, hdim, inter, gpu_layers, nh, nkv, hd, EPS)
+    tr = _trace(layers, m, hdim, inter, hdim + 2 * kvd)
+    y = bl.block_forward(spec, gpu(x), trace=tr)
+    for l in range(layers):
+        _compare_layer(tr, l, refs[l])
+    assert_rel(host(y), xo, what="stack output")
+    y2 = bl.block_forward(spec, gpu(x))
+    assert_equal(host(y2), host(y), "untraced output")
+
+
 def test_decoder_stack_30_layers():
     """30 layers at the 2B4T shapes (H 2560, I 6912, 20 / 5 heads of 128, gains 1):
     M = 1 in full, and 3 sampled tokens of M = 64, all from the same weights."""
