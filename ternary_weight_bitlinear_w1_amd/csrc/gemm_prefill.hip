@@ -210,7 +210,21 @@ typedef const __attribute__((address_space(1))) void gbl_void_t;
 #ifndef BL_GEMM_SMALL_STAGES
 #define BL_GEMM_SMALL_STAGES 4
 #endif
+// tile of the 8-wave kernel for shapes whose 128 x 256 tiles fill the chip
+// unevenly (the down projection: 4096 x 2560 has 320 of them for 512 slots):
+// 128 x 320 with waves 4 x 2, one workgroup per CU
+#ifndef BL_GEMM_WIDE_CFG
+#define BL_GEMM_WIDE_CFG 4, 2, 1, 5
+#define BL_GEMM_WIDE_BN 320
+#endif
+#ifndef BL_GEMM_WIDE_STAGES
+#define BL_GEMM_WIDE_STAGES 4
+#endif
 constexpr int kGroupM = 4;
+
+// Workgroups per CU of the persistent kernel: 8-wave workgroups run one per CU,
+// smaller ones two (both give two waves per SIMD).
+constexpr int wgs_per_cu(int waves) { return waves >= 8 ? 1 : 2; }
 
 // 16-byte global -> LDS copy: lane l's 16 bytes go to LDS byte address
 // lds_base + 16 l (lds_base must be the same on every lane). Issued as a plain
@@ -284,7 +298,7 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds_base)
 // part[s][m][n]; the row sums, rescale and sum over s are left to the
 // consumer (integer sums: the total is the same in any order).
 template <int WM, int WN, int TM, int TN, int P, bool GLU>
-__global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8_t *__restrict__ A,
+__global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_kernel(const int8_t *__restrict__ A,
                                                                       const uint8_t *__restrict__ B,
                                                                       const float *__restrict__ deq,
                                                                       const int32_t *__restrict__ rowsum, int M,
@@ -297,19 +311,27 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int kAStage = BM * 128, kBStage = BN * 32, kStage = kAStage + kBStage;
   constexpr int LA = BM / 8 / NW;   // 1 KB activation loads per wave per chunk
-  constexpr int LB = BN / 32 / NW;  // 1 KB weight loads per wave per chunk
+  constexpr int LBT = BN / 32;      // 1 KB weight loads per chunk
+  // per wave: load j of wave w is weight load j NW + w; where LBT is not a
+  // multiple of NW the waves past the end issue a 256-byte dummy copy instead,
+  // so every wave has the same number of loads in flight
+  constexpr int LB = (LBT + NW - 1) / NW;
   static_assert(!GLU || TN % 2 == 0, "gate and up tiles come in pairs");
   constexpr int kStores = TM * (GLU ? TN / 2 : TN) * 4;  // 16-byte output stores per wave per tile
   constexpr int kRowOps = BM / 32;      // 64-dword row-data loads per tile (deq, then row sums)
-  static_assert(LA * NW * 8 == BM && LB * NW * 32 == BN, "tile must split into 1 KB wave loads");
+  static_assert(LA * NW * 8 == BM && LBT * 32 == BN, "tile must split into 1 KB wave loads");
   static_assert(kRowOps <= NW && kRowOps >= 2, "one row-data load per wave");
   constexpr int D = P - 1;  // chunks issued ahead of the one being computed
   constexpr int kWaitSteady = (D - 1) * (LA + LB);
   constexpr int kWaitAfterTile = kWaitSteady + 1 + kStores;
   static_assert(P >= 3, "ring of at least three stages");
   static_assert(kWaitAfterTile < 64, "vmcnt range");
-  static_assert(NW * 32 * 32 * 4 <= kStage, "epilogue scratch must fit in one stage");
+  // the epilogue transposes through the stage just consumed, or through an
+  // area of its own when the waves' 4 KB blocks do not fit in one stage
+  constexpr bool kOwnScratch = NW * 32 * 32 * 4 > kStage;
   __shared__ __attribute__((aligned(1024))) int8_t ring[P * kStage];
+  __shared__ __attribute__((aligned(1024))) float own_scratch[kOwnScratch ? NW * 32 * 32 : 1];
+  __shared__ __attribute__((aligned(256))) int s_dummy[64];
   __shared__ __attribute__((aligned(256))) float s_deq[2][BM];
   __shared__ __attribute__((aligned(256))) int s_rs[2][BM];
 
@@ -359,7 +381,8 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
-      const int r = 32 * (wave * LB + j) + (lane >> 1);
+      const int jj = j * NW + wave < LBT ? j * NW + wave : 0;  // (dummy loads: any valid row)
+      const int r = 32 * jj + (lane >> 1);
       const int h = (lane & 1) ^ ((r >> 3) & 1);
       const int wrow = GLU ? ((r >> 5) & 1) * I + is_n0 + 32 * (r >> 6) + (r & 31) : is_n0 + r;
       b_off[j] = (uint32_t)wrow * (uint32_t)ldb + 16u * h + 32u * (uint32_t)(is_s * nk);
@@ -370,9 +393,14 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st) + wave * 1024 * LA);
 #pragma unroll
     for (int j = 0; j < LA; ++j) copy16_to_lds(A + a_off[j] + 128 * is_kc, base + j * 1024);
-    const uint32_t bbase = __builtin_amdgcn_readfirstlane(lds_addr(st + kAStage) + wave * 1024 * LB);
+    const uint32_t bbase = __builtin_amdgcn_readfirstlane(lds_addr(st + kAStage) + wave * 1024);
 #pragma unroll
-    for (int j = 0; j < LB; ++j) copy16_to_lds(B + b_off[j] + 32 * is_kc, bbase + j * 1024);
+    for (int j = 0; j < LB; ++j) {
+      if (LBT % NW == 0 || j * NW + wave < LBT)  // wave-uniform
+        copy16_to_lds(B + b_off[j] + 32 * is_kc, bbase + j * NW * 1024);
+      else
+        copy4_to_lds(B + 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr(s_dummy)));
+    }
     if (++is_kc == nk) {
       is_kc = 0;
       if (++is_i < my_tiles) {
@@ -444,10 +472,15 @@ __global__ __launch_bounds__(WM *WN * 64, 2) void gemm_prefill_kernel(const int8
   // piece c sits at piece c ^ ((r >> 1) & 7), so both the writes (16 rows, one
   // piece) and the reads (2 rows, all pieces) of 16 lanes hit distinct banks.
   auto epilogue = [&](int8_t *scratch_stage) {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    float *sc = reinterpret_cast<float *>(scratch_stage) + wave * (32 * 32);
+    float *sc;
+    if constexpr (kOwnScratch) {
+      sc = own_scratch + wave * (32 * 32);
+    } else {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      sc = reinterpret_cast<float *>(scratch_stage) + wave * (32 * 32);
+    }
     const float *sd = s_deq[c_i & 1];
     const int *sr = s_rs[c_i & 1];
     if constexpr (GLU) {
@@ -607,7 +640,7 @@ hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const fl
                             hipStream_t stream) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * (n / BN) * splits;
-  int64_t grid = 2 * (int64_t)cu_count();  // two workgroups fit per CU
+  int64_t grid = wgs_per_cu(WM * WN) * (int64_t)cu_count();
   if (grid > tiles) grid = tiles;
   gemm_prefill_kernel<WM, WN, TM, TN, P, GLU><<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(
       codes, packed, deq, rowsum, m, n, k, ep, y, part ? nullptr : acc_out, splits, part);
@@ -648,11 +681,28 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__res
 namespace {
 
 // Tile shape of the pipelined kernel for (m, n, k), or 0 for the generic one.
-enum { CFG_GENERIC = 0, CFG_BIG = 1, CFG_2224 = 2, CFG_2222 = 3, CFG_1422 = 4, CFG_SMALL = 5 };
+enum { CFG_GENERIC = 0, CFG_BIG = 1, CFG_2224 = 2, CFG_2222 = 3, CFG_1422 = 4, CFG_SMALL = 5, CFG_WIDE = 6 };
+
+// The 8-wave 128 x 320 tile where it fills the chip better than 128 x 256:
+// with two 128 x 256 workgroups or one 128 x 320 workgroup per CU, a CU's share
+// of the time is (rounds of workgroups) x (tile work), the tile work being
+// 2 x 128 x 256 per round for the former and 128 x 320 for the latter.
+bool wide_pays(int64_t m, int64_t n) {
+  if (m <= 64 || n % BL_GEMM_WIDE_BN != 0) return false;
+  const int64_t cus = cu_count(), tm = (m + 127) / 128;
+  const int64_t t_wide = tm * (n / BL_GEMM_WIDE_BN);
+  if (t_wide < cus) return false;
+  const int64_t r_wide = (t_wide + cus - 1) / cus;
+  if (n % BL_GEMM_BIG_BN != 0) return true;
+  const int64_t t_big = tm * (n / BL_GEMM_BIG_BN), r_big = (t_big + 2 * cus - 1) / (2 * cus);
+  return r_wide * BL_GEMM_WIDE_BN < r_big * 2 * BL_GEMM_BIG_BN;
+}
+
 int pick_cfg(int64_t m, int64_t n, int64_t k, int64_t *bm, int64_t *bn) {
   *bm = 0;
   *bn = 0;
   if (k % 128 != 0) return CFG_GENERIC;
+  if (wide_pays(m, n)) { *bm = 128; *bn = BL_GEMM_WIDE_BN; return CFG_WIDE; }
   if (n % BL_GEMM_BIG_BN == 0 && m > 64) { *bm = 128; *bn = BL_GEMM_BIG_BN; return CFG_BIG; }
   if (n % 256 == 0 && m > 64) { *bm = 128; *bn = 256; return CFG_2224; }
   if (n % 128 == 0 && m > 64) { *bm = 128; *bn = 128; return CFG_2222; }
@@ -716,6 +766,10 @@ hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const
   switch (cfg) {
     case CFG_BIG:
       e = launch_pipelined<BL_GEMM_BIG_CFG, 3>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
+      break;
+    case CFG_WIDE:
+      e = launch_pipelined<BL_GEMM_WIDE_CFG, BL_GEMM_WIDE_STAGES>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S,
+                                                                  part, stream);
       break;
     case CFG_2224:
       e = launch_pipelined<2, 2, 2, 4, 3>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);

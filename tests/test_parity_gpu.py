@@ -173,7 +173,10 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           (9, 512, 4096), (5, 256, 2048), (48, 1024, 3072), (37, 512, 1024), (100, 384, 768),
           # 17..64 tokens with K % 256 == 0 (AUTO takes the skinny kernel): one and two token tiles,
           # ragged rows, few and many supersteps per wave
-          (17, 130, 512), (32, 1000, 768), (33, 48, 2560), (64, 2600, 6912), (50, 3000, 1024)]
+          (17, 130, 512), (32, 1000, 768), (33, 48, 2560), (64, 2600, 6912), (50, 3000, 1024),
+          # the 8-wave 128 x 320 tile (N % 320 == 0 and at least one tile per CU): ragged last row
+          # tile; two rounds of tiles with one K chunk each
+          (4000, 2560, 256), (4096, 5120, 128)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED)
