@@ -44,6 +44,9 @@ def _load():
             "orc_ternarize": (None, [_p, _i64, ctypes.c_double, _p]),
             "orc_pack": (ctypes.c_int, [_p, _i64, _i64, _p]),
             "orc_unpack": (_i64, [_p, _i64, _i64, _p]),
+            "orc_base3_row_bytes": (_i64, [_i64]),
+            "orc_pack_base3": (ctypes.c_int, [_p, _i64, _i64, _p]),
+            "orc_unpack_base3": (_i64, [_p, _i64, _i64, _p]),
             "orc_quant_absmax": (None, [_p, _i64, _i64, _p, _p]),
             "orc_quant_rms": (None, [_p, _i64, _i64, _p, ctypes.c_float, _p, _p, _p]),
             "orc_relu2_mul": (None, [_p, _i64, _i64, _p]),
@@ -96,6 +99,31 @@ def unpack(p, k: int):
     bad = _load().orc_unpack(pp, n, k, c.ctypes.data)
     if bad < 0:
         raise ValueError("unpack: k must be a multiple of 16")
+    return c, int(bad)
+
+
+def base3_row_bytes(k: int) -> int:
+    """Bytes of one row of k codes stored five to a byte (16 per 80 codes)."""
+    return int(_load().orc_base3_row_bytes(k))
+
+
+def pack_base3(c) -> np.ndarray:
+    """Five codes to a byte: [n][k] codes -> [n][16 ceil(k / 80)] base-3 bytes."""
+    c, pc = _c(c, np.int8)
+    n, k = c.shape
+    p = np.empty((n, base3_row_bytes(k)), dtype=np.uint8)
+    if _load().orc_pack_base3(pc, n, k, p.ctypes.data) != 0:
+        raise ValueError("pack_base3: codes must be in {-1, 0, 1}")
+    return p
+
+
+def unpack_base3(p, k: int):
+    """Inverse of :func:`pack_base3`: returns (codes [n][k], number of invalid bytes)."""
+    p, pp = _c(p, np.uint8)
+    n = p.shape[0]
+    assert p.shape[1] == base3_row_bytes(k)
+    c = np.empty((n, k), dtype=np.int8)
+    bad = _load().orc_unpack_base3(pp, n, k, c.ctypes.data)
     return c, int(bad)
 
 

@@ -87,6 +87,58 @@ int64_t orc_unpack(const uint8_t *p, int64_t n, int64_t k, int8_t *c) {
   return bad;
 }
 
+/* ---- Five codes to a byte (base 3) -------------------------------------------
+ * [tiny] "O que é" and "Arquivos": the same ternary checkpoint ships in a denser
+ * ternary format (TQ1_0, the smaller file) beside a two-bit one (TQ2_0). The
+ * pages give no layout for it; this one is our own (reading R18): a ternary
+ * code has three values, and 3^5 = 243 <= 256, so a byte holds five codes as
+ * base-3 digits. Row n of K codes takes 16 * ceil(K / 80) bytes (a whole number
+ * of 16-byte pieces of 80 codes). Code k is digit k % 5 of byte k / 5, stored
+ * as u = c + 1: byte j = sum_i u(5j + i) * 3^i. Codes past K are 0 (digit 1),
+ * so every pad byte is 121 and a full byte is at most 242; 243 .. 255 are
+ * invalid. */
+int64_t orc_base3_row_bytes(int64_t k) { return 16 * ((k + 79) / 80); }
+
+/* returns 0, or -1 when a code is outside {-1, 0, 1} */
+int orc_pack_base3(const int8_t *c, int64_t n, int64_t k, uint8_t *p) {
+  const int64_t rb = orc_base3_row_bytes(k);
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t j = 0; j < rb; ++j) {
+      int byte = 0, w = 1;
+      for (int i = 0; i < 5; ++i) {
+        const int64_t kk = 5 * j + i;
+        int u = 1;
+        if (kk < k) {
+          const int v = c[r * k + kk];
+          if (v < -1 || v > 1) return -1;
+          u = v + 1;
+        }
+        byte += u * w;
+        w *= 3;
+      }
+      p[r * rb + j] = (uint8_t)byte;
+    }
+  return 0;
+}
+
+/* decodes the first k codes of each row; returns the number of invalid bytes
+ * (243 .. 255) among those that hold them; such a byte decodes as all zeros */
+int64_t orc_unpack_base3(const uint8_t *p, int64_t n, int64_t k, int8_t *c) {
+  const int64_t rb = orc_base3_row_bytes(k);
+  int64_t bad = 0;
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t j = 0; 5 * j < k; ++j) {
+      int byte = p[r * rb + j];
+      if (byte > 242) { ++bad; byte = 121; }
+      for (int i = 0; i < 5; ++i) {
+        const int64_t kk = 5 * j + i;
+        if (kk < k) c[r * k + kk] = (int8_t)(byte % 3 - 1);
+        byte /= 3;
+      }
+    }
+  return bad;
+}
+
 /* ---- codes of one row: round(v * 127 / max|v|) to 255 levels ---------------
  * [nnterp] "The projections quantize their inputs and weights": each input is
  * rounded per token to 255 levels as round(x * 127 / max|x|); [card] "Model

@@ -158,6 +158,59 @@ def test_P4_invalid_field_detected():
     assert bad == int((fields == 3).sum()) and bad > 0
 
 
+# ------------------------------------------------------------------ five codes to a byte (R18)
+def test_golden_base3_layout():
+    """[tiny] "O que é", "Arquivos": a storage denser than two bits per weight; layout R18."""
+    for case in gold("base3_layout.json")["cases"]:
+        c = np.array([case["codes"]], dtype=np.int8)
+        p = oracle.pack_base3(c)
+        assert p.tolist() == [case["bytes"]]
+        back, bad = oracle.unpack_base3(p, c.shape[1])
+        assert bad == 0 and np.array_equal(back, c)
+
+
+def test_base3_every_byte_value():
+    """Each of the 243 valid bytes is five base-3 digits: decoding then encoding
+    gives the byte back (a bijection between 3^5 code patterns and 0..242), and
+    the digits are those of the integer division by 1, 3, 9, 27, 81."""
+    v = np.arange(243)
+    codes = np.stack([(v // 3 ** i) % 3 - 1 for i in range(5)], axis=1).astype(np.int8)  # [243][5]
+    p = oracle.pack_base3(codes)
+    assert np.array_equal(p[:, 0], v.astype(np.uint8))
+    assert (p[:, 1:] == 121).all()
+    back, bad = oracle.unpack_base3(p, 5)
+    assert bad == 0 and np.array_equal(back, codes)
+
+
+def test_base3_invalid_bytes_detected():
+    """Bytes 243..255 are not five ternary digits: unpack counts them (only in
+    bytes that hold codes of the row)."""
+    p = np.full((1, 16), 121, dtype=np.uint8)
+    p[0, :13] = np.arange(243, 256, dtype=np.uint8)
+    _, bad = oracle.unpack_base3(p, 80)
+    assert bad == 13
+    _, bad = oracle.unpack_base3(p, 10)  # only bytes 0 and 1 hold codes
+    assert bad == 2
+
+
+@pytest.mark.parametrize("k", [1, 5, 16, 79, 80, 81, 2560, 6912])
+def test_base3_roundtrip_and_row_size(k):
+    """Random codes survive pack + unpack at every row length, rows take
+    16 ceil(k / 80) bytes, and the pad digits are zeros (byte 121 past the codes)."""
+    r = rng(k)
+    c = r.integers(-1, 2, size=(6, k)).astype(np.int8)
+    p = oracle.pack_base3(c)
+    assert p.shape == (6, 16 * ((k + 79) // 80))
+    back, bad = oracle.unpack_base3(p, k)
+    assert bad == 0 and np.array_equal(back, c)
+    full = (k + 4) // 5  # bytes that hold at least one code
+    assert (p[:, full:] == 121).all()
+    # the contraction is the same through either storage
+    q = r.integers(-127, 128, size=(3, k)).astype(np.int8)
+    two_bit = oracle.unpack(oracle.pack(c), k)[0] if k % 16 == 0 else c
+    assert np.array_equal(oracle.contract(q, back), oracle.contract(q, two_bit))
+
+
 # ------------------------------------------------------------------ O4
 def test_golden_act_codes():
     """[nnterp] "The projections quantize their inputs and weights": round(x * 127 / max|x|)."""

@@ -176,7 +176,9 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           (17, 130, 512), (32, 1000, 768), (33, 48, 2560), (64, 2600, 6912), (50, 3000, 1024),
           # the 8-wave 128 x 320 tile (N % 320 == 0 and at least one tile per CU): ragged last row
           # tile; two rounds of tiles with one K chunk each
-          (4000, 2560, 256), (4096, 5120, 128)]
+          (4000, 2560, 256), (4096, 5120, 128),
+          # 576 tiles of 128 x 256 for 512 workgroups: a second, nearly empty round
+          (4000, 4608, 128)]
 
 
 @pytest.mark.parametrize("m,n,k", RAGGED)
@@ -193,6 +195,7 @@ def test_forward_ragged(m, n, k):
 
 # ------------------------------------------------------------------------------ gated up-projection
 GLU = [(200, 512, 1024), (130, 384, 256), (65, 256, 2560), (257, 640, 640),  # gating fused in the kernel
+       (1000, 8448, 128),  # 528 tiles for 512 workgroups
        (300, 200, 1040), (40, 256, 512), (5, 512, 512), (1, 96, 320)]          # gate|up through the workspace
 
 
