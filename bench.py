@@ -18,7 +18,8 @@ committed counter profile when the kernel source is unchanged since. ``decode``
 reports the weight-streaming kernel (M = 1, 4, 16) in packed-weight GB/s against
 HBM peak: the mean time per launch over back-to-back launches, each reading a
 different copy of the weights from a ring larger than the 256 MB last-level
-cache. ``cpu_baseline`` times the CPU oracle on a bounded
+cache; and the same projection at M = 1 and 4 from the weights stored five
+codes per byte (base 3), in GB/s of those stored bytes. ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same step's tokens.
 """
 from __future__ import annotations
@@ -334,6 +335,42 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
             log(f"decode {name} m={m}: {b2b_us:.2f} us/launch back-to-back, {gbs:.0f} GB/s "
                 f"(one launch between events: {us:.2f} us)")
         del ring
+        torch.cuda.empty_cache()
+        # the same projection from the base-3 storage (five codes per byte), m = 1 and 4
+        w3 = bl.pack_base3(packed, k)
+        nb3 = w3.numel()
+        copies = max(2, RING_BYTES // nb3)
+        ring = w3.unsqueeze(0).repeat(copies, 1, 1)
+        for m in (1, 4):
+            xm = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 3, m, 5), m, k,
+                                                    synth.outlier_count(k))).to(dev)
+            codes, deq, _ = bl.quantize_acts(xm)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+            def launch3(i):
+                st = L.bitlinear_forward_base3(None, codes.data_ptr(), deq.data_ptr(), m, k,
+                                               ring[i % copies].data_ptr(), n, g_c, se_c, len(gam), y.data_ptr(),
+                                               None, None, 0, sp)
+                if st != 0:
+                    raise RuntimeError(L.bitlinear_last_error().decode())
+
+            for i in range(20):
+                launch3(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                launch3(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            b2b_us = e0.elapsed_time(e1) / reps * 1e3
+            gbs = nb3 / (b2b_us * 1e-6) / 1e9
+            res[f"{name}_base3_m{m}"] = {"us": round(b2b_us, 3), "gbs_stored": round(gbs, 1),
+                                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "stored_bytes": nb3,
+                                         "us_vs_two_bit": round(b2b_us / res[f"{name}_m{m}"]["us"], 3)}
+            log(f"decode {name} base-3 m={m}: {b2b_us:.2f} us/launch back-to-back, {gbs:.0f} GB/s of "
+                f"{nb3} stored bytes ({b2b_us / res[f'{name}_m{m}']['us']:.3f} x the two-bit time)")
+        del ring, w3
         torch.cuda.empty_cache()
     return res
 

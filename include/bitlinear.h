@@ -201,6 +201,43 @@ size_t bitlinear_forward_relu2_glu_workspace_bytes(int64_t m, int64_t inter, int
                                                    int32_t path);
 
 /* ---------------------------------------------------------------------------
+ * Five codes per byte ([tiny] "O que é" and "Arquivos": the ternary checkpoint
+ * also ships in a storage denser than two bits per weight; the pages give no
+ * layout, so this one is the library's own). Row n of k codes takes
+ * bitlinear_base3_row_bytes(k) = 16 ceil(k / 80) bytes; code j is base-3 digit
+ * j % 5 of byte j / 5, stored as u = c + 1 (byte = sum_i u(5 b + i) 3^i);
+ * codes past k are 0; bytes 243..255 are invalid and read as five zero codes.
+ * ------------------------------------------------------------------------- */
+size_t bitlinear_base3_row_bytes(int64_t k);
+
+/* bitlinear_pack_base3 — rewrite two-bit packed weights in the base-3 storage.
+ *   w_packed  [n][k/4] bytes (layout of bitlinear_quantize_weights), 16-byte
+ *             aligned, k % 16 == 0. A field of 3 (not a code) becomes code 0.
+ *   w_base3   [n][bitlinear_base3_row_bytes(k)] bytes, 16-byte aligned, written.
+ * Errors: NULL pointers -> ERR_NULL; n <= 0, k <= 0, k % 16 != 0 -> ERR_SHAPE;
+ * misaligned -> ERR_ALIGN. */
+bitlinear_status bitlinear_pack_base3(const uint8_t *w_packed, int64_t n, int64_t k, uint8_t *w_base3,
+                                      void *stream);
+
+/* bitlinear_forward_base3 — bitlinear_forward for 1 to 4 tokens, reading the
+ * weights in the base-3 storage: y = fl32(fl32((float)acc deq[m]) gamma(n)),
+ * acc = sum_k q[m][k] c[n][k] exactly (the same result as bitlinear_forward on
+ * the two-bit weights, bit for bit).
+ *   x, codes_in, deq_in, m, k, n, gamma, seg_end, n_seg, y, acc_out: as
+ *              bitlinear_forward (no row sums are needed: the decoded codes
+ *              are signed).
+ *   w_base3    [n][bitlinear_base3_row_bytes(k)] bytes, 16-byte aligned.
+ *   workspace  >= bitlinear_forward_base3_workspace_bytes(m, k, x != NULL)
+ *              bytes (may be NULL when that is 0).
+ * Errors: as bitlinear_forward; m > 4 or k > 8192 -> ERR_SHAPE. m == 0 is a
+ * no-op. */
+bitlinear_status bitlinear_forward_base3(const float *x, const int8_t *codes_in, const float *deq_in, int64_t m,
+                                         int64_t k, const uint8_t *w_base3, int64_t n, const float *gamma,
+                                         const int64_t *seg_end, int32_t n_seg, float *y, int32_t *acc_out,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+size_t bitlinear_forward_base3_workspace_bytes(int64_t m, int64_t k, int32_t quantize_inside);
+
+/* ---------------------------------------------------------------------------
  * Block-level chains ("The block, in order").
  * ------------------------------------------------------------------------- */
 typedef enum {

@@ -79,6 +79,10 @@ def lib():
                                                 _sz, _p]),
             "bitlinear_forward_online_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _p, _i32]),
             "bitlinear_forward_relu2_glu_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+            "bitlinear_base3_row_bytes": (_sz, [_i64]),
+            "bitlinear_pack_base3": (_i32, [_p, _i64, _i64, _p, _p]),
+            "bitlinear_forward_base3": (_i32, [_p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _p, _p, _sz, _p]),
+            "bitlinear_forward_base3_workspace_bytes": (_sz, [_i64, _i64, _i32]),
             "bitlinear_block_forward": (_i32, [ctypes.POINTER(Block), _p, _i64, _p, ctypes.POINTER(Trace), _p, _sz,
                                                _p]),
             "bitlinear_block_workspace_bytes": (_sz, [ctypes.POINTER(Block), _i64]),
@@ -216,6 +220,43 @@ def forward_relu2_glu(packed: torch.Tensor, k: int, gamma: Sequence[float], x: O
            lib().bitlinear_forward_relu2_glu(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), inter,
                                              g, _ptr(y), path, _ptr(ws), nb, _stream(dev)))
     return y
+
+
+def base3_row_bytes(k: int) -> int:
+    """Bytes of one weight row of k codes stored five to a byte."""
+    return int(lib().bitlinear_base3_row_bytes(k))
+
+
+def pack_base3(packed: torch.Tensor, k: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Two-bit packed weights [n][k/4] -> the base-3 storage [n][base3_row_bytes(k)]."""
+    n = packed.shape[0]
+    w3 = out if out is not None else torch.empty((n, base3_row_bytes(k)), dtype=torch.uint8, device=packed.device)
+    _check("bitlinear_pack_base3",
+           lib().bitlinear_pack_base3(_ptr(packed), n, k, _ptr(w3), _stream(packed.device)))
+    return w3
+
+
+def forward_base3(w3: torch.Tensor, k: int, gamma: Sequence[float], seg_end: Optional[Sequence[int]] = None,
+                  x: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+                  deq: Optional[torch.Tensor] = None, want_acc: bool = False,
+                  out: Optional[torch.Tensor] = None):
+    """1..4-token projection reading base-3 weights -> y [m][n] (and acc when ``want_acc``)."""
+    n = w3.shape[0]
+    src = x if x is not None else codes
+    m = src.shape[0]
+    dev = w3.device
+    if seg_end is None:
+        seg_end = [n]
+    g = (ctypes.c_float * len(gamma))(*[float(v) for v in gamma])
+    se = (ctypes.c_int64 * len(seg_end))(*[int(v) for v in seg_end])
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
+    nb = lib().bitlinear_forward_base3_workspace_bytes(m, k, 1 if x is not None else 0)
+    ws = _workspace(nb, dev)
+    _check("bitlinear_forward_base3",
+           lib().bitlinear_forward_base3(_ptr(x), _ptr(codes), _ptr(deq), m, k, _ptr(w3), n, g, se, len(gamma),
+                                         _ptr(y), _ptr(acc), _ptr(ws), nb, _stream(dev)))
+    return (y, acc) if want_acc else y
 
 
 # ---------------------------------------------------------------------------------------------

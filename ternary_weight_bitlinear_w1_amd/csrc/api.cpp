@@ -393,6 +393,63 @@ bitlinear_status bitlinear_forward_relu2_glu(const float *x, const int8_t *codes
   return launched(bl::launch_relu2_glu(gu, m, inter, y, s), "relu2 gating");
 }
 
+// ---------------------------------------------------------------- five codes per byte
+size_t bitlinear_base3_row_bytes(int64_t k) { return k > 0 ? (size_t)(16 * ((k + 79) / 80)) : 0; }
+
+bitlinear_status bitlinear_pack_base3(const uint8_t *w_packed, int64_t n, int64_t k, uint8_t *w_base3,
+                                      void *stream) {
+  g_err.clear();
+  if (!w_packed || !w_base3) return fail(BITLINEAR_ERR_NULL, "w_packed and w_base3 are required");
+  if (n <= 0 || k <= 0 || k % 16 != 0 || n > kMaxDim || k > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "n = %lld, k = %lld: need n > 0, k > 0, k %% 16 == 0", (long long)n,
+                (long long)k);
+  if (!aligned16(w_packed) || !aligned16(w_base3))
+    return fail(BITLINEAR_ERR_ALIGN, "w_packed and w_base3 must be 16-byte aligned");
+  BL_TRY(check_device());
+  return launched(bl::launch_pack_base3(w_packed, n, k, w_base3, as_stream(stream)), "pack_base3");
+}
+
+size_t bitlinear_forward_base3_workspace_bytes(int64_t m, int64_t k, int32_t quantize_inside) {
+  if (m <= 0 || k <= 0 || !quantize_inside) return 0;
+  // codes, deq and the row sums the quantization kernel also writes
+  return align256((size_t)(m * k)) + align256((size_t)m * sizeof(float)) + align256((size_t)m * sizeof(int32_t));
+}
+
+bitlinear_status bitlinear_forward_base3(const float *x, const int8_t *codes_in, const float *deq_in, int64_t m,
+                                         int64_t k, const uint8_t *w_base3, int64_t n, const float *gamma,
+                                         const int64_t *seg_end, int32_t n_seg, float *y, int32_t *acc_out,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+  g_err.clear();
+  BL_TRY(check_forward_args(x, codes_in, deq_in, m, k, w_base3, n, y, BITLINEAR_PATH_DECODE));
+  if (m > 4 || k > 8192)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, k = %lld: the base-3 path takes m <= 4 and k <= 8192", (long long)m,
+                (long long)k);
+  bl::Epilogue ep;
+  BL_TRY(check_segments(gamma, seg_end, n_seg, n, &ep));
+  const size_t need = bitlinear_forward_base3_workspace_bytes(m, k, x != nullptr);
+  if (m > 0 && need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  hipStream_t s = as_stream(stream);
+  const int8_t *codes = codes_in;
+  const float *deq = deq_in;
+  if (x) {
+    char *ws = static_cast<char *>(workspace);
+    int8_t *c = reinterpret_cast<int8_t *>(ws);
+    ws += align256((size_t)(m * k));
+    float *d = reinterpret_cast<float *>(ws);
+    ws += align256((size_t)m * sizeof(float));
+    int32_t *rs = reinterpret_cast<int32_t *>(ws);
+    BL_TRY(launched(bl::launch_quant_acts(BITLINEAR_ACT_ABSMAX, x, nullptr, k, m, k, nullptr, 0.0f, 0, 1, 1, nullptr,
+                                          c, d, rs, s),
+                    "quantize_acts"));
+    codes = c;
+    deq = d;
+  }
+  return launched(bl::launch_gemv_b3(codes, w_base3, deq, m, n, k, ep, y, acc_out, s), "base-3 decode kernel");
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- blocks

@@ -173,6 +173,12 @@ struct FusedDecode {
   float *deq_out;      // optional [m]
 };
 
+// Five codes per byte (base3.hip): repacking, and the 1..4-token contraction.
+bool gemv_b3_supported(int64_t m, int64_t k);
+hipError_t launch_pack_base3(const uint8_t *packed, int64_t n, int64_t k, uint8_t *out, hipStream_t stream);
+hipError_t launch_gemv_b3(const int8_t *codes, const uint8_t *w, const float *deq, int64_t m, int64_t n, int64_t k,
+                          const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream);
+
 bool fused_decode_supported(int64_t m, int64_t k);
 hipError_t launch_gemv_fused(int mode, int epi, const FusedDecode &a, hipStream_t stream);
 

@@ -146,6 +146,51 @@ def test_forward_online_workspace_sizes():
     assert f(1, 13824, 2560, 1, None, 2) == 0
 
 
+def _b3(x=A, codes=None, deq=None, m=4, k=64, w=A, n=32, gamma=(1.0,), seg=(32,), y=A, acc=None, ws=A,
+        wsb=1 << 20):
+    g = (ctypes.c_float * max(1, len(gamma)))(*gamma)
+    s = (ctypes.c_int64 * max(1, len(seg)))(*seg)
+    return bl.lib().bitlinear_forward_base3(x, codes, deq, m, k, w, n, g, s, len(gamma), y, acc, ws, wsb, None)
+
+
+def test_base3_row_bytes():
+    f = bl.lib().bitlinear_base3_row_bytes
+    assert [f(k) for k in (16, 80, 96, 2560, 6912, 8192)] == [16, 16, 32, 512, 1392, 1648]
+    assert f(0) == 0
+
+
+def test_forward_base3_validation():
+    assert _b3(x=None) == bl.ERR_NULL
+    assert _b3(w=None) == bl.ERR_NULL
+    assert _b3(y=None) == bl.ERR_NULL
+    assert _b3(m=5) == bl.ERR_SHAPE       # one to four tokens
+    assert _b3(k=8208) == bl.ERR_SHAPE    # k <= 8192
+    assert _b3(k=24) == bl.ERR_SHAPE      # k % 16
+    assert _b3(m=-1) == bl.ERR_SHAPE
+    assert _b3(seg=(31,)) == bl.ERR_SHAPE
+    assert _b3(w=MIS) == bl.ERR_ALIGN
+    assert _b3(ws=None) == bl.ERR_WORKSPACE  # x given: the codes need room
+    assert _b3(wsb=16) == bl.ERR_WORKSPACE
+    assert _b3(m=0) == bl.OK
+
+
+def test_forward_base3_workspace_sizes():
+    f = bl.lib().bitlinear_forward_base3_workspace_bytes
+    assert f(4, 2560, 0) == 0
+    assert f(4, 2560, 1) >= 4 * 2560 + 16 + 16
+    assert f(0, 2560, 1) == 0
+
+
+def test_pack_base3_validation():
+    p = bl.lib().bitlinear_pack_base3
+    assert p(None, 32, 64, A, None) == bl.ERR_NULL
+    assert p(A, 32, 64, None, None) == bl.ERR_NULL
+    assert p(A, 0, 64, A, None) == bl.ERR_SHAPE
+    assert p(A, 32, 24, A, None) == bl.ERR_SHAPE
+    assert p(MIS, 32, 64, A, None) == bl.ERR_ALIGN
+    assert p(A, 32, 64, MIS, None) == bl.ERR_ALIGN
+
+
 def test_quantize_acts_validation():
     q = bl.lib().bitlinear_quantize_acts
     assert q(None, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_NULL
