@@ -19,7 +19,9 @@ reports the weight-streaming kernel (M = 1, 4, 16) in packed-weight GB/s against
 HBM peak: the mean time per launch over back-to-back launches, each reading a
 different copy of the weights from a ring larger than the 256 MB last-level
 cache; and the same projection at M = 1 and 4 from the weights stored five
-codes per byte (base 3), in GB/s of those stored bytes. ``cpu_baseline`` times the CPU oracle on a bounded
+codes per byte (base 3), in GB/s of those stored bytes. ``head`` times the final
+norm + bfloat16 lm_head (128256 x 2560) at 1 and 4 tokens in GB/s of the head.
+``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same step's tokens.
 """
 from __future__ import annotations
@@ -222,6 +224,11 @@ def main():
     if not args.no_decode:
         online = bench_online(torch, bl, synth, dev, args.decode_reps // 4, w_gate, w_up)
 
+    # ---------------------------------------------------------------- head
+    head = None
+    if not args.no_decode:
+        head = bench_head(torch, bl, synth, dev, args.decode_reps // 4)
+
     # ---------------------------------------------------------------- 30-layer stack
     stack = None
     if not args.no_stack:
@@ -256,6 +263,7 @@ def main():
         "kernels": kernels,
         "decode": decode,
         "online": online,
+        "head": head,
         "stack": stack,
         "cpu_baseline": cpu,
     }
@@ -372,6 +380,56 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
                 f"{nb3} stored bytes ({b2b_us / res[f'{name}_m{m}']['us']:.3f} x the two-bit time)")
         del ring, w3
         torch.cuda.empty_cache()
+    return res
+
+
+def bench_head(torch, bl, synth, dev, reps):
+    """The model's head at decode: final norm + the bfloat16 lm_head (128256 x 2560,
+    656.7 MB, larger than the last-level cache, so every launch streams it from
+    HBM), for 1 and 4 tokens: mean time per call over back-to-back calls."""
+    V, K = 128256, H
+    L = bl.lib()
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    stream = torch.cuda.current_stream(dev)
+    log("head: generating the 128256 x 2560 table")
+    table = torch.empty((V, K), dtype=torch.uint16, device=dev)
+    rows = 16032
+    for r0 in range(0, V, rows):
+        n = min(rows, V - r0)
+        w = torch.from_numpy(synth.weights(synth.stream_seed(BASE_SEED, 6, r0, 1), n, K)).to(dev)
+        table[r0:r0 + n] = w.to(torch.bfloat16).view(torch.uint16)
+        del w
+    gain = torch.full((K,), 0.1, dtype=torch.float32, device=dev)
+    nbytes = V * K * 2
+    res = {}
+    for m in (1, 4):
+        x = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 6, m, 5), m, K)).to(dev)
+        y = torch.empty((m, V), dtype=torch.float32, device=dev)
+        wsn = L.bitlinear_lm_head_workspace_bytes(m, K)
+        ws = torch.empty(max(wsn, 1), dtype=torch.uint8, device=dev)
+
+        def call():
+            st = L.bitlinear_lm_head(x.data_ptr(), m, K, gain.data_ptr(), 1e-5, table.data_ptr(), V, y.data_ptr(),
+                                     None, ws.data_ptr(), wsn, sp)
+            if st != 0:
+                raise RuntimeError(L.bitlinear_last_error().decode())
+
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[f"m{m}"] = {"us": round(us, 2), "gbs_head": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                        "head_bytes": nbytes}
+        log(f"head m={m}: {us:.1f} us per call (final norm + lm_head), {gbs:.0f} GB/s of the 656.7 MB table")
+    del table
+    torch.cuda.empty_cache()
     return res
 
 

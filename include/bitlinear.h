@@ -201,6 +201,41 @@ size_t bitlinear_forward_relu2_glu_workspace_bytes(int64_t m, int64_t inter, int
                                                    int32_t path);
 
 /* ---------------------------------------------------------------------------
+ * The model's ends ([nnterp] "Printout": embed_tokens = Embedding(128256, 2560),
+ * the final norm, lm_head = Linear(2560, 128256, bias=False); "Config": dtype
+ * bfloat16, tie_word_embeddings: the head's matrix is the embedding table).
+ * Tables are bfloat16 bit patterns (uint16), row-major [vocab][k].
+ * ------------------------------------------------------------------------- */
+
+/* bitlinear_embed — x[t][:] = the table row of ids[t], widened to fp32 (exact).
+ *   ids    device [m] int64; an id outside [0, vocab) gives a zero row.
+ *   table  device [vocab][k] bfloat16.   x  device [m][k] fp32, written.
+ * Errors: NULL pointers -> ERR_NULL; m < 0, vocab <= 0, k <= 0 -> ERR_SHAPE.
+ * m == 0 is a no-op. */
+bitlinear_status bitlinear_embed(const int64_t *ids, int64_t m, const uint16_t *table, int64_t vocab, int64_t k,
+                                 float *x, void *stream);
+
+/* bitlinear_lm_head — the final RMSNorm and the head, per token (reading R20):
+ *   ms = sum_k x_k^2 / k (fp64);  r = fl32(1 / sqrt(ms + eps));
+ *   o_k = bf16(fl32(g_k * fl32(x_k * r)));  logits[n] = sum_k o_k w[n][k],
+ * the bfloat16 products exact and the sum in fp32 (its rounding is within
+ * k 2^-24 sum_k |o_k w[n][k]|).
+ *   x          device [m][k] fp32 (the last block's output).
+ *   norm_gain  NULL (gain 1) or device [k] fp32.
+ *   w_head     device [n_vocab][k] bfloat16, 16-byte aligned; k % 8 == 0, k <= 4096.
+ *   logits     device [m][n_vocab] fp32, written.
+ *   normed_out NULL or device [m][k] bfloat16: o.
+ *   workspace  >= bitlinear_lm_head_workspace_bytes(m, k) bytes when normed_out
+ *              is NULL (0 otherwise).
+ * Tokens are taken four per pass over the head.
+ * Errors: NULL x/w_head/logits -> ERR_NULL; bad shapes -> ERR_SHAPE;
+ * misaligned -> ERR_ALIGN; small workspace -> ERR_WORKSPACE. m == 0 is a no-op. */
+bitlinear_status bitlinear_lm_head(const float *x, int64_t m, int64_t k, const float *norm_gain, float eps,
+                                   const uint16_t *w_head, int64_t n_vocab, float *logits, uint16_t *normed_out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+size_t bitlinear_lm_head_workspace_bytes(int64_t m, int64_t k);
+
+/* ---------------------------------------------------------------------------
  * Five codes per byte ([tiny] "O que é" and "Arquivos": the ternary checkpoint
  * also ships in a storage denser than two bits per weight; the pages give no
  * layout, so this one is the library's own). Row n of k codes takes

@@ -44,6 +44,10 @@ def _load():
             "orc_ternarize": (None, [_p, _i64, ctypes.c_double, _p]),
             "orc_pack": (ctypes.c_int, [_p, _i64, _i64, _p]),
             "orc_unpack": (_i64, [_p, _i64, _i64, _p]),
+            "orc_round_bf16": (None, [_p, _i64, _p]),
+            "orc_bf16_to_f32": (None, [_p, _i64, _p]),
+            "orc_final_norm": (None, [_p, _i64, _i64, _p, ctypes.c_float, _p]),
+            "orc_lm_head": (None, [_p, _i64, _i64, _p, _i64, _p, _p]),
             "orc_base3_row_bytes": (_i64, [_i64]),
             "orc_pack_base3": (ctypes.c_int, [_p, _i64, _i64, _p]),
             "orc_unpack_base3": (_i64, [_p, _i64, _i64, _p]),
@@ -125,6 +129,48 @@ def unpack_base3(p, k: int):
     c = np.empty((n, k), dtype=np.int8)
     bad = _load().orc_unpack_base3(pp, n, k, c.ctypes.data)
     return c, int(bad)
+
+
+def round_bf16(x) -> np.ndarray:
+    """O11: fp32 -> bfloat16 bit patterns (uint16), nearest, ties to even."""
+    x, px = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_round_bf16(px, x.size, out.ctypes.data)
+    return out
+
+
+def bf16_to_f32(b) -> np.ndarray:
+    """bfloat16 bit patterns -> their fp32 values (exact)."""
+    b, pb = _c(b, np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    _load().orc_bf16_to_f32(pb, b.size, out.ctypes.data)
+    return out
+
+
+def final_norm(x, gain=None, eps: float = 1e-5) -> np.ndarray:
+    """O12: the final RMSNorm of [m][k] fp32 rows, as bfloat16 bits [m][k] (R20)."""
+    x, px = _c(x, np.float32)
+    m, k = x.shape
+    pg = None
+    if gain is not None:
+        gain, pg = _c(gain, np.float32)
+    out = np.empty((m, k), dtype=np.uint16)
+    _load().orc_final_norm(px, m, k, pg, eps, out.ctypes.data)
+    return out
+
+
+def lm_head(o, w):
+    """O13: logits [m][n] fp32 of bfloat16 inputs o [m][k] and head w [n][k]
+    (both uint16 bit patterns), and sum |o w| per logit (fp64)."""
+    o, po = _c(o, np.uint16)
+    w, pw = _c(w, np.uint16)
+    m, k = o.shape
+    n = w.shape[0]
+    assert w.shape[1] == k
+    y = np.empty((m, n), dtype=np.float32)
+    a = np.empty((m, n), dtype=np.float64)
+    _load().orc_lm_head(po, m, k, pw, n, y.ctypes.data, a.ctypes.data)
+    return y, a
 
 
 def quant_absmax(x):

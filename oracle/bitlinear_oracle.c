@@ -15,7 +15,9 @@
  *  [nnterp] "nnterp encyclopedia: BitNet b1.58" (family bitnet), sections
  *           "The block, in order", "Scaling inside a sublayer is undone by the
  *           sub-norm", "The projections quantize their inputs and weights",
- *           "The MLP gates with a squared ReLU", "The two checkpoints", "Config".
+ *           "The MLP gates with a squared ReLU", "The two checkpoints", "Config",
+ *           "Printout", "Loading", "From the family module".
+ *  [tiny]   "BitNet TinyDialogues 1.58b" README, sections "O que é", "Arquivos".
  *
  * Where the pages leave a step open, the reading taken is stated at the step
  * (R-numbers match the list of readings kept with the design notes).
@@ -258,4 +260,77 @@ void orc_rescale(const int32_t *acc, int64_t m, int64_t n, const float *deq, con
       y[r * n + j] = t * g;
     }
   }
+}
+
+/* ---- O11: bfloat16 ------------------------------------------------------------
+ * [nnterp] "Config": the checkpoint's dtype is bfloat16. A bfloat16 value is
+ * the top 16 bits of a binary32 one; rounding keeps the nearest such value,
+ * ties to the one whose last kept bit is 0 (R1's rule). Inputs are finite
+ * (R17). */
+static uint16_t bf16_of(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint32_t dropped = u & 0xFFFFu, kept = u >> 16;
+  uint32_t r = kept;
+  if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) r += 1u;
+  return (uint16_t)r;
+}
+
+static float f32_of_bf16(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+void orc_round_bf16(const float *x, int64_t n, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_of(x[i]);
+}
+
+void orc_bf16_to_f32(const uint16_t *b, int64_t n, float *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_of_bf16(b[i]);
+}
+
+/* ---- O12: the final norm, as the head's bfloat16 input --------------------------
+ * [nnterp] "Printout": (norm) BitNetRMSNorm((2560,), eps=1e-05) after the last
+ * block, then lm_head; "From the family module": Llama's tree (model.norm, then
+ * lm_head). R7's norm; R20 fixes the order in our fp32 stream:
+ *   ms = sum_k x_k^2 / K in fp64, in order;  r = fl32(1 / sqrt(ms + eps));
+ *   o_k = bf16(fl32(g_k * fl32(x_k * r))).
+ * gain NULL means 1. */
+void orc_final_norm(const float *x, int64_t m, int64_t k, const float *gain, float eps, uint16_t *out) {
+  for (int64_t r = 0; r < m; ++r) {
+    const float *xr = x + r * k;
+    double ss = 0.0;
+    for (int64_t i = 0; i < k; ++i) ss += (double)xr[i] * (double)xr[i];
+    const double ms = ss / (double)k;
+    const float rf = (float)(1.0 / sqrt(ms + (double)eps));
+    for (int64_t i = 0; i < k; ++i) {
+      const float v = xr[i] * rf;
+      const float o = gain ? gain[i] * v : v;
+      out[r * k + i] = bf16_of(o);
+    }
+  }
+}
+
+/* ---- O13: the head ----------------------------------------------------------------
+ * [nnterp] "Printout": lm_head = Linear(2560 -> 128256, bias=False); "Config":
+ * bfloat16, tie_word_embeddings (the head's matrix is the embedding table).
+ * logits[r][n] = sum_k o[r][k] * w[n][k] over bfloat16 o and w: every product
+ * is exact in binary64 and the fp64 sum of K of them is within K 2^-53 of the
+ * exact one, far inside the fp32 rounding; stored rounded to fp32. absdot gets
+ * sum_k |o w| (fp64), the scale of the rounding error any fp32 summation order
+ * may make. */
+void orc_lm_head(const uint16_t *o, int64_t m, int64_t k, const uint16_t *w, int64_t n, float *y, double *absdot) {
+  for (int64_t r = 0; r < m; ++r)
+    for (int64_t j = 0; j < n; ++j) {
+      double s = 0.0, a = 0.0;
+      for (int64_t i = 0; i < k; ++i) {
+        const double p = (double)f32_of_bf16(o[r * k + i]) * (double)f32_of_bf16(w[j * k + i]);
+        s += p;
+        a += fabs(p);
+      }
+      y[r * n + j] = (float)s;
+      if (absdot) absdot[r * n + j] = a;
+    }
 }

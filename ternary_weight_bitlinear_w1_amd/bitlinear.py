@@ -79,6 +79,9 @@ def lib():
                                                 _sz, _p]),
             "bitlinear_forward_online_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _p, _i32]),
             "bitlinear_forward_relu2_glu_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+            "bitlinear_embed": (_i32, [_p, _i64, _p, _i64, _i64, _p, _p]),
+            "bitlinear_lm_head": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p, _p, _p, _sz, _p]),
+            "bitlinear_lm_head_workspace_bytes": (_sz, [_i64, _i64]),
             "bitlinear_base3_row_bytes": (_sz, [_i64]),
             "bitlinear_pack_base3": (_i32, [_p, _i64, _i64, _p, _p]),
             "bitlinear_forward_base3": (_i32, [_p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _p, _p, _sz, _p]),
@@ -220,6 +223,33 @@ def forward_relu2_glu(packed: torch.Tensor, k: int, gamma: Sequence[float], x: O
            lib().bitlinear_forward_relu2_glu(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), inter,
                                              g, _ptr(y), path, _ptr(ws), nb, _stream(dev)))
     return y
+
+
+def embed(ids: torch.Tensor, table: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows of the bfloat16 table (uint16 bits [vocab][k]) for int64 ids [m] -> fp32 [m][k]."""
+    vocab, k = table.shape
+    m = ids.shape[0]
+    x = out if out is not None else torch.empty((m, k), dtype=torch.float32, device=table.device)
+    _check("bitlinear_embed", lib().bitlinear_embed(_ptr(ids), m, _ptr(table), vocab, k, _ptr(x),
+                                                    _stream(table.device)))
+    return x
+
+
+def lm_head(x: torch.Tensor, w_head: torch.Tensor, gain: Optional[torch.Tensor] = None, eps: float = 1e-5,
+            want_normed: bool = False, out: Optional[torch.Tensor] = None):
+    """Final norm + bfloat16 head: x [m][k] fp32, w_head uint16 bits [vocab][k] ->
+    logits [m][vocab] fp32 (and the normed bfloat16 input when ``want_normed``)."""
+    m, k = x.shape
+    n = w_head.shape[0]
+    dev = x.device
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    normed = torch.empty((m, k), dtype=torch.uint16, device=dev) if want_normed else None
+    nb = 0 if want_normed else lib().bitlinear_lm_head_workspace_bytes(m, k)
+    ws = _workspace(nb, dev)
+    _check("bitlinear_lm_head",
+           lib().bitlinear_lm_head(_ptr(x), m, k, _ptr(gain), eps, _ptr(w_head), n, _ptr(y), _ptr(normed), _ptr(ws),
+                                   nb, _stream(dev)))
+    return (y, normed) if want_normed else y
 
 
 def base3_row_bytes(k: int) -> int:

@@ -393,6 +393,45 @@ bitlinear_status bitlinear_forward_relu2_glu(const float *x, const int8_t *codes
   return launched(bl::launch_relu2_glu(gu, m, inter, y, s), "relu2 gating");
 }
 
+// ---------------------------------------------------------------- the model's ends
+bitlinear_status bitlinear_embed(const int64_t *ids, int64_t m, const uint16_t *table, int64_t vocab, int64_t k,
+                                 float *x, void *stream) {
+  g_err.clear();
+  if (m != 0 && (!ids || !table || !x)) return fail(BITLINEAR_ERR_NULL, "ids, table and x are required");
+  if (m < 0 || vocab <= 0 || k <= 0 || m > kMaxDim || vocab > kMaxDim || k > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, vocab = %lld, k = %lld", (long long)m, (long long)vocab,
+                (long long)k);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  return launched(bl::launch_embed(ids, m, table, vocab, k, x, as_stream(stream)), "embedding gather");
+}
+
+size_t bitlinear_lm_head_workspace_bytes(int64_t m, int64_t k) {
+  return m > 0 && k > 0 ? align256((size_t)(m * k) * sizeof(uint16_t)) : 0;
+}
+
+bitlinear_status bitlinear_lm_head(const float *x, int64_t m, int64_t k, const float *norm_gain, float eps,
+                                   const uint16_t *w_head, int64_t n_vocab, float *logits, uint16_t *normed_out,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+  g_err.clear();
+  if (m != 0 && (!x || !w_head || !logits)) return fail(BITLINEAR_ERR_NULL, "x, w_head and logits are required");
+  if (m < 0 || n_vocab <= 0 || !bl::lm_head_supported(k) || m > kMaxDim || n_vocab > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, k = %lld, n_vocab = %lld: need k %% 8 == 0, 0 < k <= 4096",
+                (long long)m, (long long)k, (long long)n_vocab);
+  if (!(eps >= 0.0f)) return fail(BITLINEAR_ERR_ARG, "eps must be >= 0");
+  if (m != 0 && (!aligned16(x) || !aligned16(w_head) || (normed_out && !aligned16(normed_out))))
+    return fail(BITLINEAR_ERR_ALIGN, "x, w_head and normed_out must be 16-byte aligned");
+  const size_t need = normed_out ? 0 : bitlinear_lm_head_workspace_bytes(m, k);
+  if (m > 0 && need > 0 && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  hipStream_t s = as_stream(stream);
+  uint16_t *o = normed_out ? normed_out : static_cast<uint16_t *>(workspace);
+  BL_TRY(launched(bl::launch_final_norm(x, m, k, norm_gain, eps, o, s), "final norm"));
+  return launched(bl::launch_lm_head(o, m, k, w_head, n_vocab, logits, s), "lm_head");
+}
+
 // ---------------------------------------------------------------- five codes per byte
 size_t bitlinear_base3_row_bytes(int64_t k) { return k > 0 ? (size_t)(16 * ((k + 79) / 80)) : 0; }
 

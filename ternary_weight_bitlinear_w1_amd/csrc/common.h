@@ -173,6 +173,16 @@ struct FusedDecode {
   float *deq_out;      // optional [m]
 };
 
+// The head (head.hip): final norm to bfloat16, the bfloat16 lm_head, and the
+// embedding gather of the tied table.
+bool lm_head_supported(int64_t k);
+hipError_t launch_final_norm(const float *x, int64_t m, int64_t k, const float *gain, float eps, uint16_t *o,
+                             hipStream_t stream);
+hipError_t launch_lm_head(const uint16_t *o, int64_t m, int64_t k, const uint16_t *w, int64_t n, float *y,
+                          hipStream_t stream);
+hipError_t launch_embed(const int64_t *ids, int64_t m, const uint16_t *table, int64_t vocab, int64_t k, float *x,
+                        hipStream_t stream);
+
 // Five codes per byte (base3.hip): repacking, and the 1..4-token contraction.
 bool gemv_b3_supported(int64_t m, int64_t k);
 hipError_t launch_pack_base3(const uint8_t *packed, int64_t n, int64_t k, uint8_t *out, hipStream_t stream);

@@ -191,6 +191,31 @@ def test_pack_base3_validation():
     assert p(A, 32, 64, MIS, None) == bl.ERR_ALIGN
 
 
+def test_embed_and_lm_head_validation():
+    L = bl.lib()
+    assert L.bitlinear_embed(None, 4, A, 100, 64, A, None) == bl.ERR_NULL
+    assert L.bitlinear_embed(A, -1, A, 100, 64, A, None) == bl.ERR_SHAPE
+    assert L.bitlinear_embed(A, 4, A, 0, 64, A, None) == bl.ERR_SHAPE
+    assert L.bitlinear_embed(None, 0, None, 100, 64, None, None) == bl.OK
+
+    def head(x=A, m=4, k=2560, gain=None, eps=1e-5, w=A, n=1000, y=A, normed=None, ws=A, wsb=1 << 20):
+        return L.bitlinear_lm_head(x, m, k, gain, eps, w, n, y, normed, ws, wsb, None)
+
+    assert head(x=None) == bl.ERR_NULL
+    assert head(w=None) == bl.ERR_NULL
+    assert head(y=None) == bl.ERR_NULL
+    assert head(k=2564) == bl.ERR_SHAPE     # k % 8
+    assert head(k=4104) == bl.ERR_SHAPE     # k <= 4096
+    assert head(n=0) == bl.ERR_SHAPE
+    assert head(eps=-1.0) == bl.ERR_ARG
+    assert head(w=MIS) == bl.ERR_ALIGN
+    assert head(ws=None) == bl.ERR_WORKSPACE
+    assert head(wsb=16) == bl.ERR_WORKSPACE
+    assert head(m=0) == bl.OK
+    assert L.bitlinear_lm_head_workspace_bytes(4, 2560) >= 4 * 2560 * 2
+    assert L.bitlinear_lm_head_workspace_bytes(0, 2560) == 0
+
+
 def test_quantize_acts_validation():
     q = bl.lib().bitlinear_quantize_acts
     assert q(None, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_NULL

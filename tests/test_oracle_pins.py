@@ -211,6 +211,112 @@ def test_base3_roundtrip_and_row_size(k):
     assert np.array_equal(oracle.contract(q, back), oracle.contract(q, two_bit))
 
 
+# ------------------------------------------------------------------ O11 bfloat16
+def _f32_from_bits(b):
+    return np.array([b], dtype=np.uint32).view(np.float32)
+
+
+def test_golden_bf16_round():
+    for case in gold("bf16_round.json")["cases"]:
+        x = _f32_from_bits(int(case["f32_bits"], 16))
+        assert int(oracle.round_bf16(x)[0]) == int(case["bf16_bits"], 16), case
+
+
+def _bf16_exact(v: float) -> int:
+    """Nearest bfloat16 by exact rational arithmetic (ties to even), as bits."""
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    sign = 0x8000 if v < 0 else 0
+    a = Fraction(abs(v))
+    e = math.floor(math.log2(a))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                     # subnormals share the lowest exponent
+    ulp = Fraction(2) ** (e - 7)         # 8 significant bits
+    q, rem = divmod(a, ulp)
+    q = int(q)
+    if rem > ulp / 2 or (rem == ulp / 2 and q % 2 == 1):
+        q += 1
+    val = q * ulp
+    if val >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    f = np.float32(float(val))            # exactly representable: 8 bits of mantissa
+    return sign | (int(f.view(np.uint32)) >> 16)
+
+
+def test_bf16_round_against_exact_rationals():
+    r = rng(11)
+    bits = r.integers(0, 2 ** 32, size=3000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    got = oracle.round_bf16(x)
+    for v, g in zip(x.tolist(), got.tolist()):
+        assert g == _bf16_exact(v), (v, hex(g))
+    back = oracle.bf16_to_f32(got).view(np.uint32)  # widening is exact: the low 16 bits are zero
+    assert np.array_equal(back >> 16, got.astype(np.uint32)) and not (back & 0xFFFF).any()
+
+
+# ------------------------------------------------------------------ O12 final norm
+def test_final_norm_scale_and_sign():
+    """With eps = 0 the norm is exactly invariant to scaling by 2^j (ms scales by
+    4^j, r by 2^-j, all exactly), and odd in x; a zero gain gives zeros."""
+    r = rng(12)
+    x = r.normal(size=(5, 96)).astype(np.float32)
+    g = (1 + 0.1 * r.normal(size=96)).astype(np.float32)
+    base = oracle.final_norm(x, g, eps=0.0)
+    for j in (-3, 1, 5):
+        assert np.array_equal(oracle.final_norm(np.ldexp(x, j).astype(np.float32), g, eps=0.0), base)
+    neg = oracle.final_norm(-x, g, eps=0.0)
+    assert np.array_equal(neg, base ^ np.uint16(0x8000))
+    assert not (oracle.final_norm(x, np.zeros(96, np.float32)) & np.uint16(0x7FFF)).any()
+
+
+def test_final_norm_against_exact_rationals():
+    """A few rows computed with exact rationals and 60-digit decimals, following
+    R20 step by step: ms exact, r = nearest float32 to 1/sqrt(ms + eps), then two
+    float32 products and one bfloat16 rounding."""
+    getcontext().prec = 60
+    r = rng(13)
+    x = r.normal(size=(3, 16)).astype(np.float32)
+    g = (1 + 0.1 * r.normal(size=16)).astype(np.float32)
+    eps = np.float32(1e-5)
+    got = oracle.final_norm(x, g, eps=float(eps))
+    for i in range(3):
+        ms = sum(Fraction(float(v)) ** 2 for v in x[i]) / 16
+        d = Decimal(ms.numerator) / Decimal(ms.denominator) + Decimal(float(eps))
+        rr = np.float32(float(1 / d.sqrt()))
+        for j in range(16):
+            v = np.float32(x[i, j] * rr)
+            o = np.float32(g[j] * v)
+            assert int(got[i, j]) == _bf16_exact(float(o))
+
+
+# ------------------------------------------------------------------ O13 head
+def test_lm_head_against_exact_rationals():
+    r = rng(14)
+    o = oracle.round_bf16(r.normal(size=(3, 40)).astype(np.float32))
+    w = oracle.round_bf16((0.02 * r.normal(size=(7, 40))).astype(np.float32))
+    y, a = oracle.lm_head(o, w)
+    of, wf = oracle.bf16_to_f32(o), oracle.bf16_to_f32(w)
+    for i in range(3):
+        for j in range(7):
+            exact = sum(Fraction(float(of[i, t])) * Fraction(float(wf[j, t])) for t in range(40))
+            assert y[i, j] == np.float32(float(exact))
+            assert a[i, j] >= abs(float(exact))
+
+
+def test_lm_head_one_hot_rows_select_columns():
+    """A head row that is one-hot at column t returns o[:, t] exactly."""
+    r = rng(15)
+    o = oracle.round_bf16(r.normal(size=(4, 32)).astype(np.float32))
+    w = np.zeros((32, 32), dtype=np.uint16)
+    w[np.arange(32), np.arange(32)] = 0x3F80  # 1.0
+    y, _ = oracle.lm_head(o, w)
+    assert np.array_equal(y, oracle.bf16_to_f32(o))
+
+
 # ------------------------------------------------------------------ O4
 def test_golden_act_codes():
     """[nnterp] "The projections quantize their inputs and weights": round(x * 127 / max|x|)."""
