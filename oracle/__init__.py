@@ -48,6 +48,9 @@ def _load():
             "orc_bf16_to_f32": (None, [_p, _i64, _p]),
             "orc_final_norm": (None, [_p, _i64, _i64, _p, ctypes.c_float, _p]),
             "orc_lm_head": (None, [_p, _i64, _i64, _p, _i64, _p, _p]),
+            "orc_rope": (None, [_p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _p, ctypes.c_double]),
+            "orc_attention": (_i64, [_p, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p, _i64, _i64,
+                                     _p, _p, _p, _p, _p, _p]),
             "orc_base3_row_bytes": (_i64, [_i64]),
             "orc_pack_base3": (ctypes.c_int, [_p, _i64, _i64, _p]),
             "orc_unpack_base3": (_i64, [_p, _i64, _i64, _p]),
@@ -171,6 +174,54 @@ def lm_head(o, w):
     a = np.empty((m, n), dtype=np.float64)
     _load().orc_lm_head(po, m, k, pw, n, y.ctypes.data, a.ctypes.data)
     return y, a
+
+
+def rope(x, pos, n_heads: int, head_dim: int, theta: float, col0: int = 0) -> np.ndarray:
+    """O14 (R19): rotate-half RoPE of the n_heads head vectors starting at column
+    col0 of each row of x [m][ld], token r at position pos[r]; returns a copy."""
+    y = np.array(x, dtype=np.float32, order="C", copy=True)
+    m, ld = y.shape
+    p, pp = _c(np.asarray(pos, dtype=np.int64), np.int64)
+    _load().orc_rope(y.ctypes.data, m, ld, col0, n_heads, head_dim, pp, theta)
+    return y
+
+
+def attention(q, k_cache, v_cache, slot, pos, n_heads: int, n_kv: int, head_dim: int):
+    """O15 (R21): each token's attention over positions 0..pos of its slot.
+    q [m][ldq] fp32 (heads from column 0); caches [n_slots][n_kv][t_max][hd]
+    bfloat16 bits. Returns (out [m][n_heads hd] fp32, vmag, smag [m][n_heads],
+    number of tokens out of range)."""
+    q, pq = _c(q, np.float32)
+    kc, pk = _c(k_cache, np.uint16)
+    vc, pv = _c(v_cache, np.uint16)
+    n_slots, _, tmax, _ = kc.shape
+    m = q.shape[0]
+    sl, ps = _c(np.asarray(slot, dtype=np.int64), np.int64)
+    po, pp = _c(np.asarray(pos, dtype=np.int64), np.int64)
+    out = np.empty((m, n_heads * head_dim), dtype=np.float32)
+    vmag = np.empty((m, n_heads * head_dim), dtype=np.float64)
+    smag = np.empty((m, n_heads), dtype=np.float64)
+    scratch = np.empty(max(1, tmax), dtype=np.float64)
+    bad = _load().orc_attention(pq, m, q.shape[1], n_heads, n_kv, head_dim, pk, pv, n_slots, tmax, ps, pp,
+                                out.ctypes.data, vmag.ctypes.data, smag.ctypes.data, scratch.ctypes.data)
+    return out, vmag, smag, int(bad)
+
+
+def kv_append(k_cache, v_cache, k, v, slot, pos, n_kv: int, head_dim: int) -> int:
+    """R21: write the rows' keys k and values v ([m][n_kv hd] fp32) rounded to
+    bfloat16 into the caches (in place) at [slot][g][pos]; rows out of range are
+    skipped. Returns how many were skipped."""
+    n_slots, _, tmax, _ = k_cache.shape
+    kb = round_bf16(np.asarray(k, dtype=np.float32)).reshape(-1, n_kv, head_dim)
+    vb = round_bf16(np.asarray(v, dtype=np.float32)).reshape(-1, n_kv, head_dim)
+    skipped = 0
+    for r, (s, p) in enumerate(zip(np.asarray(slot).tolist(), np.asarray(pos).tolist())):
+        if not (0 <= s < n_slots and 0 <= p < tmax):
+            skipped += 1
+            continue
+        k_cache[s, :, p, :] = kb[r]
+        v_cache[s, :, p, :] = vb[r]
+    return skipped
 
 
 def quant_absmax(x):

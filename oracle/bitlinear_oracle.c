@@ -334,3 +334,96 @@ void orc_lm_head(const uint16_t *o, int64_t m, int64_t k, const uint16_t *w, int
       if (absdot) absdot[r * n + j] = a;
     }
 }
+
+/* ---- O14: rotary position embedding ----------------------------------------------
+ * [card] "Model Details": the model uses RoPE; [nnterp] "From the family module":
+ * Llama's block; "Config": head_dim 128, max_position_embeddings 4096. The pages
+ * give neither the pairing nor the base. R19: Llama's rotate-half pairing, the
+ * base theta an argument. For token r at position p and each head vector v of
+ * hd values (heads start at column col0 of a row of ld floats), for i < hd/2:
+ *   a = p * theta^(-2i/hd) (fp64), c = fl32(cos a), s = fl32(sin a),
+ *   v[i] <- fl32(fl32(v[i] c) - fl32(v[i + hd/2] s)),
+ *   v[i + hd/2] <- fl32(fl32(v[i + hd/2] c) + fl32(v[i] s))  (old values). */
+void orc_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
+              double theta) {
+  const int half = hd / 2;
+  for (int64_t r = 0; r < m; ++r)
+    for (int h = 0; h < n_heads; ++h) {
+      float *v = x + r * ld + col0 + (int64_t)h * hd;
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)pos[r] * pow(theta, -(2.0 * i) / (double)hd);
+        const float c = (float)cos(ang), s = (float)sin(ang);
+        const float a = v[i], b = v[i + half];
+        const float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+        v[i] = ac - bs;
+        v[i + half] = bc + as;
+      }
+    }
+}
+
+/* ---- O15: one token's attention over its sequence's cache -------------------------
+ * [nnterp] "Loading": the eager attention (no softcap, window or sink);
+ * "Printout"/"Config": 20 query heads, 5 key/value heads of 128; query head h
+ * reads key/value head h / (n_heads / n_kv). R21: the cache holds the keys
+ * (after RoPE) and values rounded to bfloat16, [slot][kv head][position][hd];
+ * token r of sequence slot[r] sits at position pos[r] and attends to positions
+ * 0 .. pos[r] of that slot (causal). In fp64:
+ *   s_t = (1/sqrt(hd)) sum_d q_d k_td;  w_t = exp(s_t - max s) / sum exp(. - max s);
+ *   out_d = fl32(sum_t w_t v_td).
+ * vmag gets sum_t w_t |v_td| and smag max_t (1/sqrt(hd)) sum_d |q_d k_td|, the
+ * scales of the fp32 rounding a kernel makes. Returns the number of tokens whose
+ * slot or position is out of range (their outputs are zero). */
+int64_t orc_attention(const float *q, int64_t m, int64_t ldq, int n_heads, int n_kv, int hd, const uint16_t *kc,
+                      const uint16_t *vc, int64_t n_slots, int64_t tmax, const int64_t *slot, const int64_t *pos,
+                      float *out, double *vmag, double *smag, double *scratch) {
+  const int group = n_heads / n_kv;
+  const double scale = 1.0 / sqrt((double)hd);
+  int64_t bad = 0;
+  for (int64_t r = 0; r < m; ++r) {
+    const int ok = slot[r] >= 0 && slot[r] < n_slots && pos[r] >= 0 && pos[r] < tmax;
+    if (!ok) ++bad;
+    for (int h = 0; h < n_heads; ++h) {
+      float *o = out + r * (int64_t)n_heads * hd + (int64_t)h * hd;
+      double *vm = vmag + r * (int64_t)n_heads * hd + (int64_t)h * hd;
+      if (!ok) {
+        for (int d = 0; d < hd; ++d) { o[d] = 0.0f; vm[d] = 0.0; }
+        smag[r * n_heads + h] = 0.0;
+        continue;
+      }
+      const int g = h / group;
+      const uint16_t *kb = kc + ((slot[r] * n_kv + g) * tmax) * (int64_t)hd;
+      const uint16_t *vb = vc + ((slot[r] * n_kv + g) * tmax) * (int64_t)hd;
+      const float *qh = q + r * ldq + (int64_t)h * hd;
+      const int64_t T = pos[r] + 1;
+      double mx = -INFINITY, sm = 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        double dot = 0.0, ad = 0.0;
+        for (int d = 0; d < hd; ++d) {
+          const double p = (double)qh[d] * (double)f32_of_bf16(kb[t * hd + d]);
+          dot += p;
+          ad += fabs(p);
+        }
+        scratch[t] = scale * dot;
+        if (scratch[t] > mx) mx = scratch[t];
+        if (scale * ad > sm) sm = scale * ad;
+      }
+      double L = 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        scratch[t] = exp(scratch[t] - mx);
+        L += scratch[t];
+      }
+      for (int d = 0; d < hd; ++d) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+          const double v = (double)f32_of_bf16(vb[t * hd + d]);
+          acc += scratch[t] * v;
+          mag += scratch[t] * fabs(v);
+        }
+        o[d] = (float)(acc / L);
+        vm[d] = mag / L;
+      }
+      smag[r * n_heads + h] = sm;
+    }
+  }
+  return bad;
+}

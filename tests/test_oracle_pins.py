@@ -317,6 +317,101 @@ def test_lm_head_one_hot_rows_select_columns():
     assert np.array_equal(y, oracle.bf16_to_f32(o))
 
 
+# ------------------------------------------------------------------ O14 RoPE (R19)
+def test_golden_rope():
+    g = gold("rope.json")
+    for case in g["cases"]:
+        x = np.array([case["x"]], dtype=np.float32)
+        y = oracle.rope(x, [g["position"]], 1, g["head_dim"], g["theta"])
+        assert np.array_equal(y[0], np.array(case["y"], dtype=np.float32)), (case, y)
+
+
+def test_rope_position_zero_is_identity_and_pairs_keep_length():
+    r = rng(16)
+    x = r.normal(size=(3, 2 * 128)).astype(np.float32)
+    assert np.array_equal(oracle.rope(x, [0, 0, 0], 2, 128, 5e5), x)
+    y = oracle.rope(x, [1, 517, 4095], 2, 128, 5e5).astype(np.float64).reshape(3, 2, 2, 64)
+    xx = x.astype(np.float64).reshape(3, 2, 2, 64)
+    n0 = xx[:, :, 0] ** 2 + xx[:, :, 1] ** 2
+    n1 = y[:, :, 0] ** 2 + y[:, :, 1] ** 2
+    assert np.allclose(n1, n0, rtol=2e-6, atol=1e-30)
+
+
+def test_rope_scores_depend_on_relative_position():
+    """<rope(q, a), rope(k, b)> is a function of a - b: shifting both positions by
+    the same amount keeps every head's score (to fp32 rounding)."""
+    r = rng(17)
+    q = r.normal(size=(1, 128)).astype(np.float32)
+    k = r.normal(size=(1, 128)).astype(np.float32)
+    base = None
+    for a, b in ((7, 3), (107, 103), (2007, 2003)):
+        s = float(np.dot(oracle.rope(q, [a], 1, 128, 5e5)[0].astype(np.float64),
+                         oracle.rope(k, [b], 1, 128, 5e5)[0].astype(np.float64)))
+        if base is None:
+            base = s
+        assert abs(s - base) <= 1e-4 * float(np.abs(q).sum() * np.abs(k).max()), (a, b, s, base)
+
+
+# ------------------------------------------------------------------ O15 attention (R21)
+def _caches(r, n_slots, n_kv, tmax, hd, scale=1.0):
+    kc = oracle.round_bf16((scale * r.normal(size=(n_slots, n_kv, tmax, hd))).astype(np.float32))
+    vc = oracle.round_bf16(r.normal(size=(n_slots, n_kv, tmax, hd)).astype(np.float32))
+    return kc, vc
+
+
+def test_attention_single_position_returns_the_value():
+    r = rng(18)
+    kc, vc = _caches(r, 2, 2, 8, 16)
+    q = r.normal(size=(2, 4 * 16)).astype(np.float32)
+    out, _, _, bad = oracle.attention(q, kc, vc, [1, 0], [0, 0], 4, 2, 16)
+    assert bad == 0
+    for t, s in enumerate((1, 0)):
+        for h in range(4):
+            assert np.array_equal(out[t, 16 * h:16 * h + 16], oracle.bf16_to_f32(vc[s, h // 2, 0]))
+
+
+def test_attention_equal_keys_average_and_heads_share_kv():
+    """Equal keys give equal weights: the output is the mean of the values. Values
+    that are constant per key/value head show which head each query head reads."""
+    n_heads, n_kv, hd, T = 8, 2, 8, 5
+    kc = np.zeros((1, n_kv, 16, hd), dtype=np.uint16)
+    kc[...] = oracle.round_bf16(np.full(hd, 0.5, np.float32))
+    vc = oracle.round_bf16(np.random.default_rng(1).normal(size=(1, n_kv, 16, hd)).astype(np.float32))
+    q = np.random.default_rng(2).normal(size=(1, n_heads * hd)).astype(np.float32)
+    out, _, _, _ = oracle.attention(q, kc, vc, [0], [T - 1], n_heads, n_kv, hd)
+    vf = oracle.bf16_to_f32(vc).astype(np.float64)
+    for h in range(n_heads):
+        want = vf[0, h // (n_heads // n_kv), :T].mean(axis=0)
+        assert np.allclose(out[0, h * hd:(h + 1) * hd], want, rtol=1e-6, atol=1e-7)
+    const = np.zeros_like(vc)
+    for g in range(n_kv):
+        const[0, g] = oracle.round_bf16(np.full(hd, g + 1.0, np.float32))
+    out2, _, _, _ = oracle.attention(q, oracle.round_bf16(np.random.default_rng(3).normal(
+        size=(1, n_kv, 16, hd)).astype(np.float32)), const, [0], [9], n_heads, n_kv, hd)
+    for h in range(n_heads):
+        assert np.all(out2[0, h * hd:(h + 1) * hd] == np.float32(h // (n_heads // n_kv) + 1))
+
+
+def test_attention_permutation_dominance_and_range():
+    r = rng(19)
+    kc, vc = _caches(r, 1, 1, 32, 16)
+    q = r.normal(size=(1, 16)).astype(np.float32)
+    out, _, _, _ = oracle.attention(q, kc, vc, [0], [20], 1, 1, 16)
+    perm = r.permutation(21)
+    kp, vp = kc.copy(), vc.copy()
+    kp[0, 0, :21], vp[0, 0, :21] = kc[0, 0, perm], vc[0, 0, perm]
+    outp, _, _, _ = oracle.attention(q, kp, vp, [0], [20], 1, 1, 16)
+    assert np.allclose(outp, out, rtol=1e-12, atol=1e-12)
+    # a key along q with a score 40 above the rest takes all the weight
+    kd = kc.copy()
+    kd[0, 0, :21] = 0
+    kd[0, 0, 7] = oracle.round_bf16((q[0] * (40.0 * 4.0 / float(np.dot(q[0], q[0])))).astype(np.float32))
+    outd, _, _, _ = oracle.attention(q, kd, vc, [0], [20], 1, 1, 16)
+    assert np.allclose(outd[0], oracle.bf16_to_f32(vc[0, 0, 7]), rtol=1e-12, atol=1e-12)
+    outb, _, _, bad = oracle.attention(np.vstack([q, q, q]), kc, vc, [0, 1, 0], [3, 3, 32], 1, 1, 16)
+    assert bad == 2 and not outb[1:].any()
+
+
 # ------------------------------------------------------------------ O4
 def test_golden_act_codes():
     """[nnterp] "The projections quantize their inputs and weights": round(x * 127 / max|x|)."""
