@@ -236,6 +236,47 @@ bitlinear_status bitlinear_lm_head(const float *x, int64_t m, int64_t k, const f
 size_t bitlinear_lm_head_workspace_bytes(int64_t m, int64_t k);
 
 /* ---------------------------------------------------------------------------
+ * Attention with a KV cache ([card] "Model Details": RoPE; [nnterp] "Loading":
+ * eager attention, no softcap, window or sink; "Config": 20 heads, 5 kv heads,
+ * head_dim 128, bfloat16). Caches are bfloat16 bit patterns laid out
+ * [n_slots][n_kv][t_max][head_dim] (reading R21): one slot per sequence. Token r
+ * belongs to sequence slot[r] at position pos[r] (device int64 arrays); a token
+ * whose slot or position is out of range writes nothing and gets zeros.
+ * ------------------------------------------------------------------------- */
+
+/* bitlinear_rope — rotate, in place, the n_heads head vectors of each row of x
+ * that start at column col0 (row stride ld floats), token r at position pos[r]
+ * (reading R19: pairs (i, i + head_dim/2), angle pos theta^(-2i/head_dim) with
+ * its cosine and sine in fp64 rounded to fp32, the rotation in fp32).
+ * Errors: NULL -> ERR_NULL; m < 0, head_dim odd or <= 0, n_heads <= 0,
+ * col0 + n_heads head_dim > ld -> ERR_SHAPE; theta <= 0 -> ERR_ARG. */
+bitlinear_status bitlinear_rope(float *x, int64_t m, int64_t ld, int64_t col0, int32_t n_heads, int32_t head_dim,
+                                const int64_t *pos, double theta, void *stream);
+
+/* bitlinear_kv_append — write each token's keys and values (rows of k and v,
+ * stride ld floats, n_kv head_dim values each) rounded to bfloat16 into the
+ * caches at [slot[r]][g][pos[r]][:].
+ * Errors: NULL -> ERR_NULL; bad sizes -> ERR_SHAPE. */
+bitlinear_status bitlinear_kv_append(const float *k, const float *v, int64_t m, int64_t ld, int32_t n_kv,
+                                     int32_t head_dim, const int64_t *slot, const int64_t *pos, uint16_t *k_cache,
+                                     uint16_t *v_cache, int64_t n_slots, int64_t t_max, void *stream);
+
+/* bitlinear_attention_decode — out[r][h head_dim + d] = sum over t <= pos[r] of
+ * softmax_t(q_h . k_t / sqrt(head_dim)) v_t[d], with q head h (columns
+ * h head_dim .. of row r of q, stride ldq) reading kv head h / (n_heads / n_kv)
+ * of sequence slot[r]; fp32 arithmetic, causal. out has row stride ldo.
+ * Supported: head_dim == 128, n_heads % n_kv == 0, n_heads / n_kv <= 8.
+ *   workspace  >= bitlinear_attention_workspace_bytes(m, n_heads, t_max) bytes.
+ * Errors: NULL -> ERR_NULL; unsupported or bad sizes -> ERR_SHAPE; small
+ * workspace -> ERR_WORKSPACE. m == 0 is a no-op. */
+bitlinear_status bitlinear_attention_decode(const float *q, int64_t m, int64_t ldq, int32_t n_heads, int32_t n_kv,
+                                            int32_t head_dim, const uint16_t *k_cache, const uint16_t *v_cache,
+                                            int64_t n_slots, int64_t t_max, const int64_t *slot, const int64_t *pos,
+                                            float *out, int64_t ldo, void *workspace, size_t workspace_bytes,
+                                            void *stream);
+size_t bitlinear_attention_workspace_bytes(int64_t m, int32_t n_heads, int64_t t_max);
+
+/* ---------------------------------------------------------------------------
  * Five codes per byte ([tiny] "O que é" and "Arquivos": the ternary checkpoint
  * also ships in a storage denser than two bits per weight; the pages give no
  * layout, so this one is the library's own). Row n of k codes takes

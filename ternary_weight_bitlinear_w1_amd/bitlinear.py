@@ -82,6 +82,11 @@ def lib():
             "bitlinear_embed": (_i32, [_p, _i64, _p, _i64, _i64, _p, _p]),
             "bitlinear_lm_head": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p, _p, _p, _sz, _p]),
             "bitlinear_lm_head_workspace_bytes": (_sz, [_i64, _i64]),
+            "bitlinear_rope": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, ctypes.c_double, _p]),
+            "bitlinear_kv_append": (_i32, [_p, _p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _i64, _i64, _p]),
+            "bitlinear_attention_decode": (_i32, [_p, _i64, _i64, _i32, _i32, _i32, _p, _p, _i64, _i64, _p, _p, _p,
+                                                  _i64, _p, _sz, _p]),
+            "bitlinear_attention_workspace_bytes": (_sz, [_i64, _i32, _i64]),
             "bitlinear_base3_row_bytes": (_sz, [_i64]),
             "bitlinear_pack_base3": (_i32, [_p, _i64, _i64, _p, _p]),
             "bitlinear_forward_base3": (_i32, [_p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _p, _p, _sz, _p]),
@@ -250,6 +255,43 @@ def lm_head(x: torch.Tensor, w_head: torch.Tensor, gain: Optional[torch.Tensor] 
            lib().bitlinear_lm_head(_ptr(x), m, k, _ptr(gain), eps, _ptr(w_head), n, _ptr(y), _ptr(normed), _ptr(ws),
                                    nb, _stream(dev)))
     return (y, normed) if want_normed else y
+
+
+def rope(x: torch.Tensor, pos: torch.Tensor, n_heads: int, head_dim: int, theta: float = 5e5, col0: int = 0):
+    """RoPE in place on the heads of x [m][ld] fp32 starting at column col0."""
+    m, ld = x.shape
+    _check("bitlinear_rope", lib().bitlinear_rope(_ptr(x), m, ld, col0, n_heads, head_dim, _ptr(pos), theta,
+                                                  _stream(x.device)))
+    return x
+
+
+def kv_append(k: torch.Tensor, v: torch.Tensor, slot: torch.Tensor, pos: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor) -> None:
+    """Write rows of k, v ([m][n_kv hd] fp32 views with a common row stride) into
+    the bfloat16 caches [n_slots][n_kv][t_max][hd] at (slot, pos)."""
+    n_slots, n_kv, t_max, hd = k_cache.shape
+    m = k.shape[0]
+    assert k.stride(0) == v.stride(0) and k.stride(1) == 1 and v.stride(1) == 1
+    _check("bitlinear_kv_append",
+           lib().bitlinear_kv_append(_ptr(k), _ptr(v), m, k.stride(0), n_kv, hd, _ptr(slot), _ptr(pos),
+                                     _ptr(k_cache), _ptr(v_cache), n_slots, t_max, _stream(k.device)))
+
+
+def attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, slot: torch.Tensor,
+                     pos: torch.Tensor, n_heads: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Each token's causal attention over its slot's cache -> [m][n_heads hd] fp32.
+    q rows hold the query heads from column 0 (any row stride)."""
+    n_slots, n_kv, t_max, hd = k_cache.shape
+    m = q.shape[0]
+    dev = q.device
+    o = out if out is not None else torch.empty((m, n_heads * hd), dtype=torch.float32, device=dev)
+    nb = lib().bitlinear_attention_workspace_bytes(m, n_heads, t_max)
+    ws = _workspace(nb, dev)
+    _check("bitlinear_attention_decode",
+           lib().bitlinear_attention_decode(_ptr(q), m, q.stride(0), n_heads, n_kv, hd, _ptr(k_cache), _ptr(v_cache),
+                                            n_slots, t_max, _ptr(slot), _ptr(pos), _ptr(o), o.stride(0), _ptr(ws), nb,
+                                            _stream(dev)))
+    return o
 
 
 def base3_row_bytes(k: int) -> int:

@@ -432,6 +432,65 @@ bitlinear_status bitlinear_lm_head(const float *x, int64_t m, int64_t k, const f
   return launched(bl::launch_lm_head(o, m, k, w_head, n_vocab, logits, s), "lm_head");
 }
 
+// ---------------------------------------------------------------- attention with a KV cache
+bitlinear_status bitlinear_rope(float *x, int64_t m, int64_t ld, int64_t col0, int32_t n_heads, int32_t head_dim,
+                                const int64_t *pos, double theta, void *stream) {
+  g_err.clear();
+  if (m != 0 && (!x || !pos)) return fail(BITLINEAR_ERR_NULL, "x and pos are required");
+  if (m < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2 != 0 || col0 < 0 ||
+      col0 + (int64_t)n_heads * head_dim > ld || m > kMaxDim || ld > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, ld = %lld, col0 = %lld, %d heads of %d", (long long)m, (long long)ld,
+                (long long)col0, n_heads, head_dim);
+  if (!(theta > 0.0)) return fail(BITLINEAR_ERR_ARG, "theta must be > 0");
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  return launched(bl::launch_rope(x, m, ld, col0, n_heads, head_dim, pos, theta, as_stream(stream)), "rope");
+}
+
+bitlinear_status bitlinear_kv_append(const float *k, const float *v, int64_t m, int64_t ld, int32_t n_kv,
+                                     int32_t head_dim, const int64_t *slot, const int64_t *pos, uint16_t *k_cache,
+                                     uint16_t *v_cache, int64_t n_slots, int64_t t_max, void *stream) {
+  g_err.clear();
+  if (m != 0 && (!k || !v || !slot || !pos || !k_cache || !v_cache))
+    return fail(BITLINEAR_ERR_NULL, "k, v, slot, pos and both caches are required");
+  if (m < 0 || n_kv <= 0 || head_dim <= 0 || (int64_t)n_kv * head_dim > ld || n_slots <= 0 || t_max <= 0 ||
+      m > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, ld = %lld, %d kv heads of %d, %lld slots of %lld", (long long)m,
+                (long long)ld, n_kv, head_dim, (long long)n_slots, (long long)t_max);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  return launched(bl::launch_kv_append(k, v, m, ld, n_kv, head_dim, slot, pos, k_cache, v_cache, n_slots, t_max,
+                                       as_stream(stream)),
+                  "kv append");
+}
+
+size_t bitlinear_attention_workspace_bytes(int64_t m, int32_t n_heads, int64_t t_max) {
+  if (m <= 0 || n_heads <= 0 || t_max <= 0) return 0;
+  return align256(bl::attention_workspace_floats(m, n_heads, t_max) * sizeof(float));
+}
+
+bitlinear_status bitlinear_attention_decode(const float *q, int64_t m, int64_t ldq, int32_t n_heads, int32_t n_kv,
+                                            int32_t head_dim, const uint16_t *k_cache, const uint16_t *v_cache,
+                                            int64_t n_slots, int64_t t_max, const int64_t *slot, const int64_t *pos,
+                                            float *out, int64_t ldo, void *workspace, size_t workspace_bytes,
+                                            void *stream) {
+  g_err.clear();
+  if (m != 0 && (!q || !k_cache || !v_cache || !slot || !pos || !out))
+    return fail(BITLINEAR_ERR_NULL, "q, the caches, slot, pos and out are required");
+  if (m < 0 || !bl::attention_supported(n_heads, n_kv, head_dim) || (int64_t)n_heads * head_dim > ldq ||
+      (int64_t)n_heads * head_dim > ldo || n_slots <= 0 || t_max <= 0 || m > kMaxDim || t_max > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, %d heads / %d kv heads of %d (need 128, at most 8 per kv head), "
+                "ldq = %lld, ldo = %lld", (long long)m, n_heads, n_kv, head_dim, (long long)ldq, (long long)ldo);
+  const size_t need = bitlinear_attention_workspace_bytes(m, n_heads, t_max);
+  if (m > 0 && (!workspace || workspace_bytes < need))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  if (m == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  return launched(bl::launch_attention(q, m, ldq, n_heads, n_kv, head_dim, k_cache, v_cache, n_slots, t_max, slot, pos,
+                                       out, ldo, static_cast<float *>(workspace), as_stream(stream)),
+                  "attention");
+}
+
 // ---------------------------------------------------------------- five codes per byte
 size_t bitlinear_base3_row_bytes(int64_t k) { return k > 0 ? (size_t)(16 * ((k + 79) / 80)) : 0; }
 

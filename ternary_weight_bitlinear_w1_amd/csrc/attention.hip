@@ -1,0 +1,280 @@
+// Rotary position embedding, the bfloat16 KV cache, and each token's causal
+// attention over its own sequence's cache.
+//
+// What is computed ([card] "Model Details": RoPE; [nnterp] "Loading": eager
+// attention without softcap, window or sink; "Config": 20 query and 5
+// key/value heads of 128, bfloat16; readings R19 and R21):
+//   RoPE, per head vector v, i < hd/2: a = p theta^(-2i/hd) (fp64), c = fl32(cos a),
+//     s = fl32(sin a); v[i], v[i + hd/2] <- v[i] c - v[i + hd/2] s, v[i + hd/2] c + v[i] s
+//   cache[slot][g][p][:] = bf16(k after RoPE), bf16(v)
+//   out_h = sum_{t <= p} softmax_t(q_h . k_t / sqrt(hd)) v_t, kv head g = h / (heads / kv heads)
+//
+// Attention runs as flash-decoding in two kernels. attn_partial_kernel: a
+// workgroup takes one token, one key/value head and a chunk of 256 positions;
+// thread j scores position j for every query head of the group (the query
+// vectors are LDS broadcasts, the key row is read whole by its thread), then
+// lanes split the head dimension to accumulate the values (a wave reads one
+// 256-byte value row per load). It stores the chunk's max, sum of
+// exponentials and unnormalized output. attn_combine_kernel rescales and adds
+// the chunks. Tokens whose slot or position is out of range get zeros and
+// write nothing to the cache.
+#include "common.h"
+
+namespace bl {
+namespace {
+
+constexpr int kAttnChunk = 256;   // positions per workgroup
+constexpr int kAttnMaxGroup = 8;  // query heads per key/value head
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t kept = u >> 16, dropped = u & 0xFFFFu;
+  return kept + ((dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) ? 1u : 0u);
+}
+
+// one thread per rotated pair
+__global__ __launch_bounds__(256) void rope_kernel(float *__restrict__ x, int64_t m, int64_t ld, int64_t col0,
+                                                   int n_heads, int hd, const int64_t *__restrict__ pos,
+                                                   double theta) {
+  const int half = hd / 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= m * n_heads * half) return;
+  const int64_t r = i / (n_heads * half);
+  const int rem = (int)(i - r * n_heads * half);
+  const int h = rem / half, e = rem - h * half;
+  const double ang = (double)pos[r] * pow(theta, -(2.0 * e) / (double)hd);
+  const float c = (float)cos(ang), s = (float)sin(ang);
+  float *v = x + r * ld + col0 + (int64_t)h * hd;
+  const float a = v[e], b = v[e + half];
+  v[e] = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s));
+  v[e + half] = __fadd_rn(__fmul_rn(b, c), __fmul_rn(a, s));
+}
+
+// one thread per element of a token's keys (and values)
+__global__ __launch_bounds__(256) void kv_append_kernel(const float *__restrict__ k, const float *__restrict__ v,
+                                                        int64_t m, int64_t ld, int n_kv, int hd,
+                                                        const int64_t *__restrict__ slot,
+                                                        const int64_t *__restrict__ pos, uint16_t *__restrict__ kc,
+                                                        uint16_t *__restrict__ vc, int64_t n_slots, int64_t tmax) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int row = n_kv * hd;
+  if (i >= m * row) return;
+  const int64_t r = i / row;
+  const int e = (int)(i - r * row);
+  const int64_t sl = slot[r], p = pos[r];
+  if (sl < 0 || sl >= n_slots || p < 0 || p >= tmax) return;
+  const int g = e / hd, d = e - g * hd;
+  const int64_t dst = ((sl * n_kv + g) * tmax + p) * hd + d;
+  kc[dst] = (uint16_t)f32_to_bf16(k[r * ld + e]);
+  vc[dst] = (uint16_t)f32_to_bf16(v[r * ld + e]);
+}
+
+// Partials of token r, kv head g, chunk s: po [r][g][s][group][HD] (sum of
+// exp(score - max) v), pml [r][g][s][group][2] (max, sum of exp).
+template <int HD>
+__global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int64_t ldq, int n_heads,
+                                                           int n_kv, const uint16_t *__restrict__ kc,
+                                                           const uint16_t *__restrict__ vc, int64_t n_slots,
+                                                           int64_t tmax, const int64_t *__restrict__ slot,
+                                                           const int64_t *__restrict__ pos, int S,
+                                                           float *__restrict__ po, float *__restrict__ pml) {
+  static_assert(HD == 128, "lanes split the head dimension in pairs");
+  __shared__ float qs[kAttnMaxGroup][HD];
+  __shared__ float ps[kAttnMaxGroup][kAttnChunk];
+  __shared__ float red[kAttnMaxGroup][4];
+  __shared__ float accs[4][kAttnMaxGroup][HD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, g = blockIdx.y;
+  const int64_t r = blockIdx.z;
+  const int group = n_heads / n_kv;
+  const int64_t sl = slot[r], p = pos[r];
+  const bool ok = sl >= 0 && sl < n_slots && p >= 0 && p < tmax;
+  const int64_t T = ok ? p + 1 : 0;
+  const int64_t t0 = (int64_t)s * kAttnChunk;
+  const int64_t part = ((r * n_kv + g) * S + s) * group;
+  if (t0 >= T) {  // nothing to attend in this chunk
+    for (int e = tid; e < group * HD; e += 256) po[part * HD + e] = 0.0f;
+    if (tid < group) {
+      pml[(part + tid) * 2] = -INFINITY;
+      pml[(part + tid) * 2 + 1] = 0.0f;
+    }
+    return;
+  }
+  const int cnt = (int)(T - t0 < kAttnChunk ? T - t0 : kAttnChunk);
+  for (int e = tid; e < group * HD; e += 256) {
+    const int hh = e / HD, d = e - hh * HD;
+    qs[hh][d] = q[r * ldq + (int64_t)(g * group + hh) * HD + d];
+  }
+  __syncthreads();
+  const float scale = (float)(1.0 / sqrt((double)HD));
+  const int64_t base = (sl * n_kv + g) * tmax;
+  // ---- scores: thread j takes position t0 + j
+  float sc[kAttnMaxGroup];
+#pragma unroll
+  for (int hh = 0; hh < kAttnMaxGroup; ++hh) sc[hh] = -INFINITY;
+  if (tid < cnt) {
+    const v4i *krow = reinterpret_cast<const v4i *>(kc + (base + t0 + tid) * HD);
+    float dot[kAttnMaxGroup];
+#pragma unroll
+    for (int hh = 0; hh < kAttnMaxGroup; ++hh) dot[hh] = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < HD / 8; ++c) {
+      const v4i kw = krow[c];
+      float kf[8];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        kf[2 * q2] = bf16_to_f32((uint32_t)kw[q2] & 0xFFFFu);
+        kf[2 * q2 + 1] = bf16_to_f32((uint32_t)kw[q2] >> 16);
+      }
+#pragma unroll
+      for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
+        if (hh < group) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dot[hh] = __fmaf_rn(qs[hh][8 * c + e], kf[e], dot[hh]);
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < kAttnMaxGroup; ++hh)
+      if (hh < group) sc[hh] = __fmul_rn(dot[hh], scale);
+  }
+  // ---- chunk max per head
+#pragma unroll
+  for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
+    if (hh >= group) break;
+    float mx = sc[hh];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[hh][wave] = mx;
+  }
+  __syncthreads();
+  float cmax[kAttnMaxGroup];
+#pragma unroll
+  for (int hh = 0; hh < kAttnMaxGroup; ++hh)
+    cmax[hh] = hh < group ? fmaxf(fmaxf(red[hh][0], red[hh][1]), fmaxf(red[hh][2], red[hh][3])) : 0.0f;
+  __syncthreads();
+  // ---- exp(score - max), and the chunk sums (fixed order)
+#pragma unroll
+  for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
+    if (hh >= group) break;
+    const float e = tid < cnt ? expf(sc[hh] - cmax[hh]) : 0.0f;
+    ps[hh][tid] = e;
+    float sum = e;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane == 0) red[hh][wave] = sum;
+  }
+  __syncthreads();
+  if (tid < group) {
+    const float l = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
+    pml[(part + tid) * 2] = cmax[tid];
+    pml[(part + tid) * 2 + 1] = l;
+  }
+  // ---- values: wave w takes positions 64 w .. 64 w + 63 of the chunk, lane l dims 2l, 2l+1
+  float acc[kAttnMaxGroup][2];
+#pragma unroll
+  for (int hh = 0; hh < kAttnMaxGroup; ++hh) acc[hh][0] = acc[hh][1] = 0.0f;
+  const int j_end = min(64 * wave + 64, cnt);
+  for (int j = 64 * wave; j < j_end; ++j) {
+    const uint32_t vw = reinterpret_cast<const uint32_t *>(vc + (base + t0 + j) * HD)[lane];
+    const float v0 = bf16_to_f32(vw & 0xFFFFu), v1 = bf16_to_f32(vw >> 16);
+#pragma unroll
+    for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
+      if (hh < group) {
+        const float w = ps[hh][j];
+        acc[hh][0] = __fmaf_rn(w, v0, acc[hh][0]);
+        acc[hh][1] = __fmaf_rn(w, v1, acc[hh][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
+    if (hh < group) {
+      accs[wave][hh][2 * lane] = acc[hh][0];
+      accs[wave][hh][2 * lane + 1] = acc[hh][1];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < group * HD; e += 256) {
+    const int hh = e / HD, d = e - hh * HD;
+    po[part * HD + e] = ((accs[0][hh][d] + accs[1][hh][d]) + accs[2][hh][d]) + accs[3][hh][d];
+  }
+}
+
+// out[r][h HD + d] from the chunks of token r's kv head
+template <int HD>
+__global__ __launch_bounds__(HD) void attn_combine_kernel(const float *__restrict__ po, const float *__restrict__ pml,
+                                                          int n_heads, int n_kv, int S, float *__restrict__ out,
+                                                          int64_t ldo) {
+  const int64_t r = blockIdx.y;
+  const int h = blockIdx.x, d = threadIdx.x;
+  const int group = n_heads / n_kv, g = h / group, hh = h - g * group;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pml[(((r * n_kv + g) * S + s) * group + hh) * 2]);
+  float L = 0.0f, acc = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const int64_t part = ((r * n_kv + g) * S + s) * group + hh;
+      const float ms = pml[part * 2];
+      if (ms == -INFINITY) continue;
+      const float f = expf(ms - M);
+      L = __fmaf_rn(pml[part * 2 + 1], f, L);
+      acc = __fmaf_rn(po[part * HD + d], f, acc);
+    }
+  }
+  out[r * ldo + (int64_t)h * HD + d] = M != -INFINITY ? __fdiv_rn(acc, L) : 0.0f;
+}
+
+}  // namespace
+
+int attention_splits(int64_t tmax) { return (int)((tmax + kAttnChunk - 1) / kAttnChunk); }
+
+bool attention_supported(int n_heads, int n_kv, int hd) {
+  return hd == 128 && n_kv > 0 && n_heads % n_kv == 0 && n_heads / n_kv <= kAttnMaxGroup;
+}
+
+hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
+                       double theta, hipStream_t stream) {
+  const int64_t n = m * n_heads * (hd / 2);
+  if (n == 0) return hipSuccess;
+  rope_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(x, m, ld, col0, n_heads, hd, pos, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const float *k, const float *v, int64_t m, int64_t ld, int n_kv, int hd,
+                            const int64_t *slot, const int64_t *pos, uint16_t *kc, uint16_t *vc, int64_t n_slots,
+                            int64_t tmax, hipStream_t stream) {
+  const int64_t n = m * n_kv * hd;
+  if (n == 0) return hipSuccess;
+  kv_append_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(k, v, m, ld, n_kv, hd, slot, pos, kc,
+                                                                              vc, n_slots, tmax);
+  return hipGetLastError();
+}
+
+// workspace: attention_workspace_floats(m, n_heads, tmax) floats
+size_t attention_workspace_floats(int64_t m, int n_heads, int64_t tmax) {
+  const int64_t S = attention_splits(tmax);
+  return (size_t)(m * n_heads * S) * (128 + 2);
+}
+
+hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads, int n_kv, int hd,
+                            const uint16_t *kc, const uint16_t *vc, int64_t n_slots, int64_t tmax,
+                            const int64_t *slot, const int64_t *pos, float *out, int64_t ldo, float *ws,
+                            hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  if (!attention_supported(n_heads, n_kv, hd)) return hipErrorInvalidValue;
+  const int S = attention_splits(tmax);
+  float *po = ws;
+  float *pml = ws + (size_t)(m * n_heads * S) * 128;
+  attn_partial_kernel<128><<<dim3((unsigned)S, (unsigned)n_kv, (unsigned)m), dim3(256), 0, stream>>>(
+      q, ldq, n_heads, n_kv, kc, vc, n_slots, tmax, slot, pos, S, po, pml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_combine_kernel<128><<<dim3((unsigned)n_heads, (unsigned)m), dim3(128), 0, stream>>>(po, pml, n_heads, n_kv, S,
+                                                                                          out, ldo);
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -183,6 +183,20 @@ hipError_t launch_lm_head(const uint16_t *o, int64_t m, int64_t k, const uint16_
 hipError_t launch_embed(const int64_t *ids, int64_t m, const uint16_t *table, int64_t vocab, int64_t k, float *x,
                         hipStream_t stream);
 
+// RoPE, the bfloat16 KV cache and causal attention (attention.hip).
+bool attention_supported(int n_heads, int n_kv, int hd);
+int attention_splits(int64_t tmax);
+size_t attention_workspace_floats(int64_t m, int n_heads, int64_t tmax);
+hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
+                       double theta, hipStream_t stream);
+hipError_t launch_kv_append(const float *k, const float *v, int64_t m, int64_t ld, int n_kv, int hd,
+                            const int64_t *slot, const int64_t *pos, uint16_t *kc, uint16_t *vc, int64_t n_slots,
+                            int64_t tmax, hipStream_t stream);
+hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads, int n_kv, int hd,
+                            const uint16_t *kc, const uint16_t *vc, int64_t n_slots, int64_t tmax,
+                            const int64_t *slot, const int64_t *pos, float *out, int64_t ldo, float *ws,
+                            hipStream_t stream);
+
 // Five codes per byte (base3.hip): repacking, and the 1..4-token contraction.
 bool gemv_b3_supported(int64_t m, int64_t k);
 hipError_t launch_pack_base3(const uint8_t *packed, int64_t n, int64_t k, uint8_t *out, hipStream_t stream);

@@ -216,6 +216,32 @@ def test_embed_and_lm_head_validation():
     assert L.bitlinear_lm_head_workspace_bytes(0, 2560) == 0
 
 
+def test_rope_cache_attention_validation():
+    L = bl.lib()
+    assert L.bitlinear_rope(None, 4, 3840, 0, 20, 128, A, 5e5, None) == bl.ERR_NULL
+    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 127, A, 5e5, None) == bl.ERR_SHAPE   # odd head_dim
+    assert L.bitlinear_rope(A, 4, 2560, 128, 20, 128, A, 5e5, None) == bl.ERR_SHAPE  # past the row
+    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 128, A, 0.0, None) == bl.ERR_ARG
+    assert L.bitlinear_rope(None, 0, 3840, 0, 20, 128, None, 5e5, None) == bl.OK
+    app = L.bitlinear_kv_append
+    assert app(A, A, 4, 3840, 5, 128, None, A, A, A, 8, 4096, None) == bl.ERR_NULL
+    assert app(A, A, 4, 600, 5, 128, A, A, A, A, 8, 4096, None) == bl.ERR_SHAPE     # 640 > ld
+    assert app(A, A, 4, 3840, 5, 128, A, A, A, A, 0, 4096, None) == bl.ERR_SHAPE
+    att = L.bitlinear_attention_decode
+
+    def call(m=4, ldq=3840, nh=20, nkv=5, hd=128, ws=A, wsb=1 << 30, q=A):
+        return att(q, m, ldq, nh, nkv, hd, A, A, 8, 4096, A, A, A, 2560, ws, wsb, None)
+
+    assert call(q=None) == bl.ERR_NULL
+    assert call(hd=64) == bl.ERR_SHAPE        # head_dim 128 only
+    assert call(nh=21) == bl.ERR_SHAPE        # heads % kv heads
+    assert call(nh=40) == bl.ERR_SHAPE        # at most 8 query heads per kv head
+    assert call(ldq=2000) == bl.ERR_SHAPE
+    assert call(ws=None) == bl.ERR_WORKSPACE
+    assert call(m=0) == bl.OK
+    assert L.bitlinear_attention_workspace_bytes(4, 20, 4096) >= 4 * 20 * 16 * 130 * 4
+
+
 def test_quantize_acts_validation():
     q = bl.lib().bitlinear_quantize_acts
     assert q(None, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_NULL
