@@ -46,7 +46,7 @@ typedef enum {
   BITLINEAR_ERR_ARG = 6        /* an enum or flag argument is out of range */
 } bitlinear_status;
 
-#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_ABI_VERSION 2
 #define BITLINEAR_MAX_SEGMENTS 4
 
 /* ---------------------------------------------------------------------------
@@ -328,7 +328,14 @@ typedef enum {
      one-token sequence at position 0): the output of query head i is the
      value of key/value head i / (n_heads / n_kv_heads) ("Loading": 20 query
      heads share 5 key/value heads). q and k are computed but not consumed. */
-  BITLINEAR_BLOCK_DECODER = 1
+  BITLINEAR_BLOCK_DECODER = 1,
+  /* The same stack with the attention of a decode step: after q|k|v, RoPE on
+     q and k (bitlinear_rope, base rope_theta), the token's keys and values
+     appended to its layer's caches at (slot[r], pos[r]) (bitlinear_kv_append),
+     and each token's causal attention over its sequence's cache
+     (bitlinear_attention_decode) feeds attn_sub_norm. Needs head_dim 128 and at
+     most 8 query heads per key/value head. */
+  BITLINEAR_BLOCK_DECODER_CACHED = 2
 } bitlinear_block_kind;
 
 typedef struct {
@@ -344,6 +351,7 @@ typedef struct {
   const float *attn_sub_norm_gain;  /* DECODER: [H] or NULL */
   const float *post_attn_norm_gain; /* DECODER: [H] or NULL */
   const float *ffn_sub_norm_gain;   /* [I] or NULL */
+  uint16_t *k_cache, *v_cache;      /* DECODER_CACHED: [n_slots][n_kv_heads][t_max][head_dim] bfloat16 */
 } bitlinear_layer;
 
 typedef struct {
@@ -354,6 +362,11 @@ typedef struct {
   int32_t n_heads, n_kv_heads, head_dim; /* DECODER: H == n_heads * head_dim, KV = n_kv_heads * head_dim */
   float eps;             /* RMSNorm epsilon */
   const bitlinear_layer *layers; /* HOST array of n_layers (device pointers inside) */
+  /* DECODER_CACHED: token r of the call belongs to sequence slot[r] at position
+     pos[r] (device [m] int64); caches hold n_slots sequences of t_max positions. */
+  const int64_t *slot, *pos;
+  int64_t n_slots, t_max;
+  double rope_theta;
 } bitlinear_block;
 
 /* Optional per-stage outputs for checking a chain stage by stage. Every pointer
@@ -374,6 +387,7 @@ typedef struct {
   int32_t *acc_o;       /* [L][m][H] */
   int32_t *acc_gate_up; /* [L][m][2I] */
   int32_t *acc_down;    /* [L][m][H] */
+  float *attn;          /* [L][m][H]  DECODER_CACHED: the attention output (attn_sub_norm's input) */
 } bitlinear_block_trace;
 
 /* bitlinear_block_forward — run a block chain on x [m][H] fp32 into y [m][H].

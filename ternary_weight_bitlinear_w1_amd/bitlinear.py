@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DEVICE, ERR_ARG = range(7)
 ACT_ABSMAX, ACT_RMSNORM, ACT_RELU2_RMSNORM = 0, 1, 2
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
-BLOCK_FFN, BLOCK_DECODER = 0, 1
+BLOCK_FFN, BLOCK_DECODER, BLOCK_DECODER_CACHED = 0, 1, 2
 MAX_SEGMENTS = 4
 
 _p = ctypes.c_void_p
@@ -41,18 +41,20 @@ class Layer(ctypes.Structure):
     _fields_ = [("qkv", _p), ("qkv_gamma", ctypes.c_float * 3), ("o", _p), ("o_gamma", ctypes.c_float),
                 ("gate_up", _p), ("gate_up_gamma", ctypes.c_float * 2), ("down", _p), ("down_gamma", ctypes.c_float),
                 ("input_norm_gain", _p), ("attn_sub_norm_gain", _p), ("post_attn_norm_gain", _p),
-                ("ffn_sub_norm_gain", _p)]
+                ("ffn_sub_norm_gain", _p), ("k_cache", _p), ("v_cache", _p)]
 
 
 class Block(ctypes.Structure):
     _fields_ = [("kind", _i32), ("n_layers", _i32), ("hidden", _i64), ("intermediate", _i64),
                 ("n_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("eps", ctypes.c_float),
-                ("layers", ctypes.POINTER(Layer))]
+                ("layers", ctypes.POINTER(Layer)), ("slot", _p), ("pos", _p), ("n_slots", _i64), ("t_max", _i64),
+                ("rope_theta", ctypes.c_double)]
 
 
 class Trace(ctypes.Structure):
     _fields_ = [(name, _p) for name in ("codes_in", "codes_attn", "codes_post", "codes_ffn", "deq", "qkv", "h",
-                                        "gate_up", "x_out", "acc_qkv", "acc_o", "acc_gate_up", "acc_down")]
+                                        "gate_up", "x_out", "acc_qkv", "acc_o", "acc_gate_up", "acc_down",
+                                        "attn")]
 
 
 _lib = None
@@ -347,6 +349,8 @@ class LayerWeights:
     attn_sub_norm_gain: Optional[torch.Tensor] = None
     post_attn_norm_gain: Optional[torch.Tensor] = None
     ffn_sub_norm_gain: Optional[torch.Tensor] = None
+    k_cache: Optional[torch.Tensor] = None  # BLOCK_DECODER_CACHED: [n_slots][n_kv][t_max][hd] bfloat16 bits
+    v_cache: Optional[torch.Tensor] = None
 
 
 @dataclass
@@ -359,6 +363,9 @@ class BlockSpec:
     n_kv_heads: int = 0
     head_dim: int = 0
     eps: float = 1e-5
+    slot: Optional[torch.Tensor] = None   # BLOCK_DECODER_CACHED: device int64 [m]
+    pos: Optional[torch.Tensor] = None
+    rope_theta: float = 5e5
 
     def to_c(self):
         arr = (Layer * len(self.layers))()
@@ -367,9 +374,13 @@ class BlockSpec:
                            float(L.o_gamma), _ptr(L.gate_up),
                            (ctypes.c_float * 2)(*[float(v) for v in L.gate_up_gamma]), _ptr(L.down),
                            float(L.down_gamma), _ptr(L.input_norm_gain), _ptr(L.attn_sub_norm_gain),
-                           _ptr(L.post_attn_norm_gain), _ptr(L.ffn_sub_norm_gain))
+                           _ptr(L.post_attn_norm_gain), _ptr(L.ffn_sub_norm_gain), _ptr(L.k_cache), _ptr(L.v_cache))
+        n_slots = t_max = 0
+        kc = self.layers[0].k_cache if self.layers else None
+        if kc is not None:
+            n_slots, t_max = kc.shape[0], kc.shape[2]
         blk = Block(self.kind, len(self.layers), self.hidden, self.intermediate, self.n_heads, self.n_kv_heads,
-                    self.head_dim, self.eps, arr)
+                    self.head_dim, self.eps, arr, _ptr(self.slot), _ptr(self.pos), n_slots, t_max, self.rope_theta)
         return blk, arr
 
 

@@ -561,11 +561,15 @@ struct BlockBufs {
   int32_t *rowsum2; // stage's deq and row sums while it writes its own
   float *qkv, *o, *h, *x, *gu, *d;
   int32_t *split;  // split-K partial sums of the widest projection, or NULL
+  float *att;      // cached decoder: attention output [m][H]
+  float *attn_ws;  // cached decoder: attention chunk partials
 };
+
+bool is_decoder(int32_t kind) { return kind == BITLINEAR_BLOCK_DECODER || kind == BITLINEAR_BLOCK_DECODER_CACHED; }
 
 size_t block_layout(const bitlinear_block *blk, int64_t m, BlockBufs *b, char *base) {
   const int64_t H = blk->hidden, I = blk->intermediate;
-  const bool dec = blk->kind == BITLINEAR_BLOCK_DECODER;
+  const bool dec = is_decoder(blk->kind), cached = blk->kind == BITLINEAR_BLOCK_DECODER_CACHED;
   const int64_t Q = dec ? H + 2 * (int64_t)blk->n_kv_heads * blk->head_dim : 0;
   const int64_t widest = H > I ? H : I;
   size_t off = 0;
@@ -595,31 +599,47 @@ size_t block_layout(const bitlinear_block *blk, int64_t m, BlockBufs *b, char *b
     if (so > split) split = so;
   }
   t.split = reinterpret_cast<int32_t *>(split ? take(split) : nullptr);
+  t.att = reinterpret_cast<float *>(take(cached ? (size_t)(m * H) * 4 : 0));
+  t.attn_ws = reinterpret_cast<float *>(
+      take(cached ? bl::attention_workspace_floats(m, blk->n_heads, blk->t_max) * sizeof(float) : 0));
   if (b) *b = t;
   return off;
 }
 
 bitlinear_status check_block(const bitlinear_block *blk) {
   if (!blk || !blk->layers) return fail(BITLINEAR_ERR_NULL, "blk and blk->layers are required");
-  if (blk->kind != BITLINEAR_BLOCK_FFN && blk->kind != BITLINEAR_BLOCK_DECODER)
+  if (blk->kind != BITLINEAR_BLOCK_FFN && !is_decoder(blk->kind))
     return fail(BITLINEAR_ERR_ARG, "unknown block kind %d", blk->kind);
   const int64_t H = blk->hidden, I = blk->intermediate;
   if (blk->n_layers < 1 || H <= 0 || I <= 0 || H % 16 || I % 16 || H > kMaxDim || I > kMaxDim)
     return fail(BITLINEAR_ERR_SHAPE, "need n_layers >= 1 and hidden, intermediate positive multiples of 16");
   if (blk->kind == BITLINEAR_BLOCK_FFN && blk->n_layers != 1) return fail(BITLINEAR_ERR_SHAPE, "an FFN block has 1 layer");
-  if (blk->kind == BITLINEAR_BLOCK_DECODER) {
+  if (is_decoder(blk->kind)) {
     if (blk->n_heads <= 0 || blk->n_kv_heads <= 0 || blk->head_dim <= 0 || blk->head_dim % 4 ||
         blk->n_heads % blk->n_kv_heads || (int64_t)blk->n_heads * blk->head_dim != H)
       return fail(BITLINEAR_ERR_SHAPE, "need n_heads * head_dim == hidden, n_kv_heads | n_heads, head_dim %% 4 == 0");
     if (((int64_t)blk->n_kv_heads * blk->head_dim) % 16)
       return fail(BITLINEAR_ERR_SHAPE, "n_kv_heads * head_dim must be a multiple of 16");
   }
+  if (blk->kind == BITLINEAR_BLOCK_DECODER_CACHED) {
+    if (!bl::attention_supported(blk->n_heads, blk->n_kv_heads, blk->head_dim))
+      return fail(BITLINEAR_ERR_SHAPE, "the cached decoder needs head_dim 128 and at most 8 heads per kv head");
+    if (!blk->slot || !blk->pos) return fail(BITLINEAR_ERR_NULL, "slot and pos are required");
+    if (blk->n_slots <= 0 || blk->t_max <= 0 || blk->n_slots > kMaxDim || blk->t_max > kMaxDim)
+      return fail(BITLINEAR_ERR_SHAPE, "n_slots = %lld, t_max = %lld", (long long)blk->n_slots,
+                  (long long)blk->t_max);
+    if (!(blk->rope_theta > 0.0)) return fail(BITLINEAR_ERR_ARG, "rope_theta must be > 0");
+  }
   for (int l = 0; l < blk->n_layers; ++l) {
     const bitlinear_layer &L = blk->layers[l];
     if (!L.gate_up || !L.down) return fail(BITLINEAR_ERR_NULL, "layer %d: gate_up and down are required", l);
     if (!aligned16(L.gate_up) || !aligned16(L.down)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: misaligned weights", l);
     if (L.ffn_sub_norm_gain && !aligned16(L.ffn_sub_norm_gain)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: gain", l);
-    if (blk->kind == BITLINEAR_BLOCK_DECODER) {
+    if (blk->kind == BITLINEAR_BLOCK_DECODER_CACHED) {
+      if (!L.k_cache || !L.v_cache) return fail(BITLINEAR_ERR_NULL, "layer %d: k_cache and v_cache are required", l);
+      if (!aligned16(L.k_cache) || !aligned16(L.v_cache)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: caches", l);
+    }
+    if (is_decoder(blk->kind)) {
       if (!L.qkv || !L.o) return fail(BITLINEAR_ERR_NULL, "layer %d: qkv and o are required", l);
       if (!aligned16(L.qkv) || !aligned16(L.o)) return fail(BITLINEAR_ERR_ALIGN, "layer %d: misaligned weights", l);
       const float *g[3] = {L.input_norm_gain, L.attn_sub_norm_gain, L.post_attn_norm_gain};
@@ -676,6 +696,23 @@ bitlinear_status fused(int mode, int epi, const bl::ActSrc &src, float eps, int6
   return launched(bl::launch_gemv_fused(mode, epi, a, s), "fused decode projection");
 }
 
+// The attention of the cached decoder on the q|k|v rows in qkv ([m][Q]): RoPE
+// on q and k (adjacent heads from column 0), the keys and values into layer
+// L's caches, each token's causal attention into b.att ([m][H]).
+bitlinear_status cached_attention(const bitlinear_block *blk, const bitlinear_layer &L, int64_t m, float *qkv,
+                                  const BlockBufs &b, float *tr_attn, hipStream_t s) {
+  const int hd = blk->head_dim, nh = blk->n_heads, nkv = blk->n_kv_heads;
+  const int64_t H = blk->hidden, KV = (int64_t)nkv * hd, Q = H + 2 * KV;
+  BL_TRY(launched(bl::launch_rope(qkv, m, Q, 0, nh + nkv, hd, blk->pos, blk->rope_theta, s), "rope"));
+  BL_TRY(launched(bl::launch_kv_append(qkv + H, qkv + H + KV, m, Q, nkv, hd, blk->slot, blk->pos, L.k_cache,
+                                       L.v_cache, blk->n_slots, blk->t_max, s),
+                  "kv append"));
+  BL_TRY(launched(bl::launch_attention(qkv, m, Q, nh, nkv, hd, L.k_cache, L.v_cache, blk->n_slots, blk->t_max,
+                                       blk->slot, blk->pos, b.att, H, b.attn_ws, s),
+                  "attention"));
+  return copy_to(tr_attn, b.att, (size_t)(m * H) * 4, s);
+}
+
 // The block chains for a decode step of at most bl::kFusedMaxM tokens: four
 // launches per decoder layer (two for the FFN block), each projection
 // quantizing its own input and applying the block's elementwise step.
@@ -698,25 +735,36 @@ bitlinear_status block_forward_fused(const bitlinear_block *blk, const float *x,
   const int hd = blk->head_dim, group = blk->n_heads / blk->n_kv_heads;
   const int64_t KV = (int64_t)blk->n_kv_heads * hd, Q = H + 2 * KV;
   const int64_t qkv_seg[3] = {H, H + KV, Q};
+  const bool cached = blk->kind == BITLINEAR_BLOCK_DECODER_CACHED;
   const float *xin = x;
   for (int l = 0; l < blk->n_layers; ++l) {
     const bitlinear_layer &L = blk->layers[l];
     const int64_t oH = (int64_t)l * m * H, oI = (int64_t)l * m * I, oQ = (int64_t)l * m * Q;
     float *dq = at(tr.deq, 4 * m * l);
-    float *qkv = tr.qkv ? tr.qkv + oQ : b.qkv;
+    // (the cached decoder rotates q and k in place: its trace copy is taken first)
+    float *qkv = tr.qkv && !cached ? tr.qkv + oQ : b.qkv;
     float *h = tr.h ? tr.h + oH : b.h;
     float *xnext = tr.x_out ? tr.x_out + oH : (l + 1 == blk->n_layers ? y : b.x);
     // input_layernorm -> q|k|v
     BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_PLAIN, act_src(xin, H, H, L.input_norm_gain), eps, m, L.qkv, Q,
                  L.qkv_gamma, qkv_seg, 3, qkv, at(tr.acc_qkv, oQ), nullptr, nullptr, nullptr, at(tr.codes_in, oH), dq,
                  s));
-    // self-only attention -> attn_sub_norm -> o_proj; h = x + o
-    bl::ActSrc att = act_src(qkv, Q, H, L.attn_sub_norm_gain);
-    att.gqa_offset = (int)(H + KV);
-    att.head_dim = hd;
-    att.group = group;
-    BL_TRY(fused(bl::ACT_GQA_RMSNORM, bl::FUSED_EPI_RESID, att, eps, m, L.o, H, &L.o_gamma, h_seg, 1, nullptr,
-                 at(tr.acc_o, oH), xin, h, nullptr, at(tr.codes_attn, oH), at(dq, m), s));
+    if (cached) {
+      // RoPE, cache append, attention -> attn_sub_norm -> o_proj; h = x + o
+      BL_TRY(copy_to(at(tr.qkv, oQ), qkv, (size_t)(m * Q) * 4, s));
+      BL_TRY(cached_attention(blk, L, m, qkv, b, at(tr.attn, oH), s));
+      BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_RESID, act_src(b.att, H, H, L.attn_sub_norm_gain), eps, m,
+                   L.o, H, &L.o_gamma, h_seg, 1, nullptr, at(tr.acc_o, oH), xin, h, nullptr, at(tr.codes_attn, oH),
+                   at(dq, m), s));
+    } else {
+      // self-only attention -> attn_sub_norm -> o_proj; h = x + o
+      bl::ActSrc att = act_src(qkv, Q, H, L.attn_sub_norm_gain);
+      att.gqa_offset = (int)(H + KV);
+      att.head_dim = hd;
+      att.group = group;
+      BL_TRY(fused(bl::ACT_GQA_RMSNORM, bl::FUSED_EPI_RESID, att, eps, m, L.o, H, &L.o_gamma, h_seg, 1, nullptr,
+                   at(tr.acc_o, oH), xin, h, nullptr, at(tr.codes_attn, oH), at(dq, m), s));
+    }
     // post_attention_layernorm -> gate|up -> ReLU^2(gate) * up
     BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_RELU2, act_src(h, H, H, L.post_attn_norm_gain), eps, m,
                  L.gate_up, 2 * I, L.gate_up_gamma, gu_seg, 2, at(tr.gate_up, 2 * oI), at(tr.acc_gate_up, 2 * oI),
@@ -841,6 +889,7 @@ bitlinear_status block_forward_chain(const bitlinear_block *blk, const float *x,
   const int hd = blk->head_dim, group = blk->n_heads / blk->n_kv_heads;
   const int64_t KV = (int64_t)blk->n_kv_heads * hd, Q = H + 2 * KV;
   const int64_t qkv_seg[3] = {H, H + KV, Q};
+  const bool cached = blk->kind == BITLINEAR_BLOCK_DECODER_CACHED;
   ProjOut d;  // the previous layer's down projection
   for (int l = 0; l < blk->n_layers; ++l) {
     const bitlinear_layer &L = blk->layers[l];
@@ -860,10 +909,15 @@ bitlinear_status block_forward_chain(const bitlinear_block *blk, const float *x,
     BL_TRY(copy_to(at(tr.codes_in, oH), b.codes, (size_t)(m * H), s));
     BL_TRY(copy_to(at(tr.deq, 4 * m * l), c.deq(), (size_t)m * 4, s));
     ProjOut qkv;
-    BL_TRY(c.proj(H, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, b.qkv, at(tr.acc_qkv, oQ), !tr.qkv && !tr.acc_qkv, &qkv));
+    BL_TRY(c.proj(H, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, b.qkv, at(tr.acc_qkv, oQ),
+                  !tr.qkv && !tr.acc_qkv && !cached, &qkv));
     BL_TRY(copy_to(at(tr.qkv, oQ), b.qkv, (size_t)(m * Q) * 4, s));
-    // self-only attention output -> attn_sub_norm -> o_proj
-    {
+    if (cached) {
+      // RoPE, cache append, attention -> attn_sub_norm -> o_proj
+      BL_TRY(cached_attention(blk, L, m, b.qkv, b, at(tr.attn, oH), s));
+      BL_TRY(c.quant(BITLINEAR_ACT_RMSNORM, act_src(b.att, H, H, L.attn_sub_norm_gain)));
+    } else {
+      // self-only attention output -> attn_sub_norm -> o_proj
       bl::ActSrc src = act_src(qkv.y, Q, H, L.attn_sub_norm_gain);
       src.gqa_offset = (int)(H + KV);
       src.head_dim = hd;

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bl.lib().bitlinear_abi_version() == 1
+    assert bl.lib().bitlinear_abi_version() == 2
     for s in range(7):
         assert bl.status_name(s)
     assert bl.status_name(0) == "ok"

@@ -251,3 +251,87 @@ def _rows(v, rows):
     if isinstance(v, dict):
         return {k: _rows(a, rows) for k, a in v.items()}
     return v[rows]
+
+
+# ------------------------------------------------------------------------------ decoder with a KV cache
+def _attn_bound_ok(got, ref, vmag, smag, hd, tmax):
+    S = (tmax + 255) // 256
+    factor = 2.0 ** -24 * (2 * (hd + 1) * np.repeat(smag, hd, axis=1) + 2 * (192 + S))
+    return np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= factor * vmag
+
+
+@pytest.mark.parametrize("positions", [[0, 5, 300], [0, 1, 2, 100, 257, 511]])
+def test_decoder_cached_teacher_forced(positions):
+    """Two decoder layers with RoPE, KV caches and causal attention (H = 512: 4
+    query heads of 128 on 1 key/value head; I = 768). Three tokens take the
+    fused decode form, six the quantize -> contract chain. Every stage is
+    checked against the oracle fed the GPU's own input to that stage: ints
+    bit-exact, the projections' fp32 outputs bit-exact, the rotated keys within
+    one bfloat16 step, the attention within its fp32 bound."""
+    hdim, inter, nh, nkv, hd, layers, tmax, theta = 512, 768, 4, 1, 128, 2, 512, 5e5
+    m = len(positions)
+    note(f"block decoder cached m={m}")
+    kvd = nkv * hd
+    Q = hdim + 2 * kvd
+    r = np.random.default_rng(50 + m)
+    slot = np.arange(m, dtype=np.int64)[::-1].copy()
+    pos = np.array(positions, dtype=np.int64)
+    x = synth.activations(seed(9, m, 5), m, hdim, 1)
+    mats, gains, caches0, gpu_layers = [], [], [], []
+    for l in range(layers):
+        mt = _decoder_layer_mats(9, l, hdim, inter, kvd)
+        g = None
+        if l == 0:
+            g = {nm: (1.0 + 0.1 * synth.normal_f32(seed(9, l, 30 + i), n)).astype(np.float32)
+                 for i, (nm, n) in enumerate((("n_in", hdim), ("n_attn", hdim), ("n_post", hdim), ("n_ffn", inter)))}
+        kc = oracle.round_bf16(r.normal(size=(m, nkv, tmax, hd)).astype(np.float32))
+        vc = oracle.round_bf16(r.normal(size=(m, nkv, tmax, hd)).astype(np.float32))
+        lw = _gpu_layer(mt, g)
+        lw.k_cache, lw.v_cache = gpu(kc), gpu(vc)
+        mats.append(mt), gains.append(g), caches0.append((kc, vc)), gpu_layers.append(lw)
+    spec = bl.BlockSpec(bl.BLOCK_DECODER_CACHED, hdim, inter, gpu_layers, nh, nkv, hd, EPS, slot=gpu(slot),
+                        pos=gpu(pos), rope_theta=theta)
+    tr = _trace(layers, m, hdim, inter, Q)
+    tr["attn"] = torch.zeros((layers, m, hdim), dtype=torch.float32, device=DEV)
+    y = bl.block_forward(spec, gpu(x), trace=tr)
+    g_ = {k: host(v) for k, v in tr.items()}
+    xin = x
+    for l in range(layers):
+        w = _oracle_weights(mats[l], gains[l])
+        gl = gains[l] or {}
+        s_qkv = oracle.forward(xin, w["qkv"], w["g_qkv"], [hdim, hdim + kvd, Q], gl.get("n_in"), EPS)
+        assert_equal(g_["codes_in"][l], s_qkv["q"], f"layer {l} input codes")
+        assert_equal(g_["acc_qkv"][l], s_qkv["acc"], f"layer {l} qkv acc")
+        assert_equal(g_["qkv"][l], s_qkv["y"], f"layer {l} qkv")
+        # RoPE on q and k, the appended cache rows
+        qk = oracle.rope(g_["qkv"][l][:, :hdim + kvd], pos, nh + nkv, hd, theta)
+        kc_gpu = host(gpu_layers[l].k_cache).view(np.uint16)
+        vc_gpu = host(gpu_layers[l].v_cache).view(np.uint16)
+        kc_ref, vc_ref = caches0[l][0].copy(), caches0[l][1].copy()
+        oracle.kv_append(kc_ref, vc_ref, qk[:, hdim:], g_["qkv"][l][:, hdim + kvd:], slot, pos, nkv, hd)
+        assert_equal(vc_gpu, vc_ref, f"layer {l} value cache")
+        diff = np.abs(kc_gpu.astype(np.int32) - kc_ref.astype(np.int32))
+        assert diff.max() <= 1, f"layer {l} key cache: {int(diff.max())} bfloat16 steps"
+        # attention over the GPU's caches
+        att, vmag, smag, bad = oracle.attention(qk[:, :hdim], kc_gpu, vc_gpu, slot, pos, nh, nkv, hd)
+        assert bad == 0
+        assert _attn_bound_ok(g_["attn"][l], att, vmag, smag, hd, tmax).all(), f"layer {l} attention"
+        # attn_sub_norm -> o_proj; h = x + o
+        s_o = oracle.forward(g_["attn"][l], w["o"], [w["g_o"]], None, gl.get("n_attn"), EPS)
+        assert_equal(g_["codes_attn"][l], s_o["q"], f"layer {l} attn_sub_norm codes")
+        assert_equal(g_["acc_o"][l], s_o["acc"], f"layer {l} o acc")
+        h = (xin.astype(np.float32) + s_o["y"]).astype(np.float32)
+        assert_equal(g_["h"][l], h, f"layer {l} h")
+        # MLP
+        s_gu = oracle.forward(h, w["gu"], w["g_gu"], [inter, 2 * inter], gl.get("n_post"), EPS)
+        assert_equal(g_["codes_post"][l], s_gu["q"], f"layer {l} post-norm codes")
+        assert_equal(g_["acc_gate_up"][l], s_gu["acc"], f"layer {l} gate|up acc")
+        assert_equal(g_["gate_up"][l], s_gu["y"], f"layer {l} gate|up")
+        s_d = oracle.forward(oracle.relu2_mul(s_gu["y"], inter), w["down"], [w["g_down"]], None, gl.get("n_ffn"),
+                             EPS)
+        assert_equal(g_["codes_ffn"][l], s_d["q"], f"layer {l} ffn_sub_norm codes")
+        assert_equal(g_["acc_down"][l], s_d["acc"], f"layer {l} down acc")
+        x_next = (h + s_d["y"]).astype(np.float32)
+        assert_equal(g_["x_out"][l], x_next, f"layer {l} output")
+        xin = g_["x_out"][l]
+    assert_equal(host(y), g_["x_out"][-1], "block output")
