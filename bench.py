@@ -21,7 +21,10 @@ different copy of the weights from a ring larger than the 256 MB last-level
 cache; and the same projection at M = 1 and 4 from the weights stored five
 codes per byte (base 3), in GB/s of those stored bytes. ``head`` times the final
 norm + bfloat16 lm_head (128256 x 2560) at 1 and 4 tokens in GB/s of the head.
-``cpu_baseline`` times the CPU oracle on a bounded
+``stack`` times the 30-layer projection stack at M = 1 and 64, and
+``stack.token_step`` a whole-model decode step (embedding, 30 layers with RoPE,
+KV cache and attention over 4096 positions, final norm, head) for 1 and 4
+sequences. ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same step's tokens.
 """
 from __future__ import annotations
@@ -41,6 +44,8 @@ METRIC = "BitLinear prefill int8 TOPS & decode packed-weight GB/s, % of roofline
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 M, H, I = 4096, 2560, 6912
+VOCAB = 128256
+ROPE_THETA = 5e5  # the RoPE base of the released 2B4T model (the pages name RoPE only)
 BASE_SEED = 1234
 RING_BYTES = 600 * 2 ** 20  # > 2 x the 256 MB last-level cache
 
@@ -84,7 +89,8 @@ def main():
     torch.cuda.set_device(dev)
     bl.lib()  # fails loudly if the HIP library is missing
     if args.stack_only:
-        log(json.dumps(bench_stack(torch, bl, synth, dev, args.stack_steps, max(2, args.warmup // 2))))
+        log(json.dumps(bench_stack(torch, bl, synth, dev, args.stack_steps, max(2, args.warmup // 2),
+                                   head_table(torch, synth, dev))))
         return
 
     def seed(layer, tensor):
@@ -226,13 +232,17 @@ def main():
 
     # ---------------------------------------------------------------- head
     head = None
+    table = None
+    if not args.no_decode or not args.no_stack:
+        table = head_table(torch, synth, dev)
     if not args.no_decode:
-        head = bench_head(torch, bl, synth, dev, args.decode_reps // 4)
+        head = bench_head(torch, bl, synth, dev, args.decode_reps // 4, table)
 
-    # ---------------------------------------------------------------- 30-layer stack
+    # ---------------------------------------------------------------- 30-layer stack, token step
     stack = None
     if not args.no_stack:
-        stack = bench_stack(torch, bl, synth, dev, args.stack_steps, max(2, args.warmup // 2))
+        stack = bench_stack(torch, bl, synth, dev, args.stack_steps, max(2, args.warmup // 2), table)
+    del table
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -383,22 +393,28 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
     return res
 
 
-def bench_head(torch, bl, synth, dev, reps):
+def head_table(torch, synth, dev):
+    """The tied embedding / head table, 128256 x 2560 bfloat16 (as uint16 bits),
+    N(0, 0.02) rounded to bfloat16."""
+    log("head: generating the 128256 x 2560 table")
+    table = torch.empty((VOCAB, H), dtype=torch.uint16, device=dev)
+    rows = 16032
+    for r0 in range(0, VOCAB, rows):
+        n = min(rows, VOCAB - r0)
+        w = torch.from_numpy(synth.weights(synth.stream_seed(BASE_SEED, 6, r0, 1), n, H)).to(dev)
+        table[r0:r0 + n] = w.to(torch.bfloat16).view(torch.uint16)
+        del w
+    return table
+
+
+def bench_head(torch, bl, synth, dev, reps, table):
     """The model's head at decode: final norm + the bfloat16 lm_head (128256 x 2560,
     656.7 MB, larger than the last-level cache, so every launch streams it from
     HBM), for 1 and 4 tokens: mean time per call over back-to-back calls."""
-    V, K = 128256, H
+    V, K = VOCAB, H
     L = bl.lib()
     sp = torch.cuda.current_stream(dev).cuda_stream
     stream = torch.cuda.current_stream(dev)
-    log("head: generating the 128256 x 2560 table")
-    table = torch.empty((V, K), dtype=torch.uint16, device=dev)
-    rows = 16032
-    for r0 in range(0, V, rows):
-        n = min(rows, V - r0)
-        w = torch.from_numpy(synth.weights(synth.stream_seed(BASE_SEED, 6, r0, 1), n, K)).to(dev)
-        table[r0:r0 + n] = w.to(torch.bfloat16).view(torch.uint16)
-        del w
     gain = torch.full((K,), 0.1, dtype=torch.float32, device=dev)
     nbytes = V * K * 2
     res = {}
@@ -428,8 +444,6 @@ def bench_head(torch, bl, synth, dev, reps):
         res[f"m{m}"] = {"us": round(us, 2), "gbs_head": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                         "head_bytes": nbytes}
         log(f"head m={m}: {us:.1f} us per call (final norm + lm_head), {gbs:.0f} GB/s of the 656.7 MB table")
-    del table
-    torch.cuda.empty_cache()
     return res
 
 
@@ -476,7 +490,7 @@ def bench_online(torch, bl, synth, dev, reps, w_gate, w_up):
 STACK_LAYERS, STACK_HEADS, STACK_KV_HEADS, STACK_HEAD_DIM = 30, 20, 5, 128
 
 
-def bench_stack(torch, bl, synth, dev, steps, warmup):
+def bench_stack(torch, bl, synth, dev, steps, warmup, table):
     """One step of the 30-layer decoder projection stack of the 2B4T shapes
     (q|k|v, self-only attention, o, gate|up, ReLU^2, down, residuals; gains 1)
     through bitlinear_block_forward at M = 1 and M = 64. Reports the step time
@@ -558,7 +572,93 @@ def bench_stack(torch, bl, synth, dev, steps, warmup):
         log(f"stack m={m}: graph {ms:.3f} ms/step, {gbs:.0f} GB/s packed, {ops / (ms * 1e-3) / 1e12:.1f} TOPS; "
             f"eager {np.median(t_eager):.3f} ms/step (host {host_eager:.3f} ms/step)")
         del graph, x, y, ws
+    res["token_step"] = bench_token_step(torch, bl, dev, layers, table, steps, warmup)
     del keep, layers
+    return res
+
+
+def bench_token_step(torch, bl, dev, layers, table, steps, warmup):
+    """One decode step of the whole model for B sequences (B = 1 and 4) at position
+    4095 of a 4096-position context: embedding gather, 30 decoder layers with RoPE,
+    bfloat16 KV cache append and causal attention over 4096 positions, final norm
+    and the bfloat16 head. Caches hold seeded N(0, 1) values; the step is captured
+    into a HIP graph and replayed. Reports ms per step, tokens/s, and the bytes a
+    step must read (packed weights, head, the sequences' caches) per second."""
+    T = 4096
+    kvd = STACK_KV_HEADS * STACK_HEAD_DIM
+    L = bl.lib()
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    packed = sum(l.qkv.numel() + l.o.numel() + l.gate_up.numel() + l.down.numel() for l in layers)
+    for B in (1, 4):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(BASE_SEED + B)
+        caches = []
+        for _ in layers:
+            kc = torch.randn((B, STACK_KV_HEADS, T, STACK_HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+            vc = torch.randn((B, STACK_KV_HEADS, T, STACK_HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+            caches.append((kc.view(torch.uint16), vc.view(torch.uint16)))
+        cl = [bl.LayerWeights(qkv=l.qkv, qkv_gamma=l.qkv_gamma, o=l.o, o_gamma=l.o_gamma, gate_up=l.gate_up,
+                              gate_up_gamma=l.gate_up_gamma, down=l.down, down_gamma=l.down_gamma, k_cache=kc,
+                              v_cache=vc) for l, (kc, vc) in zip(layers, caches)]
+        slot = torch.arange(B, dtype=torch.int64, device=dev)
+        pos = torch.full((B,), T - 1, dtype=torch.int64, device=dev)
+        spec = bl.BlockSpec(bl.BLOCK_DECODER_CACHED, H, I, cl, STACK_HEADS, STACK_KV_HEADS, STACK_HEAD_DIM, 1e-5,
+                            slot=slot, pos=pos, rope_theta=ROPE_THETA)
+        blk, keep = spec.to_c()
+        ids = torch.arange(B, dtype=torch.int64, device=dev) * 7919 + 11
+        x = torch.empty((B, H), dtype=torch.float32, device=dev)
+        h = torch.empty_like(x)
+        logits = torch.empty((B, VOCAB), dtype=torch.float32, device=dev)
+        gain = torch.full((H,), 0.1, dtype=torch.float32, device=dev)
+        nb = int(L.bitlinear_block_workspace_bytes(bl.ctypes.byref(blk), B))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        nh = int(L.bitlinear_lm_head_workspace_bytes(B, H))
+        wsh = torch.empty(max(nh, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            sp = torch.cuda.current_stream(dev).cuda_stream
+            for name, st in (("embed", L.bitlinear_embed(ids.data_ptr(), B, table.data_ptr(), VOCAB, H, x.data_ptr(),
+                                                          sp)),
+                             ("block", L.bitlinear_block_forward(bl.ctypes.byref(blk), x.data_ptr(), B, h.data_ptr(),
+                                                                 None, ws.data_ptr(), nb, sp)),
+                             ("head", L.bitlinear_lm_head(h.data_ptr(), B, H, gain.data_ptr(), 1e-5, table.data_ptr(),
+                                                          VOCAB, logits.data_ptr(), None, wsh.data_ptr(), nh, sp))):
+                if st != 0:
+                    raise RuntimeError(f"token step {name}: {bl.status_name(st)} {L.bitlinear_last_error().decode()}")
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        eager = logits.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(logits, eager):
+            raise RuntimeError(f"token step B={B}: graph replay differs from the eager step")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        ms = float(np.median(t))
+        kv_bytes = B * len(layers) * T * 2 * kvd * 2
+        step_bytes = packed + VOCAB * H * 2 + kv_bytes
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        res[f"b{B}"] = {"ms_per_step": round(ms, 4), "p10_ms": round(t[len(t) // 10], 4),
+                        "p90_ms": round(t[(9 * len(t)) // 10], 4), "tokens_per_s": round(B / (ms * 1e-3), 1),
+                        "bytes_per_step": step_bytes, "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                        "context": T}
+        log(f"token step B={B} (position {T - 1}): {ms:.3f} ms/step, {B / (ms * 1e-3):.0f} tokens/s, "
+            f"{step_bytes / 1e6:.0f} MB read per step = {gbs:.0f} GB/s")
+        del graph, keep, caches, cl, ws, wsh
+        torch.cuda.empty_cache()
     return res
 
 

@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
                                                            const int64_t *__restrict__ pos, int S,
                                                            float *__restrict__ po, float *__restrict__ pml) {
   static_assert(HD == 128, "lanes split the head dimension in pairs");
-  __shared__ float qs[kAttnMaxGroup][HD];
-  __shared__ float ps[kAttnMaxGroup][kAttnChunk];
+  __shared__ __attribute__((aligned(16))) float qs[kAttnMaxGroup][HD];
+  __shared__ __attribute__((aligned(16))) float ps[kAttnChunk][kAttnMaxGroup];  // position-major: one read per position
   __shared__ float red[kAttnMaxGroup][4];
   __shared__ float accs[4][kAttnMaxGroup][HD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -110,18 +110,31 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   __syncthreads();
   const float scale = (float)(1.0 / sqrt((double)HD));
   const int64_t base = (sl * n_kv + g) * tmax;
-  // ---- scores: thread j takes position t0 + j
+  // ---- scores: thread j takes position t0 + j. Its whole key row (16 loads of
+  // 16 bytes) is issued at once, and a wave's value rows below too, so each
+  // thread waits for memory once per phase, not once per load.
   float sc[kAttnMaxGroup];
 #pragma unroll
   for (int hh = 0; hh < kAttnMaxGroup; ++hh) sc[hh] = -INFINITY;
-  if (tid < cnt) {
-    const v4i *krow = reinterpret_cast<const v4i *>(kc + (base + t0 + tid) * HD);
+  const int j0 = 64 * wave, j_end = min(j0 + 64, cnt);
+  uint32_t vr[64];
+  {
+    // (threads past the chunk end reload the chunk's first row, unused)
+    const v4i *krow = reinterpret_cast<const v4i *>(kc + (base + t0 + (tid < cnt ? tid : 0)) * HD);
+    v4i kr[HD / 8];
+#pragma unroll
+    for (int c = 0; c < HD / 8; ++c) kr[c] = krow[c];
+    // the value rows of this wave's 64 positions (lane l: dims 2l, 2l+1); past
+    // the chunk end the chunk's first row, weight 0 below
+#pragma unroll
+    for (int jj = 0; jj < 64; ++jj)
+      vr[jj] = reinterpret_cast<const uint32_t *>(vc + (base + t0 + (j0 + jj < j_end ? j0 + jj : 0)) * HD)[lane];
     float dot[kAttnMaxGroup];
 #pragma unroll
     for (int hh = 0; hh < kAttnMaxGroup; ++hh) dot[hh] = 0.0f;
-#pragma unroll 4
+#pragma unroll
     for (int c = 0; c < HD / 8; ++c) {
-      const v4i kw = krow[c];
+      const v4i kw = kr[c];
       float kf[8];
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
@@ -131,14 +144,23 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
 #pragma unroll
       for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
         if (hh < group) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dot[hh] = __fmaf_rn(qs[hh][8 * c + e], kf[e], dot[hh]);
+          // the 8 query values as two 16-byte LDS broadcasts
+          const float4 qa = *reinterpret_cast<const float4 *>(&qs[hh][8 * c]);
+          const float4 qb = *reinterpret_cast<const float4 *>(&qs[hh][8 * c + 4]);
+          dot[hh] = __fmaf_rn(qa.x, kf[0], dot[hh]);
+          dot[hh] = __fmaf_rn(qa.y, kf[1], dot[hh]);
+          dot[hh] = __fmaf_rn(qa.z, kf[2], dot[hh]);
+          dot[hh] = __fmaf_rn(qa.w, kf[3], dot[hh]);
+          dot[hh] = __fmaf_rn(qb.x, kf[4], dot[hh]);
+          dot[hh] = __fmaf_rn(qb.y, kf[5], dot[hh]);
+          dot[hh] = __fmaf_rn(qb.z, kf[6], dot[hh]);
+          dot[hh] = __fmaf_rn(qb.w, kf[7], dot[hh]);
         }
       }
     }
 #pragma unroll
     for (int hh = 0; hh < kAttnMaxGroup; ++hh)
-      if (hh < group) sc[hh] = __fmul_rn(dot[hh], scale);
+      if (hh < group && tid < cnt) sc[hh] = __fmul_rn(dot[hh], scale);
   }
   // ---- chunk max per head
 #pragma unroll
@@ -160,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
     if (hh >= group) break;
     const float e = tid < cnt ? expf(sc[hh] - cmax[hh]) : 0.0f;
-    ps[hh][tid] = e;
+    ps[tid][hh] = e;
     float sum = e;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
@@ -176,16 +198,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   float acc[kAttnMaxGroup][2];
 #pragma unroll
   for (int hh = 0; hh < kAttnMaxGroup; ++hh) acc[hh][0] = acc[hh][1] = 0.0f;
-  const int j_end = min(64 * wave + 64, cnt);
-  for (int j = 64 * wave; j < j_end; ++j) {
-    const uint32_t vw = reinterpret_cast<const uint32_t *>(vc + (base + t0 + j) * HD)[lane];
+#pragma unroll
+  for (int jj = 0; jj < 64; ++jj) {
+    const int j = j0 + jj;
+    if (j >= j_end) break;
+    const uint32_t vw = vr[jj];
     const float v0 = bf16_to_f32(vw & 0xFFFFu), v1 = bf16_to_f32(vw >> 16);
+    float w[kAttnMaxGroup];
+    *reinterpret_cast<float4 *>(&w[0]) = *reinterpret_cast<const float4 *>(&ps[j][0]);
+    if (group > 4) *reinterpret_cast<float4 *>(&w[4]) = *reinterpret_cast<const float4 *>(&ps[j][4]);
 #pragma unroll
     for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
       if (hh < group) {
-        const float w = ps[hh][j];
-        acc[hh][0] = __fmaf_rn(w, v0, acc[hh][0]);
-        acc[hh][1] = __fmaf_rn(w, v1, acc[hh][1]);
+        acc[hh][0] = __fmaf_rn(w[hh], v0, acc[hh][0]);
+        acc[hh][1] = __fmaf_rn(w[hh], v1, acc[hh][1]);
       }
     }
   }
@@ -211,18 +237,35 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(const float *__restric
   const int64_t r = blockIdx.y;
   const int h = blockIdx.x, d = threadIdx.x;
   const int group = n_heads / n_kv, g = h / group, hh = h - g * group;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pml[(((r * n_kv + g) * S + s) * group + hh) * 2]);
-  float L = 0.0f, acc = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
+  // the chunks' (max, sum) and outputs, 16 at a time, all loads issued first
+  constexpr int kB = 16;
+  float M = -INFINITY, L = 0.0f, acc = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kB) {
+    float ms[kB], ls[kB], os[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int s = s0 + i < S ? s0 + i : S - 1;  // (repeats are not added)
       const int64_t part = ((r * n_kv + g) * S + s) * group + hh;
-      const float ms = pml[part * 2];
-      if (ms == -INFINITY) continue;
-      const float f = expf(ms - M);
-      L = __fmaf_rn(pml[part * 2 + 1], f, L);
-      acc = __fmaf_rn(po[part * HD + d], f, acc);
+      ms[i] = pml[part * 2];
+      ls[i] = pml[part * 2 + 1];
+      os[i] = po[part * HD + d];
     }
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (s0 + i < S) mb = fmaxf(mb, ms[i]);
+    if (mb == -INFINITY) continue;
+    const float f0 = expf(M - mb);  // rescale what earlier batches added (exp(-inf) = 0 at the start)
+    L = __fmul_rn(L, f0);
+    acc = __fmul_rn(acc, f0);
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      if (s0 + i >= S || ms[i] == -INFINITY) continue;
+      const float f = expf(ms[i] - mb);
+      L = __fmaf_rn(ls[i], f, L);
+      acc = __fmaf_rn(os[i], f, acc);
+    }
+    M = mb;
   }
   out[r * ldo + (int64_t)h * HD + d] = M != -INFINITY ? __fdiv_rn(acc, L) : 0.0f;
 }
