@@ -13,8 +13,9 @@
 // workgroup takes one token, one key/value head and a chunk of 256 positions;
 // thread j scores position j for every query head of the group (the query
 // vectors are LDS broadcasts, the key row is read whole by its thread), then
-// lanes split the head dimension to accumulate the values (a wave reads one
-// 256-byte value row per load). It stores the chunk's max, sum of
+// each wave accumulates the values of its 64 positions (a wave load moves four
+// whole 256-byte rows; a lane holds 8 dims of every fourth position, and the
+// four position groups are added with shuffles). It stores the chunk's max, sum of
 // exponentials and unnormalized output. attn_combine_kernel rescales and adds
 // the chunks. Tokens whose slot or position is out of range get zeros and
 // write nothing to the cache.
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   __shared__ __attribute__((aligned(16))) float qs[kAttnMaxGroup][HD];
   __shared__ __attribute__((aligned(16))) float ps[kAttnChunk][kAttnMaxGroup];  // position-major: one read per position
   __shared__ float red[kAttnMaxGroup][4];
-  __shared__ float accs[4][kAttnMaxGroup][HD];
+  __shared__ __attribute__((aligned(16))) float accs[4][kAttnMaxGroup][HD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = blockIdx.x, g = blockIdx.y;
   const int64_t r = blockIdx.z;
@@ -116,19 +117,23 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   float sc[kAttnMaxGroup];
 #pragma unroll
   for (int hh = 0; hh < kAttnMaxGroup; ++hh) sc[hh] = -INFINITY;
-  const int j0 = 64 * wave, j_end = min(j0 + 64, cnt);
-  uint32_t vr[64];
+  // values: wave w takes positions 64 w .. 64 w + 63 of the chunk; lane l takes
+  // dims 8 (l % 16) .. + 7 of positions 64 w + 4 i + l / 16 (i < 16), so each
+  // wave load moves 4 whole 256-byte rows
+  const int j0 = 64 * wave, vsub = lane >> 4, vd = 8 * (lane & 15);
+  v4i vr[16];
   {
     // (threads past the chunk end reload the chunk's first row, unused)
     const v4i *krow = reinterpret_cast<const v4i *>(kc + (base + t0 + (tid < cnt ? tid : 0)) * HD);
     v4i kr[HD / 8];
 #pragma unroll
     for (int c = 0; c < HD / 8; ++c) kr[c] = krow[c];
-    // the value rows of this wave's 64 positions (lane l: dims 2l, 2l+1); past
-    // the chunk end the chunk's first row, weight 0 below
+    // (past the chunk end: the chunk's first row, weight 0 below)
 #pragma unroll
-    for (int jj = 0; jj < 64; ++jj)
-      vr[jj] = reinterpret_cast<const uint32_t *>(vc + (base + t0 + (j0 + jj < j_end ? j0 + jj : 0)) * HD)[lane];
+    for (int i = 0; i < 16; ++i) {
+      const int j = j0 + 4 * i + vsub;
+      vr[i] = *reinterpret_cast<const v4i *>(vc + (base + t0 + (j < cnt ? j : 0)) * HD + vd);
+    }
     float dot[kAttnMaxGroup];
 #pragma unroll
     for (int hh = 0; hh < kAttnMaxGroup; ++hh) dot[hh] = 0.0f;
@@ -194,32 +199,48 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     pml[(part + tid) * 2] = cmax[tid];
     pml[(part + tid) * 2 + 1] = l;
   }
-  // ---- values: wave w takes positions 64 w .. 64 w + 63 of the chunk, lane l dims 2l, 2l+1
-  float acc[kAttnMaxGroup][2];
+  // ---- values
+  float acc[kAttnMaxGroup][8];
 #pragma unroll
-  for (int hh = 0; hh < kAttnMaxGroup; ++hh) acc[hh][0] = acc[hh][1] = 0.0f;
+  for (int hh = 0; hh < kAttnMaxGroup; ++hh)
 #pragma unroll
-  for (int jj = 0; jj < 64; ++jj) {
-    const int j = j0 + jj;
-    if (j >= j_end) break;
-    const uint32_t vw = vr[jj];
-    const float v0 = bf16_to_f32(vw & 0xFFFFu), v1 = bf16_to_f32(vw >> 16);
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int j = j0 + 4 * i + vsub;  // (weights past the chunk end are 0)
+    float vf[8];
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      vf[2 * q2] = bf16_to_f32((uint32_t)vr[i][q2] & 0xFFFFu);
+      vf[2 * q2 + 1] = bf16_to_f32((uint32_t)vr[i][q2] >> 16);
+    }
     float w[kAttnMaxGroup];
     *reinterpret_cast<float4 *>(&w[0]) = *reinterpret_cast<const float4 *>(&ps[j][0]);
     if (group > 4) *reinterpret_cast<float4 *>(&w[4]) = *reinterpret_cast<const float4 *>(&ps[j][4]);
 #pragma unroll
     for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
       if (hh < group) {
-        acc[hh][0] = __fmaf_rn(w[hh], v0, acc[hh][0]);
-        acc[hh][1] = __fmaf_rn(w[hh], v1, acc[hh][1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] = __fmaf_rn(w[hh], vf[e], acc[hh][e]);
       }
     }
   }
+  // the four position subgroups of the wave, in a fixed order
 #pragma unroll
   for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
     if (hh < group) {
-      accs[wave][hh][2 * lane] = acc[hh][0];
-      accs[wave][hh][2 * lane + 1] = acc[hh][1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = acc[hh][e];
+        a += __shfl_xor(a, 16, 64);
+        a += __shfl_xor(a, 32, 64);
+        acc[hh][e] = a;
+      }
+      if (vsub == 0) {
+        *reinterpret_cast<float4 *>(&accs[wave][hh][vd]) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+        *reinterpret_cast<float4 *>(&accs[wave][hh][vd + 4]) =
+            make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+      }
     }
   }
   __syncthreads();
