@@ -10,13 +10,13 @@
 //   out_h = sum_{t <= p} softmax_t(q_h . k_t / sqrt(hd)) v_t, kv head g = h / (heads / kv heads)
 //
 // Attention runs as flash-decoding in two kernels. attn_partial_kernel: a
-// workgroup takes one token, one key/value head and a chunk of 256 positions;
-// thread j scores position j for every query head of the group (the query
-// vectors are LDS broadcasts, the key row is read whole by its thread), then
-// each wave accumulates the values of its 64 positions (a wave load moves four
-// whole 256-byte rows; a lane holds 8 dims of every fourth position, and the
-// four position groups are added with shuffles). It stores the chunk's max, sum of
-// exponentials and unnormalized output. attn_combine_kernel rescales and adds
+// workgroup takes one token, one key/value head and a chunk of 128 positions,
+// a wave 32 of them. Lanes split each row into 16 pieces of 8 dims, so a wave
+// load moves four whole 256-byte key (or value) rows, the query stays in
+// registers, and a score is summed over its row's 16 lanes with xor-shuffles;
+// the lanes that scored a position then weight its value row. It stores the
+// chunk's max, sum of exponentials and unnormalized output. attn_combine_kernel
+// rescales and adds
 // the chunks. Tokens whose slot or position is out of range get zeros and
 // write nothing to the cache.
 #include "common.h"
@@ -24,8 +24,7 @@
 namespace bl {
 namespace {
 
-constexpr int kAttnChunk = 256;   // positions per workgroup
-constexpr int kAttnMaxGroup = 8;  // query heads per key/value head
+constexpr int kAttnChunk = 128;   // positions per workgroup
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -72,179 +71,157 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float *__restrict_
   vc[dst] = (uint16_t)f32_to_bf16(v[r * ld + e]);
 }
 
-// Partials of token r, kv head g, chunk s: po [r][g][s][group][HD] (sum of
-// exp(score - max) v), pml [r][g][s][group][2] (max, sum of exp).
-template <int HD>
-__global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int64_t ldq, int n_heads,
-                                                           int n_kv, const uint16_t *__restrict__ kc,
+// Partials of token r, kv head g, chunk s (kAttnChunk positions): po
+// [r][g][s][group][HD] (sum of exp(score - max) v), pml [r][g][s][group][2]
+// (max, sum of exp). Wave w takes positions 32 w .. 32 w + 31 of the chunk;
+// lane l takes dims 8 (l % 16) .. + 7 of positions 32 w + 4 i + l / 16 (i < 8),
+// for keys and values alike, so every wave load moves four whole 256-byte rows,
+// the query's 8 dims of each head stay in registers, and a position's score
+// (summed over its 16 lanes with xor-shuffles) is already in the lanes that
+// weight its value row.
+template <int HD, int G>
+__global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int64_t ldq, int n_kv,
+                                                           const uint16_t *__restrict__ kc,
                                                            const uint16_t *__restrict__ vc, int64_t n_slots,
                                                            int64_t tmax, const int64_t *__restrict__ slot,
                                                            const int64_t *__restrict__ pos, int S,
                                                            float *__restrict__ po, float *__restrict__ pml) {
-  static_assert(HD == 128, "lanes split the head dimension in pairs");
-  __shared__ __attribute__((aligned(16))) float qs[kAttnMaxGroup][HD];
-  __shared__ __attribute__((aligned(16))) float ps[kAttnChunk][kAttnMaxGroup];  // position-major: one read per position
-  __shared__ float red[kAttnMaxGroup][4];
-  __shared__ __attribute__((aligned(16))) float accs[4][kAttnMaxGroup][HD];
+  static_assert(HD == 128, "16 lanes of 8 dims cover a row");
+  constexpr int PW = kAttnChunk / 4 / 4;  // positions per lane (8)
+  __shared__ float red[G][4];
+  __shared__ __attribute__((aligned(16))) float accs[4][G][HD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = blockIdx.x, g = blockIdx.y;
   const int64_t r = blockIdx.z;
-  const int group = n_heads / n_kv;
   const int64_t sl = slot[r], p = pos[r];
   const bool ok = sl >= 0 && sl < n_slots && p >= 0 && p < tmax;
   const int64_t T = ok ? p + 1 : 0;
   const int64_t t0 = (int64_t)s * kAttnChunk;
-  const int64_t part = ((r * n_kv + g) * S + s) * group;
+  const int64_t part = ((r * n_kv + g) * S + s) * G;
   if (t0 >= T) {  // nothing to attend in this chunk
-    for (int e = tid; e < group * HD; e += 256) po[part * HD + e] = 0.0f;
-    if (tid < group) {
+    for (int e = tid; e < G * HD; e += 256) po[part * HD + e] = 0.0f;
+    if (tid < G) {
       pml[(part + tid) * 2] = -INFINITY;
       pml[(part + tid) * 2 + 1] = 0.0f;
     }
     return;
   }
   const int cnt = (int)(T - t0 < kAttnChunk ? T - t0 : kAttnChunk);
-  for (int e = tid; e < group * HD; e += 256) {
-    const int hh = e / HD, d = e - hh * HD;
-    qs[hh][d] = q[r * ldq + (int64_t)(g * group + hh) * HD + d];
+  const int64_t base = (sl * n_kv + g) * tmax + t0;
+  const int sub = lane >> 4, d0 = 8 * (lane & 15);
+  // loads in issue order: keys, values (past the chunk end: the chunk's first
+  // row, weight 0 below), the query's 8 dims of each head
+  v4i kr[PW], vr[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int j = 32 * wave + 4 * i + sub;
+    kr[i] = *reinterpret_cast<const v4i *>(kc + (base + (j < cnt ? j : 0)) * HD + d0);
   }
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int j = 32 * wave + 4 * i + sub;
+    vr[i] = *reinterpret_cast<const v4i *>(vc + (base + (j < cnt ? j : 0)) * HD + d0);
+  }
+  float qv[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const float4 a = *reinterpret_cast<const float4 *>(q + r * ldq + (int64_t)(g * G + hh) * HD + d0);
+    const float4 b = *reinterpret_cast<const float4 *>(q + r * ldq + (int64_t)(g * G + hh) * HD + d0 + 4);
+    qv[hh][0] = a.x; qv[hh][1] = a.y; qv[hh][2] = a.z; qv[hh][3] = a.w;
+    qv[hh][4] = b.x; qv[hh][5] = b.y; qv[hh][6] = b.z; qv[hh][7] = b.w;
+  }
   const float scale = (float)(1.0 / sqrt((double)HD));
-  const int64_t base = (sl * n_kv + g) * tmax;
-  // ---- scores: thread j takes position t0 + j. Its whole key row (16 loads of
-  // 16 bytes) is issued at once, and a wave's value rows below too, so each
-  // thread waits for memory once per phase, not once per load.
-  float sc[kAttnMaxGroup];
+  // ---- scores, and this lane's max over its positions
+  float sc[PW][G], mx[G];
 #pragma unroll
-  for (int hh = 0; hh < kAttnMaxGroup; ++hh) sc[hh] = -INFINITY;
-  // values: wave w takes positions 64 w .. 64 w + 63 of the chunk; lane l takes
-  // dims 8 (l % 16) .. + 7 of positions 64 w + 4 i + l / 16 (i < 16), so each
-  // wave load moves 4 whole 256-byte rows
-  const int j0 = 64 * wave, vsub = lane >> 4, vd = 8 * (lane & 15);
-  v4i vr[16];
-  {
-    // (threads past the chunk end reload the chunk's first row, unused)
-    const v4i *krow = reinterpret_cast<const v4i *>(kc + (base + t0 + (tid < cnt ? tid : 0)) * HD);
-    v4i kr[HD / 8];
+  for (int hh = 0; hh < G; ++hh) mx[hh] = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < HD / 8; ++c) kr[c] = krow[c];
-    // (past the chunk end: the chunk's first row, weight 0 below)
+  for (int i = 0; i < PW; ++i) {
+    float kf[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = j0 + 4 * i + vsub;
-      vr[i] = *reinterpret_cast<const v4i *>(vc + (base + t0 + (j < cnt ? j : 0)) * HD + vd);
+    for (int q2 = 0; q2 < 4; ++q2) {
+      kf[2 * q2] = bf16_to_f32((uint32_t)kr[i][q2] & 0xFFFFu);
+      kf[2 * q2 + 1] = bf16_to_f32((uint32_t)kr[i][q2] >> 16);
     }
-    float dot[kAttnMaxGroup];
+    const bool valid = 32 * wave + 4 * i + sub < cnt;
 #pragma unroll
-    for (int hh = 0; hh < kAttnMaxGroup; ++hh) dot[hh] = 0.0f;
+    for (int hh = 0; hh < G; ++hh) {
+      float d = 0.0f;
 #pragma unroll
-    for (int c = 0; c < HD / 8; ++c) {
-      const v4i kw = kr[c];
-      float kf[8];
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        kf[2 * q2] = bf16_to_f32((uint32_t)kw[q2] & 0xFFFFu);
-        kf[2 * q2 + 1] = bf16_to_f32((uint32_t)kw[q2] >> 16);
-      }
-#pragma unroll
-      for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
-        if (hh < group) {
-          // the 8 query values as two 16-byte LDS broadcasts
-          const float4 qa = *reinterpret_cast<const float4 *>(&qs[hh][8 * c]);
-          const float4 qb = *reinterpret_cast<const float4 *>(&qs[hh][8 * c + 4]);
-          dot[hh] = __fmaf_rn(qa.x, kf[0], dot[hh]);
-          dot[hh] = __fmaf_rn(qa.y, kf[1], dot[hh]);
-          dot[hh] = __fmaf_rn(qa.z, kf[2], dot[hh]);
-          dot[hh] = __fmaf_rn(qa.w, kf[3], dot[hh]);
-          dot[hh] = __fmaf_rn(qb.x, kf[4], dot[hh]);
-          dot[hh] = __fmaf_rn(qb.y, kf[5], dot[hh]);
-          dot[hh] = __fmaf_rn(qb.z, kf[6], dot[hh]);
-          dot[hh] = __fmaf_rn(qb.w, kf[7], dot[hh]);
-        }
-      }
+      for (int e = 0; e < 8; ++e) d = __fmaf_rn(qv[hh][e], kf[e], d);
+      // the 16 lanes of the row, in a fixed order
+      d += __shfl_xor(d, 8, 64);
+      d += __shfl_xor(d, 4, 64);
+      d += __shfl_xor(d, 2, 64);
+      d += __shfl_xor(d, 1, 64);
+      sc[i][hh] = valid ? __fmul_rn(d, scale) : -INFINITY;
+      mx[hh] = fmaxf(mx[hh], sc[i][hh]);
     }
-#pragma unroll
-    for (int hh = 0; hh < kAttnMaxGroup; ++hh)
-      if (hh < group && tid < cnt) sc[hh] = __fmul_rn(dot[hh], scale);
   }
-  // ---- chunk max per head
+  // ---- chunk max per head: the wave's four position groups, then the four waves
 #pragma unroll
-  for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
-    if (hh >= group) break;
-    float mx = sc[hh];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    if (lane == 0) red[hh][wave] = mx;
+  for (int hh = 0; hh < G; ++hh) {
+    float m = mx[hh];
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (lane == 0) red[hh][wave] = m;
   }
   __syncthreads();
-  float cmax[kAttnMaxGroup];
+  float cmax[G];
 #pragma unroll
-  for (int hh = 0; hh < kAttnMaxGroup; ++hh)
-    cmax[hh] = hh < group ? fmaxf(fmaxf(red[hh][0], red[hh][1]), fmaxf(red[hh][2], red[hh][3])) : 0.0f;
+  for (int hh = 0; hh < G; ++hh) cmax[hh] = fmaxf(fmaxf(red[hh][0], red[hh][1]), fmaxf(red[hh][2], red[hh][3]));
   __syncthreads();
-  // ---- exp(score - max), and the chunk sums (fixed order)
+  // ---- exp(score - max), the sums (fixed order), and the values
+  float acc[G][8];
 #pragma unroll
-  for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
-    if (hh >= group) break;
-    const float e = tid < cnt ? expf(sc[hh] - cmax[hh]) : 0.0f;
-    ps[tid][hh] = e;
-    float sum = e;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    if (lane == 0) red[hh][wave] = sum;
-  }
-  __syncthreads();
-  if (tid < group) {
-    const float l = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
-    pml[(part + tid) * 2] = cmax[tid];
-    pml[(part + tid) * 2 + 1] = l;
-  }
-  // ---- values
-  float acc[kAttnMaxGroup][8];
-#pragma unroll
-  for (int hh = 0; hh < kAttnMaxGroup; ++hh)
+  for (int hh = 0; hh < G; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+  float lsum[G];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int j = j0 + 4 * i + vsub;  // (weights past the chunk end are 0)
+  for (int hh = 0; hh < G; ++hh) lsum[hh] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
     float vf[8];
 #pragma unroll
     for (int q2 = 0; q2 < 4; ++q2) {
       vf[2 * q2] = bf16_to_f32((uint32_t)vr[i][q2] & 0xFFFFu);
       vf[2 * q2 + 1] = bf16_to_f32((uint32_t)vr[i][q2] >> 16);
     }
-    float w[kAttnMaxGroup];
-    *reinterpret_cast<float4 *>(&w[0]) = *reinterpret_cast<const float4 *>(&ps[j][0]);
-    if (group > 4) *reinterpret_cast<float4 *>(&w[4]) = *reinterpret_cast<const float4 *>(&ps[j][4]);
 #pragma unroll
-    for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
-      if (hh < group) {
+    for (int hh = 0; hh < G; ++hh) {
+      const float w = sc[i][hh] == -INFINITY ? 0.0f : expf(sc[i][hh] - cmax[hh]);
+      lsum[hh] += w;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = __fmaf_rn(w[hh], vf[e], acc[hh][e]);
-      }
+      for (int e = 0; e < 8; ++e) acc[hh][e] = __fmaf_rn(w, vf[e], acc[hh][e]);
     }
   }
-  // the four position subgroups of the wave, in a fixed order
 #pragma unroll
-  for (int hh = 0; hh < kAttnMaxGroup; ++hh) {
-    if (hh < group) {
+  for (int hh = 0; hh < G; ++hh) {
+    // (each position's weight sits in the 16 lanes of its group: add one lane per group)
+    float l = lsum[hh];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (lane == 0) red[hh][wave] = l;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = acc[hh][e];
-        a += __shfl_xor(a, 16, 64);
-        a += __shfl_xor(a, 32, 64);
-        acc[hh][e] = a;
-      }
-      if (vsub == 0) {
-        *reinterpret_cast<float4 *>(&accs[wave][hh][vd]) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
-        *reinterpret_cast<float4 *>(&accs[wave][hh][vd + 4]) =
-            make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      float a = acc[hh][e];
+      a += __shfl_xor(a, 16, 64);
+      a += __shfl_xor(a, 32, 64);
+      acc[hh][e] = a;
+    }
+    if (sub == 0) {
+      *reinterpret_cast<float4 *>(&accs[wave][hh][d0]) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+      *reinterpret_cast<float4 *>(&accs[wave][hh][d0 + 4]) =
+          make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
     }
   }
   __syncthreads();
-  for (int e = tid; e < group * HD; e += 256) {
+  if (tid < G) {
+    pml[(part + tid) * 2] = cmax[tid];
+    pml[(part + tid) * 2 + 1] = ((red[tid][0] + red[tid][1]) + red[tid][2]) + red[tid][3];
+  }
+  for (int e = tid; e < G * HD; e += 256) {
     const int hh = e / HD, d = e - hh * HD;
     po[part * HD + e] = ((accs[0][hh][d] + accs[1][hh][d]) + accs[2][hh][d]) + accs[3][hh][d];
   }
@@ -296,7 +273,9 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(const float *__restric
 int attention_splits(int64_t tmax) { return (int)((tmax + kAttnChunk - 1) / kAttnChunk); }
 
 bool attention_supported(int n_heads, int n_kv, int hd) {
-  return hd == 128 && n_kv > 0 && n_heads % n_kv == 0 && n_heads / n_kv <= kAttnMaxGroup;
+  if (hd != 128 || n_kv <= 0 || n_heads % n_kv != 0) return false;
+  const int g = n_heads / n_kv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
 hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
@@ -332,8 +311,17 @@ hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads,
   const int S = attention_splits(tmax);
   float *po = ws;
   float *pml = ws + (size_t)(m * n_heads * S) * 128;
-  attn_partial_kernel<128><<<dim3((unsigned)S, (unsigned)n_kv, (unsigned)m), dim3(256), 0, stream>>>(
-      q, ldq, n_heads, n_kv, kc, vc, n_slots, tmax, slot, pos, S, po, pml);
+  const dim3 grid((unsigned)S, (unsigned)n_kv, (unsigned)m), block(256);
+  switch (n_heads / n_kv) {
+    case 1: attn_partial_kernel<128, 1><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, S,
+                                                                    po, pml); break;
+    case 2: attn_partial_kernel<128, 2><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, S,
+                                                                    po, pml); break;
+    case 4: attn_partial_kernel<128, 4><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, S,
+                                                                    po, pml); break;
+    default: attn_partial_kernel<128, 8><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos,
+                                                                     S, po, pml); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   attn_combine_kernel<128><<<dim3((unsigned)n_heads, (unsigned)m), dim3(128), 0, stream>>>(po, pml, n_heads, n_kv, S,
