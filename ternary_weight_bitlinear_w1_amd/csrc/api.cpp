@@ -703,10 +703,9 @@ bitlinear_status cached_attention(const bitlinear_block *blk, const bitlinear_la
                                   const BlockBufs &b, float *tr_attn, hipStream_t s) {
   const int hd = blk->head_dim, nh = blk->n_heads, nkv = blk->n_kv_heads;
   const int64_t H = blk->hidden, KV = (int64_t)nkv * hd, Q = H + 2 * KV;
-  BL_TRY(launched(bl::launch_rope(qkv, m, Q, 0, nh + nkv, hd, blk->pos, blk->rope_theta, s), "rope"));
-  BL_TRY(launched(bl::launch_kv_append(qkv + H, qkv + H + KV, m, Q, nkv, hd, blk->slot, blk->pos, L.k_cache,
-                                       L.v_cache, blk->n_slots, blk->t_max, s),
-                  "kv append"));
+  BL_TRY(launched(bl::launch_rope_append(qkv, m, Q, nh, nkv, hd, blk->slot, blk->pos, blk->rope_theta, L.k_cache,
+                                         L.v_cache, blk->n_slots, blk->t_max, s),
+                  "rope and kv append"));
   BL_TRY(launched(bl::launch_attention(qkv, m, Q, nh, nkv, hd, L.k_cache, L.v_cache, blk->n_slots, blk->t_max,
                                        blk->slot, blk->pos, b.att, H, b.attn_ws, s),
                   "attention"));

@@ -52,6 +52,41 @@ __global__ __launch_bounds__(256) void rope_kernel(float *__restrict__ x, int64_
   v[e + half] = __fadd_rn(__fmul_rn(b, c), __fmul_rn(a, s));
 }
 
+// RoPE on the q and k heads of a q|k|v row and the keys and values into the
+// caches, one thread per rotated pair of q or k (plus the matching value pair)
+__global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, int64_t m, int64_t ld,
+                                                          int n_heads, int n_kv, int hd,
+                                                          const int64_t *__restrict__ slot,
+                                                          const int64_t *__restrict__ pos, double theta,
+                                                          uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
+                                                          int64_t n_slots, int64_t tmax) {
+  const int half = hd / 2, heads = n_heads + n_kv;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= m * heads * half) return;
+  const int64_t r = i / (heads * half);
+  const int rem = (int)(i - r * heads * half);
+  const int h = rem / half, e = rem - h * half;
+  const int64_t p = pos[r];
+  const double ang = (double)p * pow(theta, -(2.0 * e) / (double)hd);
+  const float c = (float)cos(ang), s = (float)sin(ang);
+  float *v = qkv + r * ld + (int64_t)h * hd;
+  const float a = v[e], b = v[e + half];
+  const float ra = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s));
+  const float rb = __fadd_rn(__fmul_rn(b, c), __fmul_rn(a, s));
+  v[e] = ra;
+  v[e + half] = rb;
+  if (h < n_heads) return;  // a query head
+  const int64_t sl = slot[r];
+  if (sl < 0 || sl >= n_slots || p < 0 || p >= tmax) return;
+  const int g = h - n_heads;
+  const int64_t dst = ((sl * n_kv + g) * tmax + p) * hd;
+  kc[dst + e] = (uint16_t)f32_to_bf16(ra);
+  kc[dst + e + half] = (uint16_t)f32_to_bf16(rb);
+  const float *vrow = qkv + r * ld + (int64_t)(n_heads + n_kv) * hd + (int64_t)g * hd;
+  vc[dst + e] = (uint16_t)f32_to_bf16(vrow[e]);
+  vc[dst + e + half] = (uint16_t)f32_to_bf16(vrow[e + half]);
+}
+
 // one thread per element of a token's keys (and values)
 __global__ __launch_bounds__(256) void kv_append_kernel(const float *__restrict__ k, const float *__restrict__ v,
                                                         int64_t m, int64_t ld, int n_kv, int hd,
@@ -235,8 +270,9 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(const float *__restric
   const int64_t r = blockIdx.y;
   const int h = blockIdx.x, d = threadIdx.x;
   const int group = n_heads / n_kv, g = h / group, hh = h - g * group;
-  // the chunks' (max, sum) and outputs, 16 at a time, all loads issued first
-  constexpr int kB = 16;
+  // the chunks' (max, sum) and outputs, 32 at a time (a 4096-position context
+  // in one batch), all loads issued first
+  constexpr int kB = 32;
   float M = -INFINITY, L = 0.0f, acc = 0.0f;
   for (int s0 = 0; s0 < S; s0 += kB) {
     float ms[kB], ls[kB], os[kB];
@@ -283,6 +319,16 @@ hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_head
   const int64_t n = m * n_heads * (hd / 2);
   if (n == 0) return hipSuccess;
   rope_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(x, m, ld, col0, n_heads, hd, pos, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append(float *qkv, int64_t m, int64_t ld, int n_heads, int n_kv, int hd, const int64_t *slot,
+                              const int64_t *pos, double theta, uint16_t *kc, uint16_t *vc, int64_t n_slots,
+                              int64_t tmax, hipStream_t stream) {
+  const int64_t n = m * (n_heads + n_kv) * (hd / 2);
+  if (n == 0) return hipSuccess;
+  rope_append_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(qkv, m, ld, n_heads, n_kv, hd, slot,
+                                                                                 pos, theta, kc, vc, n_slots, tmax);
   return hipGetLastError();
 }
 

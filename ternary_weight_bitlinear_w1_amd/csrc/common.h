@@ -189,6 +189,10 @@ int attention_splits(int64_t tmax);
 size_t attention_workspace_floats(int64_t m, int n_heads, int64_t tmax);
 hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
                        double theta, hipStream_t stream);
+// both of the above on a q|k|v row (q heads, then k heads, then v heads), one launch
+hipError_t launch_rope_append(float *qkv, int64_t m, int64_t ld, int n_heads, int n_kv, int hd, const int64_t *slot,
+                              const int64_t *pos, double theta, uint16_t *kc, uint16_t *vc, int64_t n_slots,
+                              int64_t tmax, hipStream_t stream);
 hipError_t launch_kv_append(const float *k, const float *v, int64_t m, int64_t ld, int n_kv, int hd,
                             const int64_t *slot, const int64_t *pos, uint16_t *kc, uint16_t *vc, int64_t n_slots,
                             int64_t tmax, hipStream_t stream);
