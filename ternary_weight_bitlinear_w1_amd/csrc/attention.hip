@@ -10,21 +10,25 @@
 //   out_h = sum_{t <= p} softmax_t(q_h . k_t / sqrt(hd)) v_t, kv head g = h / (heads / kv heads)
 //
 // Attention runs as flash-decoding in two kernels. attn_partial_kernel: a
-// workgroup takes one token, one key/value head and a chunk of 128 positions,
-// a wave 32 of them. Lanes split each row into 16 pieces of 8 dims, so a wave
-// load moves four whole 256-byte key (or value) rows, the query stays in
+// workgroup takes one token, one key/value head and a chunk of positions, a
+// wave a quarter of them. Lanes split each row into 16 pieces of 8 dims, so a
+// wave load moves four whole 256-byte key (or value) rows, the query stays in
 // registers, and a score is summed over its row's 16 lanes with xor-shuffles;
 // the lanes that scored a position then weight its value row. It stores the
-// chunk's max, sum of exponentials and unnormalized output. attn_combine_kernel
-// rescales and adds
-// the chunks. Tokens whose slot or position is out of range get zeros and
-// write nothing to the cache.
+// chunk's max, sum of exponentials and unnormalized output.
+// attn_combine_kernel rescales and adds the chunks, one exponential per chunk
+// and head. Tokens whose slot or position is out of range get zeros and write
+// nothing to the cache.
 #include "common.h"
 
 namespace bl {
 namespace {
 
-constexpr int kAttnChunk = 128;   // positions per workgroup
+#ifndef BL_ATTN_CHUNK
+#define BL_ATTN_CHUNK 128
+#endif
+constexpr int kAttnChunk = BL_ATTN_CHUNK;  // positions per workgroup (a multiple of 16)
+static_assert(kAttnChunk % 16 == 0 && kAttnChunk <= 256, "four waves, four positions per wave load");
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -108,40 +112,35 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float *__restrict_
 
 // Partials of token r, kv head g, chunk s (kAttnChunk positions): po
 // [r][g][s][group][HD] (sum of exp(score - max) v), pml [r][g][s][group][2]
-// (max, sum of exp). Wave w takes positions 32 w .. 32 w + 31 of the chunk;
-// lane l takes dims 8 (l % 16) .. + 7 of positions 32 w + 4 i + l / 16 (i < 8),
-// for keys and values alike, so every wave load moves four whole 256-byte rows,
-// the query's 8 dims of each head stay in registers, and a position's score
-// (summed over its 16 lanes with xor-shuffles) is already in the lanes that
-// weight its value row.
+// (max, sum of exp); chunks past the token's position are not written. Wave w
+// takes positions kAttnChunk/4 w .. + kAttnChunk/4 - 1 of the chunk; lane l
+// takes dims 8 (l % 16) .. + 7 of positions kAttnChunk/4 w + 4 i + l / 16
+// (i < PW), for keys and values alike, so every wave load moves four whole
+// 256-byte rows, the query's 8 dims of each head stay in registers, and a
+// position's score (summed over its 16 lanes with xor-shuffles) is already in
+// the lanes that weight its value row.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int64_t ldq, int n_kv,
                                                            const uint16_t *__restrict__ kc,
                                                            const uint16_t *__restrict__ vc, int64_t n_slots,
                                                            int64_t tmax, const int64_t *__restrict__ slot,
-                                                           const int64_t *__restrict__ pos, int S,
-                                                           float *__restrict__ po, float *__restrict__ pml) {
+                                                           const int64_t *__restrict__ pos, float *__restrict__ po,
+                                                           float *__restrict__ pml) {
   static_assert(HD == 128, "16 lanes of 8 dims cover a row");
-  constexpr int PW = kAttnChunk / 4 / 4;  // positions per lane (8)
+  constexpr int PW = kAttnChunk / 16;  // positions per lane
+  constexpr int kWavePos = kAttnChunk / 4;
   __shared__ float red[G][4];
   __shared__ __attribute__((aligned(16))) float accs[4][G][HD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.x, g = blockIdx.y;
+  const int s = blockIdx.x, g = blockIdx.y, S = gridDim.x;
   const int64_t r = blockIdx.z;
   const int64_t sl = slot[r], p = pos[r];
   const bool ok = sl >= 0 && sl < n_slots && p >= 0 && p < tmax;
   const int64_t T = ok ? p + 1 : 0;
   const int64_t t0 = (int64_t)s * kAttnChunk;
-  const int64_t part = ((r * n_kv + g) * S + s) * G;
-  if (t0 >= T) {  // nothing to attend in this chunk
-    for (int e = tid; e < G * HD; e += 256) po[part * HD + e] = 0.0f;
-    if (tid < G) {
-      pml[(part + tid) * 2] = -INFINITY;
-      pml[(part + tid) * 2 + 1] = 0.0f;
-    }
-    return;
-  }
-  const int cnt = (int)(T - t0 < kAttnChunk ? T - t0 : kAttnChunk);
+  const int64_t pb = (r * n_kv + g) * S;  // first chunk of (r, g)
+  if (t0 >= T) return;  // nothing to attend in this chunk
+  const int cnt_pos = (int)(T - t0 < kAttnChunk ? T - t0 : kAttnChunk);
   const int64_t base = (sl * n_kv + g) * tmax + t0;
   const int sub = lane >> 4, d0 = 8 * (lane & 15);
   // loads in issue order: keys, values (past the chunk end: the chunk's first
@@ -149,13 +148,13 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   v4i kr[PW], vr[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const int j = 32 * wave + 4 * i + sub;
-    kr[i] = *reinterpret_cast<const v4i *>(kc + (base + (j < cnt ? j : 0)) * HD + d0);
+    const int j = kWavePos * wave + 4 * i + sub;
+    kr[i] = *reinterpret_cast<const v4i *>(kc + (base + (j < cnt_pos ? j : 0)) * HD + d0);
   }
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const int j = 32 * wave + 4 * i + sub;
-    vr[i] = *reinterpret_cast<const v4i *>(vc + (base + (j < cnt ? j : 0)) * HD + d0);
+    const int j = kWavePos * wave + 4 * i + sub;
+    vr[i] = *reinterpret_cast<const v4i *>(vc + (base + (j < cnt_pos ? j : 0)) * HD + d0);
   }
   float qv[G][8];
 #pragma unroll
@@ -178,7 +177,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
       kf[2 * q2] = bf16_to_f32((uint32_t)kr[i][q2] & 0xFFFFu);
       kf[2 * q2 + 1] = bf16_to_f32((uint32_t)kr[i][q2] >> 16);
     }
-    const bool valid = 32 * wave + 4 * i + sub < cnt;
+    const bool valid = kWavePos * wave + 4 * i + sub < cnt_pos;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float d = 0.0f;
@@ -246,12 +245,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
       acc[hh][e] = a;
     }
     if (sub == 0) {
-      *reinterpret_cast<float4 *>(&accs[wave][hh][d0]) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+      *reinterpret_cast<float4 *>(&accs[wave][hh][d0]) =
+          make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
       *reinterpret_cast<float4 *>(&accs[wave][hh][d0 + 4]) =
           make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
     }
   }
   __syncthreads();
+  const int64_t part = (pb + s) * G;
   if (tid < G) {
     pml[(part + tid) * 2] = cmax[tid];
     pml[(part + tid) * 2 + 1] = ((red[tid][0] + red[tid][1]) + red[tid][2]) + red[tid][3];
@@ -262,46 +263,71 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   }
 }
 
-// out[r][h HD + d] from the chunks of token r's kv head
-template <int HD>
-__global__ __launch_bounds__(HD) void attn_combine_kernel(const float *__restrict__ po, const float *__restrict__ pml,
-                                                          int n_heads, int n_kv, int S, float *__restrict__ out,
-                                                          int64_t ldo) {
+// out[r][h HD + d] from the chunks of token r's kv head g: one wave per head
+// of the group (two per wave for groups of 8), 32 chunks per round. Every load
+// of a round (each lane's two dims of the 32 chunk outputs; lane j's chunk j
+// max and sum) is issued before any arithmetic, the first round's before the
+// max over all chunks is formed. Lane j then forms exp(max_j - max) and its
+// share of the sum of exponentials, and every lane adds its two dims of the
+// chunk outputs, weighted by those factors, in chunk order.
+template <int HD, int G>
+__global__ __launch_bounds__(64 * (G < 4 ? G : 4)) void attn_combine_kernel(
+    const float *__restrict__ po, const float *__restrict__ pml, int n_kv, int S, int64_t n_slots, int64_t tmax,
+    const int64_t *__restrict__ slot, const int64_t *__restrict__ pos, float *__restrict__ out, int64_t ldo) {
+  constexpr int kWaves = G < 4 ? G : 4;
+  constexpr int kR = 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = blockIdx.x;
   const int64_t r = blockIdx.y;
-  const int h = blockIdx.x, d = threadIdx.x;
-  const int group = n_heads / n_kv, g = h / group, hh = h - g * group;
-  // the chunks' (max, sum) and outputs, 32 at a time (a 4096-position context
-  // in one batch), all loads issued first
-  constexpr int kB = 32;
-  float M = -INFINITY, L = 0.0f, acc = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += kB) {
-    float ms[kB], ls[kB], os[kB];
+  const int64_t sl = slot[r], p = pos[r];
+  const bool ok = sl >= 0 && sl < n_slots && p >= 0 && p < tmax;
+  const int nch = ok ? (int)(p / kAttnChunk) + 1 : 0;  // chunks that hold positions
+  const int64_t pb = (r * n_kv + g) * S;
+#pragma unroll 1
+  for (int hh = wave; hh < G; hh += kWaves) {
+    float2 o[kR];
+    float mc = -INFINITY, lc = 0.0f;
+    // the loads of the round that starts at chunk c0 (past the last chunk:
+    // the last chunk's finite values, weighted 0)
+    auto issue = [&](int c0) {
+      const int n_here = nch - c0 < kR ? nch - c0 : kR;
 #pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      const int s = s0 + i < S ? s0 + i : S - 1;  // (repeats are not added)
-      const int64_t part = ((r * n_kv + g) * S + s) * group + hh;
-      ms[i] = pml[part * 2];
-      ls[i] = pml[part * 2 + 1];
-      os[i] = po[part * HD + d];
+      for (int j = 0; j < kR; ++j) {
+        const int cj = c0 + (j < n_here ? j : n_here - 1);
+        o[j] = *reinterpret_cast<const float2 *>(po + ((pb + cj) * G + hh) * HD + 2 * lane);
+      }
+      mc = -INFINITY;
+      lc = 0.0f;
+      if (lane < n_here) {
+        mc = pml[((pb + c0 + lane) * G + hh) * 2];
+        lc = pml[((pb + c0 + lane) * G + hh) * 2 + 1];
+      }
+    };
+    float M = -INFINITY, L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    if (nch > 0) {
+      issue(0);
+      M = mc;
+      for (int c = kR + lane; c < nch; c += 64) M = fmaxf(M, pml[((pb + c) * G + hh) * 2]);
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh, 64));
+      for (int c0 = 0; c0 < nch; c0 += kR) {
+        if (c0 > 0) issue(c0);
+        const float f = mc == -INFINITY ? 0.0f : expf(mc - M);
+        float lw = __fmul_rn(f, lc);
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1) lw += __shfl_xor(lw, sh, 64);
+        L += lw;
+#pragma unroll
+        for (int j = 0; j < kR; ++j) {
+          const float fj = __shfl(f, j, 64);
+          a0 = __fmaf_rn(fj, o[j].x, a0);
+          a1 = __fmaf_rn(fj, o[j].y, a1);
+        }
+      }
     }
-    float mb = M;
-#pragma unroll
-    for (int i = 0; i < kB; ++i)
-      if (s0 + i < S) mb = fmaxf(mb, ms[i]);
-    if (mb == -INFINITY) continue;
-    const float f0 = expf(M - mb);  // rescale what earlier batches added (exp(-inf) = 0 at the start)
-    L = __fmul_rn(L, f0);
-    acc = __fmul_rn(acc, f0);
-#pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      if (s0 + i >= S || ms[i] == -INFINITY) continue;
-      const float f = expf(ms[i] - mb);
-      L = __fmaf_rn(ls[i], f, L);
-      acc = __fmaf_rn(os[i], f, acc);
-    }
-    M = mb;
+    const float2 res = nch > 0 ? make_float2(__fdiv_rn(a0, L), __fdiv_rn(a1, L)) : make_float2(0.0f, 0.0f);
+    *reinterpret_cast<float2 *>(out + r * ldo + (int64_t)(g * G + hh) * HD + 2 * lane) = res;
   }
-  out[r * ldo + (int64_t)h * HD + d] = M != -INFINITY ? __fdiv_rn(acc, L) : 0.0f;
 }
 
 }  // namespace
@@ -342,7 +368,8 @@ hipError_t launch_kv_append(const float *k, const float *v, int64_t m, int64_t l
   return hipGetLastError();
 }
 
-// workspace: attention_workspace_floats(m, n_heads, tmax) floats
+// workspace: attention_workspace_floats(m, n_heads, tmax) floats: the chunks'
+// outputs [m][n_heads][S][HD], then their (max, sum) [m][n_heads][S][2]
 size_t attention_workspace_floats(int64_t m, int n_heads, int64_t tmax) {
   const int64_t S = attention_splits(tmax);
   return (size_t)(m * n_heads * S) * (128 + 2);
@@ -357,21 +384,21 @@ hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads,
   const int S = attention_splits(tmax);
   float *po = ws;
   float *pml = ws + (size_t)(m * n_heads * S) * 128;
-  const dim3 grid((unsigned)S, (unsigned)n_kv, (unsigned)m), block(256);
+  const dim3 grid((unsigned)S, (unsigned)n_kv, (unsigned)m), block(256), cgrid((unsigned)n_kv, (unsigned)m);
+#define BL_ATTN(G_)                                                                                                   \
+  attn_partial_kernel<128, G_><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, po, pml); \
+  e = hipGetLastError();                                                                                             \
+  if (e != hipSuccess) return e;                                                                                     \
+  attn_combine_kernel<128, G_><<<cgrid, dim3(64 * (G_ < 4 ? G_ : 4)), 0, stream>>>(po, pml, n_kv, S, n_slots, tmax,  \
+                                                                                  slot, pos, out, ldo)
+  hipError_t e;
   switch (n_heads / n_kv) {
-    case 1: attn_partial_kernel<128, 1><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, S,
-                                                                    po, pml); break;
-    case 2: attn_partial_kernel<128, 2><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, S,
-                                                                    po, pml); break;
-    case 4: attn_partial_kernel<128, 4><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, S,
-                                                                    po, pml); break;
-    default: attn_partial_kernel<128, 8><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos,
-                                                                     S, po, pml); break;
+    case 1: BL_ATTN(1); break;
+    case 2: BL_ATTN(2); break;
+    case 4: BL_ATTN(4); break;
+    default: BL_ATTN(8); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  attn_combine_kernel<128><<<dim3((unsigned)n_heads, (unsigned)m), dim3(128), 0, stream>>>(po, pml, n_heads, n_kv, S,
-                                                                                          out, ldo);
+#undef BL_ATTN
   return hipGetLastError();
 }
 

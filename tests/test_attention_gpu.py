@@ -7,7 +7,10 @@ the oracle's bit for bit. Attention: fp32 softmax and sums against the oracle's
 fp64, within the bound the fp32 arithmetic allows,
   |out - ref| <= 2^-24 (2 (hd + 1) smag + 2 (192 + S)) vmag,
 smag being the largest scaled sum |q k| and vmag the weighted sum |v| the
-oracle reports, S the number of 256-position chunks.
+oracle reports, and S = ceil(t_max / 64), at least the number of chunks the
+kernel splits the context into (the combine adds the chunk outputs in turn;
+within a chunk a sum takes at most 12 steps, and the constant 192 covers those
+and the two exponentials of each weight).
 """
 import numpy as np
 import pytest
@@ -75,7 +78,7 @@ def _check_attention(q, kc, vc, slot, pos, what):
     tmax = kc.shape[2]
     out = host(bl.attention_decode(gpu(q), gpu(kc), gpu(vc), gpu(slot), gpu(pos), NH))
     ref, vmag, smag, _ = oracle.attention(q, kc, vc, slot, pos, NH, NKV, HD)
-    S = (tmax + 255) // 256
+    S = (tmax + 63) // 64
     factor = 2.0 ** -24 * (2 * (HD + 1) * np.repeat(smag, HD, axis=1) + 2 * (192 + S))
     err = np.abs(out.astype(np.float64) - ref.astype(np.float64))
     bound = factor * vmag
@@ -83,8 +86,10 @@ def _check_attention(q, kc, vc, slot, pos, what):
     return out, ref
 
 
-# (positions, t_max, q scale): one position; chunk edges 255/256/257; a sharp softmax; the full context
-CASES = [([0, 0], 64, 1.0), ([255, 256, 257], 512, 1.0), ([1000, 31], 1024, 8.0), ([4095, 2047, 100, 0], 4096, 1.0)]
+# (positions, t_max, q scale): one position; chunk edges; a sharp softmax; the full 4096 context; more
+# than 64 chunks (the combine's second round)
+CASES = [([0, 0], 64, 1.0), ([255, 256, 257], 512, 1.0), ([63, 64, 65, 127], 512, 1.0), ([1000, 31], 1024, 8.0),
+         ([4095, 2047, 100, 0], 4096, 1.0), ([5000, 8191], 8192, 1.0)]
 
 
 @pytest.mark.parametrize("positions,tmax,qscale", CASES)
