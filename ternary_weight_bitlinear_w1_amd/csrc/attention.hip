@@ -32,6 +32,44 @@ static_assert(kAttnChunk % 16 == 0 && kAttnChunk <= 256, "four waves, four posit
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Cross-lane sums and maxima that leave the same bits in every lane taking
+// part: each step combines a value with its partner's, and a + b = b + a.
+// Within a row of 16 lanes (DPP): lane ^ 1 and lane ^ 2 (quad permutes), then
+// the partner quad in the half row (7 - lane) and the partner half (15 - lane).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  return fmaxf(v, dpp<0x140>(v));
+}
+// Across the four rows of a wave: rows 0 and 1 (and 2 and 3) with
+// v_permlane16_swap, then the two halves with v_permlane32_swap; with both
+// operands the same value, the two results hold a lane's value and its
+// partner's, in the same order in both lanes.
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
   const uint32_t kept = u >> 16, dropped = u & 0xFFFFu;
@@ -183,11 +221,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
       float d = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = __fmaf_rn(qv[hh][e], kf[e], d);
-      // the 16 lanes of the row, in a fixed order
-      d += __shfl_xor(d, 8, 64);
-      d += __shfl_xor(d, 4, 64);
-      d += __shfl_xor(d, 2, 64);
-      d += __shfl_xor(d, 1, 64);
+      d = row16_sum(d);  // the 16 lanes of the row
       sc[i][hh] = valid ? __fmul_rn(d, scale) : -INFINITY;
       mx[hh] = fmaxf(mx[hh], sc[i][hh]);
     }
@@ -195,9 +229,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   // ---- chunk max per head: the wave's four position groups, then the four waves
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    float m = mx[hh];
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const float m = rows_max(mx[hh]);
     if (lane == 0) red[hh][wave] = m;
   }
   __syncthreads();
@@ -233,17 +265,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     // (each position's weight sits in the 16 lanes of its group: add one lane per group)
-    float l = lsum[hh];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = rows_sum(lsum[hh]);
     if (lane == 0) red[hh][wave] = l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float a = acc[hh][e];
-      a += __shfl_xor(a, 16, 64);
-      a += __shfl_xor(a, 32, 64);
-      acc[hh][e] = a;
-    }
+    for (int e = 0; e < 8; ++e) acc[hh][e] = rows_sum(acc[hh][e]);
     if (sub == 0) {
       *reinterpret_cast<float4 *>(&accs[wave][hh][d0]) =
           make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
@@ -308,18 +333,14 @@ __global__ __launch_bounds__(64 * (G < 4 ? G : 4)) void attn_combine_kernel(
       issue(0);
       M = mc;
       for (int c = kR + lane; c < nch; c += 64) M = fmaxf(M, pml[((pb + c) * G + hh) * 2]);
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh, 64));
+      M = rows_max(row16_max(M));
       for (int c0 = 0; c0 < nch; c0 += kR) {
         if (c0 > 0) issue(c0);
         const float f = mc == -INFINITY ? 0.0f : expf(mc - M);
-        float lw = __fmul_rn(f, lc);
-#pragma unroll
-        for (int sh = 32; sh >= 1; sh >>= 1) lw += __shfl_xor(lw, sh, 64);
-        L += lw;
+        L += rows_sum(row16_sum(__fmul_rn(f, lc)));
 #pragma unroll
         for (int j = 0; j < kR; ++j) {
-          const float fj = __shfl(f, j, 64);
+          const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
           a0 = __fmaf_rn(fj, o[j].x, a0);
           a1 = __fmaf_rn(fj, o[j].y, a1);
         }
