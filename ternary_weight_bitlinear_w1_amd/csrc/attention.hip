@@ -13,7 +13,7 @@
 // workgroup takes one token, one key/value head and a chunk of positions, a
 // wave a quarter of them. Lanes split each row into 16 pieces of 8 dims, so a
 // wave load moves four whole 256-byte key (or value) rows, the query stays in
-// registers, and a score is summed over its row's 16 lanes with xor-shuffles;
+// registers, and a score is summed over its row's 16 lanes with DPP adds;
 // the lanes that scored a position then weight its value row. It stores the
 // chunk's max, sum of exponentials and unnormalized output.
 // attn_combine_kernel rescales and adds the chunks, one exponential per chunk
@@ -31,44 +31,6 @@ constexpr int kAttnChunk = BL_ATTN_CHUNK;  // positions per workgroup (a multipl
 static_assert(kAttnChunk % 16 == 0 && kAttnChunk <= 256, "four waves, four positions per wave load");
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-// Cross-lane sums and maxima that leave the same bits in every lane taking
-// part: each step combines a value with its partner's, and a + b = b + a.
-// Within a row of 16 lanes (DPP): lane ^ 1 and lane ^ 2 (quad permutes), then
-// the partner quad in the half row (7 - lane) and the partner half (15 - lane).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  v += dpp<0x140>(v);  // row_mirror
-  return v;
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  return fmaxf(v, dpp<0x140>(v));
-}
-// Across the four rows of a wave: rows 0 and 1 (and 2 and 3) with
-// v_permlane16_swap, then the two halves with v_permlane32_swap; with both
-// operands the same value, the two results hold a lane's value and its
-// partner's, in the same order in both lanes.
-__device__ __forceinline__ float rows_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float rows_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -155,7 +117,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float *__restrict_
 // takes dims 8 (l % 16) .. + 7 of positions kAttnChunk/4 w + 4 i + l / 16
 // (i < PW), for keys and values alike, so every wave load moves four whole
 // 256-byte rows, the query's 8 dims of each head stay in registers, and a
-// position's score (summed over its 16 lanes with xor-shuffles) is already in
+// position's score (summed over its 16 lanes with DPP adds) is already in
 // the lanes that weight its value row.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int64_t ldq, int n_kv,

@@ -191,9 +191,7 @@ __global__ __launch_bounds__(256) void gemv_b3_kernel(const int8_t *__restrict__
   // 8 lanes per row
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    acc[t] += __shfl_xor(acc[t], 4, 64);
-    acc[t] += __shfl_xor(acc[t], 2, 64);
-    acc[t] += __shfl_xor(acc[t], 1, 64);
+    acc[t] = lanes8_sum(acc[t]);
   }
   if (p == 0) {
 #pragma unroll

@@ -51,19 +51,65 @@ __device__ __forceinline__ float rescale(int acc, float deq, float gamma) {
 }
 
 // ---------------------------------------------------------------- reductions
-// Wave64 butterflies: every lane ends with the result. The order of
-// combination is fixed, so fp64 sums are reproducible run to run.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+// Cross-lane sums and maxima that leave the same bits in every lane taking
+// part: each step combines a value with its partner's (a + b = b + a), in a
+// fixed order, so results repeat run to run. Within a row of 16 lanes, DPP:
+// lane ^ 1 and lane ^ 2 (quad permutes), the partner quad of the half row
+// (row_half_mirror, 7 - lane) and the partner half (row_mirror, 15 - lane).
+// Across the four rows: v_permlane16_swap (rows 0|1, 2|3), then
+// v_permlane32_swap (the two halves); with both operands the same value the
+// two results hold a lane's value and its partner's, in the same order in
+// both lanes.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <typename T>
+__device__ __forceinline__ T lanes8_sum(T v) {  // lanes 8 g .. 8 g + 7
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  return v + dpp<kDppHalfMirror>(v);
+}
+template <typename T>
+__device__ __forceinline__ T row16_sum(T v) {  // lanes 16 g .. 16 g + 15
+  v = lanes8_sum(v);
+  return v + dpp<kDppMirror>(v);
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ uint32_t bits_of(int v) { return (uint32_t)v; }
+__device__ __forceinline__ uint32_t bits_of(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ int from_bits(uint32_t b, int) { return (int)b; }
+__device__ __forceinline__ float from_bits(uint32_t b, float) { return __uint_as_float(b); }
+template <typename T>
+__device__ __forceinline__ T rows_sum(T v) {  // the four rows (values equal within each row)
+  const auto a = __builtin_amdgcn_permlane16_swap(bits_of(v), bits_of(v), false, false);
+  v = from_bits(a[0], v) + from_bits(a[1], v);
+  const auto b = __builtin_amdgcn_permlane32_swap(bits_of(v), bits_of(v), false, false);
+  return from_bits(b[0], v) + from_bits(b[1], v);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Wave64 results in every lane.
+__device__ __forceinline__ float wave_max(float v) { return rows_max(row16_max(v)); }
+__device__ __forceinline__ int wave_sum(int v) { return rows_sum(row16_sum(v)); }
+// fp64: xor butterflies (DPP moves 32 bits), the order fixed
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;

@@ -19,7 +19,7 @@
 // weight row and read 16-byte pieces of its 128-byte lines (a wave reads 8
 // rows x 128 contiguous bytes), the fields are expanded with
 // (w >> 2j) & 0x03030303 and fed to v_dot4_i32_i8 against the codes in LDS,
-// and the 8 lanes of a row are summed with xor shuffles. KS waves split the
+// and the 8 lanes of a row are summed with DPP adds. KS waves split the
 // lines of a row; their partial sums are added in LDS in a fixed order.
 // In the ReLU^2 form, workgroup b owns gate rows [b R/2, (b + 1) R/2) and the
 // up rows I + the same range, so it can form its slice of mi itself.
@@ -129,9 +129,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    acc[t] += __shfl_xor(acc[t], 4, 64);
-    acc[t] += __shfl_xor(acc[t], 2, 64);
-    acc[t] += __shfl_xor(acc[t], 1, 64);
+    acc[t] = lanes8_sum(acc[t]);
   }
   if (p == 0) {
 #pragma unroll

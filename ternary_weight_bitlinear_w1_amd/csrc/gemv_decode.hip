@@ -243,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_loop_kernel(const int8_t *__rest
 // piece read the same bytes (broadcast). Each packed dword d gives, with one
 // shift and one AND, the four weight bytes (d >> 2j) & 0x03030303 of codes
 // 16g + 4j .. +3, contracted against the matching code dword by v_dot4_i32_i8.
-// The 8 partial sums of a row are added with cross-lane shuffles, the KS
+// The 8 partial sums of a row are added with DPP adds, the KS
 // waves that split a row's K range through LDS, all in exact integers.
 constexpr int kDot4MaxK = 8192;
 
@@ -332,9 +332,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict
   // 8 lanes per row
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    acc[t] += __shfl_xor(acc[t], 4, 64);
-    acc[t] += __shfl_xor(acc[t], 2, 64);
-    acc[t] += __shfl_xor(acc[t], 1, 64);
+    acc[t] = lanes8_sum(acc[t]);
   }
   if (p == 0) {
 #pragma unroll

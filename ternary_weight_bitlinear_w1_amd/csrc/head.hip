@@ -16,7 +16,8 @@
 // bfloat16 each), so lane l always reads the same columns 512 c + 8 l .. + 7 and
 // keeps the tokens' o for exactly those columns in registers for the whole
 // kernel. Products use v_dot2_f32_bf16 (exact bfloat16 products, fp32 sums);
-// the 64 lane partials of a row are added with xor-shuffles.
+// the 64 lane partials of a row are added with DPP adds within rows of 16
+// lanes and permlane swaps across them.
 #include "common.h"
 
 namespace bl {
@@ -105,10 +106,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict
   for (int r = 0; r < kHeadRowsPerWave; ++r)
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      float a = acc[r][t];
-#pragma unroll
-      for (int s = 32; s >= 1; s >>= 1) a += __shfl_xor(a, s, 64);
-      acc[r][t] = a;
+      acc[r][t] = rows_sum(row16_sum(acc[r][t]));
     }
   if (lane < kHeadRowsPerWave * MT) {
     const int r = lane / MT, t = lane - r * MT;
