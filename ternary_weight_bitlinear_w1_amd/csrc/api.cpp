@@ -678,8 +678,9 @@ bl::ActSrc act_src(const float *x, int64_t ld, int64_t k, const float *gain) {
 // contract, then the plain / residual / ReLU^2 epilogue.
 bitlinear_status fused(int mode, int epi, const bl::ActSrc &src, float eps, int64_t m, const uint8_t *w, int64_t n,
                        const float *gam, const int64_t *seg, int n_seg, float *y, int32_t *acc, const float *res,
-                       float *out2, float *mi, int8_t *codes_out, float *deq_out, hipStream_t s) {
-  bl::FusedDecode a;
+                       float *out2, float *mi, int8_t *codes_out, float *deq_out, hipStream_t s,
+                       const bitlinear_block *rope_blk = nullptr, const bitlinear_layer *rope_layer = nullptr) {
+  bl::FusedDecode a{};
   a.src = src;
   a.eps = eps;
   a.m = (int)m;
@@ -693,6 +694,18 @@ bitlinear_status fused(int mode, int epi, const bl::ActSrc &src, float eps, int6
   a.mi = mi;
   a.codes_out = codes_out;
   a.deq_out = deq_out;
+  if (rope_blk) {  // the RoPE form: positions, caches and head layout of the cached decoder
+    a.slot = rope_blk->slot;
+    a.pos = rope_blk->pos;
+    a.theta = rope_blk->rope_theta;
+    a.kc = rope_layer->k_cache;
+    a.vc = rope_layer->v_cache;
+    a.n_slots = rope_blk->n_slots;
+    a.tmax = rope_blk->t_max;
+    a.n_heads = rope_blk->n_heads;
+    a.n_kv = rope_blk->n_kv_heads;
+    a.hd = rope_blk->head_dim;
+  }
   return launched(bl::launch_gemv_fused(mode, epi, a, s), "fused decode projection");
 }
 
@@ -744,14 +757,24 @@ bitlinear_status block_forward_fused(const bitlinear_block *blk, const float *x,
     float *qkv = tr.qkv && !cached ? tr.qkv + oQ : b.qkv;
     float *h = tr.h ? tr.h + oH : b.h;
     float *xnext = tr.x_out ? tr.x_out + oH : (l + 1 == blk->n_layers ? y : b.x);
-    // input_layernorm -> q|k|v
-    BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_PLAIN, act_src(xin, H, H, L.input_norm_gain), eps, m, L.qkv, Q,
-                 L.qkv_gamma, qkv_seg, 3, qkv, at(tr.acc_qkv, oQ), nullptr, nullptr, nullptr, at(tr.codes_in, oH), dq,
-                 s));
+    // input_layernorm -> q|k|v; the cached decoder without a q|k|v trace takes
+    // RoPE and the cache append in the same launch
+    const bool rope_fused = cached && !tr.qkv;
+    BL_TRY(fused(BITLINEAR_ACT_RMSNORM, rope_fused ? bl::FUSED_EPI_ROPE : bl::FUSED_EPI_PLAIN,
+                 act_src(xin, H, H, L.input_norm_gain), eps, m, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, qkv,
+                 at(tr.acc_qkv, oQ), nullptr, nullptr, nullptr, at(tr.codes_in, oH), dq, s,
+                 rope_fused ? blk : nullptr, rope_fused ? &L : nullptr));
     if (cached) {
       // RoPE, cache append, attention -> attn_sub_norm -> o_proj; h = x + o
-      BL_TRY(copy_to(at(tr.qkv, oQ), qkv, (size_t)(m * Q) * 4, s));
-      BL_TRY(cached_attention(blk, L, m, qkv, b, at(tr.attn, oH), s));
+      if (rope_fused) {
+        BL_TRY(launched(bl::launch_attention(qkv, m, Q, blk->n_heads, blk->n_kv_heads, hd, L.k_cache, L.v_cache,
+                                             blk->n_slots, blk->t_max, blk->slot, blk->pos, b.att, H, b.attn_ws, s),
+                        "attention"));
+        BL_TRY(copy_to(at(tr.attn, oH), b.att, (size_t)(m * H) * 4, s));
+      } else {
+        BL_TRY(copy_to(at(tr.qkv, oQ), qkv, (size_t)(m * Q) * 4, s));
+        BL_TRY(cached_attention(blk, L, m, qkv, b, at(tr.attn, oH), s));
+      }
       BL_TRY(fused(BITLINEAR_ACT_RMSNORM, bl::FUSED_EPI_RESID, act_src(b.att, H, H, L.attn_sub_norm_gain), eps, m,
                    L.o, H, &L.o_gamma, h_seg, 1, nullptr, at(tr.acc_o, oH), xin, h, nullptr, at(tr.codes_attn, oH),
                    at(dq, m), s));

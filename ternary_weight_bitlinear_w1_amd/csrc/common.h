@@ -44,6 +44,13 @@ __device__ __forceinline__ float epi_gamma(const Epilogue &ep, int n) {
   return g;
 }
 
+// nearest bfloat16 of a finite float (its upper 16 bits), ties to an even last kept bit
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t kept = u >> 16, dropped = u & 0xFFFFu;
+  return kept + ((dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) ? 1u : 0u);
+}
+
 // y = fl32(fl32((float)acc * deq) * gamma); acc is the exact int32 sum.
 __device__ __forceinline__ float rescale(int acc, float deq, float gamma) {
   const float t = __fmul_rn((float)acc, deq);
@@ -179,7 +186,7 @@ enum { ACT_RESID_RMSNORM = 16, ACT_GQA_RMSNORM = 17 };
 
 // ---------------------------------------------------------------- fused decode
 // A decode projection that quantizes its own input (decode_fused.hip).
-enum { FUSED_EPI_PLAIN = 0, FUSED_EPI_RESID = 1, FUSED_EPI_RELU2 = 2 };
+enum { FUSED_EPI_PLAIN = 0, FUSED_EPI_RESID = 1, FUSED_EPI_RELU2 = 2, FUSED_EPI_ROPE = 3 };
 constexpr int kFusedMaxM = 4;
 
 struct ActSrc {
@@ -217,6 +224,15 @@ struct FusedDecode {
   float *mi;           // ReLU^2 form: [m][n/2]
   int8_t *codes_out;   // optional [m][k] codes of the input
   float *deq_out;      // optional [m]
+  // RoPE form (q|k|v rows: n_heads q heads, n_kv k heads, n_kv v heads of hd):
+  // y gets q and k rotated at pos[t] and v as is; k and v also go to the
+  // bfloat16 caches [n_slots][n_kv][tmax][hd] at (slot[t], pos[t]) when both
+  // are in range
+  const int64_t *slot, *pos;
+  double theta;
+  uint16_t *kc, *vc;
+  int64_t n_slots, tmax;
+  int n_heads, n_kv, hd;
 };
 
 // The head (head.hip): final norm to bfloat16, the bfloat16 lm_head, and the

@@ -7,6 +7,8 @@
 //   plain     y = fl32(fl32((float)acc * deq) * gamma(n))
 //   residual  out2 = fl32(res + y)                 (h = x + o, x' = h + down)
 //   ReLU^2    mi = fl32(fl32(max(g, 0)^2) * u)     (gate and up rows paired)
+//   RoPE      q and k rotated at the token's position, k and v into the
+//             bfloat16 KV cache (rows i and i + hd/2 of a head paired)
 // (nnterp "BitNet b1.58" page: "The projections quantize their inputs and
 // weights", "The block, in order", "The MLP gates with a squared ReLU").
 //
@@ -22,7 +24,10 @@
 // and the 8 lanes of a row are summed with DPP adds. KS waves split the
 // lines of a row; their partial sums are added in LDS in a fixed order.
 // In the ReLU^2 form, workgroup b owns gate rows [b R/2, (b + 1) R/2) and the
-// up rows I + the same range, so it can form its slice of mi itself.
+// up rows I + the same range, so it can form its slice of mi itself. In the
+// RoPE form a workgroup of the q and k heads owns R/2 rotated pairs of one
+// head (rows e and e + hd/2), so it rotates them itself; the angles (fp64, as
+// the standalone RoPE kernel takes them) are formed while the weights load.
 #include "act_prologue.h"
 
 namespace bl {
@@ -43,7 +48,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
   __shared__ float red_f[4];
   __shared__ double red_d[4];
   __shared__ int red_i[4];
-  __shared__ float ybuf[EPI == FUSED_EPI_RELU2 ? MT * R : 1];
+  __shared__ float ybuf[EPI == FUSED_EPI_RELU2 || EPI == FUSED_EPI_ROPE ? MT * R : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ks = wave % KS, rg = wave / KS;
@@ -52,9 +57,17 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
   const int N = a.n, K = a.src.k;
   const Epilogue ep = resolve_gamma(a.ep);
   int n;
+  // RoPE form: workgroups [0, rot_wgs) hold rotated pairs, hd / R per head
+  const int rot_wgs = EPI == FUSED_EPI_ROPE ? (a.n_heads + a.n_kv) * (a.hd / R) : 0;
+  const int rh = EPI == FUSED_EPI_ROPE && (int)blockIdx.x < rot_wgs ? blockIdx.x / (a.hd / R) : 0;
+  const int rj = EPI == FUSED_EPI_ROPE && (int)blockIdx.x < rot_wgs ? blockIdx.x - rh * (a.hd / R) : 0;
   if constexpr (EPI == FUSED_EPI_RELU2) {
     const int half = R / 2, inter = N / 2;
     n = r < half ? blockIdx.x * half + r : inter + blockIdx.x * half + (r - half);
+  } else if constexpr (EPI == FUSED_EPI_ROPE) {
+    const int half = R / 2;
+    n = (int)blockIdx.x < rot_wgs ? rh * a.hd + (r < half ? rj * half + r : a.hd / 2 + rj * half + (r - half))
+                                  : blockIdx.x * R + r;
   } else {
     n = blockIdx.x * R + r;
   }
@@ -80,6 +93,17 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
     w[i] = *reinterpret_cast<const v4i *>(use ? a.w + (int64_t)n * ldb + off : a.w);
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  // RoPE form: thread t (R/2) + i < MT (R/2) takes pair i of token t
+  float rc = 0.0f, rsn = 0.0f;
+  if constexpr (EPI == FUSED_EPI_ROPE) {
+    const int t = threadIdx.x / (R / 2), e = rj * (R / 2) + (int)threadIdx.x % (R / 2);
+    if ((int)blockIdx.x < rot_wgs && t < a.m && threadIdx.x < MT * (R / 2)) {
+      const double ang = (double)a.pos[t] * pow(a.theta, -(2.0 * e) / (double)a.hd);
+      rc = (float)cos(ang);
+      rsn = (float)sin(ang);
+    }
+  }
 
   // the codes of every token of the step, into LDS
   RowQuant q[MT];
@@ -148,9 +172,9 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
         const float yv = rescale(av, q[t].deq, g);
         const int64_t o = (int64_t)t * N + n;
         if (a.acc_out) a.acc_out[o] = av;
-        if (EPI == FUSED_EPI_PLAIN || a.y) a.y[o] = yv;
+        if (EPI == FUSED_EPI_PLAIN || (EPI != FUSED_EPI_ROPE && a.y)) a.y[o] = yv;
         if constexpr (EPI == FUSED_EPI_RESID) a.out2[o] = __fadd_rn(a.res[o], yv);
-        if constexpr (EPI == FUSED_EPI_RELU2) ybuf[t * R + r] = yv;
+        if constexpr (EPI == FUSED_EPI_RELU2 || EPI == FUSED_EPI_ROPE) ybuf[t * R + r] = yv;
       }
     }
   }
@@ -167,6 +191,41 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
       }
     }
   }
+  if constexpr (EPI == FUSED_EPI_ROPE) {
+    constexpr int half = R / 2;
+    __syncthreads();
+    const int hd = a.hd, tid = threadIdx.x;
+    if ((int)blockIdx.x < rot_wgs) {
+      const int t = tid / half, i = tid - t * half;
+      if (tid < MT * half && t < a.m) {
+        const float x0 = ybuf[t * R + i], x1 = ybuf[t * R + half + i];
+        const float ra = __fsub_rn(__fmul_rn(x0, rc), __fmul_rn(x1, rsn));
+        const float rb = __fadd_rn(__fmul_rn(x1, rc), __fmul_rn(x0, rsn));
+        const int e = rj * half + i;
+        const int64_t row = (int64_t)t * N + (int64_t)rh * hd + e;
+        a.y[row] = ra;
+        a.y[row + hd / 2] = rb;
+        const int64_t sl = a.slot[t], p = a.pos[t];
+        if (rh >= a.n_heads && sl >= 0 && sl < a.n_slots && p >= 0 && p < a.tmax) {  // a key head
+          const int64_t dst = ((sl * a.n_kv + (rh - a.n_heads)) * a.tmax + p) * hd;
+          a.kc[dst + e] = (uint16_t)bf16_rne(ra);
+          a.kc[dst + e + hd / 2] = (uint16_t)bf16_rne(rb);
+        }
+      }
+    } else {
+      const int t = tid / R, i = tid - t * R;
+      if (tid < MT * R && t < a.m) {
+        const int nn = blockIdx.x * R + i;
+        const float yv = ybuf[t * R + i];
+        a.y[(int64_t)t * N + nn] = yv;
+        const int64_t sl = a.slot[t], p = a.pos[t];
+        if (sl >= 0 && sl < a.n_slots && p >= 0 && p < a.tmax) {
+          const int vr = nn - (a.n_heads + a.n_kv) * hd, g = vr / hd;
+          a.vc[((sl * a.n_kv + g) * a.tmax + p) * hd + (vr - g * hd)] = (uint16_t)bf16_rne(yv);
+        }
+      }
+    }
+  }
 }
 
 template <int MODE, int EPI, int MT>
@@ -180,7 +239,11 @@ hipError_t launch_mt(const FusedDecode &a, hipStream_t stream) {
   const int nv = a.src.k <= 4096 ? 4 : 8;
   if ((lines + ks - 1) / ks > 2 * nv / ks) return hipErrorInvalidValue;
   int grid;
-  if (EPI == FUSED_EPI_RELU2) {
+  if (EPI == FUSED_EPI_ROPE) {
+    // whole heads of hd rows, hd a multiple of R; every row in a workgroup
+    if (a.hd <= 0 || a.hd % R != 0 || a.n != (a.n_heads + 2 * a.n_kv) * a.hd || a.n_kv <= 0) return hipErrorInvalidValue;
+    grid = a.n / R;
+  } else if (EPI == FUSED_EPI_RELU2) {
     if (a.n % 2 != 0 || (a.n / 2) % (R / 2) != 0) return hipErrorInvalidValue;
     grid = (a.n / 2) / (R / 2);
   } else {
@@ -218,6 +281,8 @@ hipError_t launch_gemv_fused(int mode, int epi, const FusedDecode &a, hipStream_
     return launch_pair<BITLINEAR_ACT_RMSNORM, FUSED_EPI_RESID>(a, stream);
   if (mode == BITLINEAR_ACT_RMSNORM && epi == FUSED_EPI_RELU2)
     return launch_pair<BITLINEAR_ACT_RMSNORM, FUSED_EPI_RELU2>(a, stream);
+  if (mode == BITLINEAR_ACT_RMSNORM && epi == FUSED_EPI_ROPE)
+    return launch_pair<BITLINEAR_ACT_RMSNORM, FUSED_EPI_ROPE>(a, stream);
   if (mode == ACT_GQA_RMSNORM && epi == FUSED_EPI_RESID) return launch_pair<ACT_GQA_RMSNORM, FUSED_EPI_RESID>(a, stream);
   if (mode == BITLINEAR_ACT_ABSMAX && epi == FUSED_EPI_RELU2)
     return launch_pair<BITLINEAR_ACT_ABSMAX, FUSED_EPI_RELU2>(a, stream);

@@ -8,6 +8,8 @@ page's "The block, in order", attention taken for tokens that attend only to
 themselves; 30 layers at the 2B4T shapes (M = 1, and sampled tokens of M = 64;
 tokens are independent, so the oracle computes only the sampled rows).
 """
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -258,6 +260,57 @@ def _attn_bound_ok(got, ref, vmag, smag, hd, tmax):
     S = (tmax + 255) // 256
     factor = 2.0 ** -24 * (2 * (hd + 1) * np.repeat(smag, hd, axis=1) + 2 * (192 + S))
     return np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= factor * vmag
+
+
+# (hidden, intermediate, q heads, kv heads, layers, t_max, positions): the small layout above; a token whose
+# position is past t_max (zeros from attention, nothing appended); the 2B4T layout (20 q heads on 5 kv heads)
+ROPE_FUSED = [(512, 768, 4, 1, 2, 512, [0, 5, 300]), (512, 768, 4, 1, 2, 512, [511]),
+              (512, 768, 4, 1, 2, 512, [3, 512, 77, 0]), (2560, 6912, 20, 5, 1, 1024, [1023, 64])]
+
+
+@pytest.mark.parametrize("hdim,inter,nh,nkv,layers,tmax,positions", ROPE_FUSED)
+def test_decoder_cached_rope_fused(hdim, inter, nh, nkv, layers, tmax, positions):
+    """Without a q|k|v trace the fused decode form takes RoPE and the cache
+    append in the q|k|v projection's epilogue. Its output and both caches equal
+    those of the traced run bit for bit (that run rotates and appends in a
+    kernel of its own, and the test above checks its stages against the
+    oracle), with no trace and with an attention trace alone."""
+    hd, theta = 128, 5e5
+    m = len(positions)
+    note(f"block decoder cached, fused rope m={m} hidden={hdim}")
+    kvd = nkv * hd
+    Q = hdim + 2 * kvd
+    r = np.random.default_rng(60 + m)
+    slot = np.arange(m, dtype=np.int64)[::-1].copy()
+    pos = np.array(positions, dtype=np.int64)
+    x = synth.activations(seed(10, m, 5), m, hdim, 1)
+    layers_w, caches0 = [], []
+    for l in range(layers):
+        mt = _decoder_layer_mats(10, l, hdim, inter, kvd)
+        layers_w.append(_gpu_layer(mt, None))
+        caches0.append((oracle.round_bf16(r.normal(size=(m, nkv, tmax, hd)).astype(np.float32)),
+                        oracle.round_bf16(r.normal(size=(m, nkv, tmax, hd)).astype(np.float32))))
+
+    def run(trace):
+        lws = []
+        for lw, (kc, vc) in zip(layers_w, caches0):
+            c = copy.copy(lw)
+            c.k_cache, c.v_cache = gpu(kc), gpu(vc)
+            lws.append(c)
+        spec = bl.BlockSpec(bl.BLOCK_DECODER_CACHED, hdim, inter, lws, nh, nkv, hd, EPS, slot=gpu(slot),
+                            pos=gpu(pos), rope_theta=theta)
+        y = host(bl.block_forward(spec, gpu(x), trace=trace))
+        return y, [(host(c.k_cache), host(c.v_cache)) for c in lws]
+
+    y_ref, c_ref = run(_trace(layers, m, hdim, inter, Q))
+    att = torch.zeros((layers, m, hdim), dtype=torch.float32, device=DEV)
+    for trace in (None, {"attn": att}):
+        y, c = run(trace)
+        assert_equal(y, y_ref, "block output")
+        for l in range(layers):
+            assert_equal(c[l][0].view(np.uint16), c_ref[l][0].view(np.uint16), f"layer {l} key cache")
+            assert_equal(c[l][1].view(np.uint16), c_ref[l][1].view(np.uint16), f"layer {l} value cache")
+    assert host(att).any()
 
 
 @pytest.mark.parametrize("positions", [[0, 5, 300], [0, 1, 2, 100, 257, 511]])
