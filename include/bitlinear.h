@@ -210,8 +210,9 @@ size_t bitlinear_forward_relu2_glu_workspace_bytes(int64_t m, int64_t inter, int
 /* bitlinear_embed — x[t][:] = the table row of ids[t], widened to fp32 (exact).
  *   ids    device [m] int64; an id outside [0, vocab) gives a zero row.
  *   table  device [vocab][k] bfloat16.   x  device [m][k] fp32, written.
- * Errors: NULL pointers -> ERR_NULL; m < 0, vocab <= 0, k <= 0 -> ERR_SHAPE.
- * m == 0 is a no-op. */
+ *   k % 8 == 0, 0 < k <= 4096; table and x 16-byte aligned.
+ * Errors: NULL pointers -> ERR_NULL; m < 0, vocab <= 0, bad k -> ERR_SHAPE;
+ * misaligned table or x -> ERR_ALIGN. m == 0 is a no-op. */
 bitlinear_status bitlinear_embed(const int64_t *ids, int64_t m, const uint16_t *table, int64_t vocab, int64_t k,
                                  float *x, void *stream);
 

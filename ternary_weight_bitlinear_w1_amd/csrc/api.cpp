@@ -398,10 +398,11 @@ bitlinear_status bitlinear_embed(const int64_t *ids, int64_t m, const uint16_t *
                                  float *x, void *stream) {
   g_err.clear();
   if (m != 0 && (!ids || !table || !x)) return fail(BITLINEAR_ERR_NULL, "ids, table and x are required");
-  if (m < 0 || vocab <= 0 || k <= 0 || m > kMaxDim || vocab > kMaxDim || k > kMaxDim)
-    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, vocab = %lld, k = %lld", (long long)m, (long long)vocab,
-                (long long)k);
+  if (m < 0 || vocab <= 0 || !bl::lm_head_supported(k) || m > kMaxDim || vocab > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, vocab = %lld, k = %lld: need k %% 8 == 0, 0 < k <= 4096",
+                (long long)m, (long long)vocab, (long long)k);
   if (m == 0) return BITLINEAR_OK;
+  if (!aligned16(table) || !aligned16(x)) return fail(BITLINEAR_ERR_ALIGN, "table and x must be 16-byte aligned");
   BL_TRY(check_device());
   return launched(bl::launch_embed(ids, m, table, vocab, k, x, as_stream(stream)), "embedding gather");
 }

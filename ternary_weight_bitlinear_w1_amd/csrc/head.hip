@@ -36,14 +36,30 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return kept + ((dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) ? 1u : 0u);
 }
 
+constexpr int kNormPer = 512 * kHeadMaxChunks / kNormThreads;  // values per thread at the largest K
+
+// (every load of the row and the gain is issued before the sum)
 __global__ __launch_bounds__(kNormThreads) void final_norm_kernel(const float *__restrict__ x, int K,
                                                                   const float *__restrict__ gain, float eps,
                                                                   uint16_t *__restrict__ o) {
   __shared__ double red[kNormThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *xr = x + (int64_t)blockIdx.x * K;
+  float xv[kNormPer], gv[kNormPer];
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int k = tid + kNormThreads * i;
+    xv[i] = k < K ? xr[k] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int k = tid + kNormThreads * i;
+    gv[i] = gain && k < K ? gain[k] : 1.0f;
+  }
   double ss = 0.0;
-  for (int k = tid; k < K; k += kNormThreads) ss += (double)xr[k] * (double)xr[k];
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i)
+    if (tid + kNormThreads * i < K) ss += (double)xv[i] * (double)xv[i];
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s, 64);
   if (lane == 0) red[wave] = ss;
@@ -53,10 +69,14 @@ __global__ __launch_bounds__(kNormThreads) void final_norm_kernel(const float *_
   for (int w = 1; w < kNormThreads / 64; ++w) tot += red[w];
   const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
   uint16_t *orow = o + (int64_t)blockIdx.x * K;
-  for (int k = tid; k < K; k += kNormThreads) {
-    const float v = __fmul_rn(xr[k], r);
-    const float g = gain ? __fmul_rn(gain[k], v) : v;
-    orow[k] = (uint16_t)bf16_bits(g);
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int k = tid + kNormThreads * i;
+    if (k < K) {
+      const float v = __fmul_rn(xv[i], r);
+      const float g = gain ? __fmul_rn(gv[i], v) : v;
+      orow[k] = (uint16_t)bf16_bits(g);
+    }
   }
 }
 
@@ -121,14 +141,34 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict
 }
 
 // x[t] = the table row of token ids[t], widened to fp32 (exact); an id outside
-// [0, vocab) gives a zero row
+// [0, vocab) gives a zero row. Each thread moves 8 values (16 bytes) per piece,
+// all pieces loaded before any is stored.
+constexpr int kEmbedPieces = 512 * kHeadMaxChunks / (256 * 8);
 __global__ __launch_bounds__(256) void embed_kernel(const int64_t *__restrict__ ids, const uint16_t *__restrict__ table,
                                                     int64_t vocab, int K, float *__restrict__ x) {
   const int64_t id = ids[blockIdx.x];
   const bool ok = id >= 0 && id < vocab;
   float *xr = x + (int64_t)blockIdx.x * K;
-  for (int k = threadIdx.x; k < K; k += 256)
-    xr[k] = ok ? __uint_as_float((uint32_t)table[id * K + k] << 16) : 0.0f;
+  v4i w[kEmbedPieces];
+#pragma unroll
+  for (int i = 0; i < kEmbedPieces; ++i) {
+    const int k = 8 * (threadIdx.x + 256 * i);
+    w[i] = ok && k < K ? *reinterpret_cast<const v4i *>(table + id * K + k) : v4i{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < kEmbedPieces; ++i) {
+    const int k = 8 * (threadIdx.x + 256 * i);
+    if (k < K) {
+      const uint32_t w0 = (uint32_t)w[i][0], w1 = (uint32_t)w[i][1];
+      const uint32_t w2 = (uint32_t)w[i][2], w3 = (uint32_t)w[i][3];
+      *reinterpret_cast<float4 *>(xr + k) =
+          make_float4(__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u), __uint_as_float(w1 << 16),
+                      __uint_as_float(w1 & 0xFFFF0000u));
+      *reinterpret_cast<float4 *>(xr + k + 4) =
+          make_float4(__uint_as_float(w2 << 16), __uint_as_float(w2 & 0xFFFF0000u), __uint_as_float(w3 << 16),
+                      __uint_as_float(w3 & 0xFFFF0000u));
+    }
+  }
 }
 
 template <int MT>

@@ -196,6 +196,9 @@ def test_embed_and_lm_head_validation():
     assert L.bitlinear_embed(None, 4, A, 100, 64, A, None) == bl.ERR_NULL
     assert L.bitlinear_embed(A, -1, A, 100, 64, A, None) == bl.ERR_SHAPE
     assert L.bitlinear_embed(A, 4, A, 0, 64, A, None) == bl.ERR_SHAPE
+    assert L.bitlinear_embed(A, 4, A, 100, 60, A, None) == bl.ERR_SHAPE     # k % 8 != 0
+    assert L.bitlinear_embed(A, 4, A, 100, 4104, A, None) == bl.ERR_SHAPE   # k > 4096
+    assert L.bitlinear_embed(A, 4, MIS, 100, 64, A, None) == bl.ERR_ALIGN
     assert L.bitlinear_embed(None, 0, None, 100, 64, None, None) == bl.OK
 
     def head(x=A, m=4, k=2560, gain=None, eps=1e-5, w=A, n=1000, y=A, normed=None, ws=A, wsb=1 << 20):
