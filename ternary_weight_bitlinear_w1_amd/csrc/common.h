@@ -75,6 +75,12 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {  // the two 32-bit halves
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)u), hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
 template <typename T>
@@ -115,12 +121,19 @@ __device__ __forceinline__ float rows_max(float v) {
 // Wave64 results in every lane.
 __device__ __forceinline__ float wave_max(float v) { return rows_max(row16_max(v)); }
 __device__ __forceinline__ int wave_sum(int v) { return rows_sum(row16_sum(v)); }
-// fp64: xor butterflies (DPP moves 32 bits), the order fixed
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// fp64: the same steps, moving the two 32-bit halves
+__device__ __forceinline__ double rows_sum(double v) {
+  auto join = [](uint32_t lo, uint32_t hi) { return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)); };
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  const auto al = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto ah = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  v = join(al[0], ah[0]) + join(al[1], ah[1]);
+  u = (uint64_t)__double_as_longlong(v);
+  const auto bl_ = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto bh = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  return join(bl_[0], bh[0]) + join(bl_[1], bh[1]);
 }
+__device__ __forceinline__ double wave_sum(double v) { return rows_sum(row16_sum(v)); }
 
 // ---------------------------------------------------------------- launchers
 // Implemented next to their kernels; all enqueue on `stream` and return the
