@@ -138,13 +138,14 @@ __device__ __forceinline__ float4 gain_of(const RawIn &v, float4 p) {
   return p;
 }
 
+// round(v pre s) half to even. With s = fl(127 / fl(a pre)) and |v| <= a, the
+// product stays below 127.5 in magnitude (two roundings of relative size
+// 2^-24), so the code lies in [-127, 127] without a clamp; a NaN product
+// converts to 0. pre is 1 except on rows whose max is below 2^-64.
 __device__ __forceinline__ int code_of(float v, float pre, float s) {
-  float p = __fmul_rn(__fmul_rn(v, pre), s);
-  float r = __builtin_rintf(p);
-  r = r > 127.0f ? 127.0f : r;
-  r = r < -127.0f ? -127.0f : r;
-  return (int)r;
+  return (int)__builtin_rintf(__fmul_rn(__fmul_rn(v, pre), s));
 }
+__device__ __forceinline__ int code_of(float v, float s) { return (int)__builtin_rintf(__fmul_rn(v, s)); }
 
 struct RowQuant {
   float deq;   // dequantization factor of the row's codes
@@ -267,10 +268,12 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
   auto visit1 = [&](int f, const RawIn &raw) -> float4 {
     const float4 p = pre_of<MODE>(s, r, f, raw, true);
     if (kRms) {
-      ss += (double)p.x * (double)p.x;
-      ss += (double)p.y * (double)p.y;
-      ss += (double)p.z * (double)p.z;
-      ss += (double)p.w * (double)p.w;
+      // the square of an fp32 value is exact in fp64, so the fused form adds
+      // the same product as a multiply then an add would
+      ss = __fma_rn((double)p.x, (double)p.x, ss);
+      ss = __fma_rn((double)p.y, (double)p.y, ss);
+      ss = __fma_rn((double)p.z, (double)p.z, ss);
+      ss = __fma_rn((double)p.w, (double)p.w, ss);
     }
     const float4 v = gain_of<MODE>(raw, p);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
@@ -316,10 +319,24 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
       words[f] = (q0 & 0xff) | ((q1 & 0xff) << 8) | ((q2 & 0xff) << 16) | ((int)((unsigned)(q3 & 0xff) << 24));
     };
     if constexpr (NV > 0) {
+      if (pre == 1.0f) {  // (v 1 = v exactly: one multiply per element)
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int f = tid + j * kQuantThreads;
-        if (f < nf) emit(f, cache[j]);
+        for (int j = 0; j < NV; ++j) {
+          const int f = tid + j * kQuantThreads;
+          if (f < nf) {
+            const float4 v = cache[j];
+            const int q0 = code_of(v.x, sc), q1 = code_of(v.y, sc), q2 = code_of(v.z, sc), q3 = code_of(v.w, sc);
+            rs += q0 + q1 + q2 + q3;
+            words[f] =
+                (q0 & 0xff) | ((q1 & 0xff) << 8) | ((q2 & 0xff) << 16) | ((int)((unsigned)(q3 & 0xff) << 24));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int f = tid + j * kQuantThreads;
+          if (f < nf) emit(f, cache[j]);
+        }
       }
     } else {
       for (int f = tid; f < nf; f += kQuantThreads) {

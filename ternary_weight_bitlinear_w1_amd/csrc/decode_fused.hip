@@ -233,7 +233,10 @@ hipError_t launch_mt(const FusedDecode &a, hipStream_t stream) {
   // split K over the waves of a workgroup until the workgroups cover the CUs
   const int rows = EPI == FUSED_EPI_RELU2 ? a.n / 2 : a.n;  // output rows that set the grid
   const int per32 = EPI == FUSED_EPI_RELU2 ? rows / 16 : rows / 32;
-  const int ks = per32 >= 256 ? 1 : (2 * per32 >= 256 ? 2 : 4);
+  // (one token: at most about one workgroup per CU, since every workgroup
+  // quantizes the whole input row; more tokens: at least 256 workgroups)
+  const int min_wgs = MT == 1 ? 128 : 256;
+  const int ks = per32 >= min_wgs ? 1 : (2 * per32 >= min_wgs ? 2 : 4);
   const int R = 32 / ks;
   const int lines = ((a.src.k >> 2) + 127) >> 7;
   const int nv = a.src.k <= 4096 ? 4 : 8;
