@@ -352,7 +352,26 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
                                    "packed_bytes": nbytes, "ring_copies": copies}
             log(f"decode {name} m={m}: {b2b_us:.2f} us/launch back-to-back, {gbs:.0f} GB/s "
                 f"(one launch between events: {us:.2f} us)")
-        del ring
+        # reference: a device copy of the same bytes (one ring copy per launch,
+        # back to back; it reads them once and writes them once) -- the cost of
+        # one launch that moves these bytes on this GPU
+        dst = torch.empty_like(ring[0])
+        for i in range(20):
+            dst.copy_(ring[i % copies])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            dst.copy_(ring[i % copies])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        floor_us = e0.elapsed_time(e1) / reps * 1e3
+        res[f"{name}_copy_reference"] = {"us": round(floor_us, 3),
+                                         "gbs_read": round(nbytes / (floor_us * 1e-6) / 1e9, 1),
+                                         "what": "device copy of the same packed bytes, one ring copy per launch"}
+        log(f"decode {name}: a device copy of the same {nbytes} bytes takes {floor_us:.2f} us/launch "
+            f"({nbytes / (floor_us * 1e-6) / 1e9:.0f} GB/s read)")
+        del ring, dst
         torch.cuda.empty_cache()
         # the same projection from the base-3 storage (five codes per byte), m = 1 and 4
         w3 = bl.pack_base3(packed, k)
