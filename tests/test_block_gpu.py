@@ -263,9 +263,12 @@ def _attn_bound_ok(got, ref, vmag, smag, hd, tmax):
 
 
 # (hidden, intermediate, q heads, kv heads, layers, t_max, positions): the small layout above; a token whose
-# position is past t_max (zeros from attention, nothing appended); the 2B4T layout (20 q heads on 5 kv heads)
+# position is past t_max (zeros from attention, nothing appended); groups of 1 and 8 q heads per kv head; the
+# 2B4T layout (20 q heads on 5 kv heads) with one token (16 rows per workgroup) and two (8 rows)
 ROPE_FUSED = [(512, 768, 4, 1, 2, 512, [0, 5, 300]), (512, 768, 4, 1, 2, 512, [511]),
-              (512, 768, 4, 1, 2, 512, [3, 512, 77, 0]), (2560, 6912, 20, 5, 1, 1024, [1023, 64])]
+              (512, 768, 4, 1, 2, 512, [3, 512, 77, 0]), (512, 768, 4, 4, 1, 256, [100, 5]),
+              (1024, 768, 8, 1, 1, 256, [255, 0, 31]), (2560, 6912, 20, 5, 1, 512, [511]),
+              (2560, 6912, 20, 5, 1, 1024, [1023, 64])]
 
 
 @pytest.mark.parametrize("hdim,inter,nh,nkv,layers,tmax,positions", ROPE_FUSED)
