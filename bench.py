@@ -48,6 +48,7 @@ VOCAB = 128256
 ROPE_THETA = 5e5  # the RoPE base of the released 2B4T model (the pages name RoPE only)
 BASE_SEED = 1234
 RING_BYTES = 600 * 2 ** 20  # > 2 x the 256 MB last-level cache
+TOKEN_STEP_BATCHES = (1, 4)  # sequences per whole-model decode step
 
 
 def parse():
@@ -609,7 +610,7 @@ def bench_token_step(torch, bl, dev, layers, table, steps, warmup):
     stream = torch.cuda.current_stream(dev)
     res = {}
     packed = sum(l.qkv.numel() + l.o.numel() + l.gate_up.numel() + l.down.numel() for l in layers)
-    for B in (1, 4):
+    for B in TOKEN_STEP_BATCHES:
         gen = torch.Generator(device=dev)
         gen.manual_seed(BASE_SEED + B)
         caches = []

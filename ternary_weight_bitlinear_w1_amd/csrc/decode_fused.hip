@@ -1,4 +1,4 @@
-// Decode projection that quantizes its own input (m <= 4 tokens).
+// Decode projection that quantizes its own input (one or two tokens).
 //
 // One launch computes, for the tokens of a decode step, the per-token int8
 // codes of the projection's input (with the block's prologue: RMSNorm gain,
@@ -267,7 +267,7 @@ hipError_t launch_mt(const FusedDecode &a, hipStream_t stream) {
 
 template <int MODE, int EPI>
 hipError_t launch_pair(const FusedDecode &a, hipStream_t stream) {
-  return a.m == 1 ? launch_mt<MODE, EPI, 1>(a, stream) : launch_mt<MODE, EPI, 4>(a, stream);
+  return a.m == 1 ? launch_mt<MODE, EPI, 1>(a, stream) : launch_mt<MODE, EPI, kFusedMaxM>(a, stream);
 }
 
 }  // namespace

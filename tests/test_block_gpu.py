@@ -160,8 +160,8 @@ def test_decoder_stack_small(m, layers):
 @pytest.mark.parametrize("m,layers", [(1, 3), (2, 2), (3, 2), (4, 2), (5, 2)])
 def test_decoder_stack_fused_sizes(m, layers):
     """Dims that the one-launch-per-projection decode form takes (every
-    projection input a multiple of 64; m <= 4), random gains: H=128 (8 heads
-    of 16), 2 kv heads, I=192. m = 5 takes the unfused chain."""
+    projection input a multiple of 64; m <= 2), random gains: H=128 (8 heads
+    of 16), 2 kv heads, I=192. m = 3 to 5 take the quantize -> contract chain."""
     hdim, inter, nh, nkv, hd = 128, 192, 8, 2, 16
     note(f"block decoder fused sizes m={m} layers={layers}")
     kvd = nkv * hd
@@ -265,9 +265,9 @@ def _attn_bound_ok(got, ref, vmag, smag, hd, tmax):
 # (hidden, intermediate, q heads, kv heads, layers, t_max, positions): the small layout above; a token whose
 # position is past t_max (zeros from attention, nothing appended); groups of 1 and 8 q heads per kv head; the
 # 2B4T layout (20 q heads on 5 kv heads) with one token (16 rows per workgroup) and two (8 rows)
-ROPE_FUSED = [(512, 768, 4, 1, 2, 512, [0, 5, 300]), (512, 768, 4, 1, 2, 512, [511]),
-              (512, 768, 4, 1, 2, 512, [3, 512, 77, 0]), (512, 768, 4, 4, 1, 256, [100, 5]),
-              (1024, 768, 8, 1, 1, 256, [255, 0, 31]), (2560, 6912, 20, 5, 1, 512, [511]),
+ROPE_FUSED = [(512, 768, 4, 1, 2, 512, [5, 300]), (512, 768, 4, 1, 2, 512, [511]),
+              (512, 768, 4, 1, 2, 512, [512, 77]), (512, 768, 4, 4, 1, 256, [100, 5]),
+              (1024, 768, 8, 1, 1, 256, [255, 31]), (2560, 6912, 20, 5, 1, 512, [511]),
               (2560, 6912, 20, 5, 1, 1024, [1023, 64])]
 
 
@@ -316,11 +316,11 @@ def test_decoder_cached_rope_fused(hdim, inter, nh, nkv, layers, tmax, positions
     assert host(att).any()
 
 
-@pytest.mark.parametrize("positions", [[0, 5, 300], [0, 1, 2, 100, 257, 511]])
+@pytest.mark.parametrize("positions", [[5, 300], [0, 1, 2, 100, 257, 511], [0, 7, 300]])
 def test_decoder_cached_teacher_forced(positions):
     """Two decoder layers with RoPE, KV caches and causal attention (H = 512: 4
-    query heads of 128 on 1 key/value head; I = 768). Three tokens take the
-    fused decode form, six the quantize -> contract chain. Every stage is
+    query heads of 128 on 1 key/value head; I = 768). Two tokens take the
+    fused decode form, three and six the quantize -> contract chain. Every stage is
     checked against the oracle fed the GPU's own input to that stage: ints
     bit-exact, the projections' fp32 outputs bit-exact, the rotated keys within
     one bfloat16 step, the attention within its fp32 bound."""
