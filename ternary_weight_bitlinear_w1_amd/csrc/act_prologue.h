@@ -1,8 +1,10 @@
-// Per-token activation quantization of one row by a 256-thread workgroup:
-// the prologue transforms of a BitNet b1.58 block, the max |v|, the fp64 sum
-// of squares, the int8 codes and their row sum. Shared by the standalone
-// quantization kernel and by the decode contraction that quantizes its own
-// input, so that both produce the same codes and the same deq bit for bit.
+// Per-token activation quantization of one row by a workgroup of TH threads
+// (256 unless stated): the prologue transforms of a BitNet b1.58 block, the
+// max |v|, the fp64 sum of squares, the int8 codes and their row sum. Shared
+// by the standalone quantization kernel and by the decode contraction that
+// quantizes its own input. Codes and row sums do not depend on TH; deq does
+// only through the order of the fp64 sum of squares, and at equal TH both
+// produce the same deq bit for bit.
 //
 // Codes: round(v * 127 / max|v|), half to even, in [-127, 127]; deq = max|v| / 127
 // (nnterp "BitNet b1.58" page, "The projections quantize their inputs and
@@ -176,14 +178,14 @@ __device__ __forceinline__ int part_col(const Src &s, int f, int p) {
 // plane by plane, two planes at a time for every slot of the thread, so a row
 // takes about S / 2 memory round trips rather than S per slot. Integer sums are
 // exact, so the order of the planes does not matter.
-template <int MODE, int NV>
+template <int MODE, int NV, int TH>
 __device__ __forceinline__ void row_load_part(const Src &s, int64_t r, RowStage<NV> &st) {
   constexpr int NP = MODE == BITLINEAR_ACT_RELU2_RMSNORM ? 2 : 1;
   const int nf = s.k >> 2;
   int col[NV][NP];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    int f = threadIdx.x + j * kQuantThreads;
+    int f = threadIdx.x + j * TH;
     f = f < nf ? f : 0;
 #pragma unroll
     for (int p = 0; p < NP; ++p) col[j][p] = part_col<MODE>(s, f, p);
@@ -232,18 +234,18 @@ __device__ __forceinline__ void row_load_part(const Src &s, int64_t r, RowStage<
   }
 }
 
-template <int MODE, int NV, bool PART = false>
+template <int MODE, int NV, bool PART = false, int TH = kQuantThreads>
 __device__ __forceinline__ void row_load(const Src &s, int64_t r, RowStage<NV> &st) {
   static_assert(NV > 0, "register-resident rows only");
   if constexpr (PART) {
-    row_load_part<MODE, NV>(s, r, st);
+    row_load_part<MODE, NV, TH>(s, r, st);
   } else {
     const int nf = s.k >> 2;
     // every lane issues the same NV loads (past the row end it reloads element
     // 0, unused), so the number of loads in flight is known where they are used
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int f = threadIdx.x + j * kQuantThreads;
+      const int f = threadIdx.x + j * TH;
       st.in[j] = raw_load<MODE, PART>(s, r, f < nf ? f : 0);
     }
   }
@@ -254,7 +256,7 @@ __device__ __forceinline__ void row_load(const Src &s, int64_t r, RowStage<NV> &
 // to global memory. The LDS arrays hold the cross-wave partials. Every thread
 // returns the same deq and row sum; words in LDS are visible to the whole
 // workgroup on return. NV = 0 streams the row twice instead of holding it.
-template <int MODE, int NV, bool PART = false>
+template <int MODE, int NV, bool PART = false, int TH = kQuantThreads>
 __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float eps, const RowStage<(NV > 0 ? NV : 1)> &st,
                                                int *words, float *red_f, double *red_d, int *red_i) {
   constexpr bool kRms = MODE != BITLINEAR_ACT_ABSMAX;
@@ -282,11 +284,11 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
   if constexpr (NV > 0) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int f = tid + j * kQuantThreads;
+      const int f = tid + j * TH;
       if (f < nf) cache[j] = visit1(f, st.in[j]);
     }
   } else {
-    for (int f = tid; f < nf; f += kQuantThreads) (void)visit1(f, raw_load<MODE, PART>(s, r, f));
+    for (int f = tid; f < nf; f += TH) (void)visit1(f, raw_load<MODE, PART>(s, r, f));
   }
   amax = wave_max(amax);
   if (kRms) ss = wave_sum(ss);
@@ -298,7 +300,7 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
   float a = red_f[0];
   double sum_sq = red_d[0];
 #pragma unroll
-  for (int w = 1; w < kQuantThreads / 64; ++w) {
+  for (int w = 1; w < TH / 64; ++w) {
     a = fmaxf(a, red_f[w]);
     sum_sq += red_d[w];
   }
@@ -306,7 +308,7 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
   // ---- pass 2: codes
   int rs = 0;
   if (a == 0.0f) {
-    for (int f = tid; f < nf; f += kQuantThreads) words[f] = 0;
+    for (int f = tid; f < nf; f += TH) words[f] = 0;
   } else {
     // rows whose max is below 2^-64 are scaled by 2^64 first (exact), which
     // keeps 127 / a finite and changes no code the unscaled steps reach
@@ -322,7 +324,7 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
       if (pre == 1.0f) {  // (v 1 = v exactly: one multiply per element)
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          const int f = tid + j * kQuantThreads;
+          const int f = tid + j * TH;
           if (f < nf) {
             const float4 v = cache[j];
             const int q0 = code_of(v.x, sc), q1 = code_of(v.y, sc), q2 = code_of(v.z, sc), q3 = code_of(v.w, sc);
@@ -334,12 +336,12 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
       } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          const int f = tid + j * kQuantThreads;
+          const int f = tid + j * TH;
           if (f < nf) emit(f, cache[j]);
         }
       }
     } else {
-      for (int f = tid; f < nf; f += kQuantThreads) {
+      for (int f = tid; f < nf; f += TH) {
         const RawIn raw = raw_load<MODE, PART>(s, r, f);
         emit(f, gain_of<MODE>(raw, pre_of<MODE>(s, r, f, raw, false)));
       }
@@ -351,7 +353,7 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
   RowQuant out;
   out.rowsum = 0;
 #pragma unroll
-  for (int w = 0; w < kQuantThreads / 64; ++w) out.rowsum += red_i[w];
+  for (int w = 0; w < TH / 64; ++w) out.rowsum += red_i[w];
   out.deq = 0.0f;
   if (a != 0.0f) {
     if (kRms) {
@@ -365,12 +367,12 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
   return out;
 }
 
-template <int MODE, int NV, bool PART = false>
+template <int MODE, int NV, bool PART = false, int TH = kQuantThreads>
 __device__ __forceinline__ RowQuant quant_row(const Src &s, int64_t r, float eps, int *words, float *red_f,
                                               double *red_d, int *red_i) {
   RowStage<(NV > 0 ? NV : 1)> st;
-  if constexpr (NV > 0) row_load<MODE, NV, PART>(s, r, st);
-  return row_finish<MODE, NV, PART>(s, r, eps, st, words, red_f, red_d, red_i);
+  if constexpr (NV > 0) row_load<MODE, NV, PART, TH>(s, r, st);
+  return row_finish<MODE, NV, PART, TH>(s, r, eps, st, words, red_f, red_d, red_i);
 }
 
 }  // namespace bl

@@ -13,9 +13,9 @@
 // weights", "The block, in order", "The MLP gates with a squared ReLU").
 //
 // Each workgroup re-derives the codes of the whole input row with quant_row
-// (act_prologue.h), the same arithmetic as the standalone quantization kernel,
-// so codes and deq equal that kernel's bit for bit; the input is a few KB read
-// from L2, while the weights, issued first, stream from HBM.
+// (act_prologue.h), the same arithmetic as the standalone quantization kernel
+// at 256 threads, so codes and deq equal that kernel's bit for bit; the input
+// is a few KB read from L2, while the weights, issued first, stream from HBM.
 //
 // Contraction as the one-token kernel of gemv_decode.hip: 8 lanes share one
 // weight row and read 16-byte pieces of its 128-byte lines (a wave reads 8

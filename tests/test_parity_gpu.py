@@ -85,8 +85,9 @@ def test_validate_packed_counts_invalid_fields():
 
 
 # ------------------------------------------------------------------------------ activations
+# (17 to 128 rows take 1024-thread workgroups; (100, 9216) gives them 3 float4 per thread)
 ACT_CASES = [(128, 256, 4), (1, 2560, 26), (4, 2560, 26), (16, 6912, 69), (130, 48, 0), (3, 16, 0),
-             (5, 9216, 3), (1024, 512, 0), (64, 2560, 0)]
+             (5, 9216, 3), (1024, 512, 0), (64, 2560, 0), (17, 6912, 69), (100, 9216, 3)]
 
 
 def _edge_rows(x):
@@ -126,7 +127,8 @@ def test_quantize_acts_rmsnorm(m, k, with_gain):
     assert_equal(host(rowsum), qo.astype(np.int64).sum(axis=1).astype(np.int32), "row sums")
 
 
-@pytest.mark.parametrize("m,inter,with_gain", [(1024, 2048, False), (1, 6912, False), (16, 6912, True), (5, 48, True)])
+@pytest.mark.parametrize("m,inter,with_gain", [(1024, 2048, False), (1, 6912, False), (16, 6912, True), (5, 48, True),
+                                               (40, 6912, True)])
 def test_quantize_acts_relu2(m, inter, with_gain):
     note(f"quantize_acts relu2 m={m} I={inter}")
     gu = synth.activations(seed(4, m, inter), m, 2 * inter)
