@@ -868,6 +868,26 @@ struct Chain {
     *out = o;
     return BITLINEAR_OK;
   }
+  // the cached decoder's q|k|v projection (2 to 16 tokens) with RoPE on q and
+  // k and the keys and values appended to layer L's caches in its epilogue
+  bitlinear_status proj_rope(const bitlinear_block *blk, const bitlinear_layer &L, int64_t k, int64_t n,
+                             const int64_t *seg, float *y, int32_t *acc) {
+    bl::Epilogue ep;
+    BL_TRY(check_segments(L.qkv_gamma, seg, 3, n, &ep));
+    bl::DecodeRope r;
+    r.slot = blk->slot;
+    r.pos = blk->pos;
+    r.theta = blk->rope_theta;
+    r.kc = L.k_cache;
+    r.vc = L.v_cache;
+    r.n_slots = blk->n_slots;
+    r.tmax = blk->t_max;
+    r.n_heads = blk->n_heads;
+    r.n_kv = blk->n_kv_heads;
+    r.hd = blk->head_dim;
+    return launched(bl::launch_gemv_decode_rope(b.codes, L.qkv, deq(), rowsum(), m, k, ep, y, acc, r, s),
+                    "q|k|v projection with RoPE");
+  }
   // gate|up -> ReLU^2 -> ffn_sub_norm quantization (codes of the down input)
   bitlinear_status ffn_input(int64_t H, int64_t I, const bitlinear_layer &L, float *tr_gate_up,
                              int32_t *tr_acc_gate_up) {
@@ -932,12 +952,27 @@ bitlinear_status block_forward_chain(const bitlinear_block *blk, const float *x,
     BL_TRY(copy_to(at(tr.codes_in, oH), b.codes, (size_t)(m * H), s));
     BL_TRY(copy_to(at(tr.deq, 4 * m * l), c.deq(), (size_t)m * 4, s));
     ProjOut qkv;
-    BL_TRY(c.proj(H, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, b.qkv, at(tr.acc_qkv, oQ),
-                  !tr.qkv && !tr.acc_qkv && !cached, &qkv));
-    BL_TRY(copy_to(at(tr.qkv, oQ), b.qkv, (size_t)(m * Q) * 4, s));
+    // the cached decoder at 2 to 16 tokens without a q|k|v trace takes RoPE and
+    // the cache append in the projection's epilogue
+    const bool rope_fused =
+        cached && !tr.qkv && bl::gemv_decode_rope_supported(m, H, blk->n_heads, blk->n_kv_heads, hd);
+    if (rope_fused) {
+      BL_TRY(c.proj_rope(blk, L, H, Q, qkv_seg, b.qkv, at(tr.acc_qkv, oQ)));
+    } else {
+      BL_TRY(c.proj(H, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, b.qkv, at(tr.acc_qkv, oQ),
+                    !tr.qkv && !tr.acc_qkv && !cached, &qkv));
+      BL_TRY(copy_to(at(tr.qkv, oQ), b.qkv, (size_t)(m * Q) * 4, s));
+    }
     if (cached) {
       // RoPE, cache append, attention -> attn_sub_norm -> o_proj
-      BL_TRY(cached_attention(blk, L, m, b.qkv, b, at(tr.attn, oH), s));
+      if (rope_fused) {
+        BL_TRY(launched(bl::launch_attention(b.qkv, m, Q, blk->n_heads, blk->n_kv_heads, hd, L.k_cache, L.v_cache,
+                                             blk->n_slots, blk->t_max, blk->slot, blk->pos, b.att, H, b.attn_ws, s),
+                        "attention"));
+        BL_TRY(copy_to(at(tr.attn, oH), b.att, (size_t)(m * H) * 4, s));
+      } else {
+        BL_TRY(cached_attention(blk, L, m, b.qkv, b, at(tr.attn, oH), s));
+      }
       BL_TRY(c.quant(BITLINEAR_ACT_RMSNORM, act_src(b.att, H, H, L.attn_sub_norm_gain)));
     } else {
       // self-only attention output -> attn_sub_norm -> o_proj

@@ -190,6 +190,19 @@ hipError_t launch_splitk_finish(const int32_t *part, int splits, const float *de
 bool gemm_glu_supported(int64_t m, int64_t inter, int64_t k);
 hipError_t launch_gemm_glu(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,
                            int64_t m, int64_t inter, int64_t k, const Epilogue &ep, float *y, hipStream_t stream);
+// RoPE and the cache append in a decode projection's epilogue (the cached
+// decoder's q|k|v rows: n_heads q heads, n_kv k heads, n_kv v heads of hd)
+struct DecodeRope {
+  const int64_t *slot = nullptr, *pos = nullptr;
+  double theta = 0.0;
+  uint16_t *kc = nullptr, *vc = nullptr;
+  int64_t n_slots = 0, tmax = 0;
+  int n_heads = 0, n_kv = 0, hd = 0;
+};
+bool gemv_decode_rope_supported(int64_t m, int64_t k, int n_heads, int n_kv, int hd);
+hipError_t launch_gemv_decode_rope(const int8_t *codes, const uint8_t *packed, const float *deq,
+                                   const int32_t *rowsum, int64_t m, int64_t k, const Epilogue &ep, float *y,
+                                   int32_t *acc_out, const DecodeRope &rope, hipStream_t stream);
 hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const float *deq,
                               const int32_t *rowsum, int64_t m, int64_t n, int64_t k, const Epilogue &ep,
                               float *y, int32_t *acc_out, hipStream_t stream);

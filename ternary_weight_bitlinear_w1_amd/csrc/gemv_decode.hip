@@ -58,17 +58,34 @@ __device__ __forceinline__ v4i unpack16(uint32_t p) {
 // [S w / NW, S (w + 1) / NW) (at most SPW of them) and issues every load of its
 // slice before its first MFMA, so a wave waits for memory once, not once per
 // superstep.
-template <int RT, int NW, int SPW>
+//
+// ROPE form (RT = 2, the cached decoder's q|k|v projection): a workgroup of the
+// q and k heads owns rows e (tile 0) and e + hd/2 (tile 1) of one head for 16
+// consecutive e, so it rotates each pair itself, with the angles formed in fp64
+// while the weights load (the arithmetic of rope_append_kernel), and writes the
+// keys to the bfloat16 cache; workgroups of the value heads append the values.
+template <int RT, int NW, int SPW, bool ROPE = false>
 __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__restrict__ A,
                                                               const uint8_t *__restrict__ B,
                                                               const float *__restrict__ deq,
                                                               const int32_t *__restrict__ rowsum, int M, int N, int K,
                                                               Epilogue ep_in, float *__restrict__ Y,
-                                                              int32_t *__restrict__ acc_out) {
+                                                              int32_t *__restrict__ acc_out, DecodeRope rope) {
+  static_assert(!ROPE || RT == 2, "rotated pairs take the two row tiles");
   const Epilogue ep = resolve_gamma(ep_in);
   __shared__ int red[NW][RT][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16 * RT;
+  // ROPE form: workgroups [0, rot_wgs) hold rotated pairs, hd / 32 per head
+  const int rot_wgs = ROPE ? (rope.n_heads + rope.n_kv) * (rope.hd / 32) : 0;
+  const bool rotated = ROPE && (int)blockIdx.x < rot_wgs;
+  const int rh = rotated ? (int)blockIdx.x / (rope.hd / 32) : 0;
+  const int rj = rotated ? (int)blockIdx.x - rh * (rope.hd / 32) : 0;
+  // output row of row tile rt, tile row rr
+  auto row_of = [&](int rt, int rr) -> int {
+    if (rotated) return rh * rope.hd + rt * (rope.hd / 2) + 16 * rj + rr;
+    return n0 + rt * 16 + rr;
+  };
   const int G = K >> 4;
   const int S = (G + 15) >> 4;
   const int s_lo = S * wave / NW, cnt = S * (wave + 1) / NW - s_lo;
@@ -98,7 +115,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
     const int g0 = (s_lo + i) * 16 + 4 * kb;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int n = n0 + rt * 16 + row;
+      const int n = row_of(rt, row);
       b[i][rt] = v4i{0, 0, 0, 0};
       if (i < cnt && n < N) {
         const uint8_t *p = B + (int64_t)n * ldb + 4 * (int64_t)g0;
@@ -124,6 +141,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
         a[i][t] = *reinterpret_cast<const v4i *>(A + (int64_t)row * K + 16 * (g0 + t));
     }
   }
+  // ROPE form: the angle of each of this thread's pairs (epilogue entries in
+  // tile 0: token m, pair e = 16 rj + l % 16)
+  float rc[kEpi], rsn[kEpi];
+#pragma unroll
+  for (int j = 0; j < kEpi; ++j) {
+    rc[j] = 0.0f;
+    rsn[j] = 0.0f;
+    if constexpr (ROPE) {
+      const int e = threadIdx.x + j * NW * 64;
+      const int l = (e >> 2) & 63, m = 4 * (l >> 4) + (e & 3);
+      if (rotated && e < 256 && m < M) {
+        const int pe = 16 * rj + (l & 15);
+        const double ang = (double)rope.pos[m] * pow(rope.theta, -(2.0 * pe) / (double)rope.hd);
+        rc[j] = (float)cos(ang);
+        rsn[j] = (float)sin(ang);
+      }
+    }
+  }
   v4i acc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt] = v4i{0, 0, 0, 0};
@@ -140,6 +175,52 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][rt][lane][r] = acc[rt][r];
   __syncthreads();
+  if constexpr (ROPE) {
+    // entries of tile 0 take their tile-1 partner: (rows e, e + hd/2) rotated,
+    // or two value rows appended
+#pragma unroll
+    for (int j = 0; j < kEpi; ++j) {
+      const int e = threadIdx.x + j * NW * 64;
+      if (e >= 256) break;
+      const int l = (e >> 2) & 63, r = e & 3;
+      int s0 = 0, s1 = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        s0 += red[w][0][l][r];
+        s1 += red[w][1][l][r];
+      }
+      const int m = 4 * (l >> 4) + r, na = row_of(0, l & 15), nb = row_of(1, l & 15);
+      if (m >= M) continue;
+      const int a0 = s0 - e_rs[j], a1 = s1 - e_rs[j];
+      float y0 = rescale(a0, e_dq[j], epi_gamma(ep, na)), y1 = rescale(a1, e_dq[j], epi_gamma(ep, nb));
+      if (acc_out) {
+        acc_out[(int64_t)m * N + na] = a0;
+        acc_out[(int64_t)m * N + nb] = a1;
+      }
+      const int64_t sl = rope.slot[m], p = rope.pos[m];
+      const bool put = sl >= 0 && sl < rope.n_slots && p >= 0 && p < rope.tmax;
+      if (rotated) {
+        const float ra = __fsub_rn(__fmul_rn(y0, rc[j]), __fmul_rn(y1, rsn[j]));
+        const float rb = __fadd_rn(__fmul_rn(y1, rc[j]), __fmul_rn(y0, rsn[j]));
+        y0 = ra;
+        y1 = rb;
+        if (rh >= rope.n_heads && put) {  // a key head
+          const int pe = 16 * rj + (l & 15);
+          const int64_t dst = ((sl * rope.n_kv + (rh - rope.n_heads)) * rope.tmax + p) * rope.hd;
+          rope.kc[dst + pe] = (uint16_t)bf16_rne(ra);
+          rope.kc[dst + pe + rope.hd / 2] = (uint16_t)bf16_rne(rb);
+        }
+      } else if (put) {  // value rows
+        const int v0 = na - (rope.n_heads + rope.n_kv) * rope.hd, v1 = nb - (rope.n_heads + rope.n_kv) * rope.hd;
+        const int g0 = v0 / rope.hd, g1 = v1 / rope.hd;
+        rope.vc[((sl * rope.n_kv + g0) * rope.tmax + p) * rope.hd + (v0 - g0 * rope.hd)] = (uint16_t)bf16_rne(y0);
+        rope.vc[((sl * rope.n_kv + g1) * rope.tmax + p) * rope.hd + (v1 - g1 * rope.hd)] = (uint16_t)bf16_rne(y1);
+      }
+      Y[(int64_t)m * N + na] = y0;
+      Y[(int64_t)m * N + nb] = y1;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kEpi; ++j) {
     const int e = threadIdx.x + j * NW * 64;
@@ -382,12 +463,13 @@ hipError_t launch_dot4_mt(const int8_t *codes, const uint8_t *packed, const floa
 #undef BL_DOT4
 }
 
-template <int RT, int NW, int SPW>
+template <int RT, int NW, int SPW, bool ROPE = false>
 hipError_t launch_cfg(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
-                      int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
+                      int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream,
+                      const DecodeRope &rope = DecodeRope{}) {
   const int blocks = (n + 16 * RT - 1) / (16 * RT);
-  gemv_decode_kernel<RT, NW, SPW>
-      <<<dim3((unsigned)blocks), dim3(NW * 64), 0, stream>>>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out);
+  gemv_decode_kernel<RT, NW, SPW, ROPE><<<dim3((unsigned)blocks), dim3(NW * 64), 0, stream>>>(
+      codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, rope);
   return hipGetLastError();
 }
 
@@ -409,6 +491,27 @@ hipError_t launch_rt(const int8_t *codes, const uint8_t *packed, const float *de
 }
 
 }  // namespace
+
+bool gemv_decode_rope_supported(int64_t m, int64_t k, int n_heads, int n_kv, int hd) {
+  const int64_t S = ((k >> 4) + 15) >> 4;
+  return m >= 2 && m <= 16 && k % 16 == 0 && S <= 4 * 16 && hd > 0 && hd % 32 == 0 && n_heads > 0 && n_kv > 0;
+}
+
+// The cached decoder's q|k|v projection with RoPE and the cache append in its
+// epilogue (2 to 16 tokens, n = (n_heads + 2 n_kv) hd rows)
+hipError_t launch_gemv_decode_rope(const int8_t *codes, const uint8_t *packed, const float *deq,
+                                   const int32_t *rowsum, int64_t m, int64_t k, const Epilogue &ep, float *y,
+                                   int32_t *acc_out, const DecodeRope &rope, hipStream_t stream) {
+  const int64_t n = (int64_t)(rope.n_heads + 2 * rope.n_kv) * rope.hd;
+  if (!gemv_decode_rope_supported(m, k, rope.n_heads, rope.n_kv, rope.hd)) return hipErrorInvalidValue;
+  const int S = ((int)(k >> 4) + 15) >> 4;
+  if (S <= 4 * BL_GEMV_MIN_WAVES)
+    return launch_cfg<2, BL_GEMV_MIN_WAVES, (4 * BL_GEMV_MIN_WAVES + BL_GEMV_MIN_WAVES - 1) / BL_GEMV_MIN_WAVES, true>(
+        codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream, rope);
+  if (S <= 4 * 8)
+    return launch_cfg<2, 8, 4, true>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream, rope);
+  return launch_cfg<2, 16, 4, true>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream, rope);
+}
 
 hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,
                               int64_t m, int64_t n, int64_t k, const Epilogue &ep, float *y, int32_t *acc_out,

@@ -268,13 +268,18 @@ def _attn_bound_ok(got, ref, vmag, smag, hd, tmax):
 ROPE_FUSED = [(512, 768, 4, 1, 2, 512, [5, 300]), (512, 768, 4, 1, 2, 512, [511]),
               (512, 768, 4, 1, 2, 512, [512, 77]), (512, 768, 4, 4, 1, 256, [100, 5]),
               (1024, 768, 8, 1, 1, 256, [255, 31]), (2560, 6912, 20, 5, 1, 512, [511]),
-              (2560, 6912, 20, 5, 1, 1024, [1023, 64])]
+              (2560, 6912, 20, 5, 1, 1024, [1023, 64]),
+              # 3 to 16 tokens: the decode contraction's RoPE form; 17 takes the separate kernel
+              (512, 768, 4, 1, 2, 512, [0, 5, 300]), (512, 768, 4, 1, 2, 512, [3, 512, 77, 0]),
+              (1024, 768, 8, 1, 1, 256, [255, 0, 31, 100, 7]), (512, 768, 4, 4, 1, 256, list(range(0, 160, 10))),
+              (2560, 6912, 20, 5, 1, 1024, [1023, 64, 5, 900]), (512, 768, 4, 1, 1, 256, list(range(3, 255, 15)))]
 
 
 @pytest.mark.parametrize("hdim,inter,nh,nkv,layers,tmax,positions", ROPE_FUSED)
 def test_decoder_cached_rope_fused(hdim, inter, nh, nkv, layers, tmax, positions):
-    """Without a q|k|v trace the fused decode form takes RoPE and the cache
-    append in the q|k|v projection's epilogue. Its output and both caches equal
+    """Without a q|k|v trace the q|k|v projection takes RoPE and the cache
+    append in its epilogue: the fused decode form for one or two tokens, the
+    decode contraction for 3 to 16. Its output and both caches equal
     those of the traced run bit for bit (that run rotates and appends in a
     kernel of its own, and the test above checks its stages against the
     oracle), with no trace and with an attention trace alone."""
