@@ -87,7 +87,7 @@ def test_validate_packed_counts_invalid_fields():
 # ------------------------------------------------------------------------------ activations
 # (17 to 128 rows take 1024-thread workgroups; (100, 9216) gives them 3 float4 per thread)
 ACT_CASES = [(128, 256, 4), (1, 2560, 26), (4, 2560, 26), (16, 6912, 69), (130, 48, 0), (3, 16, 0),
-             (5, 9216, 3), (1024, 512, 0), (64, 2560, 0), (17, 6912, 69), (100, 9216, 3)]
+             (5, 9216, 3), (1024, 512, 0), (64, 2560, 0), (17, 6912, 69), (100, 9216, 3), (1025, 2560, 26)]
 
 
 def _edge_rows(x):
@@ -115,7 +115,7 @@ def test_quantize_acts_absmax(m, k, nout):
 
 
 @pytest.mark.parametrize("m,k,with_gain", [(128, 256, False), (16, 2560, True), (7, 6912, False), (64, 2560, True),
-                                           (3, 9216, True)])
+                                           (3, 9216, True), (1500, 1024, True)])
 def test_quantize_acts_rmsnorm(m, k, with_gain):
     note(f"quantize_acts rmsnorm m={m} k={k} gain={with_gain}")
     x = _edge_rows(synth.activations(seed(3, m, k), m, k, 2))
