@@ -28,6 +28,9 @@ namespace {
 #define BL_ATTN_CHUNK 128
 #endif
 constexpr int kAttnChunk = BL_ATTN_CHUNK;  // positions per workgroup (a multiple of 16)
+#ifndef BL_ATTN_SPLIT_MAX_M
+#define BL_ATTN_SPLIT_MAX_M 2
+#endif
 static_assert(kAttnChunk % 16 == 0 && kAttnChunk <= 256, "four waves, four positions per wave load");
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float *__restrict_
 // position's score (summed over its 16 lanes with DPP adds) is already in
 // the lanes that weight its value row.
 template <int HD, int G>
-__global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int64_t ldq, int n_kv,
+__global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int64_t ldq, int n_kv, int grp,
                                                            const uint16_t *__restrict__ kc,
                                                            const uint16_t *__restrict__ vc, int64_t n_slots,
                                                            int64_t tmax, const int64_t *__restrict__ slot,
@@ -132,7 +135,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   __shared__ float red[G][4];
   __shared__ __attribute__((aligned(16))) float accs[4][G][HD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.x, g = blockIdx.y, S = gridDim.x;
+  // G of the kv head's grp query heads per workgroup: head part hs of kv head g
+  const int s = blockIdx.x, S = gridDim.x, hsn = grp / G;
+  const int g = blockIdx.y / hsn, hs = blockIdx.y - g * hsn;
   const int64_t r = blockIdx.z;
   const int64_t sl = slot[r], p = pos[r];
   const bool ok = sl >= 0 && sl < n_slots && p >= 0 && p < tmax;
@@ -159,8 +164,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   float qv[G][8];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const float4 a = *reinterpret_cast<const float4 *>(q + r * ldq + (int64_t)(g * G + hh) * HD + d0);
-    const float4 b = *reinterpret_cast<const float4 *>(q + r * ldq + (int64_t)(g * G + hh) * HD + d0 + 4);
+    const float4 a = *reinterpret_cast<const float4 *>(q + r * ldq + (int64_t)(g * grp + hs * G + hh) * HD + d0);
+    const float4 b = *reinterpret_cast<const float4 *>(q + r * ldq + (int64_t)(g * grp + hs * G + hh) * HD + d0 + 4);
     qv[hh][0] = a.x; qv[hh][1] = a.y; qv[hh][2] = a.z; qv[hh][3] = a.w;
     qv[hh][4] = b.x; qv[hh][5] = b.y; qv[hh][6] = b.z; qv[hh][7] = b.w;
   }
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     }
   }
   __syncthreads();
-  const int64_t part = (pb + s) * G;
+  const int64_t part = (pb + s) * grp + hs * G;
   if (tid < G) {
     pml[(part + tid) * 2] = cmax[tid];
     pml[(part + tid) * 2 + 1] = ((red[tid][0] + red[tid][1]) + red[tid][2]) + red[tid][3];
@@ -367,20 +372,32 @@ hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads,
   const int S = attention_splits(tmax);
   float *po = ws;
   float *pml = ws + (size_t)(m * n_heads * S) * 128;
-  const dim3 grid((unsigned)S, (unsigned)n_kv, (unsigned)m), block(256), cgrid((unsigned)n_kv, (unsigned)m);
-#define BL_ATTN(G_)                                                                                                   \
-  attn_partial_kernel<128, G_><<<grid, block, 0, stream>>>(q, ldq, n_kv, kc, vc, n_slots, tmax, slot, pos, po, pml); \
+  // one or two tokens fill few CUs: two workgroups per (chunk, kv head), each
+  // with half of the kv head's query heads (both read the same keys and values)
+  const int grp = n_heads / n_kv;
+  const int hsn = m <= BL_ATTN_SPLIT_MAX_M && grp >= 2 ? 2 : 1;
+  const dim3 grid((unsigned)S, (unsigned)(n_kv * hsn), (unsigned)m), block(256), cgrid((unsigned)n_kv, (unsigned)m);
+#define BL_PART(GW_) \
+  attn_partial_kernel<128, GW_><<<grid, block, 0, stream>>>(q, ldq, n_kv, grp, kc, vc, n_slots, tmax, slot, pos, po, pml)
+#define BL_ATTN(G_)                                                                                                  \
+  switch (G_ / hsn) {                                                                                                \
+    case 1: BL_PART(1); break;                                                                                       \
+    case 2: BL_PART(2); break;                                                                                       \
+    case 4: BL_PART(4); break;                                                                                       \
+    default: BL_PART(8); break;                                                                                      \
+  }                                                                                                                  \
   e = hipGetLastError();                                                                                             \
   if (e != hipSuccess) return e;                                                                                     \
   attn_combine_kernel<128, G_><<<cgrid, dim3(64 * (G_ < 4 ? G_ : 4)), 0, stream>>>(po, pml, n_kv, S, n_slots, tmax,  \
                                                                                   slot, pos, out, ldo)
   hipError_t e;
-  switch (n_heads / n_kv) {
+  switch (grp) {
     case 1: BL_ATTN(1); break;
     case 2: BL_ATTN(2); break;
     case 4: BL_ATTN(4); break;
     default: BL_ATTN(8); break;
   }
+#undef BL_PART
 #undef BL_ATTN
   return hipGetLastError();
 }
