@@ -74,10 +74,10 @@ def test_kv_append():
     assert_equal(host(vg).view(np.uint16), v_ref, "value cache")
 
 
-def _check_attention(q, kc, vc, slot, pos, what):
+def _check_attention(q, kc, vc, slot, pos, what, nh=NH, nkv=NKV):
     tmax = kc.shape[2]
-    out = host(bl.attention_decode(gpu(q), gpu(kc), gpu(vc), gpu(slot), gpu(pos), NH))
-    ref, vmag, smag, _ = oracle.attention(q, kc, vc, slot, pos, NH, NKV, HD)
+    out = host(bl.attention_decode(gpu(q), gpu(kc), gpu(vc), gpu(slot), gpu(pos), nh))
+    ref, vmag, smag, _ = oracle.attention(q, kc, vc, slot, pos, nh, nkv, HD)
     S = (tmax + 63) // 64
     factor = 2.0 ** -24 * (2 * (HD + 1) * np.repeat(smag, HD, axis=1) + 2 * (192 + S))
     err = np.abs(out.astype(np.float64) - ref.astype(np.float64))
@@ -119,3 +119,20 @@ def test_attention_shared_slot_and_out_of_range():
     pos = np.array([10, 260, 3, 300], dtype=np.int64)
     out, _ = _check_attention(q, kc, vc, slot, pos, "shared slot")
     assert not out[2:].any()
+
+
+# (q heads, kv heads, positions): groups of 2, 8 and 1 query heads per kv head, at one to three tokens (one
+# and two tokens split a kv head's query heads over several workgroups)
+GROUPS = [(8, 4, [300]), (8, 4, [5, 511]), (8, 1, [511]), (8, 1, [0, 77, 400]), (4, 4, [200, 3])]
+
+
+@pytest.mark.parametrize("nh,nkv,positions", GROUPS)
+def test_attention_groups(nh, nkv, positions):
+    note(f"attention heads {nh}/{nkv} positions={positions}")
+    m, tmax = len(positions), 512
+    r = np.random.default_rng(seed(44, nh * 10 + nkv, m) % (2 ** 32))
+    kc = oracle.round_bf16(r.normal(size=(m, nkv, tmax, HD)).astype(np.float32))
+    vc = oracle.round_bf16(r.normal(size=(m, nkv, tmax, HD)).astype(np.float32))
+    q = r.normal(size=(m, nh * HD)).astype(np.float32)
+    slot = np.arange(m, dtype=np.int64)
+    _check_attention(q, kc, vc, slot, np.array(positions, dtype=np.int64), "attention groups", nh, nkv)
