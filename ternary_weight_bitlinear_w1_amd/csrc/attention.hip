@@ -372,11 +372,12 @@ hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads,
   const int S = attention_splits(tmax);
   float *po = ws;
   float *pml = ws + (size_t)(m * n_heads * S) * 128;
-  // one or two tokens fill few CUs: up to four workgroups per (chunk, kv
-  // head), each with a share of the kv head's query heads (all read the same
-  // keys and values)
+  // few tokens fill few CUs: several workgroups per (chunk, kv head), each
+  // with a share of the kv head's query heads (all read the same keys and
+  // values): up to four at one or two tokens, two at three or four (measured:
+  // at four tokens four were slower than two, and two faster than one)
   const int grp = n_heads / n_kv;
-  const int hsn = m > BL_ATTN_SPLIT_MAX_M ? 1 : (grp >= 4 ? 4 : grp);
+  const int hsn = m <= BL_ATTN_SPLIT_MAX_M ? (grp >= 4 ? 4 : grp) : (m <= 4 && grp >= 2 ? 2 : 1);
   const dim3 grid((unsigned)S, (unsigned)(n_kv * hsn), (unsigned)m), block(256), cgrid((unsigned)n_kv, (unsigned)m);
 #define BL_PART(GW_) \
   attn_partial_kernel<128, GW_><<<grid, block, 0, stream>>>(q, ldq, n_kv, grp, kc, vc, n_slots, tmax, slot, pos, po, pml)
