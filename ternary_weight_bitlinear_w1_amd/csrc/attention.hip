@@ -17,7 +17,7 @@
 // the lanes that scored a position then weight its value row. It stores the
 // chunk's max, sum of exponentials and unnormalized output.
 // attn_combine_kernel rescales and adds the chunks, one exponential per chunk
-// and head. Tokens whose slot or position is out of range get zeros and write
+// and head, one wave per head and token. Tokens whose slot or position is out of range get zeros and write
 // nothing to the cache.
 #include "common.h"
 
@@ -255,28 +255,26 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
   }
 }
 
-// out[r][h HD + d] from the chunks of token r's kv head g: one wave per head
-// of the group (two per wave for groups of 8), 32 chunks per round. Every load
+// out[r][h HD + d] from the chunks of token r's query head h (kv head h / G):
+// one single-wave workgroup per head and token, 32 chunks per round. Every load
 // of a round (each lane's two dims of the 32 chunk outputs; lane j's chunk j
 // max and sum) is issued before any arithmetic, the first round's before the
 // max over all chunks is formed. Lane j then forms exp(max_j - max) and its
 // share of the sum of exponentials, and every lane adds its two dims of the
 // chunk outputs, weighted by those factors, in chunk order.
 template <int HD, int G>
-__global__ __launch_bounds__(64 * (G < 4 ? G : 4)) void attn_combine_kernel(
+__global__ __launch_bounds__(64) void attn_combine_kernel(
     const float *__restrict__ po, const float *__restrict__ pml, int n_kv, int S, int64_t n_slots, int64_t tmax,
     const int64_t *__restrict__ slot, const int64_t *__restrict__ pos, float *__restrict__ out, int64_t ldo) {
-  constexpr int kWaves = G < 4 ? G : 4;
   constexpr int kR = 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x / G, hh = blockIdx.x - g * G;
   const int64_t r = blockIdx.y;
   const int64_t sl = slot[r], p = pos[r];
   const bool ok = sl >= 0 && sl < n_slots && p >= 0 && p < tmax;
   const int nch = ok ? (int)(p / kAttnChunk) + 1 : 0;  // chunks that hold positions
   const int64_t pb = (r * n_kv + g) * S;
-#pragma unroll 1
-  for (int hh = wave; hh < G; hh += kWaves) {
+  {
     float2 o[kR];
     float mc = -INFINITY, lc = 0.0f;
     // the loads of the round that starts at chunk c0 (past the last chunk:
@@ -378,7 +376,7 @@ hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads,
   // at four tokens four were slower than two, and two faster than one)
   const int grp = n_heads / n_kv;
   const int hsn = m <= BL_ATTN_SPLIT_MAX_M ? (grp >= 4 ? 4 : grp) : (m <= 4 && grp >= 2 ? 2 : 1);
-  const dim3 grid((unsigned)S, (unsigned)(n_kv * hsn), (unsigned)m), block(256), cgrid((unsigned)n_kv, (unsigned)m);
+  const dim3 grid((unsigned)S, (unsigned)(n_kv * hsn), (unsigned)m), block(256), cgrid((unsigned)n_heads, (unsigned)m);
 #define BL_PART(GW_) \
   attn_partial_kernel<128, GW_><<<grid, block, 0, stream>>>(q, ldq, n_kv, grp, kc, vc, n_slots, tmax, slot, pos, po, pml)
 #define BL_ATTN(G_)                                                                                                  \
@@ -390,8 +388,7 @@ hipError_t launch_attention(const float *q, int64_t m, int64_t ldq, int n_heads,
   }                                                                                                                  \
   e = hipGetLastError();                                                                                             \
   if (e != hipSuccess) return e;                                                                                     \
-  attn_combine_kernel<128, G_><<<cgrid, dim3(64 * (G_ < 4 ? G_ : 4)), 0, stream>>>(po, pml, n_kv, S, n_slots, tmax,  \
-                                                                                  slot, pos, out, ldo)
+  attn_combine_kernel<128, G_><<<cgrid, dim3(64), 0, stream>>>(po, pml, n_kv, S, n_slots, tmax, slot, pos, out, ldo)
   hipError_t e;
   switch (grp) {
     case 1: BL_ATTN(1); break;
