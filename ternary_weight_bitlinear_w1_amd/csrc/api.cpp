@@ -564,6 +564,7 @@ struct BlockBufs {
   int32_t *split;  // split-K partial sums of the widest projection, or NULL
   float *att;      // cached decoder: attention output [m][H]
   float *attn_ws;  // cached decoder: attention chunk partials
+  float2 *rope_cs; // cached decoder: [m][head_dim/2] (cosine, sine) of each token's rotated pairs
 };
 
 bool is_decoder(int32_t kind) { return kind == BITLINEAR_BLOCK_DECODER || kind == BITLINEAR_BLOCK_DECODER_CACHED; }
@@ -603,6 +604,7 @@ size_t block_layout(const bitlinear_block *blk, int64_t m, BlockBufs *b, char *b
   t.att = reinterpret_cast<float *>(take(cached ? (size_t)(m * H) * 4 : 0));
   t.attn_ws = reinterpret_cast<float *>(
       take(cached ? bl::attention_workspace_floats(m, blk->n_heads, blk->t_max) * sizeof(float) : 0));
+  t.rope_cs = reinterpret_cast<float2 *>(take(cached ? (size_t)(m * (blk->head_dim / 2)) * sizeof(float2) : 0));
   if (b) *b = t;
   return off;
 }
@@ -680,7 +682,8 @@ bl::ActSrc act_src(const float *x, int64_t ld, int64_t k, const float *gain) {
 bitlinear_status fused(int mode, int epi, const bl::ActSrc &src, float eps, int64_t m, const uint8_t *w, int64_t n,
                        const float *gam, const int64_t *seg, int n_seg, float *y, int32_t *acc, const float *res,
                        float *out2, float *mi, int8_t *codes_out, float *deq_out, hipStream_t s,
-                       const bitlinear_block *rope_blk = nullptr, const bitlinear_layer *rope_layer = nullptr) {
+                       const bitlinear_block *rope_blk = nullptr, const bitlinear_layer *rope_layer = nullptr,
+                       const float2 *rope_cs = nullptr) {
   bl::FusedDecode a{};
   a.src = src;
   a.eps = eps;
@@ -698,7 +701,7 @@ bitlinear_status fused(int mode, int epi, const bl::ActSrc &src, float eps, int6
   if (rope_blk) {  // the RoPE form: positions, caches and head layout of the cached decoder
     a.slot = rope_blk->slot;
     a.pos = rope_blk->pos;
-    a.theta = rope_blk->rope_theta;
+    a.cs = rope_cs;
     a.kc = rope_layer->k_cache;
     a.vc = rope_layer->v_cache;
     a.n_slots = rope_blk->n_slots;
@@ -717,7 +720,7 @@ bitlinear_status cached_attention(const bitlinear_block *blk, const bitlinear_la
                                   const BlockBufs &b, float *tr_attn, hipStream_t s) {
   const int hd = blk->head_dim, nh = blk->n_heads, nkv = blk->n_kv_heads;
   const int64_t H = blk->hidden, KV = (int64_t)nkv * hd, Q = H + 2 * KV;
-  BL_TRY(launched(bl::launch_rope_append(qkv, m, Q, nh, nkv, hd, blk->slot, blk->pos, blk->rope_theta, L.k_cache,
+  BL_TRY(launched(bl::launch_rope_append(qkv, m, Q, nh, nkv, hd, blk->slot, blk->pos, b.rope_cs, L.k_cache,
                                          L.v_cache, blk->n_slots, blk->t_max, s),
                   "rope and kv append"));
   BL_TRY(launched(bl::launch_attention(qkv, m, Q, nh, nkv, hd, L.k_cache, L.v_cache, blk->n_slots, blk->t_max,
@@ -764,7 +767,7 @@ bitlinear_status block_forward_fused(const bitlinear_block *blk, const float *x,
     BL_TRY(fused(BITLINEAR_ACT_RMSNORM, rope_fused ? bl::FUSED_EPI_ROPE : bl::FUSED_EPI_PLAIN,
                  act_src(xin, H, H, L.input_norm_gain), eps, m, L.qkv, Q, L.qkv_gamma, qkv_seg, 3, qkv,
                  at(tr.acc_qkv, oQ), nullptr, nullptr, nullptr, at(tr.codes_in, oH), dq, s,
-                 rope_fused ? blk : nullptr, rope_fused ? &L : nullptr));
+                 rope_fused ? blk : nullptr, rope_fused ? &L : nullptr, b.rope_cs));
     if (cached) {
       // RoPE, cache append, attention -> attn_sub_norm -> o_proj; h = x + o
       if (rope_fused) {
@@ -877,7 +880,7 @@ struct Chain {
     bl::DecodeRope r;
     r.slot = blk->slot;
     r.pos = blk->pos;
-    r.theta = blk->rope_theta;
+    r.cs = b.rope_cs;
     r.kc = L.k_cache;
     r.vc = L.v_cache;
     r.n_slots = blk->n_slots;
@@ -1039,6 +1042,9 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
   bitlinear_block_trace tr;
   memset(&tr, 0, sizeof tr);
   if (trace) tr = *trace;
+  // every layer rotates q and k at the same positions: their cosines and sines once per call
+  if (blk->kind == BITLINEAR_BLOCK_DECODER_CACHED)
+    BL_TRY(launched(bl::launch_rope_table(blk->pos, m, blk->head_dim, blk->rope_theta, b.rope_cs, s), "rope table"));
 
   if (bl::fused_decode_supported(m, H) && bl::fused_decode_supported(m, I) && I % 16 == 0)
     return block_forward_fused(blk, x, m, y, tr, b, s);

@@ -59,12 +59,29 @@ __global__ __launch_bounds__(256) void rope_kernel(float *__restrict__ x, int64_
   v[e + half] = __fadd_rn(__fmul_rn(b, c), __fmul_rn(a, s));
 }
 
+// The (cosine, sine) of every rotated pair of every token, cs[r][e] for
+// e < hd/2: the angle p theta^(-2e/hd) in fp64, each rounded to fp32. All
+// layers of a decode step rotate at the same positions, so a step forms this
+// table once and the RoPE epilogues read it.
+__global__ __launch_bounds__(256) void rope_table_kernel(const int64_t *__restrict__ pos, int64_t m, int hd,
+                                                         double theta, float2 *__restrict__ cs) {
+  const int half = hd / 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= m * half) return;
+  const int64_t r = i / half;
+  const int e = (int)(i - r * half);
+  const double ang = (double)pos[r] * pow(theta, -(2.0 * e) / (double)hd);
+  cs[i] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
 // RoPE on the q and k heads of a q|k|v row and the keys and values into the
-// caches, one thread per rotated pair of q or k (plus the matching value pair)
+// caches, one thread per rotated pair of q or k (plus the matching value pair);
+// the (cosine, sine) come from rope_table_kernel's table
 __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, int64_t m, int64_t ld,
                                                           int n_heads, int n_kv, int hd,
                                                           const int64_t *__restrict__ slot,
-                                                          const int64_t *__restrict__ pos, double theta,
+                                                          const int64_t *__restrict__ pos,
+                                                          const float2 *__restrict__ cs,
                                                           uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
                                                           int64_t n_slots, int64_t tmax) {
   const int half = hd / 2, heads = n_heads + n_kv;
@@ -74,8 +91,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   const int rem = (int)(i - r * heads * half);
   const int h = rem / half, e = rem - h * half;
   const int64_t p = pos[r];
-  const double ang = (double)p * pow(theta, -(2.0 * e) / (double)hd);
-  const float c = (float)cos(ang), s = (float)sin(ang);
+  const float2 csv = cs[r * half + e];
+  const float c = csv.x, s = csv.y;
   float *v = qkv + r * ld + (int64_t)h * hd;
   const float a = v[e], b = v[e + half];
   const float ra = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s));
@@ -334,13 +351,20 @@ hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_head
   return hipGetLastError();
 }
 
+hipError_t launch_rope_table(const int64_t *pos, int64_t m, int hd, double theta, float2 *cs, hipStream_t stream) {
+  const int64_t n = m * (hd / 2);
+  if (n == 0) return hipSuccess;
+  rope_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(pos, m, hd, theta, cs);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_append(float *qkv, int64_t m, int64_t ld, int n_heads, int n_kv, int hd, const int64_t *slot,
-                              const int64_t *pos, double theta, uint16_t *kc, uint16_t *vc, int64_t n_slots,
+                              const int64_t *pos, const float2 *cs, uint16_t *kc, uint16_t *vc, int64_t n_slots,
                               int64_t tmax, hipStream_t stream) {
   const int64_t n = m * (n_heads + n_kv) * (hd / 2);
   if (n == 0) return hipSuccess;
   rope_append_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(qkv, m, ld, n_heads, n_kv, hd, slot,
-                                                                                 pos, theta, kc, vc, n_slots, tmax);
+                                                                                 pos, cs, kc, vc, n_slots, tmax);
   return hipGetLastError();
 }
 

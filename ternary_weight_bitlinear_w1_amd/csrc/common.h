@@ -194,7 +194,7 @@ hipError_t launch_gemm_glu(const int8_t *codes, const uint8_t *packed, const flo
 // decoder's q|k|v rows: n_heads q heads, n_kv k heads, n_kv v heads of hd)
 struct DecodeRope {
   const int64_t *slot = nullptr, *pos = nullptr;
-  double theta = 0.0;
+  const float2 *cs = nullptr;  // [m][hd/2] (cosine, sine) of each token's rotated pairs (launch_rope_table)
   uint16_t *kc = nullptr, *vc = nullptr;
   int64_t n_slots = 0, tmax = 0;
   int n_heads = 0, n_kv = 0, hd = 0;
@@ -260,7 +260,7 @@ struct FusedDecode {
   // bfloat16 caches [n_slots][n_kv][tmax][hd] at (slot[t], pos[t]) when both
   // are in range
   const int64_t *slot, *pos;
-  double theta;
+  const float2 *cs;  // [m][hd/2] (cosine, sine) of each token's rotated pairs (launch_rope_table)
   uint16_t *kc, *vc;
   int64_t n_slots, tmax;
   int n_heads, n_kv, hd;
@@ -282,9 +282,12 @@ int attention_splits(int64_t tmax);
 size_t attention_workspace_floats(int64_t m, int n_heads, int64_t tmax);
 hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
                        double theta, hipStream_t stream);
-// both of the above on a q|k|v row (q heads, then k heads, then v heads), one launch
+// the (cosine, sine) table of every token's rotated pairs, cs [m][hd/2]
+hipError_t launch_rope_table(const int64_t *pos, int64_t m, int hd, double theta, float2 *cs, hipStream_t stream);
+// both of the above on a q|k|v row (q heads, then k heads, then v heads), one
+// launch, with the angles from a launch_rope_table table
 hipError_t launch_rope_append(float *qkv, int64_t m, int64_t ld, int n_heads, int n_kv, int hd, const int64_t *slot,
-                              const int64_t *pos, double theta, uint16_t *kc, uint16_t *vc, int64_t n_slots,
+                              const int64_t *pos, const float2 *cs, uint16_t *kc, uint16_t *vc, int64_t n_slots,
                               int64_t tmax, hipStream_t stream);
 hipError_t launch_kv_append(const float *k, const float *v, int64_t m, int64_t ld, int n_kv, int hd,
                             const int64_t *slot, const int64_t *pos, uint16_t *kc, uint16_t *vc, int64_t n_slots,

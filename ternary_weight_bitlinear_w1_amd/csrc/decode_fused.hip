@@ -26,8 +26,9 @@
 // In the ReLU^2 form, workgroup b owns gate rows [b R/2, (b + 1) R/2) and the
 // up rows I + the same range, so it can form its slice of mi itself. In the
 // RoPE form a workgroup of the q and k heads owns R/2 rotated pairs of one
-// head (rows e and e + hd/2), so it rotates them itself; the angles (fp64, as
-// the standalone RoPE kernel takes them) are formed while the weights load.
+// head (rows e and e + hd/2), so it rotates them itself, with the cosine and
+// sine of each pair read from the step's table (rope_table_kernel) while the
+// weights load.
 #include "act_prologue.h"
 
 namespace bl {
@@ -94,14 +95,15 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // RoPE form: thread t (R/2) + i < MT (R/2) takes pair i of token t
+  // RoPE form: thread t (R/2) + i < MT (R/2) takes pair i of token t (its
+  // cosine and sine from the step's table)
   float rc = 0.0f, rsn = 0.0f;
   if constexpr (EPI == FUSED_EPI_ROPE) {
     const int t = threadIdx.x / (R / 2), e = rj * (R / 2) + (int)threadIdx.x % (R / 2);
     if ((int)blockIdx.x < rot_wgs && t < a.m && threadIdx.x < MT * (R / 2)) {
-      const double ang = (double)a.pos[t] * pow(a.theta, -(2.0 * e) / (double)a.hd);
-      rc = (float)cos(ang);
-      rsn = (float)sin(ang);
+      const float2 cs = a.cs[t * (a.hd / 2) + e];
+      rc = cs.x;
+      rsn = cs.y;
     }
   }
 

@@ -61,8 +61,8 @@ __device__ __forceinline__ v4i unpack16(uint32_t p) {
 //
 // ROPE form (RT = 2, the cached decoder's q|k|v projection): a workgroup of the
 // q and k heads owns rows e (tile 0) and e + hd/2 (tile 1) of one head for 16
-// consecutive e, so it rotates each pair itself, with the angles formed in fp64
-// while the weights load (the arithmetic of rope_append_kernel), and writes the
+// consecutive e, so it rotates each pair itself, with the cosine and sine read
+// from the step's table (rope_table_kernel) while the weights load, and writes the
 // keys to the bfloat16 cache; workgroups of the value heads append the values.
 template <int RT, int NW, int SPW, bool ROPE = false>
 __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__restrict__ A,
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
         a[i][t] = *reinterpret_cast<const v4i *>(A + (int64_t)row * K + 16 * (g0 + t));
     }
   }
-  // ROPE form: the angle of each of this thread's pairs (epilogue entries in
+  // ROPE form: the cosine and sine of each of this thread's pairs (epilogue entries in
   // tile 0: token m, pair e = 16 rj + l % 16)
   float rc[kEpi], rsn[kEpi];
 #pragma unroll
@@ -153,9 +153,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
       const int l = (e >> 2) & 63, m = 4 * (l >> 4) + (e & 3);
       if (rotated && e < 256 && m < M) {
         const int pe = 16 * rj + (l & 15);
-        const double ang = (double)rope.pos[m] * pow(rope.theta, -(2.0 * pe) / (double)rope.hd);
-        rc[j] = (float)cos(ang);
-        rsn[j] = (float)sin(ang);
+        const float2 cs = rope.cs[m * (rope.hd / 2) + pe];
+        rc[j] = cs.x;
+        rsn[j] = cs.y;
       }
     }
   }
