@@ -353,6 +353,9 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
                                    "packed_bytes": nbytes, "ring_copies": copies}
             log(f"decode {name} m={m}: {b2b_us:.2f} us/launch back-to-back, {gbs:.0f} GB/s "
                 f"(one launch between events: {us:.2f} us)")
+            if m <= 4:
+                res[f"{name}_m{m}_whole_ring"] = bench_decode_tall(torch, L, bl, ring, k, gam[0], seg[0], codes, deq,
+                                                                   rs, y, reps, name, m, sp, stream)
         # reference: a device copy of the same bytes (one ring copy per launch,
         # back to back; it reads them once and writes them once) -- the cost of
         # one launch that moves these bytes on this GPU
@@ -411,6 +414,48 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
         del ring, w3
         torch.cuda.empty_cache()
     return res
+
+
+def bench_decode_tall(torch, L, bl, ring, k, gamma, seg0, codes, deq, rs, y_ref, reps, name, m, sp, stream):
+    """The same decode kernel in one launch over every copy of the ring at once
+    (copies x n rows, one gamma): a launch that streams more than twice the
+    last-level cache, so its fixed cost no longer sets the time. The first
+    seg0 outputs must equal those of the ordinary launch bit for bit."""
+    copies, n = ring.shape[0], ring.shape[1]
+    tall = ring.view(copies * n, ring.shape[2])
+    nt = tall.shape[0]
+    g_c = (bl.ctypes.c_float * 1)(gamma)
+    se_c = (bl.ctypes.c_int64 * 1)(nt)
+    y = torch.empty((m, nt), dtype=torch.float32, device=y_ref.device)
+    ws_n = L.bitlinear_forward_workspace_bytes(m, nt, k, 0)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=y_ref.device)
+
+    def launch():
+        st = L.bitlinear_forward(None, codes.data_ptr(), deq.data_ptr(), rs.data_ptr(), m, k, tall.data_ptr(), nt,
+                                 g_c, se_c, 1, y.data_ptr(), None, bl.PATH_DECODE, ws.data_ptr(), ws_n, sp)
+        if st != 0:
+            raise RuntimeError(L.bitlinear_last_error().decode())
+
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    if not torch.equal(y[:, :seg0], y_ref[:, :seg0]):
+        raise RuntimeError(f"decode {name} m={m}: the whole-ring launch differs from the ordinary one")
+    n_rep = max(5, reps // 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_rep):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n_rep * 1e3
+    nbytes = tall.numel()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"decode {name} m={m}, one launch over the whole ring ({nt} rows, {nbytes / 1e6:.0f} MB): {us:.1f} us, "
+        f"{gbs:.0f} GB/s packed ({gbs / PEAK_HBM_GBS:.2f} of HBM)")
+    del y, ws
+    return {"us": round(us, 2), "rows": nt, "packed_bytes": nbytes, "gbs_packed": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def head_table(torch, synth, dev):
