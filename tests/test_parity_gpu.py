@@ -305,6 +305,29 @@ def test_forward_decode_full_size(m, proj):
         assert_equal(host(y_dec), host(y_pre), "decode == prefill")
 
 
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_forward_decode_tall(m, proj):
+    """The decode kernels in one launch over many stacked copies of a 2B4T matrix
+    (the form the benchmark streams 628 MB with): 16 copies, 110,592 gate rows or
+    40,960 down rows. One copy is checked against the oracle (codes, int32 sums
+    and outputs); every copy of the tall launch must equal it bit for bit."""
+    note(f"forward decode tall {proj} m={m}")
+    k, n = (2560, 6912) if proj == "gate_up" else (6912, 2560)
+    mat = Matrix(n, k, seed(5, 0, 1 if proj == "gate_up" else 2))
+    x = synth.activations(seed(5, m, k), m, k, synth.outlier_count(k))
+    y_one = host(_check_forward(x, [mat], bl.PATH_DECODE, f"decode {proj}"))
+    copies = 16
+    tall = gpu_pack([mat]).repeat(copies, 1)
+    y_tall, acc_tall = bl.forward(tall, k, [mat.gamma_f], [copies * n], x=gpu(x), want_acc=True,
+                                  path=bl.PATH_DECODE)
+    yt, at = host(y_tall), host(acc_tall)
+    ref_acc = oracle.forward(x, mat.codes, [mat.gamma], [n])["acc"]
+    for c in range(copies):
+        assert_equal(yt[:, c * n:(c + 1) * n], y_one, f"copy {c} outputs")
+        assert_equal(at[:, c * n:(c + 1) * n], ref_acc, f"copy {c} int32 sums")
+
+
 @pytest.mark.parametrize("proj", ["gate_up", "down"])
 def test_forward_prefill_full_size(proj):
     """M=4096 prefill at the 2B4T shapes: every code, sampled rows and columns of the
