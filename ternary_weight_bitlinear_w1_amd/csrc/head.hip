@@ -12,7 +12,8 @@
 // reduced in a fixed order, so o repeats run to run.
 //
 // lm_head_kernel: bound by HBM on the head (656.7 MB at 128256 x 2560). A wave
-// owns four rows; for each it issues C loads of 1 KB (64 lanes x 16 bytes, 8
+// owns R rows (2, 2, 4, 8 for one to four tokens, measured); for each it issues C
+// loads of 1 KB (64 lanes x 16 bytes, 8
 // bfloat16 each), so lane l always reads the same columns 512 c + 8 l .. + 7 and
 // keeps the tokens' o for exactly those columns in registers for the whole
 // kernel. Products use v_dot2_f32_bf16 (exact bfloat16 products, fp32 sums);
@@ -26,7 +27,6 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kNormThreads = 256;
-constexpr int kHeadRowsPerWave = 4;
 constexpr int kHeadMaxChunks = 8;  // K <= 8 * 512
 
 // nearest bfloat16 of a finite float, ties to an even last kept bit
@@ -80,9 +80,19 @@ __global__ __launch_bounds__(kNormThreads) void final_norm_kernel(const float *_
   }
 }
 
+// rows per wave, by tokens: the fastest of 2, 4 and 8 on the 2B4T head
+// (one and two tokens 107.0 and 107.5 us with 2 rows; three 108.7 us with 4;
+// four 113.3 us with 8, against 117.3 with 4)
+template <int MT>
+constexpr int head_rows_per_wave() {
+  return MT <= 2 ? 2 : (MT == 3 ? 4 : 8);
+}
+
 template <int MT, int C>
 __global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict__ o, const uint16_t *__restrict__ W,
                                                       int N, int K, float *__restrict__ Y) {
+  constexpr int kHeadRowsPerWave = head_rows_per_wave<MT>();
+  static_assert(kHeadRowsPerWave * MT <= 64, "one lane per output of the wave");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * 4 + wave) * kHeadRowsPerWave;
   // the weights first (HBM), then the tokens' o (a few KB from L2)
@@ -173,6 +183,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int64_t *__restrict__ 
 
 template <int MT>
 hipError_t launch_head_mt(const uint16_t *o, const uint16_t *w, int n, int k, float *y, hipStream_t stream) {
+  constexpr int kHeadRowsPerWave = head_rows_per_wave<MT>();
   const int chunks = (k + 511) / 512;
   const dim3 grid((unsigned)((n + 4 * kHeadRowsPerWave - 1) / (4 * kHeadRowsPerWave))), block(256);
 #define BL_HEAD(C_) \
