@@ -277,6 +277,21 @@ ROPE_FUSED = [(512, 768, 4, 1, 2, 512, [5, 300]), (512, 768, 4, 1, 2, 512, [511]
 
 @pytest.mark.parametrize("hdim,inter,nh,nkv,layers,tmax,positions", ROPE_FUSED)
 def test_decoder_cached_rope_fused(hdim, inter, nh, nkv, layers, tmax, positions):
+    _rope_fused_case(hdim, inter, nh, nkv, layers, tmax, positions, None)
+
+
+# a token whose slot is outside the caches (no append, zeros from attention): one token, two (the fused
+# decode form) and three (the decode contraction's RoPE form)
+ROPE_FUSED_SLOTS = [(512, 768, 4, 1, 2, 512, [5], [3]), (512, 768, 4, 1, 2, 512, [5, 300], [1, -1]),
+                    (512, 768, 4, 1, 2, 512, [0, 5, 300], [2, 7, 0])]
+
+
+@pytest.mark.parametrize("hdim,inter,nh,nkv,layers,tmax,positions,slots", ROPE_FUSED_SLOTS)
+def test_decoder_cached_rope_fused_bad_slot(hdim, inter, nh, nkv, layers, tmax, positions, slots):
+    _rope_fused_case(hdim, inter, nh, nkv, layers, tmax, positions, slots)
+
+
+def _rope_fused_case(hdim, inter, nh, nkv, layers, tmax, positions, slots):
     """Without a q|k|v trace the q|k|v projection takes RoPE and the cache
     append in its epilogue: the fused decode form for one or two tokens, the
     decode contraction for 3 to 16. Its output and both caches equal
@@ -289,7 +304,7 @@ def test_decoder_cached_rope_fused(hdim, inter, nh, nkv, layers, tmax, positions
     kvd = nkv * hd
     Q = hdim + 2 * kvd
     r = np.random.default_rng(60 + m)
-    slot = np.arange(m, dtype=np.int64)[::-1].copy()
+    slot = np.arange(m, dtype=np.int64)[::-1].copy() if slots is None else np.array(slots, dtype=np.int64)
     pos = np.array(positions, dtype=np.int64)
     x = synth.activations(seed(10, m, 5), m, hdim, 1)
     layers_w, caches0 = [], []
@@ -318,7 +333,9 @@ def test_decoder_cached_rope_fused(hdim, inter, nh, nkv, layers, tmax, positions
         for l in range(layers):
             assert_equal(c[l][0].view(np.uint16), c_ref[l][0].view(np.uint16), f"layer {l} key cache")
             assert_equal(c[l][1].view(np.uint16), c_ref[l][1].view(np.uint16), f"layer {l} value cache")
-    assert host(att).any()
+    valid = (slot >= 0) & (slot < m) & (pos >= 0) & (pos < tmax)
+    a = host(att)
+    assert (not valid.any() or a[:, valid].any()) and not a[:, ~valid].any(), "attention: tokens in range only"
 
 
 @pytest.mark.parametrize("positions", [[5, 300], [0, 1, 2, 100, 257, 511], [0, 7, 300]])
