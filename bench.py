@@ -272,6 +272,7 @@ def main():
                      "algorithmic_ops_per_launch": ops_gu,
                      "algorithmic_bytes_per_launch": M * H + 2 * I * H // 4 + 4 * M * I + 8 * M},
         "kernels": kernels,
+        "decode_roofline": decode_roofline(decode),
         "decode": decode,
         "online": online,
         "head": head,
@@ -279,6 +280,22 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_roofline(decode):
+    """The one-token gate|up GEMV against 8 TB/s of packed-weight reads: one
+    2B4T projection per launch (bound by the launch's fixed cost, with a device
+    copy of the same bytes beside it) and one launch over the whole ring."""
+    if not decode or "gate_up_m1" not in decode:
+        return None
+    one, ring = decode["gate_up_m1"], decode.get("gate_up_m1_whole_ring")
+    copy = decode.get("gate_up_copy_reference")
+    return {"bound": "hbm", "kernel": "gemv_dot4 m=1, gate|up 2560 -> 2x6912 packed 2-bit", "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "one_projection": {"achieved": one["gbs_packed"], "frac": one["frac_hbm"], "us": one["us"],
+                               "device_copy_us": copy["us"] if copy else None},
+            "whole_ring": ({"achieved": ring["gbs_packed"], "frac": ring["frac_hbm"], "us": ring["us"],
+                            "bytes": ring["packed_bytes"]} if ring else None)}
 
 
 def measured_traffic():
