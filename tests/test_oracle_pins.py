@@ -392,6 +392,62 @@ def test_attention_equal_keys_average_and_heads_share_kv():
         assert np.all(out2[0, h * hd:(h + 1) * hd] == np.float32(h // (n_heads // n_kv) + 1))
 
 
+def test_golden_attention_scale():
+    """[nnterp] "Loading" and "Config": two keys with hand-worked softmax weights
+    under the 1/sqrt(head_dim) score scale (tests/golden/attention_scale.json);
+    dropping or squaring the scale moves the weights far outside the bound."""
+    g = gold("attention_scale.json")
+    bf = {2.0: 0x4000, 16.0: 0x4180, 1.0: 0x3F80}  # bfloat16 bit patterns of exact values
+    for case in g["cases"]:
+        hd = case["head_dim"]
+        kc = np.zeros((1, 1, 2, hd), dtype=np.uint16)
+        vc = np.zeros((1, 1, 2, hd), dtype=np.uint16)
+        kc[0, 0, 1, 0] = bf[case["key1_dim0"]]
+        vc[0, 0, 0, 0] = bf[1.0]
+        vc[0, 0, 1, 1] = bf[1.0]
+        q = np.zeros((1, hd), dtype=np.float32)
+        q[0, 0] = 1.0
+        out, _, _, bad = oracle.attention(q, kc, vc, [0], [1], 1, 1, hd)
+        assert bad == 0
+        want = np.zeros(hd)
+        want[0], want[1] = case["out_dim0"], case["out_dim1"]
+        # the only rounding is the final one to fp32
+        assert np.all(np.abs(out[0].astype(np.float64) - want) <= 2.0 ** -24 * np.abs(want) + 1e-300), (hd, out[0, :2])
+
+
+def test_golden_kv_append_layout():
+    """[nnterp] "Config" and "Loading"; reading R21: [slot][kv head][position][hd]
+    bfloat16 caches, out-of-range tokens skipped (tests/golden/kv_append_layout.json)."""
+    g = gold("kv_append_layout.json")
+    ns, nkv, tmax, hd = g["n_slots"], g["n_kv"], g["t_max"], g["head_dim"]
+    keys = np.array([[float.fromhex(v) if isinstance(v, str) else float(v) for v in row] for row in g["keys"]],
+                    dtype=np.float32)
+    kc = np.full((ns, nkv, tmax, hd), g["sentinel"], dtype=np.uint16)
+    vc = kc.copy()
+    skipped = oracle.kv_append(kc, vc, keys, -keys, g["slot"], g["pos"], nkv, hd)
+    assert skipped == 3
+    want_k = np.full(kc.size, g["sentinel"], dtype=np.uint16)
+    want_v = want_k.copy()
+    for off, bits in g["expect_k_hex"].items():
+        want_k[int(off):int(off) + hd] = [int(b, 16) for b in bits]
+    for off, bits in g["expect_v_hex"].items():
+        want_v[int(off):int(off) + hd] = [int(b, 16) for b in bits]
+    assert np.array_equal(kc.reshape(-1), want_k)
+    assert np.array_equal(vc.reshape(-1), want_v)
+
+
+def test_golden_rescale_order():
+    """[nnterp] "The two checkpoints"; reading R10: the per-token factor first, then
+    gamma (tests/golden/rescale_order.json); the other order, or one rounding of
+    the exact product, gives a different fp32 value on this case."""
+    g = gold("rescale_order.json")
+    deq = np.array([float.fromhex(g["deq"])], dtype=np.float32)
+    gam = float.fromhex(g["gamma"])
+    y = oracle.rescale(np.array([[g["acc"]]], dtype=np.int32), deq, [gam], [1])
+    assert float(y[0, 0]) == float.fromhex(g["y"])
+    assert float.fromhex(g["y"]) != float.fromhex(g["y_other_order"])
+
+
 def test_attention_permutation_dominance_and_range():
     r = rng(19)
     kc, vc = _caches(r, 1, 1, 32, 16)
@@ -604,8 +660,8 @@ def test_P9_closed_forms():
 
 # ------------------------------------------------------------------ O8
 def test_P10_rescale_equals_dequantized_linear_map():
-    """[nnterp] "The projections quantize their inputs and weights": the output equals
-    the linear map of the rounded input by the ternarized weight. In fp64,
+    """[nnterp] "The projections quantize their inputs and weights": the projection's
+    output is the exact product of the quantized input and the ternary weights. In fp64,
     y64 = (q * deq) @ (c * gamma)^T; the fp32 result is within 3 * 2^-24 |y| of it."""
     x = synth.activations(synth.stream_seed(16, tensor=synth.T_ACT), 32, 256, n_outliers=3)
     w = synth.weights(synth.stream_seed(16, tensor=synth.T_WEIGHT), 96, 256)
