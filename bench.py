@@ -45,7 +45,8 @@ PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 M, H, I = 4096, 2560, 6912
 VOCAB = 128256
-ROPE_THETA = 5e5  # the RoPE base of the released 2B4T model (the pages name RoPE only)
+ROPE_THETA = 5e5  # rope_theta 500,000 over 4096 positions ([nnterp] "Loading")
+ROPE_POSITIONS = 4096
 BASE_SEED = 1234
 RING_BYTES = 600 * 2 ** 20  # > 2 x the 256 MB last-level cache
 TOKEN_STEP_BATCHES = (1, 4)  # sequences per whole-model decode step
@@ -672,6 +673,7 @@ def bench_token_step(torch, bl, dev, layers, table, steps, warmup):
     stream = torch.cuda.current_stream(dev)
     res = {}
     packed = sum(l.qkv.numel() + l.o.numel() + l.gate_up.numel() + l.down.numel() for l in layers)
+    rope_tab = bl.rope_table(ROPE_THETA, STACK_HEAD_DIM, ROPE_POSITIONS, dev)
     for B in TOKEN_STEP_BATCHES:
         gen = torch.Generator(device=dev)
         gen.manual_seed(BASE_SEED + B)
@@ -686,7 +688,7 @@ def bench_token_step(torch, bl, dev, layers, table, steps, warmup):
         slot = torch.arange(B, dtype=torch.int64, device=dev)
         pos = torch.full((B,), T - 1, dtype=torch.int64, device=dev)
         spec = bl.BlockSpec(bl.BLOCK_DECODER_CACHED, H, I, cl, STACK_HEADS, STACK_KV_HEADS, STACK_HEAD_DIM, 1e-5,
-                            slot=slot, pos=pos, rope_theta=ROPE_THETA)
+                            slot=slot, pos=pos, rope_table=rope_tab)
         blk, keep = spec.to_c()
         ids = torch.arange(B, dtype=torch.int64, device=dev) * 7919 + 11
         x = torch.empty((B, H), dtype=torch.float32, device=dev)

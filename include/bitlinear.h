@@ -46,7 +46,7 @@ typedef enum {
   BITLINEAR_ERR_ARG = 6        /* an enum or flag argument is out of range */
 } bitlinear_status;
 
-#define BITLINEAR_ABI_VERSION 2
+#define BITLINEAR_ABI_VERSION 3
 #define BITLINEAR_MAX_SEGMENTS 4
 
 /* ---------------------------------------------------------------------------
@@ -245,14 +245,32 @@ size_t bitlinear_lm_head_workspace_bytes(int64_t m, int64_t k);
  * whose slot or position is out of range writes nothing and gets zeros.
  * ------------------------------------------------------------------------- */
 
+/* bitlinear_rope_table — the rotary table, formed on the HOST ([nnterp]
+ * "Loading": Llama's rotate_half with rope_theta 500,000, over 4096 positions;
+ * reading R19): for position p < n_pos and pair e < head_dim/2,
+ *   a = p theta^(-2e/head_dim) in fp64 (the host's libm pow),
+ *   table[p][e] = { fl32(cos a), fl32(sin a) }   (the host's libm cos, sin),
+ * written to the HOST array table of n_pos * head_dim floats. The caller
+ * copies it to the device once (4096 x 64 pairs: 2 MB) and passes it to
+ * bitlinear_rope and to the cached decoder block; forming it once on the host
+ * keeps every RoPE path on identical angles.
+ * Errors: NULL table -> ERR_NULL; head_dim odd or <= 0, n_pos <= 0 ->
+ * ERR_SHAPE; theta not finite and > 0 -> ERR_ARG. Enqueues nothing. */
+bitlinear_status bitlinear_rope_table(double theta, int32_t head_dim, int64_t n_pos, float *table);
+
 /* bitlinear_rope — rotate, in place, the n_heads head vectors of each row of x
  * that start at column col0 (row stride ld floats), token r at position pos[r]
- * (reading R19: pairs (i, i + head_dim/2), angle pos theta^(-2i/head_dim) with
- * its cosine and sine in fp64 rounded to fp32, the rotation in fp32).
+ * (reading R19: pairs (i, i + head_dim/2); v[i], v[i + head_dim/2] <-
+ * v[i] c - v[i + head_dim/2] s, v[i + head_dim/2] c + v[i] s in fp32, with
+ * (c, s) = rope_table[pos[r]][i]).
+ *   rope_table  device [n_pos][head_dim/2][2] fp32 from bitlinear_rope_table,
+ *               8-byte aligned. A position outside [0, n_pos) takes row 0
+ *               (angle 0: the vector is unchanged).
  * Errors: NULL -> ERR_NULL; m < 0, head_dim odd or <= 0, n_heads <= 0,
- * col0 + n_heads head_dim > ld -> ERR_SHAPE; theta <= 0 -> ERR_ARG. */
+ * col0 + n_heads head_dim > ld, n_pos <= 0 -> ERR_SHAPE; misaligned table ->
+ * ERR_ALIGN. m == 0 is a no-op. */
 bitlinear_status bitlinear_rope(float *x, int64_t m, int64_t ld, int64_t col0, int32_t n_heads, int32_t head_dim,
-                                const int64_t *pos, double theta, void *stream);
+                                const int64_t *pos, const float *rope_table, int64_t n_pos, void *stream);
 
 /* bitlinear_kv_append — write each token's keys and values (rows of k and v,
  * stride ld floats, n_kv head_dim values each) rounded to bfloat16 into the
@@ -331,7 +349,7 @@ typedef enum {
      heads share 5 key/value heads). q and k are computed but not consumed. */
   BITLINEAR_BLOCK_DECODER = 1,
   /* The same stack with the attention of a decode step: after q|k|v, RoPE on
-     q and k (bitlinear_rope, base rope_theta), the token's keys and values
+     q and k (bitlinear_rope with the block's rope_table), the token's keys and values
      appended to its layer's caches at (slot[r], pos[r]) (bitlinear_kv_append),
      and each token's causal attention over its sequence's cache
      (bitlinear_attention_decode) feeds attn_sub_norm. Needs head_dim 128 and at
@@ -367,7 +385,10 @@ typedef struct {
      pos[r] (device [m] int64); caches hold n_slots sequences of t_max positions. */
   const int64_t *slot, *pos;
   int64_t n_slots, t_max;
-  double rope_theta;
+  /* DECODER_CACHED: the rotary table (bitlinear_rope_table), device
+     [rope_n_pos][head_dim/2][2] fp32, 8-byte aligned */
+  const float *rope_table;
+  int64_t rope_n_pos;
 } bitlinear_block;
 
 /* Optional per-stage outputs for checking a chain stage by stage. Every pointer

@@ -48,7 +48,7 @@ def _load():
             "orc_bf16_to_f32": (None, [_p, _i64, _p]),
             "orc_final_norm": (None, [_p, _i64, _i64, _p, ctypes.c_float, _p]),
             "orc_lm_head": (None, [_p, _i64, _i64, _p, _i64, _p, _p]),
-            "orc_rope": (None, [_p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _p, ctypes.c_double]),
+            "orc_rope": (None, [_p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _p, ctypes.c_double, _i64]),
             "orc_attention": (_i64, [_p, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p, _i64, _i64,
                                      _p, _p, _p, _p, _p, _p]),
             "orc_base3_row_bytes": (_i64, [_i64]),
@@ -176,13 +176,14 @@ def lm_head(o, w):
     return y, a
 
 
-def rope(x, pos, n_heads: int, head_dim: int, theta: float, col0: int = 0) -> np.ndarray:
+def rope(x, pos, n_heads: int, head_dim: int, theta: float, col0: int = 0, n_pos: int = 4096) -> np.ndarray:
     """O14 (R19): rotate-half RoPE of the n_heads head vectors starting at column
-    col0 of each row of x [m][ld], token r at position pos[r]; returns a copy."""
+    col0 of each row of x [m][ld], token r at position pos[r]; positions outside
+    [0, n_pos) turn by angle 0. Returns a copy."""
     y = np.array(x, dtype=np.float32, order="C", copy=True)
     m, ld = y.shape
     p, pp = _c(np.asarray(pos, dtype=np.int64), np.int64)
-    _load().orc_rope(y.ctypes.data, m, ld, col0, n_heads, head_dim, pp, theta)
+    _load().orc_rope(y.ctypes.data, m, ld, col0, n_heads, head_dim, pp, theta, n_pos)
     return y
 
 

@@ -225,9 +225,9 @@ void orc_relu2_mul(const float *gu, int64_t m, int64_t inter, float *out) {
 }
 
 /* ---- O7: the ternary x int8 contraction ---------------------------------------
- * [nnterp] "The projections quantize their inputs and weights": the projection
- * multiplies the rounded input by the ternary weights, and its output equals
- * the linear map of the rounded input by the ternarized weight.
+ * [nnterp] "The projections quantize their inputs and weights": a projection's
+ * output is exactly the product of its per-token quantized input with its
+ * ternary codes (then rescaled, O8).
  * acc[r][n] = sum_k q[r][k] * c[n][k], exact in int64. R15: stored as int32;
  * returns -1 if a sum does not fit (it cannot for |q| <= 127, K < 2^24). */
 int orc_contract(const int8_t *q, int64_t m, int64_t k, const int8_t *c, int64_t n, int32_t *acc) {
@@ -336,22 +336,26 @@ void orc_lm_head(const uint16_t *o, int64_t m, int64_t k, const uint16_t *w, int
 }
 
 /* ---- O14: rotary position embedding ----------------------------------------------
- * [card] "Model Details": the model uses RoPE; [nnterp] "From the family module":
- * Llama's block; "Config": head_dim 128, max_position_embeddings 4096. The pages
- * give neither the pairing nor the base. R19: Llama's rotate-half pairing, the
- * base theta an argument. For token r at position p and each head vector v of
- * hd values (heads start at column col0 of a row of ld floats), for i < hd/2:
+ * [card] "Model Details": the model uses RoPE; [nnterp] "Loading": Llama's
+ * rotate_half with rope_theta 500,000, over 4096 positions; "Config": head_dim
+ * 128, max_position_embeddings 4096. rotate_half pairs element i of a head with
+ * element i + hd/2. R19 (the pages leave the precision open): for token r at
+ * position p and each head vector v of hd values (heads start at column col0
+ * of a row of ld floats), for i < hd/2:
  *   a = p * theta^(-2i/hd) (fp64), c = fl32(cos a), s = fl32(sin a),
  *   v[i] <- fl32(fl32(v[i] c) - fl32(v[i + hd/2] s)),
- *   v[i + hd/2] <- fl32(fl32(v[i + hd/2] c) + fl32(v[i] s))  (old values). */
+ *   v[i + hd/2] <- fl32(fl32(v[i + hd/2] c) + fl32(v[i] s))  (old values).
+ * The rotary covers positions 0 .. n_pos - 1; a position outside that range
+ * is turned by angle 0 (as position 0 is). */
 void orc_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
-              double theta) {
+              double theta, int64_t n_pos) {
   const int half = hd / 2;
-  for (int64_t r = 0; r < m; ++r)
+  for (int64_t r = 0; r < m; ++r) {
+    const int64_t p = (pos[r] >= 0 && pos[r] < n_pos) ? pos[r] : 0;
     for (int h = 0; h < n_heads; ++h) {
       float *v = x + r * ld + col0 + (int64_t)h * hd;
       for (int i = 0; i < half; ++i) {
-        const double ang = (double)pos[r] * pow(theta, -(2.0 * i) / (double)hd);
+        const double ang = (double)p * pow(theta, -(2.0 * i) / (double)hd);
         const float c = (float)cos(ang), s = (float)sin(ang);
         const float a = v[i], b = v[i + half];
         const float ac = a * c, bs = b * s, bc = b * c, as = a * s;
@@ -359,6 +363,7 @@ void orc_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd
         v[i + half] = bc + as;
       }
     }
+  }
 }
 
 /* ---- O15: one token's attention over its sequence's cache -------------------------

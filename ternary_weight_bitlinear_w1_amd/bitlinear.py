@@ -48,7 +48,7 @@ class Block(ctypes.Structure):
     _fields_ = [("kind", _i32), ("n_layers", _i32), ("hidden", _i64), ("intermediate", _i64),
                 ("n_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("eps", ctypes.c_float),
                 ("layers", ctypes.POINTER(Layer)), ("slot", _p), ("pos", _p), ("n_slots", _i64), ("t_max", _i64),
-                ("rope_theta", ctypes.c_double)]
+                ("rope_table", _p), ("rope_n_pos", _i64)]
 
 
 class Trace(ctypes.Structure):
@@ -84,7 +84,8 @@ def lib():
             "bitlinear_embed": (_i32, [_p, _i64, _p, _i64, _i64, _p, _p]),
             "bitlinear_lm_head": (_i32, [_p, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p, _p, _p, _sz, _p]),
             "bitlinear_lm_head_workspace_bytes": (_sz, [_i64, _i64]),
-            "bitlinear_rope": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, ctypes.c_double, _p]),
+            "bitlinear_rope_table": (_i32, [ctypes.c_double, _i32, _i64, _p]),
+            "bitlinear_rope": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _i64, _p]),
             "bitlinear_kv_append": (_i32, [_p, _p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _i64, _i64, _p]),
             "bitlinear_attention_decode": (_i32, [_p, _i64, _i64, _i32, _i32, _i32, _p, _p, _i64, _i64, _p, _p, _p,
                                                   _i64, _p, _sz, _p]),
@@ -259,11 +260,20 @@ def lm_head(x: torch.Tensor, w_head: torch.Tensor, gain: Optional[torch.Tensor] 
     return (y, normed) if want_normed else y
 
 
-def rope(x: torch.Tensor, pos: torch.Tensor, n_heads: int, head_dim: int, theta: float = 5e5, col0: int = 0):
-    """RoPE in place on the heads of x [m][ld] fp32 starting at column col0."""
+def rope_table(theta: float, head_dim: int, n_pos: int, device) -> torch.Tensor:
+    """The rotary table [n_pos][head_dim/2][2] fp32, formed by the library on the
+    host and copied to ``device``."""
+    host = torch.empty((n_pos, head_dim // 2, 2), dtype=torch.float32)
+    _check("bitlinear_rope_table", lib().bitlinear_rope_table(theta, head_dim, n_pos, host.data_ptr()))
+    return host.to(device)
+
+
+def rope(x: torch.Tensor, pos: torch.Tensor, n_heads: int, head_dim: int, table: torch.Tensor, col0: int = 0):
+    """RoPE in place on the heads of x [m][ld] fp32 starting at column col0, with
+    the rotary table from :func:`rope_table`."""
     m, ld = x.shape
-    _check("bitlinear_rope", lib().bitlinear_rope(_ptr(x), m, ld, col0, n_heads, head_dim, _ptr(pos), theta,
-                                                  _stream(x.device)))
+    _check("bitlinear_rope", lib().bitlinear_rope(_ptr(x), m, ld, col0, n_heads, head_dim, _ptr(pos), _ptr(table),
+                                                  table.shape[0], _stream(x.device)))
     return x
 
 
@@ -365,7 +375,7 @@ class BlockSpec:
     eps: float = 1e-5
     slot: Optional[torch.Tensor] = None   # BLOCK_DECODER_CACHED: device int64 [m]
     pos: Optional[torch.Tensor] = None
-    rope_theta: float = 5e5
+    rope_table: Optional[torch.Tensor] = None  # BLOCK_DECODER_CACHED: device [n_pos][head_dim/2][2] (rope_table())
 
     def to_c(self):
         arr = (Layer * len(self.layers))()
@@ -380,7 +390,8 @@ class BlockSpec:
         if kc is not None:
             n_slots, t_max = kc.shape[0], kc.shape[2]
         blk = Block(self.kind, len(self.layers), self.hidden, self.intermediate, self.n_heads, self.n_kv_heads,
-                    self.head_dim, self.eps, arr, _ptr(self.slot), _ptr(self.pos), n_slots, t_max, self.rope_theta)
+                    self.head_dim, self.eps, arr, _ptr(self.slot), _ptr(self.pos), n_slots, t_max,
+                    _ptr(self.rope_table), self.rope_table.shape[0] if self.rope_table is not None else 0)
         return blk, arr
 
 

@@ -4,6 +4,7 @@
 // status without touching the HIP runtime when they are wrong; then it checks
 // that the current device is gfx950, and enqueues kernels on the caller's
 // stream without synchronizing.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -434,18 +435,37 @@ bitlinear_status bitlinear_lm_head(const float *x, int64_t m, int64_t k, const f
 }
 
 // ---------------------------------------------------------------- attention with a KV cache
-bitlinear_status bitlinear_rope(float *x, int64_t m, int64_t ld, int64_t col0, int32_t n_heads, int32_t head_dim,
-                                const int64_t *pos, double theta, void *stream) {
+bitlinear_status bitlinear_rope_table(double theta, int32_t head_dim, int64_t n_pos, float *table) {
   g_err.clear();
-  if (m != 0 && (!x || !pos)) return fail(BITLINEAR_ERR_NULL, "x and pos are required");
+  if (!table) return fail(BITLINEAR_ERR_NULL, "table is required");
+  if (head_dim <= 0 || head_dim % 2 != 0 || n_pos <= 0 || n_pos > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "head_dim = %d, n_pos = %lld", head_dim, (long long)n_pos);
+  if (!(theta > 0.0) || !std::isfinite(theta)) return fail(BITLINEAR_ERR_ARG, "theta must be finite and > 0");
+  const int half = head_dim / 2;
+  for (int64_t p = 0; p < n_pos; ++p)
+    for (int e = 0; e < half; ++e) {
+      const double ang = (double)p * std::pow(theta, -(2.0 * e) / (double)head_dim);
+      table[2 * (p * half + e)] = (float)std::cos(ang);
+      table[2 * (p * half + e) + 1] = (float)std::sin(ang);
+    }
+  return BITLINEAR_OK;
+}
+
+bitlinear_status bitlinear_rope(float *x, int64_t m, int64_t ld, int64_t col0, int32_t n_heads, int32_t head_dim,
+                                const int64_t *pos, const float *rope_table, int64_t n_pos, void *stream) {
+  g_err.clear();
+  if (m != 0 && (!x || !pos || !rope_table)) return fail(BITLINEAR_ERR_NULL, "x, pos and rope_table are required");
   if (m < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2 != 0 || col0 < 0 ||
-      col0 + (int64_t)n_heads * head_dim > ld || m > kMaxDim || ld > kMaxDim)
-    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, ld = %lld, col0 = %lld, %d heads of %d", (long long)m, (long long)ld,
-                (long long)col0, n_heads, head_dim);
-  if (!(theta > 0.0)) return fail(BITLINEAR_ERR_ARG, "theta must be > 0");
+      col0 + (int64_t)n_heads * head_dim > ld || m > kMaxDim || ld > kMaxDim || n_pos <= 0 || n_pos > kMaxDim)
+    return fail(BITLINEAR_ERR_SHAPE, "m = %lld, ld = %lld, col0 = %lld, %d heads of %d, n_pos = %lld", (long long)m,
+                (long long)ld, (long long)col0, n_heads, head_dim, (long long)n_pos);
+  if (m != 0 && reinterpret_cast<uintptr_t>(rope_table) % 8 != 0)
+    return fail(BITLINEAR_ERR_ALIGN, "rope_table must be 8-byte aligned");
   if (m == 0) return BITLINEAR_OK;
   BL_TRY(check_device());
-  return launched(bl::launch_rope(x, m, ld, col0, n_heads, head_dim, pos, theta, as_stream(stream)), "rope");
+  return launched(bl::launch_rope(x, m, ld, col0, n_heads, head_dim, pos,
+                                  reinterpret_cast<const float2 *>(rope_table), n_pos, as_stream(stream)),
+                  "rope");
 }
 
 bitlinear_status bitlinear_kv_append(const float *k, const float *v, int64_t m, int64_t ld, int32_t n_kv,
@@ -631,7 +651,11 @@ bitlinear_status check_block(const bitlinear_block *blk) {
     if (blk->n_slots <= 0 || blk->t_max <= 0 || blk->n_slots > kMaxDim || blk->t_max > kMaxDim)
       return fail(BITLINEAR_ERR_SHAPE, "n_slots = %lld, t_max = %lld", (long long)blk->n_slots,
                   (long long)blk->t_max);
-    if (!(blk->rope_theta > 0.0)) return fail(BITLINEAR_ERR_ARG, "rope_theta must be > 0");
+    if (!blk->rope_table) return fail(BITLINEAR_ERR_NULL, "rope_table is required");
+    if (reinterpret_cast<uintptr_t>(blk->rope_table) % 8 != 0)
+      return fail(BITLINEAR_ERR_ALIGN, "rope_table must be 8-byte aligned");
+    if (blk->rope_n_pos <= 0 || blk->rope_n_pos > kMaxDim)
+      return fail(BITLINEAR_ERR_SHAPE, "rope_n_pos = %lld", (long long)blk->rope_n_pos);
   }
   for (int l = 0; l < blk->n_layers; ++l) {
     const bitlinear_layer &L = blk->layers[l];
@@ -1042,9 +1066,12 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
   bitlinear_block_trace tr;
   memset(&tr, 0, sizeof tr);
   if (trace) tr = *trace;
-  // every layer rotates q and k at the same positions: their cosines and sines once per call
+  // every layer rotates q and k at the same positions: their rows of the rotary table once per call
   if (blk->kind == BITLINEAR_BLOCK_DECODER_CACHED)
-    BL_TRY(launched(bl::launch_rope_table(blk->pos, m, blk->head_dim, blk->rope_theta, b.rope_cs, s), "rope table"));
+    BL_TRY(launched(bl::launch_rope_gather(blk->pos, m, blk->head_dim,
+                                           reinterpret_cast<const float2 *>(blk->rope_table), blk->rope_n_pos,
+                                           b.rope_cs, s),
+                    "rope rows"));
 
   if (bl::fused_decode_supported(m, H) && bl::fused_decode_supported(m, I) && I % 16 == 0)
     return block_forward_fused(blk, x, m, y, tr, b, s);

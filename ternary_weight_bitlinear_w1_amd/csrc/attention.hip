@@ -4,8 +4,9 @@
 // What is computed ([card] "Model Details": RoPE; [nnterp] "Loading": eager
 // attention without softcap, window or sink; "Config": 20 query and 5
 // key/value heads of 128, bfloat16; readings R19 and R21):
-//   RoPE, per head vector v, i < hd/2: a = p theta^(-2i/hd) (fp64), c = fl32(cos a),
-//     s = fl32(sin a); v[i], v[i + hd/2] <- v[i] c - v[i + hd/2] s, v[i + hd/2] c + v[i] s
+//   RoPE, per head vector v, i < hd/2: (c, s) = the rotary table's row for the
+//     position (fl32 of cos and sin of p theta^(-2i/hd), formed on the host in
+//     fp64); v[i], v[i + hd/2] <- v[i] c - v[i + hd/2] s, v[i + hd/2] c + v[i] s
 //   cache[slot][g][p][:] = bf16(k after RoPE), bf16(v)
 //   out_h = sum_{t <= p} softmax_t(q_h . k_t / sqrt(hd)) v_t, kv head g = h / (heads / kv heads)
 //
@@ -41,18 +42,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return kept + ((dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) ? 1u : 0u);
 }
 
-// one thread per rotated pair
+// one thread per rotated pair; the (cosine, sine) come from the rotary table
+// tab [n_pos][hd/2] (bitlinear_rope_table); a position outside [0, n_pos)
+// takes row 0, angle 0
 __global__ __launch_bounds__(256) void rope_kernel(float *__restrict__ x, int64_t m, int64_t ld, int64_t col0,
                                                    int n_heads, int hd, const int64_t *__restrict__ pos,
-                                                   double theta) {
+                                                   const float2 *__restrict__ tab, int64_t n_pos) {
   const int half = hd / 2;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= m * n_heads * half) return;
   const int64_t r = i / (n_heads * half);
   const int rem = (int)(i - r * n_heads * half);
   const int h = rem / half, e = rem - h * half;
-  const double ang = (double)pos[r] * pow(theta, -(2.0 * e) / (double)hd);
-  const float c = (float)cos(ang), s = (float)sin(ang);
+  const int64_t p = pos[r];
+  const float2 csv = tab[(p >= 0 && p < n_pos ? p : 0) * half + e];
+  const float c = csv.x, s = csv.y;
   float *v = x + r * ld + col0 + (int64_t)h * hd;
   const float a = v[e], b = v[e + half];
   v[e] = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s));
@@ -60,23 +64,25 @@ __global__ __launch_bounds__(256) void rope_kernel(float *__restrict__ x, int64_
 }
 
 // The (cosine, sine) of every rotated pair of every token, cs[r][e] for
-// e < hd/2: the angle p theta^(-2e/hd) in fp64, each rounded to fp32. All
-// layers of a decode step rotate at the same positions, so a step forms this
-// table once and the RoPE epilogues read it.
-__global__ __launch_bounds__(256) void rope_table_kernel(const int64_t *__restrict__ pos, int64_t m, int hd,
-                                                         double theta, float2 *__restrict__ cs) {
+// e < hd/2, gathered from the rotary table at the token's position (row 0
+// outside [0, n_pos)). All layers of a decode step rotate at the same
+// positions, so a step gathers these rows once and the RoPE epilogues read
+// them next to the token's other per-token data.
+__global__ __launch_bounds__(256) void rope_gather_kernel(const int64_t *__restrict__ pos, int64_t m, int hd,
+                                                          const float2 *__restrict__ tab, int64_t n_pos,
+                                                          float2 *__restrict__ cs) {
   const int half = hd / 2;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= m * half) return;
   const int64_t r = i / half;
   const int e = (int)(i - r * half);
-  const double ang = (double)pos[r] * pow(theta, -(2.0 * e) / (double)hd);
-  cs[i] = make_float2((float)cos(ang), (float)sin(ang));
+  const int64_t p = pos[r];
+  cs[i] = tab[(p >= 0 && p < n_pos ? p : 0) * half + e];
 }
 
 // RoPE on the q and k heads of a q|k|v row and the keys and values into the
 // caches, one thread per rotated pair of q or k (plus the matching value pair);
-// the (cosine, sine) come from rope_table_kernel's table
+// the (cosine, sine) come from rope_gather_kernel's rows
 __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, int64_t m, int64_t ld,
                                                           int n_heads, int n_kv, int hd,
                                                           const int64_t *__restrict__ slot,
@@ -344,17 +350,19 @@ bool attention_supported(int n_heads, int n_kv, int hd) {
 }
 
 hipError_t launch_rope(float *x, int64_t m, int64_t ld, int64_t col0, int n_heads, int hd, const int64_t *pos,
-                       double theta, hipStream_t stream) {
+                       const float2 *tab, int64_t n_pos, hipStream_t stream) {
   const int64_t n = m * n_heads * (hd / 2);
   if (n == 0) return hipSuccess;
-  rope_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(x, m, ld, col0, n_heads, hd, pos, theta);
+  rope_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(x, m, ld, col0, n_heads, hd, pos, tab,
+                                                                          n_pos);
   return hipGetLastError();
 }
 
-hipError_t launch_rope_table(const int64_t *pos, int64_t m, int hd, double theta, float2 *cs, hipStream_t stream) {
+hipError_t launch_rope_gather(const int64_t *pos, int64_t m, int hd, const float2 *tab, int64_t n_pos, float2 *cs,
+                              hipStream_t stream) {
   const int64_t n = m * (hd / 2);
   if (n == 0) return hipSuccess;
-  rope_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(pos, m, hd, theta, cs);
+  rope_gather_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(pos, m, hd, tab, n_pos, cs);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@
 // up rows I + the same range, so it can form its slice of mi itself. In the
 // RoPE form a workgroup of the q and k heads owns R/2 rotated pairs of one
 // head (rows e and e + hd/2), so it rotates them itself, with the cosine and
-// sine of each pair read from the step's table (rope_table_kernel) while the
+// sine of each pair read from the step's rows of the rotary table (rope_gather_kernel) while the
 // weights load.
 #include "act_prologue.h"
 

@@ -62,7 +62,7 @@ __device__ __forceinline__ v4i unpack16(uint32_t p) {
 // ROPE form (RT = 2, the cached decoder's q|k|v projection): a workgroup of the
 // q and k heads owns rows e (tile 0) and e + hd/2 (tile 1) of one head for 16
 // consecutive e, so it rotates each pair itself, with the cosine and sine read
-// from the step's table (rope_table_kernel) while the weights load, and writes the
+// from the step's rows of the rotary table (rope_gather_kernel) while the weights load, and writes the
 // keys to the bfloat16 cache; workgroups of the value heads append the values.
 template <int RT, int NW, int SPW, bool ROPE = false>
 __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__restrict__ A,

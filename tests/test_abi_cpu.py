@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bl.lib().bitlinear_abi_version() == 2
+    assert bl.lib().bitlinear_abi_version() == 3
     for s in range(7):
         assert bl.status_name(s)
     assert bl.status_name(0) == "ok"
@@ -221,11 +221,19 @@ def test_embed_and_lm_head_validation():
 
 def test_rope_cache_attention_validation():
     L = bl.lib()
-    assert L.bitlinear_rope(None, 4, 3840, 0, 20, 128, A, 5e5, None) == bl.ERR_NULL
-    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 127, A, 5e5, None) == bl.ERR_SHAPE   # odd head_dim
-    assert L.bitlinear_rope(A, 4, 2560, 128, 20, 128, A, 5e5, None) == bl.ERR_SHAPE  # past the row
-    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 128, A, 0.0, None) == bl.ERR_ARG
-    assert L.bitlinear_rope(None, 0, 3840, 0, 20, 128, None, 5e5, None) == bl.OK
+    assert L.bitlinear_rope(None, 4, 3840, 0, 20, 128, A, A, 4096, None) == bl.ERR_NULL
+    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 128, A, None, 4096, None) == bl.ERR_NULL  # no table
+    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 127, A, A, 4096, None) == bl.ERR_SHAPE   # odd head_dim
+    assert L.bitlinear_rope(A, 4, 2560, 128, 20, 128, A, A, 4096, None) == bl.ERR_SHAPE  # past the row
+    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 128, A, A, 0, None) == bl.ERR_SHAPE     # empty table
+    assert L.bitlinear_rope(A, 4, 3840, 0, 20, 128, A, A + 4, 4096, None) == bl.ERR_ALIGN
+    assert L.bitlinear_rope(None, 0, 3840, 0, 20, 128, None, None, 4096, None) == bl.OK
+    tab = (ctypes.c_float * 8)()
+    assert L.bitlinear_rope_table(5e5, 8, 1, None) == bl.ERR_NULL
+    assert L.bitlinear_rope_table(5e5, 7, 1, tab) == bl.ERR_SHAPE
+    assert L.bitlinear_rope_table(5e5, 8, 0, tab) == bl.ERR_SHAPE
+    assert L.bitlinear_rope_table(0.0, 8, 1, tab) == bl.ERR_ARG
+    assert L.bitlinear_rope_table(float("inf"), 8, 1, tab) == bl.ERR_ARG
     app = L.bitlinear_kv_append
     assert app(A, A, 4, 3840, 5, 128, None, A, A, A, 8, 4096, None) == bl.ERR_NULL
     assert app(A, A, 4, 600, 5, 128, A, A, A, A, 8, 4096, None) == bl.ERR_SHAPE     # 640 > ld
@@ -300,6 +308,37 @@ def test_block_validation():
     bad, k6 = _block(H=72)
     assert f(ctypes.byref(bad), A, 4, A, None, A, 1 << 30, None) == bl.ERR_SHAPE
     assert f(None, A, 4, A, None, A, 1 << 30, None) == bl.ERR_NULL
+
+
+def test_cached_block_needs_a_rope_table():
+    f = bl.lib().bitlinear_block_forward
+    blk, keep = _block(kind=bl.BLOCK_DECODER_CACHED, H=256, I=96, nh=2, nkv=1, hd=128)
+    for i in range(1):
+        keep[i].k_cache = keep[i].v_cache = A
+    blk.slot = blk.pos = A
+    blk.n_slots, blk.t_max = 2, 64
+    assert f(ctypes.byref(blk), A, 4, A, None, A, 1 << 30, None) == bl.ERR_NULL  # no table
+    blk.rope_table, blk.rope_n_pos = A + 4, 4096
+    assert f(ctypes.byref(blk), A, 4, A, None, A, 1 << 30, None) == bl.ERR_ALIGN
+    blk.rope_table, blk.rope_n_pos = A, 0
+    assert f(ctypes.byref(blk), A, 4, A, None, A, 1 << 30, None) == bl.ERR_SHAPE
+
+
+def test_rope_table_equals_the_oracle_angles():
+    """The host-built rotary table ([nnterp] "Loading": theta 500,000, 4096
+    positions) holds, bit for bit, the fp32 cosines and sines the oracle rotates
+    with: rotating the unit vector on the first element of each pair gives (c, s)."""
+    import numpy as np
+    import oracle
+    hd, n_pos = 128, 4096
+    tab = np.empty((n_pos, hd // 2, 2), dtype=np.float32)
+    assert bl.lib().bitlinear_rope_table(5e5, hd, n_pos, tab.ctypes.data) == bl.OK
+    x = np.zeros((n_pos, hd), dtype=np.float32)
+    x[:, :hd // 2] = 1.0
+    ref = oracle.rope(x, np.arange(n_pos), 1, hd, 5e5, n_pos=n_pos)
+    assert np.array_equal(tab[:, :, 0].view(np.uint32), ref[:, :hd // 2].view(np.uint32))
+    assert np.array_equal(tab[:, :, 1].view(np.uint32), ref[:, hd // 2:].view(np.uint32))
+    assert np.all(tab[0, :, 0] == 1.0) and np.all(tab[0, :, 1] == 0.0)
 
 
 def test_library_refuses_to_load_when_missing(tmp_path, monkeypatch):

@@ -1,8 +1,9 @@
 """RoPE, the bfloat16 KV cache and one-token causal attention on the GPU against
 the CPU oracle (readings R19, R21).
 
-RoPE: fp32 outputs within 1e-6 relative (both sides take the angle's cosine and
-sine in fp64 and round them to fp32). Cache appends: the bfloat16 caches equal
+RoPE: fp32 outputs bit for bit (the library forms the rotary table on the host
+with the same fp64 angle and libm cosine and sine that the oracle takes, so both
+sides rotate with identical fp32 values). Cache appends: the bfloat16 caches equal
 the oracle's bit for bit. Attention: fp32 softmax and sums against the oracle's
 fp64, within the bound the fp32 arithmetic allows,
   |out - ref| <= 2^-24 (2 (hd + 1) smag + 2 (192 + S)) vmag,
@@ -44,13 +45,18 @@ def test_rope(m):
     x = synth.activations(seed(40, m, 1), m, q_cols)
     pos = np.random.default_rng(m).integers(0, 4096, size=m).astype(np.int64)
     pos[0] = 0
+    if m > 1:
+        pos[1] = 4095
+    if m > 4:
+        pos[2], pos[3] = -1, 4096  # outside the rotary's positions: angle 0
     want = oracle.rope(oracle.rope(x, pos, NH, HD, THETA, 0), pos, NKV, HD, THETA, NH * HD)
     xg = gpu(x)
     pg = gpu(pos)
-    bl.rope(xg, pg, NH, HD, THETA, 0)
-    bl.rope(xg, pg, NKV, HD, THETA, NH * HD)
+    tab = bl.rope_table(THETA, HD, 4096, DEV)
+    bl.rope(xg, pg, NH, HD, tab, 0)
+    bl.rope(xg, pg, NKV, HD, tab, NH * HD)
     got = host(xg)
-    assert_rel(got, want, tol=1e-6, what="rope")
+    assert_equal(got, want, "rope")
     assert np.array_equal(got[:, NH * HD + 2 * NKV * HD - NKV * HD:], x[:, NH * HD + NKV * HD:]), "values untouched"
 
 

@@ -330,6 +330,8 @@ def test_rope_position_zero_is_identity_and_pairs_keep_length():
     r = rng(16)
     x = r.normal(size=(3, 2 * 128)).astype(np.float32)
     assert np.array_equal(oracle.rope(x, [0, 0, 0], 2, 128, 5e5), x)
+    # outside the rotary's 4096 positions the angle is 0 (reading R19)
+    assert np.array_equal(oracle.rope(x, [-1, 4096, 10 ** 9], 2, 128, 5e5), x)
     y = oracle.rope(x, [1, 517, 4095], 2, 128, 5e5).astype(np.float64).reshape(3, 2, 2, 64)
     xx = x.astype(np.float64).reshape(3, 2, 2, 64)
     n0 = xx[:, :, 0] ** 2 + xx[:, :, 1] ** 2
