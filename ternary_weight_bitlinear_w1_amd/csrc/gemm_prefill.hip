@@ -368,8 +368,8 @@ __global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_
   // ---- issue side: the chunk stream (tile is_i, chunk is_kc)
   int is_i = 0, is_kc = 0, is_m0, is_n0, is_s;
   coords(0, is_m0, is_n0, is_s);
-  // per-lane source offsets of the current issue tile (32-bit: M K and N K / 4
-  // stay below 2^31 for every shape the host passes)
+  // per-lane source offsets of the current issue tile (32-bit: pick_cfg sends
+  // only shapes with M K and N K / 4 below 2^31 here)
   uint32_t a_off[LA], b_off[LB];
   auto set_src = [&]() {
 #pragma unroll
@@ -617,6 +617,7 @@ hipError_t launch_generic(const int8_t *codes, const uint8_t *packed, const floa
                           int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;  // one workgroup per tile
   gemm_generic_kernel<WM, WN, TM, TN>
       <<<dim3((unsigned)tiles), dim3(WM * WN * 64), 0, stream>>>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out);
   return hipGetLastError();
@@ -698,10 +699,16 @@ bool wide_pays(int64_t m, int64_t n) {
   return r_wide * BL_GEMM_WIDE_BN < r_big * 2 * BL_GEMM_BIG_BN;
 }
 
+// The pipelined kernel keeps its per-lane source offsets in 32 bits, so it
+// takes only shapes whose codes (m k bytes) and packed weights (n k / 4 bytes)
+// stay below 2^31; larger ones go to the generic kernel's 64-bit indexing.
+constexpr int64_t kPipelinedMaxBytes = (int64_t)1 << 31;
+
 int pick_cfg(int64_t m, int64_t n, int64_t k, int64_t *bm, int64_t *bn) {
   *bm = 0;
   *bn = 0;
   if (k % 128 != 0) return CFG_GENERIC;
+  if (m * k >= kPipelinedMaxBytes || n * (k / 4) >= kPipelinedMaxBytes) return CFG_GENERIC;
   if (wide_pays(m, n)) { *bm = 128; *bn = BL_GEMM_WIDE_BN; return CFG_WIDE; }
   if (n % BL_GEMM_BIG_BN == 0 && m > 64) { *bm = 128; *bn = BL_GEMM_BIG_BN; return CFG_BIG; }
   if (n % 256 == 0 && m > 64) { *bm = 128; *bn = 256; return CFG_2224; }
@@ -738,7 +745,8 @@ int gemm_prefill_splits(int64_t m, int64_t n, int64_t k) {
 }
 
 bool gemm_glu_supported(int64_t m, int64_t inter, int64_t k) {
-  return m > 64 && k % 128 == 0 && inter % (BL_GEMM_BIG_BN / 2) == 0 && inter > 0;
+  return m > 64 && k % 128 == 0 && inter % (BL_GEMM_BIG_BN / 2) == 0 && inter > 0 && m * k < kPipelinedMaxBytes &&
+         2 * inter * (k / 4) < kPipelinedMaxBytes;
 }
 
 hipError_t launch_gemm_glu(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,

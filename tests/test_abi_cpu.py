@@ -287,6 +287,15 @@ def _block(kind=bl.BLOCK_DECODER, H=64, I=96, nh=8, nkv=2, hd=8, layers=1, null_
     return bl.Block(kind, layers, H, I, nh, nkv, hd, 1e-5, arr), arr
 
 
+def test_large_shapes_leave_the_32bit_pipelined_gemm():
+    """Codes or packed weights of 2^31 bytes and more take the generic GEMM
+    (64-bit offsets), which does not split K: no partial-sum workspace."""
+    f = bl.lib().bitlinear_forward_workspace_bytes
+    k_under, k_over = (1 << 25) - 128, 1 << 25  # 256 rows of k/4 bytes: under / at 2^31
+    assert f(64, 256, k_under, 0) > 256       # the pipelined 64-token tile splits K
+    assert f(64, 256, k_over, 0) == 256       # row sums only
+
+
 def test_block_validation():
     f = bl.lib().bitlinear_block_forward
     blk, keep = _block()

@@ -364,3 +364,28 @@ def test_forward_prefill_full_size(proj):
         seg = int(np.searchsorted(ends, c, side="right"))
         y_col = oracle.rescale(acc_c[:, j:j + 1], do, [gammas[seg]], [1])
         assert_equal(yh[:, c:c + 1], y_col, f"y (column {c}, all rows)")
+
+
+def test_forward_codes_past_32bit_offsets():
+    """Codes of 65600 x 65536 bytes (4.3 GB, past 2^32): rows whose byte offset
+    does not fit 32 bits contract like the first ones. Sampled rows on both sides
+    of 2^31 and 2^32 are checked against the oracle: int32 sums and fp32 outputs
+    bit for bit."""
+    m, n, k = 65600, 256, 65536
+    note(f"forward past 32-bit offsets m={m} n={n} k={k}")
+    mat = Matrix(n, k, seed(7, 1, 1))
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed(7, 1, 2))
+    codes = torch.randint(-127, 128, (m, k), dtype=torch.int8, device=DEV, generator=gen)
+    deq = (torch.rand((m,), dtype=torch.float32, device=DEV, generator=gen) + 0.5) / 127.0
+    y, acc = bl.forward(gpu(oracle.pack(mat.codes)), k, [mat.gamma_f], codes=codes, deq=deq, want_acc=True,
+                        path=bl.PATH_PREFILL)
+    rows = [0, 1, 32767, 32768, 65535, 65536, 65599]
+    idx = torch.tensor(rows, device=DEV)
+    q = host(codes.index_select(0, idx))
+    d = host(deq.index_select(0, idx))
+    a_gpu, y_gpu = host(acc.index_select(0, idx)), host(y.index_select(0, idx))
+    del codes, y, acc
+    acc_o = oracle.contract(q, mat.codes)
+    assert_equal(a_gpu, acc_o, "acc")
+    assert_equal(y_gpu, oracle.rescale(acc_o, d, [mat.gamma], [n]), "y")
