@@ -223,7 +223,11 @@ def test_decoder_stack_split_chain(m, hdim, inter, nh, nkv, hd):
 
 def test_decoder_stack_30_layers():
     """30 layers at the 2B4T shapes (H 2560, I 6912, 20 / 5 heads of 128, gains 1):
-    M = 1 in full, and 3 sampled tokens of M = 64, all from the same weights."""
+    M = 1 in full, and 3 sampled tokens of M = 64, all from the same weights. At
+    M = 64 every projection but gate|up splits K; the traced run is compared
+    stage by stage on the sampled tokens (codes and int32 sums bit-exact), and
+    the untraced run, whose quantizations read the split partial sums, must give
+    the traced output bit for bit."""
     hdim, inter, nh, nkv, hd, layers = 2560, 6912, 20, 5, 128, 30
     kvd = nkv * hd
     note("block decoder 30 layers, M=1 and M=64")
@@ -245,7 +249,14 @@ def test_decoder_stack_30_layers():
     for l in range(layers):
         _compare_layer(tr, l, {k: _rows(v, [0]) for k, v in refs[l].items()})
     assert_rel(host(y1), xo[:1], what="M=1 output")
+    del tr
+    tr64 = _trace(layers, 64, hdim, inter, hdim + 2 * kvd)
+    y64t = bl.block_forward(spec, gpu(x64), trace=tr64)
+    for l in range(layers):
+        _compare_layer(tr64, l, {k: _rows(v, [1, 2, 3]) for k, v in refs[l].items()}, rows=samples)
+    del tr64
     y64 = bl.block_forward(spec, gpu(x64))
+    assert_equal(host(y64), host(y64t), "M=64 untraced output")
     assert_rel(host(y64)[samples], xo[1:], what="M=64 sampled outputs")
 
 
