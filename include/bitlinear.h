@@ -153,6 +153,24 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
                                    size_t workspace_bytes, void *stream);
 size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside);
 
+/* bitlinear_forward_noalloc — bitlinear_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Arguments and result as bitlinear_forward,
+ * without the workspace: the scratch is a device array inside the library of
+ * bitlinear_forward_noalloc_max_scratch_bytes() = 32 MiB, one per GPU, held
+ * from the first call on that GPU until the process ends. The call allocates
+ * nothing (no hipMalloc, no allocating library routine). A shape whose
+ * workspace (bitlinear_forward_workspace_bytes) exceeds the limit returns
+ * ERR_WORKSPACE. Nothing in the scratch needs to start at zero; it keeps the
+ * last call's contents. All calls on one GPU share the array: calls that may
+ * overlap on one GPU (concurrent streams, threads) race and must be
+ * serialized by the caller. Errors otherwise as bitlinear_forward. */
+bitlinear_status bitlinear_forward_noalloc(const float *x, const int8_t *codes_in, const float *deq_in,
+                                           const int32_t *rowsum_in, int64_t m, int64_t k, const uint8_t *w_packed,
+                                           int64_t n, const float *gamma, const int64_t *seg_end, int32_t n_seg,
+                                           float *y, int32_t *acc_out, int32_t path, void *stream);
+size_t bitlinear_forward_noalloc_max_scratch_bytes(void);
+
 /* bitlinear_forward_online — the projection in the checkpoint mode that keeps
  * the full-precision weights and ternarizes them in every forward ("The two
  * checkpoints": the online mode; "The projections quantize their inputs and

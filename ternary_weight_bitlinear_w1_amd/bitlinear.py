@@ -76,6 +76,9 @@ def lib():
             "bitlinear_forward": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _p, _i32, _p, _sz,
                                          _p]),
             "bitlinear_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+            "bitlinear_forward_noalloc": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _p, _i32,
+                                                 _p]),
+            "bitlinear_forward_noalloc_max_scratch_bytes": (_sz, []),
             "bitlinear_forward_relu2_glu": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _sz, _p]),
             "bitlinear_forward_online": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _i32, _p, _p, _p, _i32, _p,
                                                 _sz, _p]),
@@ -186,6 +189,31 @@ def forward(packed: torch.Tensor, k: int, gamma: Sequence[float], seg_end: Optio
            lib().bitlinear_forward(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), n, g, se,
                                    len(gamma), _ptr(y), _ptr(acc), path, _ptr(ws), nb, _stream(dev)))
     return (y, acc) if want_acc else y
+
+
+def forward_noalloc(packed: torch.Tensor, k: int, gamma: Sequence[float], seg_end: Optional[Sequence[int]] = None,
+                    x: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+                    deq: Optional[torch.Tensor] = None, rowsum: Optional[torch.Tensor] = None,
+                    want_acc: bool = False, path: int = PATH_AUTO, out: Optional[torch.Tensor] = None,
+                    acc_out: Optional[torch.Tensor] = None):
+    """:func:`forward` through the entry point that allocates nothing (its
+    scratch is the library's own per-device array). With ``out`` (and
+    ``acc_out``) given, this function allocates nothing either."""
+    n = packed.shape[0]
+    src = x if x is not None else codes
+    m = src.shape[0]
+    dev = packed.device
+    if seg_end is None:
+        seg_end = [n]
+    g = (ctypes.c_float * len(gamma))(*[float(v) for v in gamma])
+    se = (ctypes.c_int64 * len(seg_end))(*[int(v) for v in seg_end])
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    acc = acc_out if acc_out is not None else (
+        torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None)
+    _check("bitlinear_forward_noalloc",
+           lib().bitlinear_forward_noalloc(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(packed), n, g,
+                                           se, len(gamma), _ptr(y), _ptr(acc), path, _stream(dev)))
+    return (y, acc) if acc is not None else y
 
 
 def forward_online(w_master: torch.Tensor, seg_end: Optional[Sequence[int]] = None,

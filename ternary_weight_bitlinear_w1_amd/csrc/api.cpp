@@ -27,6 +27,12 @@ bitlinear_status fail(bitlinear_status s, const char *fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+bitlinear_status bl::report_error(bitlinear_status s, const char *reason) { return fail(s, "%s", reason); }
+
+namespace {
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }

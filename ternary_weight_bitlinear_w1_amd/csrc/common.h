@@ -9,6 +9,9 @@
 
 namespace bl {
 
+// Sets the reason bitlinear_last_error() reports on this thread; returns s.
+bitlinear_status report_error(bitlinear_status s, const char *reason);
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
