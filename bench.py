@@ -202,6 +202,20 @@ def main():
 
     gu_ms = back_to_back(f_gu, args.steps)
     d_ms = back_to_back(f_d, args.steps)
+    # the plain gate|up GEMM of the prefill workload (two weight scales, fp32
+    # [4096][13824] output: the ungated form, twice the output bytes)
+    y_gu = torch.empty((M, 2 * I), dtype=torch.float32, device=dev)
+
+    def f_gu_plain():
+        ok(L.bitlinear_forward(None, codes1.data_ptr(), deq1.data_ptr(), rs1.data_ptr(), M, H, packed_gu.data_ptr(),
+                               2 * I, g_gu_c, se_gu, 2, y_gu.data_ptr(), None, bl.PATH_PREFILL, ws.data_ptr(), ws_n,
+                               sp), "gate|up plain")
+
+    f_gu_plain()
+    gu_plain_ms = back_to_back(f_gu_plain, args.steps)
+    del y_gu
+    gu_plain_tops = ops_gu / (gu_plain_ms * 1e-3) / 1e12
+    log(f"plain gate|up (fp32 [4096][13824] out) alone {gu_plain_ms * 1e3:.1f} us ({gu_plain_tops:.0f} TOPS)")
     gu_tops = ops_gu / (gu_ms * 1e-3) / 1e12
     d_tops = ops_d / (d_ms * 1e-3) / 1e12
     log(f"gated gate|up alone {gu_ms * 1e3:.1f} us ({gu_tops:.0f} TOPS), down alone {d_ms * 1e3:.1f} us "
@@ -216,11 +230,17 @@ def main():
                                "frac_mfma": gu_tops / PEAK_INT8_TOPS},
         "gemm_down": {"ms": d_ms, "ms_in_step": per_op["gemm_down"], "tops": d_tops,
                       "frac_mfma": d_tops / PEAK_INT8_TOPS},
+        "gemm_gate_up_plain": {"ms": gu_plain_ms, "tops": gu_plain_tops, "frac_mfma": gu_plain_tops / PEAK_INT8_TOPS,
+                               "what": "gate|up 2560 -> 2 x 6912, fp32 [4096][13824] output, no gating"},
         "quant_x": {"ms": per_op["quant_x"], "gbs": q1_bytes / (per_op["quant_x"] * 1e-3) / 1e9},
         "quant_subnorm": {"ms": per_op["quant_subnorm"], "gbs": q2_bytes / (per_op["quant_subnorm"] * 1e-3) / 1e9},
     }
     for kq in ("quant_x", "quant_subnorm"):
         kernels[kq]["frac_hbm"] = kernels[kq]["gbs"] / PEAK_HBM_GBS
+
+    # ---------------------------------------------------------------- measured peaks, small workloads
+    peaks = bench_peaks(torch, bl, dev)
+    small = bench_small_configs(torch, bl, synth, dev, max(20, args.steps))
 
     # ---------------------------------------------------------------- decode
     decode = None
@@ -270,9 +290,13 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_prefill gated (gate|up + ReLU^2, M=4096 N=2x6912 K=2560)",
                      "achieved": round(gu_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tops / PEAK_INT8_TOPS, 4), "traffic": measured_traffic(),
+                     "peak_measured": peaks["mfma_int8_tops"],
+                     "frac_of_measured": round(gu_tops / peaks["mfma_int8_tops"], 4),
                      "algorithmic_ops_per_launch": ops_gu,
                      "algorithmic_bytes_per_launch": M * H + 2 * I * H // 4 + 4 * M * I + 8 * M},
         "kernels": kernels,
+        "peaks_measured": peaks,
+        "small_configs": small,
         "decode_roofline": decode_roofline(decode),
         "decode": decode,
         "online": online,
@@ -283,20 +307,122 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def bench_peaks(torch, bl, dev):
+    """What this GPU reaches on its two bounds, measured here with the library's
+    probes: a read stream over 2 GiB (larger than the last-level cache) and
+    independent int8 MFMA chains on every SIMD (two waves per SIMD)."""
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    buf = torch.ones(2 ** 29, dtype=torch.float32, device=dev)  # 2 GiB
+    nb = buf.numel() * 4
+
+    def timed(f, reps):
+        f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    t_read = timed(lambda: bl.probe_read(buf, sink=sink), 10)
+    del buf
+    torch.cuda.empty_cache()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters, wgs = 4000, 2 * cus
+    t_mfma = timed(lambda: bl.probe_mfma(iters, wgs, sink), 5)
+    mfma_ops = wgs * 4 * iters * 8 * 65536.0
+    res = {"hbm_read_gbs": round(nb / t_read / 1e9, 1), "mfma_int8_tops": round(mfma_ops / t_mfma / 1e12, 1),
+           "compute_units": cus,
+           "what": "read probe over 2 GiB; int8 MFMA probe: 2 workgroups x 4 waves per CU, 8 independent "
+                   "v_mfma_i32_32x32x32_i8 chains per wave"}
+    log(f"measured peaks: HBM read {res['hbm_read_gbs']:.0f} GB/s (spec {PEAK_HBM_GBS:.0f}), int8 MFMA "
+        f"{res['mfma_int8_tops']:.0f} TOPS (spec {PEAK_INT8_TOPS:.0f})")
+    return res
+
+
+def bench_small_configs(torch, bl, synth, dev, reps):
+    """The two small workloads, each a chain of a few launches: the single layer
+    (M=128, K=256 -> N=512, quantization inside bitlinear_forward) and the FFN
+    block (M=1024, hidden 512, intermediate 2048, bitlinear_block_forward).
+    Mean time per call over back-to-back calls, and its int8 TOPS."""
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    # single layer
+    m, k, n = 128, 256, 512
+    w = torch.from_numpy(synth.weights(synth.stream_seed(BASE_SEED, 1, 0, 1), n, k)).to(dev)
+    packed, g = bl.quantize_weights(w)
+    gam = [float(np.float32(g.item()))]
+    x = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 1, 0, 5), m, k, 4)).to(dev)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+    def timed(f):
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    us = timed(lambda: bl.forward(packed, k, gam, x=x, out=y))
+    res["single_layer"] = {"us": round(us, 2), "tops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 3),
+                           "launches": 2, "workload": "M=128, K=256 -> N=512, fp32 in and out"}
+    # FFN block
+    m, hd, it = 1024, 512, 2048
+    mats = [synth.weights(synth.stream_seed(BASE_SEED, 2, 0, t), n_, k_) for t, (n_, k_) in
+            enumerate(((it, hd), (it, hd), (hd, it)))]
+    pk, gm = [], []
+    for wm in mats:
+        p_, g_ = bl.quantize_weights(torch.from_numpy(wm).to(dev))
+        pk.append(p_)
+        gm.append(float(np.float32(g_.item())))
+    lw = bl.LayerWeights(gate_up=torch.cat(pk[:2]), gate_up_gamma=gm[:2], down=pk[2], down_gamma=gm[2])
+    spec = bl.BlockSpec(bl.BLOCK_FFN, hd, it, [lw])
+    xb = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 2, 0, 5), m, hd)).to(dev)
+    yb = torch.empty_like(xb)
+    ws = torch.empty(max(1, bl.block_workspace_bytes(spec, m)), dtype=torch.uint8, device=dev)
+    us = timed(lambda: bl.block_forward(spec, xb, out=yb, workspace=ws))
+    res["ffn_block"] = {"us": round(us, 2), "tops": round(2.0 * m * 3 * it * hd / (us * 1e-6) / 1e12, 2),
+                        "workload": "M=1024, hidden 512, intermediate 2048: quantize, gate|up + ReLU^2, "
+                                    "ffn_sub_norm quantize, down"}
+    log(f"single layer {res['single_layer']['us']:.1f} us; FFN block {res['ffn_block']['us']:.1f} us "
+        f"({res['ffn_block']['tops']:.0f} TOPS)")
+    return res
+
+
 def decode_roofline(decode):
-    """The one-token gate|up GEMV against 8 TB/s of packed-weight reads: one
-    2B4T projection per launch (bound by the launch's fixed cost, with a device
-    copy of the same bytes beside it) and one launch over the whole ring."""
+    """The decode GEMV at the decode-sweep shapes (gate|up 2560 -> 2 x 6912 and
+    down 6912 -> 2560, M = 1, 4, 16), one projection per launch, in packed-weight
+    GB/s against 8 TB/s, with the read probe's time over the same bytes (the
+    per-launch floor) beside each. The launch over the whole 628 MB ring is a
+    probe of the kernel's streaming rate without that floor, not a workload."""
     if not decode or "gate_up_m1" not in decode:
         return None
-    one, ring = decode["gate_up_m1"], decode.get("gate_up_m1_whole_ring")
-    copy = decode.get("gate_up_copy_reference")
-    return {"bound": "hbm", "kernel": "gemv_dot4 m=1, gate|up 2560 -> 2x6912 packed 2-bit", "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "one_projection": {"achieved": one["gbs_packed"], "frac": one["frac_hbm"], "us": one["us"],
-                               "device_copy_us": copy["us"] if copy else None},
-            "whole_ring": ({"achieved": ring["gbs_packed"], "frac": ring["frac_hbm"], "us": ring["us"],
-                            "bytes": ring["packed_bytes"]} if ring else None)}
+    shapes = {}
+    for name in ("gate_up", "down"):
+        floor = decode.get(f"{name}_read_floor")
+        for m in (1, 4, 16):
+            r = decode.get(f"{name}_m{m}")
+            if r:
+                shapes[f"{name}_m{m}"] = {"achieved": r["gbs_packed"], "frac": r["frac_hbm"], "us": r["us"],
+                                          "read_floor_us": floor["us"] if floor else None,
+                                          "us_vs_read_floor": r.get("us_vs_read_floor")}
+    one = decode["gate_up_m1"]
+    ring = decode.get("gate_up_m1_probe_whole_ring")
+    return {"bound": "hbm", "kernel": "decode GEMV (gemv_dot4 at m=1, gemv_decode at m=4 and 16), packed 2-bit",
+            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "achieved": one["gbs_packed"], "frac": one["frac_hbm"], "shape": "gate|up m=1",
+            "config_shapes": shapes,
+            "probe_whole_ring": ({"achieved": ring["gbs_packed"], "frac": ring["frac_hbm"], "us": ring["us"],
+                                  "bytes": ring["packed_bytes"],
+                                  "what": "one launch over every ring copy stacked (not a workload shape)"}
+                                 if ring else None)}
 
 
 def measured_traffic():
@@ -316,19 +442,43 @@ def measured_traffic():
     return None
 
 
+def graph_per_launch_us(torch, launch, reps, replays=4):
+    """Mean GPU time per launch of reps launches captured back to back in one HIP
+    graph (launch(i, stream) enqueues launch i on the given stream), so the host's
+    cost per call does not pace the GPU."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sp = torch.cuda.current_stream().cuda_stream
+        for i in range(reps):
+            launch(i, sp)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (replays * reps) * 1e3
+
+
 def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d):
     """Weight-streaming kernel at M = 1, 4, 16; each launch reads another copy of the
-    packed weights from a ring larger than the last-level cache."""
+    packed weights from a ring larger than the last-level cache. Back-to-back
+    launches are captured in a HIP graph and replayed."""
     res = {}
     L = bl.lib()
-    sp = torch.cuda.current_stream(dev).cuda_stream
     stream = torch.cuda.current_stream(dev)
+    sp0 = stream.cuda_stream
     for name, packed, k, gam, seg in (("gate_up", packed_gu, H, gam_gu, [I, 2 * I]),
                                       ("down", packed_d, I, gam_d, [H])):
         n = packed.shape[0]
         nbytes = packed.numel()
         copies = max(2, RING_BYTES // nbytes)
         ring = packed.unsqueeze(0).repeat(copies, 1, 1)
+        ptrs = [ring[i].data_ptr() for i in range(copies)]
         g_c = (bl.ctypes.c_float * len(gam))(*gam)
         se_c = (bl.ctypes.c_int64 * len(seg))(*seg)
         for m in (1, 4, 16):
@@ -338,91 +488,97 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
             ws_n = L.bitlinear_forward_workspace_bytes(m, n, k, 0)
             ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+            cp, dp, rp, yp, wp = codes.data_ptr(), deq.data_ptr(), rs.data_ptr(), y.data_ptr(), ws.data_ptr()
 
-            def launch(i):
-                st = L.bitlinear_forward(None, codes.data_ptr(), deq.data_ptr(), rs.data_ptr(), m, k,
-                                         ring[i % copies].data_ptr(), n, g_c, se_c, len(gam), y.data_ptr(), None,
-                                         bl.PATH_DECODE, ws.data_ptr(), ws_n, sp)
+            def launch(i, sp):
+                st = L.bitlinear_forward(None, cp, dp, rp, m, k, ptrs[i % copies], n, g_c, se_c, len(gam), yp, None,
+                                         bl.PATH_DECODE, wp, ws_n, sp)
                 if st != 0:
                     raise RuntimeError(L.bitlinear_last_error().decode())
 
             for i in range(20):
-                launch(i)
+                launch(i, sp0)
             torch.cuda.synchronize()
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
             for i in range(reps):
                 evs[i][0].record(stream)
-                launch(i)
+                launch(i, sp0)
                 evs[i][1].record(stream)
             torch.cuda.synchronize()
-            per = [a.elapsed_time(b) for a, b in evs]
-            us = float(np.median(per)) * 1e3
-            # back-to-back launches (includes the gaps between dispatches)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(reps):
-                launch(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            b2b_us = e0.elapsed_time(e1) / reps * 1e3
+            us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+            b2b_us = graph_per_launch_us(torch, launch, reps)
             gbs = nbytes / (b2b_us * 1e-6) / 1e9
             res[f"{name}_m{m}"] = {"us": round(b2b_us, 3), "gbs_packed": round(gbs, 1),
                                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "single_launch_event_us": round(us, 3),
                                    "packed_bytes": nbytes, "ring_copies": copies}
-            log(f"decode {name} m={m}: {b2b_us:.2f} us/launch back-to-back, {gbs:.0f} GB/s "
+            log(f"decode {name} m={m}: {b2b_us:.2f} us/launch back-to-back (graph), {gbs:.0f} GB/s "
                 f"(one launch between events: {us:.2f} us)")
             if m <= 4:
-                res[f"{name}_m{m}_whole_ring"] = bench_decode_tall(torch, L, bl, ring, k, gam[0], seg[0], codes, deq,
-                                                                   rs, y, reps, name, m, sp, stream)
+                res[f"{name}_m{m}_probe_whole_ring"] = bench_decode_tall(torch, L, bl, ring, k, gam[0], seg[0], codes,
+                                                                         deq, rs, y, reps, name, m, sp0, stream)
         # reference: a device copy of the same bytes (one ring copy per launch,
         # back to back; it reads them once and writes them once) -- the cost of
         # one launch that moves these bytes on this GPU
         dst = torch.empty_like(ring[0])
-        for i in range(20):
-            dst.copy_(ring[i % copies])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            dst.copy_(ring[i % copies])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        floor_us = e0.elapsed_time(e1) / reps * 1e3
+        views = [ring[i] for i in range(copies)]
+        floor_us = graph_per_launch_us(torch, lambda i, sp: dst.copy_(views[i % copies]), reps)
         res[f"{name}_copy_reference"] = {"us": round(floor_us, 3),
                                          "gbs_read": round(nbytes / (floor_us * 1e-6) / 1e9, 1),
                                          "what": "device copy of the same packed bytes, one ring copy per launch"}
         log(f"decode {name}: a device copy of the same {nbytes} bytes takes {floor_us:.2f} us/launch "
             f"({nbytes / (floor_us * 1e-6) / 1e9:.0f} GB/s read)")
-        del ring, dst
+        # the read floor: the library's read probe over the same bytes (one ring
+        # copy per launch, back to back), the least time one launch that reads
+        # them takes on this GPU (the best of four launch shapes: 8, 4, 2 or 1
+        # loads of 16 bytes per thread)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        shapes = {}
+        for per_thread in (8, 4, 2, 1):
+            grid = -(-nbytes // (16 * 256 * per_thread))
+
+            def probe(i, sp, grid=grid):
+                st = L.bitlinear_probe_read(ptrs[i % copies], nbytes, grid, sink.data_ptr(), sp)
+                if st != 0:
+                    raise RuntimeError(L.bitlinear_last_error().decode())
+
+            shapes[per_thread] = graph_per_launch_us(torch, probe, reps)
+        best = min(shapes, key=shapes.get)
+        read_us = shapes[best]
+        res[f"{name}_read_floor"] = {"us": round(read_us, 3),
+                                     "gbs_read": round(nbytes / (read_us * 1e-6) / 1e9, 1),
+                                     "loads_per_thread": best,
+                                     "us_by_loads_per_thread": {str(k_): round(v, 3) for k_, v in shapes.items()},
+                                     "what": "read probe over the same packed bytes, one ring copy per launch, "
+                                             "the fastest of four launch shapes"}
+        for m in (1, 4, 16):
+            res[f"{name}_m{m}"]["us_vs_read_floor"] = round(res[f"{name}_m{m}"]["us"] / read_us, 3)
+        log(f"decode {name}: the read probe over the same {nbytes} bytes takes {read_us:.2f} us/launch "
+            f"({nbytes / (read_us * 1e-6) / 1e9:.0f} GB/s)")
+        del ring, dst, views
         torch.cuda.empty_cache()
         # the same projection from the base-3 storage (five codes per byte), m = 1 and 4
         w3 = bl.pack_base3(packed, k)
         nb3 = w3.numel()
         copies = max(2, RING_BYTES // nb3)
         ring = w3.unsqueeze(0).repeat(copies, 1, 1)
+        ptrs3 = [ring[i].data_ptr() for i in range(copies)]
         for m in (1, 4):
             xm = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 3, m, 5), m, k,
                                                     synth.outlier_count(k))).to(dev)
             codes, deq, _ = bl.quantize_acts(xm)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            cp, dp, yp = codes.data_ptr(), deq.data_ptr(), y.data_ptr()
 
-            def launch3(i):
-                st = L.bitlinear_forward_base3(None, codes.data_ptr(), deq.data_ptr(), m, k,
-                                               ring[i % copies].data_ptr(), n, g_c, se_c, len(gam), y.data_ptr(),
+            def launch3(i, sp):
+                st = L.bitlinear_forward_base3(None, cp, dp, m, k, ptrs3[i % copies], n, g_c, se_c, len(gam), yp,
                                                None, None, 0, sp)
                 if st != 0:
                     raise RuntimeError(L.bitlinear_last_error().decode())
 
             for i in range(20):
-                launch3(i)
+                launch3(i, sp0)
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(reps):
-                launch3(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            b2b_us = e0.elapsed_time(e1) / reps * 1e3
+            b2b_us = graph_per_launch_us(torch, launch3, reps)
             gbs = nb3 / (b2b_us * 1e-6) / 1e9
             res[f"{name}_base3_m{m}"] = {"us": round(b2b_us, 3), "gbs_stored": round(gbs, 1),
                                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "stored_bytes": nb3,
@@ -531,11 +687,13 @@ def bench_head(torch, bl, synth, dev, reps, table):
 
 
 def bench_online(torch, bl, synth, dev, reps, w_gate, w_up):
-    """The online checkpoint mode at one decode token: the fp32 gate and up masters
+    """The online checkpoint mode at one decode token: the gate and up masters
     (2 x 6912 x 2560) are ternarized inside every forward (a mean|W| pass and a
-    ternarize pass per matrix, each reading the masters), then projected."""
-    w = torch.from_numpy(np.concatenate([w_gate, w_up])).to(dev)
-    n, k = w.shape
+    ternarize pass per matrix, each reading the masters), then projected. Both
+    master storages: fp32, and bfloat16 (the bf16 checkpoint: the fp32 masters
+    rounded to bfloat16, half the bytes)."""
+    w32 = torch.from_numpy(np.concatenate([w_gate, w_up])).to(dev)
+    n, k = w32.shape
     x = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 3, 1, 5), 1, k, synth.outlier_count(k))).to(dev)
     seg = (bl.ctypes.c_int64 * 2)(n // 2, n)
     L = bl.lib()
@@ -543,31 +701,35 @@ def bench_online(torch, bl, synth, dev, reps, w_gate, w_up):
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     y = torch.empty((1, n), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    res = {"workload": "online mode, gate|up 2560 -> 2 x 6912 masters, one token"}
+    for name, w, dt, esize in (("f32", w32, bl.MASTER_F32, 4),
+                               ("bf16", w32.to(torch.bfloat16).view(torch.uint16), bl.MASTER_BF16, 2)):
+        def run():
+            st = L.bitlinear_forward_online(x.data_ptr(), None, None, None, 1, k, w.data_ptr(), dt, n, seg, 2, None,
+                                            y.data_ptr(), None, bl.PATH_AUTO, ws.data_ptr(), nb, stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"online forward: {bl.status_name(st)} {L.bitlinear_last_error().decode()}")
 
-    def run():
-        st = L.bitlinear_forward_online(x.data_ptr(), None, None, None, 1, k, w.data_ptr(), n, seg, 2, None,
-                                        y.data_ptr(), None, bl.PATH_AUTO, ws.data_ptr(), nb, stream.cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"online forward: {bl.status_name(st)} {L.bitlinear_last_error().decode()}")
-
-    for _ in range(3):
-        run()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        run()
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / reps
-    master = 4 * n * k
-    read = 2 * master  # the mean|W| pass and the ternarize pass each read the masters
-    gbs = read / (us * 1e-6) / 1e9
-    log(f"online gate|up m=1: {us:.1f} us per forward, masters {master / 1e6:.1f} MB read twice: {gbs:.0f} GB/s")
-    del w, ws
-    return {"workload": "online mode, gate|up 2560 -> 2 x 6912 fp32 masters, one token", "us": round(us, 2),
-            "master_bytes": master, "master_bytes_read": read, "gbs_masters_read": round(gbs, 1),
-            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        master = esize * n * k
+        read = 2 * master  # the mean|W| pass and the ternarize pass each read the masters
+        gbs = read / (us * 1e-6) / 1e9
+        log(f"online gate|up m=1, {name} masters: {us:.1f} us per forward, {master / 1e6:.1f} MB read twice: "
+            f"{gbs:.0f} GB/s")
+        res[name] = {"us": round(us, 2), "master_bytes": master, "master_bytes_read": read,
+                     "gbs_masters_read": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del w
+    del w32, ws
+    return res
 
 
 STACK_LAYERS, STACK_HEADS, STACK_KV_HEADS, STACK_HEAD_DIM = 30, 20, 5, 128
@@ -746,26 +908,97 @@ def bench_token_step(torch, bl, dev, layers, table, steps, warmup):
     return res
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Host cores this process may use, at most 16 (one GPU's share of the box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(w_gate, w_up, w_down, x, seconds):
-    """The CPU oracle (single thread, as it stands) on a sample of the step's tokens;
-    tokens are independent, so TOPS scale with the sample."""
+    """The CPU oracle, as it stands (plain C, one call per step), on a bounded
+    sample of the step's tokens: once on one thread, once on the host cores
+    this process may use (up to 16; one thread per contiguous block of tokens,
+    each running the oracle on its block: tokens are independent, the per-token
+    arithmetic is the same, so is every result). TOPS scale with the sample.
+    Also times the oracle on the other workloads (single layer, FFN block,
+    one decode projection, one decoder layer at one token)."""
+    import threading
+
     import oracle
+    from ternary_weight_bitlinear_w1_amd import synth
     log("cpu baseline: oracle weights")
     gams = [oracle.absmean(w) for w in (w_gate, w_up, w_down)]
     c_gu = np.concatenate([oracle.ternarize(w_gate, gams[0]), oracle.ternarize(w_up, gams[1])])
     c_d = oracle.ternarize(w_down, gams[2])
     ops_per_token = 2.0 * (2 * I * H + H * I)
+
+    def step(rows):
+        oracle.ffn_block(rows, c_gu, gams[:2], c_d, gams[2], None, 1e-5)
+
     t = time.perf_counter()
-    oracle.ffn_block(x[:2], c_gu, gams[:2], c_d, gams[2], None, 1e-5)
+    step(x[:2])
     per_tok = (time.perf_counter() - t) / 2
-    n = int(max(2, min(M, seconds / max(per_tok, 1e-6))))
-    log(f"cpu baseline: {n} tokens (~{n * per_tok:.1f} s)")
+    # single thread: about half the CPU budget
+    n1 = int(max(2, min(M, 0.5 * seconds / max(per_tok, 1e-6))))
     t = time.perf_counter()
-    oracle.ffn_block(x[:n], c_gu, gams[:2], c_d, gams[2], None, 1e-5)
-    dt = time.perf_counter() - t
-    return {"value": round(ops_per_token * n / dt / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of the {M} tokens of the step (same weights and inputs), {dt:.1f} s",
-            "seconds": round(dt, 2)}
+    step(x[:n1])
+    dt1 = time.perf_counter() - t
+    single = {"value": round(ops_per_token * n1 / dt1 / 1e12, 6), "cores": 1, "tokens": n1, "seconds": round(dt1, 2)}
+    # every usable core: about the same wall time again
+    threads = cpu_threads()
+    nt = int(max(threads, min(M, threads * 0.5 * seconds / max(per_tok, 1e-6))))
+    bounds = np.linspace(0, nt, threads + 1).astype(int)
+    errs = []
+
+    def work(a, b):
+        try:
+            step(x[a:b])
+        except Exception as e:  # noqa: BLE001 (reported below)
+            errs.append(e)
+
+    th = [threading.Thread(target=work, args=(int(bounds[i]), int(bounds[i + 1]))) for i in range(threads)]
+    t = time.perf_counter()
+    for h in th:
+        h.start()
+    for h in th:
+        h.join()
+    dtn = time.perf_counter() - t
+    if errs:
+        raise errs[0]
+    log(f"cpu baseline: {n1} tokens on 1 thread in {dt1:.1f} s; {nt} tokens on {threads} threads in {dtn:.1f} s")
+
+    # the other workloads, on one thread (small) or all threads (the FFN block)
+    other = {}
+    xs = synth.activations(synth.stream_seed(BASE_SEED, 1, 0, 5), 128, 256, 4)
+    ws_ = synth.weights(synth.stream_seed(BASE_SEED, 1, 0, 1), 512, 256)
+    g1 = oracle.absmean(ws_)
+    c1 = oracle.ternarize(ws_, g1)
+    t = time.perf_counter()
+    oracle.forward(xs, c1, [g1])
+    other["single_layer_ms"] = round((time.perf_counter() - t) * 1e3, 2)
+    for name, c, k, seg in (("decode_gate_up_m1_ms", c_gu, H, [I, 2 * I]), ("decode_down_m1_ms", c_d, I, [H])):
+        xm = synth.activations(synth.stream_seed(BASE_SEED, 3, 1, 5), 1, k, synth.outlier_count(k))
+        t = time.perf_counter()
+        oracle.forward(xm, c, [gams[0], gams[1]] if len(seg) == 2 else [gams[2]], seg)
+        other[name] = round((time.perf_counter() - t) * 1e3, 2)
+    return {"value": round(ops_per_token * nt / dtn / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"first {nt} of the {M} tokens of the prefill MLP step (same weights and inputs), "
+                      f"{threads} threads on contiguous token blocks, {dtn:.1f} s",
+            "seconds": round(dtn, 2), "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": single, "other_workloads": other}
 
 
 if __name__ == "__main__":

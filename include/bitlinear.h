@@ -171,27 +171,37 @@ bitlinear_status bitlinear_forward_noalloc(const float *x, const int8_t *codes_i
                                            float *y, int32_t *acc_out, int32_t path, void *stream);
 size_t bitlinear_forward_noalloc_max_scratch_bytes(void);
 
+/* Storage of master weights for the online mode ("The two checkpoints": the
+ * bf16 checkpoint keeps its weights in bfloat16). */
+typedef enum {
+  BITLINEAR_MASTER_F32 = 0,  /* fp32 */
+  BITLINEAR_MASTER_BF16 = 1  /* bfloat16 bit patterns (uint16), widened to fp32 exactly */
+} bitlinear_master_dtype;
+
 /* bitlinear_forward_online — the projection in the checkpoint mode that keeps
  * the full-precision weights and ternarizes them in every forward ("The two
  * checkpoints": the online mode; "The projections quantize their inputs and
  * weights"): per segment, gamma = mean|W| (fp64), codes = sign(W) [|W| >
  * gamma / 2], packed into the workspace, then bitlinear_forward with the
  * segments' gammas rounded to fp32.
- *   w_master   [n][k] fp32 master weights, 16-byte aligned; segment j is rows
- *              [seg_end[j-1], seg_end[j]) and gets its own gamma.
+ *   w_master   [n][k] master weights in master_dtype (bitlinear_master_dtype),
+ *              16-byte aligned; segment j is rows [seg_end[j-1], seg_end[j])
+ *              and gets its own gamma. bfloat16 masters are read as their
+ *              exact fp32 values: half the bytes of fp32 masters.
  *   seg_end    HOST array of n_seg ascending int64 ends, seg_end[n_seg-1] == n.
  *   gamma_out  NULL or device [n_seg] fp64: the gammas used.
  * Other arguments as bitlinear_forward. The result equals
- * bitlinear_quantize_weights on each segment followed by bitlinear_forward
- * with those gammas, bit for bit.
+ * bitlinear_quantize_weights on each segment (of the widened masters) followed
+ * by bitlinear_forward with those gammas, bit for bit.
  *   workspace  >= bitlinear_forward_online_workspace_bytes(m, n, k, x != NULL,
  *              seg_end, n_seg) bytes.
- * Errors as bitlinear_forward; m == 0 still computes the gammas. */
+ * Errors as bitlinear_forward, plus ERR_ARG for an unknown master_dtype; m == 0
+ * still computes the gammas. */
 bitlinear_status bitlinear_forward_online(const float *x, const int8_t *codes_in, const float *deq_in,
-                                          const int32_t *rowsum_in, int64_t m, int64_t k, const float *w_master,
-                                          int64_t n, const int64_t *seg_end, int32_t n_seg, double *gamma_out,
-                                          float *y, int32_t *acc_out, int32_t path, void *workspace,
-                                          size_t workspace_bytes, void *stream);
+                                          const int32_t *rowsum_in, int64_t m, int64_t k, const void *w_master,
+                                          int32_t master_dtype, int64_t n, const int64_t *seg_end, int32_t n_seg,
+                                          double *gamma_out, float *y, int32_t *acc_out, int32_t path,
+                                          void *workspace, size_t workspace_bytes, void *stream);
 size_t bitlinear_forward_online_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside,
                                                 const int64_t *seg_end, int32_t n_seg);
 
@@ -439,6 +449,28 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
                                          const bitlinear_block_trace *trace, void *workspace,
                                          size_t workspace_bytes, void *stream);
 size_t bitlinear_block_workspace_bytes(const bitlinear_block *blk, int64_t m);
+
+/* ---------------------------------------------------------------------------
+ * Measurement probes: the denominators of the roofline fractions, measured on
+ * the running GPU (not steps of the method; they compute nothing a caller
+ * uses). The kernels above are bound by HBM reads (decode, quantization) and by
+ * the int8 matrix cores (prefill).
+ * ------------------------------------------------------------------------- */
+
+/* bitlinear_probe_read — read bytes of device memory at src once, as coalesced
+ * 16-byte loads, eight per thread in flight, and write nothing (sink, one
+ * device uint32, is never written in practice). grid <= 0 takes one 256-thread
+ * workgroup per 32 KB (at most 65536).
+ * Errors: NULL -> ERR_NULL; bytes < 0 or bytes % 16 -> ERR_SHAPE; misaligned
+ * src -> ERR_ALIGN. bytes == 0 is a no-op. */
+bitlinear_status bitlinear_probe_read(const void *src, int64_t bytes, int64_t grid, uint32_t *sink, void *stream);
+
+/* bitlinear_probe_mfma — workgroups of 4 waves, each wave issuing iters x 8
+ * independent v_mfma_i32_32x32x32_i8 (65,536 int8 ops each) with no memory
+ * traffic; sink as above.
+ * Errors: NULL sink -> ERR_NULL; iters <= 0 or workgroups outside 1..65536 ->
+ * ERR_SHAPE. */
+bitlinear_status bitlinear_probe_mfma(int32_t iters, int64_t workgroups, int32_t *sink, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Misc.

@@ -23,6 +23,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DEVICE, ERR_ARG = range(7
 ACT_ABSMAX, ACT_RMSNORM, ACT_RELU2_RMSNORM = 0, 1, 2
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 BLOCK_FFN, BLOCK_DECODER, BLOCK_DECODER_CACHED = 0, 1, 2
+MASTER_F32, MASTER_BF16 = 0, 1
 MAX_SEGMENTS = 4
 
 _p = ctypes.c_void_p
@@ -80,8 +81,8 @@ def lib():
                                                  _p]),
             "bitlinear_forward_noalloc_max_scratch_bytes": (_sz, []),
             "bitlinear_forward_relu2_glu": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _sz, _p]),
-            "bitlinear_forward_online": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _i32, _p, _p, _p, _i32, _p,
-                                                _sz, _p]),
+            "bitlinear_forward_online": (_i32, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _i64, _p, _i32, _p, _p, _p, _i32,
+                                                _p, _sz, _p]),
             "bitlinear_forward_online_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _p, _i32]),
             "bitlinear_forward_relu2_glu_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
             "bitlinear_embed": (_i32, [_p, _i64, _p, _i64, _i64, _p, _p]),
@@ -100,6 +101,8 @@ def lib():
             "bitlinear_block_forward": (_i32, [ctypes.POINTER(Block), _p, _i64, _p, ctypes.POINTER(Trace), _p, _sz,
                                                _p]),
             "bitlinear_block_workspace_bytes": (_sz, [ctypes.POINTER(Block), _i64]),
+            "bitlinear_probe_read": (_i32, [_p, _i64, _i64, _p, _p]),
+            "bitlinear_probe_mfma": (_i32, [_i32, _i64, _p, _p]),
             "bitlinear_status_str": (ctypes.c_char_p, [_i32]),
             "bitlinear_last_error": (ctypes.c_char_p, []),
             "bitlinear_abi_version": (_i32, []),
@@ -220,9 +223,12 @@ def forward_online(w_master: torch.Tensor, seg_end: Optional[Sequence[int]] = No
                    x: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
                    deq: Optional[torch.Tensor] = None, rowsum: Optional[torch.Tensor] = None,
                    want_acc: bool = False, path: int = PATH_AUTO, out: Optional[torch.Tensor] = None):
-    """Online mode: ternarize the fp32 masters [n][k] (one gamma per segment) and
-    project. Returns (y, gamma) or (y, acc, gamma); gamma is a device fp64 tensor."""
+    """Online mode: ternarize the masters [n][k] (fp32, or bfloat16 given as a
+    torch.bfloat16 or uint16 tensor; one gamma per segment) and project. Returns
+    (y, gamma) or (y, acc, gamma); gamma is a device fp64 tensor."""
     n, k = w_master.shape
+    if w_master.dtype not in (torch.float32, torch.bfloat16, torch.uint16):
+        raise TypeError("forward_online takes fp32 or bfloat16 masters")
     src = x if x is not None else codes
     m = src.shape[0]
     dev = w_master.device
@@ -235,7 +241,8 @@ def forward_online(w_master: torch.Tensor, seg_end: Optional[Sequence[int]] = No
     nb = lib().bitlinear_forward_online_workspace_bytes(m, n, k, 1 if x is not None else 0, se, len(seg_end))
     ws = _workspace(nb, dev)
     _check("bitlinear_forward_online",
-           lib().bitlinear_forward_online(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(w_master), n, se,
+           lib().bitlinear_forward_online(_ptr(x), _ptr(codes), _ptr(deq), _ptr(rowsum), m, k, _ptr(w_master),
+                                          MASTER_F32 if w_master.dtype == torch.float32 else MASTER_BF16, n, se,
                                           len(seg_end), _ptr(gamma), _ptr(y), _ptr(acc), path, _ptr(ws), nb,
                                           _stream(dev)))
     return (y, acc, gamma) if want_acc else (y, gamma)
@@ -332,6 +339,19 @@ def attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                                             n_slots, t_max, _ptr(slot), _ptr(pos), _ptr(o), o.stride(0), _ptr(ws), nb,
                                             _stream(dev)))
     return o
+
+
+def probe_read(src: torch.Tensor, nbytes: Optional[int] = None, grid: int = 0,
+               sink: Optional[torch.Tensor] = None) -> None:
+    """Measurement probe: read ``nbytes`` (default all) of ``src`` once."""
+    nb = src.numel() * src.element_size() if nbytes is None else nbytes
+    s = sink if sink is not None else torch.zeros(1, dtype=torch.int32, device=src.device)
+    _check("bitlinear_probe_read", lib().bitlinear_probe_read(_ptr(src), nb, grid, _ptr(s), _stream(src.device)))
+
+
+def probe_mfma(iters: int, workgroups: int, sink: torch.Tensor) -> None:
+    """Measurement probe: workgroups x 4 waves x iters x 8 int8 MFMA 32x32x32."""
+    _check("bitlinear_probe_mfma", lib().bitlinear_probe_mfma(iters, workgroups, _ptr(sink), _stream(sink.device)))
 
 
 def base3_row_bytes(k: int) -> int:

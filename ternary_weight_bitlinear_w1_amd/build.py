@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 SYNTH_LIB = os.path.join(HERE, "libsynth.so")
 
-SOURCES = ["quant_acts.hip", "quant_weights.hip", "gemm_prefill.hip", "gemv_decode.hip", "decode_fused.hip", "base3.hip", "head.hip", "attention.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["quant_acts.hip", "quant_weights.hip", "gemm_prefill.hip", "gemv_decode.hip", "decode_fused.hip", "base3.hip", "head.hip", "attention.hip", "noalloc.hip", "probes.hip", "api.cpp"]
 
 # -ffp-contract=off: every fp operation rounds as written (no fused multiply-add).
 # Division and sqrt stay correctly rounded. Packed-fp32 instructions are turned off.

@@ -138,6 +138,25 @@ const char *bitlinear_status_str(bitlinear_status s) {
 
 const char *bitlinear_last_error(void) { return g_err.c_str(); }
 
+bitlinear_status bitlinear_probe_read(const void *src, int64_t bytes, int64_t grid, uint32_t *sink, void *stream) {
+  g_err.clear();
+  if (bytes != 0 && (!src || !sink)) return fail(BITLINEAR_ERR_NULL, "src and sink are required");
+  if (bytes < 0 || bytes % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "bytes must be a non-negative multiple of 16");
+  if (bytes != 0 && !aligned16(src)) return fail(BITLINEAR_ERR_ALIGN, "src must be 16-byte aligned");
+  if (bytes == 0) return BITLINEAR_OK;
+  BL_TRY(check_device());
+  return launched(bl::launch_probe_read(src, bytes, sink, grid, as_stream(stream)), "probe read");
+}
+
+bitlinear_status bitlinear_probe_mfma(int32_t iters, int64_t workgroups, int32_t *sink, void *stream) {
+  g_err.clear();
+  if (!sink) return fail(BITLINEAR_ERR_NULL, "sink is required");
+  if (iters <= 0 || workgroups <= 0 || workgroups > 65536)
+    return fail(BITLINEAR_ERR_SHAPE, "iters > 0 and 0 < workgroups <= 65536");
+  BL_TRY(check_device());
+  return launched(bl::launch_probe_mfma(iters, workgroups, sink, as_stream(stream)), "probe mfma");
+}
+
 int32_t bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
 
 // ---------------------------------------------------------------- weights
@@ -295,12 +314,14 @@ size_t bitlinear_forward_online_workspace_bytes(int64_t m, int64_t n, int64_t k,
 }
 
 bitlinear_status bitlinear_forward_online(const float *x, const int8_t *codes_in, const float *deq_in,
-                                          const int32_t *rowsum_in, int64_t m, int64_t k, const float *w_master,
-                                          int64_t n, const int64_t *seg_end, int32_t n_seg, double *gamma_out,
-                                          float *y, int32_t *acc_out, int32_t path, void *workspace,
-                                          size_t workspace_bytes, void *stream) {
+                                          const int32_t *rowsum_in, int64_t m, int64_t k, const void *w_master,
+                                          int32_t master_dtype, int64_t n, const int64_t *seg_end, int32_t n_seg,
+                                          double *gamma_out, float *y, int32_t *acc_out, int32_t path,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
   g_err.clear();
   BL_TRY(check_forward_args(x, codes_in, deq_in, m, k, w_master, n, y, path));
+  if (master_dtype != BITLINEAR_MASTER_F32 && master_dtype != BITLINEAR_MASTER_BF16)
+    return fail(BITLINEAR_ERR_ARG, "unknown master dtype %d", master_dtype);
   bl::Epilogue ep;
   BL_TRY(make_segments(nullptr, seg_end, n_seg, n, &ep));
   const size_t need = bitlinear_forward_online_workspace_bytes(m, n, k, x != nullptr, seg_end, n_seg);
@@ -318,9 +339,15 @@ bitlinear_status bitlinear_forward_online(const float *x, const int8_t *codes_in
   int64_t lo = 0;
   for (int j = 0; j < n_seg; ++j) {
     const int64_t rows = seg_end[j] - lo;
-    BL_TRY(launched(bl::launch_absmean(w_master + lo * k, rows * k, partials, gam + j, s), "absmean"));
-    BL_TRY(launched(bl::launch_ternarize_pack(w_master + lo * k, rows, k, gam + j, packed + lo * (k / 4), s),
-                    "ternarize"));
+    if (master_dtype == BITLINEAR_MASTER_BF16) {
+      const uint16_t *w = static_cast<const uint16_t *>(w_master) + lo * k;
+      BL_TRY(launched(bl::launch_absmean_bf16(w, rows * k, partials, gam + j, s), "absmean"));
+      BL_TRY(launched(bl::launch_ternarize_pack_bf16(w, rows, k, gam + j, packed + lo * (k / 4), s), "ternarize"));
+    } else {
+      const float *w = static_cast<const float *>(w_master) + lo * k;
+      BL_TRY(launched(bl::launch_absmean(w, rows * k, partials, gam + j, s), "absmean"));
+      BL_TRY(launched(bl::launch_ternarize_pack(w, rows, k, gam + j, packed + lo * (k / 4), s), "ternarize"));
+    }
     lo = seg_end[j];
   }
   if (m == 0) return BITLINEAR_OK;

@@ -158,6 +158,11 @@ hipError_t launch_absmean(const float *w, int64_t count, double *partials, doubl
                           hipStream_t stream);
 hipError_t launch_ternarize_pack(const float *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
                                  hipStream_t stream);
+// the same two passes over bfloat16 masters (bit patterns, widened exactly)
+hipError_t launch_absmean_bf16(const uint16_t *w, int64_t count, double *partials, double *gamma_out,
+                               hipStream_t stream);
+hipError_t launch_ternarize_pack_bf16(const uint16_t *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
+                                      hipStream_t stream);
 hipError_t launch_copy_gamma(const double *src, double *dst, hipStream_t stream);
 hipError_t launch_validate_packed(const uint8_t *packed, int64_t n, int64_t k, int64_t *n_bad,
                                   hipStream_t stream);
@@ -278,6 +283,12 @@ hipError_t launch_lm_head(const uint16_t *o, int64_t m, int64_t k, const uint16_
                           hipStream_t stream);
 hipError_t launch_embed(const int64_t *ids, int64_t m, const uint16_t *table, int64_t vocab, int64_t k, float *x,
                         hipStream_t stream);
+
+// Measurement probes (probes.hip): a coalesced 16-byte read stream (grid <= 0:
+// one thread per 8 loads) and independent int8 MFMA chains (256-thread
+// workgroups, iters x 8 v_mfma_i32_32x32x32_i8 per wave).
+hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, int64_t grid, hipStream_t stream);
+hipError_t launch_probe_mfma(int iters, int64_t workgroups, int32_t *sink, hipStream_t stream);
 
 // RoPE, the bfloat16 KV cache and causal attention (attention.hip).
 bool attention_supported(int n_heads, int n_kv, int hd);
