@@ -1,4 +1,4 @@
-// Absmean ternarization of fp32 master weights and four-to-a-byte packing
+// Absmean ternarization of fp32 or bfloat16 master weights and four-to-a-byte packing
 // (gfx950). Offline step of the packed checkpoint mode: the nnterp "BitNet
 // b1.58" page, "The projections quantize their inputs and weights" (weights
 // rounded to {-1, 0, 1} * mean|W|, stored four to a byte with a weight_scale)
@@ -31,29 +31,47 @@ __device__ __forceinline__ double block_sum(double v, double *red) {
   return t;
 }
 
-// partials[b] = sum |w| over elements [b * per, min((b+1) * per, count)), per % 4 == 0
-__global__ __launch_bounds__(kThreads) void absmean_partial_kernel(const float *__restrict__ w, int64_t count,
+// Master weights are fp32 or bfloat16 (the bf16 checkpoint of "The two
+// checkpoints"). A 16-byte load holds E of them; a bfloat16 value widens to
+// fp32 exactly (its bits are the top half of the fp32's).
+template <typename T>
+struct Master;
+template <>
+struct Master<float> {
+  static constexpr int E = 4;
+  __device__ static float at(const v4i &r, int e) { return __int_as_float(r[e]); }
+};
+template <>
+struct Master<uint16_t> {
+  static constexpr int E = 8;
+  __device__ static float at(const v4i &r, int e) {
+    const uint32_t w = (uint32_t)r[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+
+// partials[b] = sum |w| over elements [b * per, min((b+1) * per, count)), per % 8 == 0
+template <typename T>
+__global__ __launch_bounds__(kThreads) void absmean_partial_kernel(const T *__restrict__ w, int64_t count,
                                                                    int64_t per, double *__restrict__ partials) {
+  constexpr int E = Master<T>::E;
   __shared__ double red[kThreads / 64];
   const int64_t lo = blockIdx.x * per;
   const int64_t hi = lo + per < count ? lo + per : count;
-  // thread t adds elements t, t + 256, ... (in float4 units) of the slice in
+  // thread t adds elements t, t + 256, ... (in 16-byte units) of the slice in
   // order; kUnroll loads are issued before their sums
   double s = 0.0;
-  for (int64_t i0 = lo + 4 * (int64_t)threadIdx.x; i0 < hi; i0 += 4 * kThreads * kUnroll) {
-    float4 v[kUnroll];
+  for (int64_t i0 = lo + E * (int64_t)threadIdx.x; i0 < hi; i0 += E * kThreads * kUnroll) {
+    v4i v[kUnroll];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
-      const int64_t i = i0 + 4 * (int64_t)kThreads * j;
-      v[j] = i < hi ? *reinterpret_cast<const float4 *>(w + i) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      const int64_t i = i0 + E * (int64_t)kThreads * j;
+      v[j] = i < hi ? *reinterpret_cast<const v4i *>(w + i) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      s += fabs((double)v[j].x);
-      s += fabs((double)v[j].y);
-      s += fabs((double)v[j].z);
-      s += fabs((double)v[j].w);
-    }
+    for (int j = 0; j < kUnroll; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += fabs((double)Master<T>::at(v[j], e));
   }
   s = block_sum(s, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = s;
@@ -69,22 +87,22 @@ __global__ __launch_bounds__(kThreads) void absmean_final_kernel(const double *_
 }
 
 // one thread per packed 32-bit word (16 codes)
-__global__ __launch_bounds__(kThreads) void ternarize_pack_kernel(const float *__restrict__ w, int64_t words,
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ternarize_pack_kernel(const T *__restrict__ w, int64_t words,
                                                                   const double *__restrict__ gamma,
                                                                   uint32_t *__restrict__ packed) {
+  constexpr int E = Master<T>::E;
   const double half = 0.5 * gamma[0];
   for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < words; i += (int64_t)gridDim.x * kThreads) {
-    const float4 *src = reinterpret_cast<const float4 *>(w + 16 * i);
-    float v[16];
+    const v4i *src = reinterpret_cast<const v4i *>(w + 16 * i);
+    v4i raw[16 / E];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 f = src[j];
-      v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
-    }
+    for (int j = 0; j < 16 / E; ++j) raw[j] = src[j];
     uint32_t word = 0;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint32_t u = fabs((double)v[t]) > half ? (v[t] > 0.0f ? 2u : 0u) : 1u;
+      const float v = Master<T>::at(raw[t / E], t % E);
+      const uint32_t u = fabs((double)v) > half ? (v > 0.0f ? 2u : 0u) : 1u;
       word |= u << (8 * (t & 3) + 2 * (t >> 2));
     }
     packed[i] = word;
@@ -139,25 +157,46 @@ size_t absmean_partials(int64_t count) {
   return (size_t)((count + per - 1) / per);
 }
 
-hipError_t launch_absmean(const float *w, int64_t count, double *partials, double *gamma_out, hipStream_t stream) {
+template <typename T>
+hipError_t absmean_impl(const T *w, int64_t count, double *partials, double *gamma_out, hipStream_t stream) {
   if (count <= 0) {
     zero_i64_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<int64_t *>(gamma_out));  // 0.0 is all-zero bits
     return hipGetLastError();
   }
   const int64_t per = partial_span(count);
   const int np = (int)((count + per - 1) / per);
-  absmean_partial_kernel<<<dim3(np), dim3(kThreads), 0, stream>>>(w, count, per, partials);
+  absmean_partial_kernel<T><<<dim3(np), dim3(kThreads), 0, stream>>>(w, count, per, partials);
   absmean_final_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(partials, np, count, gamma_out);
   return hipGetLastError();
 }
 
-hipError_t launch_ternarize_pack(const float *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
-                                 hipStream_t stream) {
+template <typename T>
+hipError_t ternarize_impl(const T *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
+                          hipStream_t stream) {
   const int64_t words = n * (k / 16);
   if (words == 0) return hipSuccess;
-  ternarize_pack_kernel<<<dim3(grid_for(words)), dim3(kThreads), 0, stream>>>(w, words, gamma,
-                                                                               reinterpret_cast<uint32_t *>(packed));
+  ternarize_pack_kernel<T><<<dim3(grid_for(words)), dim3(kThreads), 0, stream>>>(
+      w, words, gamma, reinterpret_cast<uint32_t *>(packed));
   return hipGetLastError();
+}
+
+hipError_t launch_absmean(const float *w, int64_t count, double *partials, double *gamma_out, hipStream_t stream) {
+  return absmean_impl(w, count, partials, gamma_out, stream);
+}
+
+hipError_t launch_absmean_bf16(const uint16_t *w, int64_t count, double *partials, double *gamma_out,
+                               hipStream_t stream) {
+  return absmean_impl(w, count, partials, gamma_out, stream);
+}
+
+hipError_t launch_ternarize_pack(const float *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
+                                 hipStream_t stream) {
+  return ternarize_impl(w, n, k, gamma, packed, stream);
+}
+
+hipError_t launch_ternarize_pack_bf16(const uint16_t *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
+                                      hipStream_t stream) {
+  return ternarize_impl(w, n, k, gamma, packed, stream);
 }
 
 hipError_t launch_copy_gamma(const double *src, double *dst, hipStream_t stream) {

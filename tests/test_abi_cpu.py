@@ -117,10 +117,10 @@ def test_forward_relu2_glu_workspace_sizes():
 
 
 def _onl(x=A, codes=None, deq=None, rowsum=None, m=4, k=64, w=A, n=32, seg=(32,), gamma=None, y=A, acc=None, path=0,
-         ws=A, wsb=1 << 24):
+         ws=A, wsb=1 << 24, dtype=bl.MASTER_F32):
     s = (ctypes.c_int64 * max(1, len(seg)))(*seg)
-    return bl.lib().bitlinear_forward_online(x, codes, deq, rowsum, m, k, w, n, s if seg else None, len(seg), gamma,
-                                             y, acc, path, ws, wsb, None)
+    return bl.lib().bitlinear_forward_online(x, codes, deq, rowsum, m, k, w, dtype, n, s if seg else None, len(seg),
+                                             gamma, y, acc, path, ws, wsb, None)
 
 
 def test_forward_online_validation():
@@ -133,6 +133,8 @@ def test_forward_online_validation():
     assert _onl(k=24) == bl.ERR_SHAPE
     assert _onl(path=5) == bl.ERR_ARG
     assert _onl(w=MIS) == bl.ERR_ALIGN
+    assert _onl(dtype=2) == bl.ERR_ARG
+    assert _onl(dtype=bl.MASTER_BF16, w=MIS) == bl.ERR_ALIGN
     assert _onl(ws=None) == bl.ERR_WORKSPACE
     assert _onl(wsb=64) == bl.ERR_WORKSPACE
 

@@ -65,6 +65,28 @@ def test_P1_grid_weights_exact_rational_mean():
     assert oracle.absmean(w) == float(exact)
 
 
+def test_P1_bf16_masters_exact_rational_mean():
+    """[nnterp] "The two checkpoints": the bf16 checkpoint stores its weights in
+    bfloat16 and ternarizes them in every forward. The oracle takes gamma over the
+    exactly widened values: for bfloat16 weights of N(0, 0.02) (8 significant
+    bits, exponents within a few dozen binades) the fp64 sum is exact, so gamma is
+    the correctly rounded rational mean of the bfloat16 values themselves; a
+    constant magnitude a gives gamma = a; codes split exactly at gamma / 2."""
+    r = rng(3)
+    bits = oracle.round_bf16((0.02 * r.normal(size=(23, 48))).astype(np.float32))
+    wide = oracle.bf16_to_f32(bits)
+    exact = sum((Fraction(float(v)).__abs__() for v in wide.reshape(-1)), Fraction(0)) / wide.size
+    g = oracle.absmean(wide)
+    assert g == float(exact)
+    c = oracle.ternarize(wide, g)
+    half = exact / 2
+    want = np.array([0 if abs(Fraction(float(v))) <= half else (1 if v > 0 else -1) for v in wide.reshape(-1)])
+    assert np.array_equal(c.reshape(-1), want)
+    a_bits = 0x3C23  # bfloat16 of 0.00994873046875
+    const = np.where(r.random((9, 32)) < 0.5, a_bits, a_bits | 0x8000).astype(np.uint16)
+    assert oracle.absmean(oracle.bf16_to_f32(const)) == 0.00994873046875
+
+
 def test_P2_codes_match_exact_rational_threshold():
     """Brute force: code = sign(W) * [ |W| > mean|W| / 2 ] in exact rationals
     (round(W / gamma) clipped to [-1, 1], ties to even)."""

@@ -269,6 +269,33 @@ def test_forward_online(m, seg, k):
     assert_equal(host(y_p), host(y), "online == quantize_weights + forward")
 
 
+@pytest.mark.parametrize("m,seg,k", [(1, [6912, 13824], 2560), (37, [100, 300], 512), (130, [2560], 6912)])
+def test_forward_online_bf16(m, seg, k):
+    """bfloat16 masters ("The two checkpoints": the bf16 checkpoint), read as their
+    exact fp32 values: gamma per segment against the oracle's absmean of the
+    widened masters (within 1e-6), y and acc bit-exact against the oracle run with
+    the GPU's gamma, and equal to the fp32-master call on the widened values."""
+    note(f"forward online bf16 m={m} seg={seg} k={k}")
+    n = seg[-1]
+    lo = [0] + seg[:-1]
+    bits = np.concatenate([oracle.round_bf16(synth.weights(seed(10, n + j, k), hi - a, k, 0.02 + 0.01 * j))
+                           for j, (a, hi) in enumerate(zip(lo, seg))])
+    wide = oracle.bf16_to_f32(bits)
+    x = synth.activations(seed(10, m, k), m, k, 1)
+    y, acc, gamma = bl.forward_online(gpu(bits), seg, x=gpu(x), want_acc=True)
+    g = host(gamma)
+    for j, (a, hi) in enumerate(zip(lo, seg)):
+        go = oracle.absmean(wide[a:hi])
+        assert abs(g[j] - go) <= GAMMA_TOL * go, (j, g[j], go)
+    codes = np.concatenate([oracle.ternarize(wide[a:hi], float(g[j])) for j, (a, hi) in enumerate(zip(lo, seg))])
+    ref = oracle.forward(x, codes, [float(v) for v in g], seg)
+    assert_equal(host(acc), ref["acc"], "online bf16 acc")
+    assert_equal(host(y), ref["y"], "online bf16 y")
+    y32, g32 = bl.forward_online(gpu(wide), seg, x=gpu(x))
+    assert_equal(host(g32), g, "gamma from the widened fp32 masters")
+    assert_equal(host(y32), host(y), "bf16 masters == their fp32 widening")
+
+
 def test_forward_codes_in_path():
     note("forward with pre-quantized codes")
     m, k, n = 37, 512, 300
