@@ -221,6 +221,11 @@ typedef const __attribute__((address_space(1))) void gbl_void_t;
 #define BL_GEMM_WIDE_STAGES 4
 #endif
 constexpr int kGroupM = 4;
+// 1: a persistent grid (workgroups per CU x CUs) walks the tiles; 0: one
+// workgroup per tile
+#ifndef BL_GEMM_PERSIST
+#define BL_GEMM_PERSIST 1
+#endif
 
 // Workgroups per CU of the persistent kernel: 8-wave workgroups run one per CU,
 // smaller ones two (both give two waves per SIMD).
@@ -641,8 +646,12 @@ hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const fl
                             hipStream_t stream) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * (n / BN) * splits;
+#if BL_GEMM_PERSIST
   int64_t grid = wgs_per_cu(WM * WN) * (int64_t)cu_count();
   if (grid > tiles) grid = tiles;
+#else
+  const int64_t grid = tiles;
+#endif
   gemm_prefill_kernel<WM, WN, TM, TN, P, GLU><<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(
       codes, packed, deq, rowsum, m, n, k, ep, y, part ? nullptr : acc_out, splits, part);
   return hipGetLastError();

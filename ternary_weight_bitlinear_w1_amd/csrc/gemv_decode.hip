@@ -36,13 +36,22 @@ constexpr uint32_t kFieldMask = 0x03030303u;
 #define BL_GEMV_MIN_WAVES 4
 #endif
 #ifndef BL_GEMV_DOT4_MAX_M
-#define BL_GEMV_DOT4_MAX_M 1
+#define BL_GEMV_DOT4_MAX_M 2
 #endif
 #ifndef BL_GEMV_MIN_WGS
 #define BL_GEMV_MIN_WGS 256
 #endif
 #ifndef BL_GEMV_RT1_MAX_M
 #define BL_GEMV_RT1_MAX_M 4
+#endif
+#ifndef BL_GEMV_CODES_FIRST
+#define BL_GEMV_CODES_FIRST 1
+#endif
+#ifndef BL_GEMV_LDS_CODES
+#define BL_GEMV_LDS_CODES 1
+#endif
+#ifndef BL_DOT4_EXACT_LPW
+#define BL_DOT4_EXACT_LPW 1
 #endif
 
 __device__ __forceinline__ v4i unpack16(uint32_t p) {
@@ -64,7 +73,7 @@ __device__ __forceinline__ v4i unpack16(uint32_t p) {
 // consecutive e, so it rotates each pair itself, with the cosine and sine read
 // from the step's rows of the rotary table (rope_gather_kernel) while the weights load, and writes the
 // keys to the bfloat16 cache; workgroups of the value heads append the values.
-template <int RT, int NW, int SPW, bool ROPE = false>
+template <int RT, int NW, int SPW, bool ROPE = false, int MC = 0>
 __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__restrict__ A,
                                                               const uint8_t *__restrict__ B,
                                                               const float *__restrict__ deq,
@@ -74,6 +83,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
   static_assert(!ROPE || RT == 2, "rotated pairs take the two row tiles");
   const Epilogue ep = resolve_gamma(ep_in);
   __shared__ int red[NW][RT][64][4];
+  __shared__ __attribute__((aligned(16))) int8_t scodes[MC > 0 ? NW : 1][MC > 0 ? MC * SPW * 256 : 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16 * RT;
   // ROPE form: workgroups [0, rot_wgs) hold rotated pairs, hd / 32 per head
@@ -110,36 +120,89 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
   }
 
   v4i b[SPW][RT];
+  v4i a[SPW][4];
+  auto load_weights = [&]() {
 #pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int g0 = (s_lo + i) * 16 + 4 * kb;
+    for (int i = 0; i < SPW; ++i) {
+      const int g0 = (s_lo + i) * 16 + 4 * kb;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int n = row_of(rt, row);
-      b[i][rt] = v4i{0, 0, 0, 0};
-      if (i < cnt && n < N) {
-        const uint8_t *p = B + (int64_t)n * ldb + 4 * (int64_t)g0;
-        if (g0 + 4 <= G) {
-          const v4i_u t = *reinterpret_cast<const v4i_u *>(p);
-          b[i][rt] = v4i{t[0], t[1], t[2], t[3]};
-        } else {
+      for (int rt = 0; rt < RT; ++rt) {
+        const int n = row_of(rt, row);
+        b[i][rt] = v4i{0, 0, 0, 0};
+        if (i < cnt && n < N) {
+          const uint8_t *p = B + (int64_t)n * ldb + 4 * (int64_t)g0;
+          if (g0 + 4 <= G) {
+            const v4i_u t = *reinterpret_cast<const v4i_u *>(p);
+            b[i][rt] = v4i{t[0], t[1], t[2], t[3]};
+          } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (g0 + t < G) b[i][rt][t] = reinterpret_cast<const int *>(p)[t];
+            for (int t = 0; t < 4; ++t)
+              if (g0 + t < G) b[i][rt][t] = reinterpret_cast<const int *>(p)[t];
+          }
         }
       }
     }
-  }
-  v4i a[SPW][4];
+  };
+  auto load_codes = [&]() {
 #pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int g0 = (s_lo + i) * 16 + 4 * kb;
+    for (int i = 0; i < SPW; ++i) {
+      const int g0 = (s_lo + i) * 16 + 4 * kb;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      a[i][t] = v4i{0, 0, 0, 0};
-      if (i < cnt && has_a && g0 + t < G)
-        a[i][t] = *reinterpret_cast<const v4i *>(A + (int64_t)row * K + 16 * (g0 + t));
+      for (int t = 0; t < 4; ++t) {
+        a[i][t] = v4i{0, 0, 0, 0};
+        if (i < cnt && has_a && g0 + t < G)
+          a[i][t] = *reinterpret_cast<const v4i *>(A + (int64_t)row * K + 16 * (g0 + t));
+      }
     }
+  };
+  if constexpr (MC > 0) {
+    // The wave's code slice goes through LDS: slot (i, t) of its area holds the
+    // 256 codes of token t in its superstep i, its 16-byte piece c at piece
+    // c ^ t, so that the 16 lanes reading one piece of 16 tokens hit 16
+    // distinct bank groups. Every code load is a full
+    // 64-lane load of 16 bytes (lane l covers slot 4 j + l / 16, piece l % 16),
+    // so a few loads carry what per-lane operand loads would take 4 cnt partly
+    // masked loads for. Slots past the token count, the wave's supersteps or
+    // the row's end load some in-range codes; those meet only zero weights or
+    // feed output rows that are never stored.
+    v4i cs[MC * SPW / 4];
+#pragma unroll
+    for (int j = 0; j < MC * SPW / 4; ++j) {
+      const int slot = 4 * j + (lane >> 4);
+      const int i = slot / MC, t = slot - i * MC;
+      if (4 * j < MC * cnt) {  // wave-uniform: slots of the wave's supersteps only
+        int off = (s_lo + i) * 256 + 16 * (lane & 15);
+        off = off < K - 16 ? off : K - 16;
+        cs[j] = *reinterpret_cast<const v4i *>(A + (int64_t)(t < M ? t : M - 1) * K + off);
+      }
+    }
+    load_weights();
+#pragma unroll
+    for (int j = 0; j < MC * SPW / 4; ++j)
+      if (4 * j < MC * cnt) {
+        const int t = (4 * j + (lane >> 4)) % MC;
+        *reinterpret_cast<v4i *>(scodes[wave] + 1024 * j + 256 * (lane >> 4) + 16 * ((lane & 15) ^ t)) = cs[j];
+      }
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own stores are in LDS
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        a[i][t] = row < MC ? *reinterpret_cast<const v4i *>(scodes[wave] + (i * MC + row) * 256 +
+                                                            16 * ((4 * kb + t) ^ row))
+                           : v4i{0, 0, 0, 0};
+  } else {
+#if BL_GEMV_CODES_FIRST
+    // the codes (a few KB, from L2) first: a wave's loads return in issue order,
+    // so they are in registers by the time the first weights arrive
+    load_codes();
+    load_weights();
+#else
+    load_weights();
+    load_codes();
+#endif
   }
   // ROPE form: the cosine and sine of each of this thread's pairs (epilogue entries in
   // tile 0: token m, pair e = 16 rj + l % 16)
@@ -362,11 +425,14 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict
   }
   __builtin_amdgcn_sched_barrier(0);
   v4i w[LPW];
+  // (a piece past the row's end reloads the first piece of the lane's own row,
+  // so such reloads spread over many lines instead of meeting on one)
+  const uint8_t *own = B + (int64_t)(n < N ? n : N - 1) * ldb + 16 * p;
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int off = 128 * (l_lo + i) + 16 * p;
     const bool use = l_lo + i < l_hi && off < ldb && n < N;
-    w[i] = *reinterpret_cast<const v4i *>(use ? B + (int64_t)n * ldb + off : B);
+    w[i] = *reinterpret_cast<const v4i *>(use ? B + (int64_t)n * ldb + off : own);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -447,29 +513,57 @@ hipError_t launch_dot4_mt(const int8_t *codes, const uint8_t *packed, const floa
 #define BL_DOT4(KS_, LPW_)                                                                                          \
   gemv_dot4_kernel<MT, KS_, LPW_><<<grid, block, 0, stream>>>(codes, packed, deq, rowsum, n, k, ep, y, acc_out); \
   return hipGetLastError()
-  if (ks == 1) {
-    if (lpw <= 4) { BL_DOT4(1, 4); }
-    if (lpw <= 8) { BL_DOT4(1, 8); }
-    BL_DOT4(1, 16);
+  // loads per wave: exactly the lines of its K range where an instantiation
+  // has that count (a longer list would issue loads that carry nothing)
+#if BL_DOT4_EXACT_LPW
+#define BL_DOT4_KS(KS_)                       \
+  switch (lpw) {                              \
+    case 1: BL_DOT4(KS_, 1);                  \
+    case 2: BL_DOT4(KS_, 2);                  \
+    case 3: BL_DOT4(KS_, 3);                  \
+    case 4: BL_DOT4(KS_, 4);                  \
+    case 5: BL_DOT4(KS_, 5);                  \
+    case 6: BL_DOT4(KS_, 6);                  \
+    case 7: BL_DOT4(KS_, 7);                  \
+    case 8: BL_DOT4(KS_, 8);                  \
+    default: BL_DOT4(KS_, 16);                \
   }
-  if (ks == 2) {
-    if (lpw <= 4) { BL_DOT4(2, 4); }
-    if (lpw <= 8) { BL_DOT4(2, 8); }
-    BL_DOT4(2, 16);
-  }
-  if (lpw <= 4) { BL_DOT4(4, 4); }
-  if (lpw <= 8) { BL_DOT4(4, 8); }
-  BL_DOT4(4, 16);
+#else
+#define BL_DOT4_KS(KS_)                       \
+  if (lpw <= 4) { BL_DOT4(KS_, 4); }          \
+  if (lpw <= 8) { BL_DOT4(KS_, 8); }          \
+  BL_DOT4(KS_, 16);
+#endif
+  if (ks == 1) { BL_DOT4_KS(1) }
+  if (ks == 2) { BL_DOT4_KS(2) }
+  BL_DOT4_KS(4)
+#undef BL_DOT4_KS
 #undef BL_DOT4
 }
 
+// (codes through LDS: 4 token rows for m <= 4, 16 for 9 <= m <= 16, where the
+// wave areas fit: NW x MC x SPW x 256 bytes; measured on MI355X, 5 to 8 tokens
+// run faster with per-lane operand loads, and an 8-row area made the compiler
+// take over 256 registers)
 template <int RT, int NW, int SPW, bool ROPE = false>
 hipError_t launch_cfg(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
                       int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream,
                       const DecodeRope &rope = DecodeRope{}) {
   const int blocks = (n + 16 * RT - 1) / (16 * RT);
-  gemv_decode_kernel<RT, NW, SPW, ROPE><<<dim3((unsigned)blocks), dim3(NW * 64), 0, stream>>>(
-      codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, rope);
+#define BL_DECODE_LAUNCH(MC_)                                                                 \
+  gemv_decode_kernel<RT, NW, SPW, ROPE, MC_><<<dim3((unsigned)blocks), dim3(NW * 64), 0, stream>>>( \
+      codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, rope)
+  if constexpr (BL_GEMV_LDS_CODES && NW * 16 * SPW * 256 <= 128 * 1024) {
+    if (m <= 4)
+      BL_DECODE_LAUNCH(4);
+    else if (m <= 8)
+      BL_DECODE_LAUNCH(0);
+    else
+      BL_DECODE_LAUNCH(16);
+  } else {
+    BL_DECODE_LAUNCH(0);
+  }
+#undef BL_DECODE_LAUNCH
   return hipGetLastError();
 }
 
@@ -520,9 +614,13 @@ hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const 
   if (m <= BL_GEMV_DOT4_MAX_M && k % 64 == 0 && k <= kDot4MaxK) {
     switch (m) {
       case 1: return launch_dot4_mt<1>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
+#if BL_GEMV_DOT4_MAX_M >= 2
       case 2: return launch_dot4_mt<2>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
       case 3: return launch_dot4_mt<3>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
       default: return launch_dot4_mt<4>(codes, packed, deq, rowsum, (int)n, (int)k, ep, y, acc_out, stream);
+#else
+      default: break;
+#endif
     }
   }
   if (m > BL_GEMV_RT1_MAX_M)
