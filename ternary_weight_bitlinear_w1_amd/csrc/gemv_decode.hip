@@ -39,7 +39,7 @@ constexpr uint32_t kFieldMask = 0x03030303u;
 #define BL_GEMV_DOT4_MAX_M 2
 #endif
 #ifndef BL_GEMV_MIN_WGS
-#define BL_GEMV_MIN_WGS 256
+#define BL_GEMV_MIN_WGS 512
 #endif
 #ifndef BL_GEMV_RT1_MAX_M
 #define BL_GEMV_RT1_MAX_M 4
