@@ -24,8 +24,12 @@ norm + bfloat16 lm_head (128256 x 2560) at 1 and 4 tokens in GB/s of the head.
 ``stack`` times the 30-layer projection stack at M = 1 and 64, and
 ``stack.token_step`` a whole-model decode step (embedding, 30 layers with RoPE,
 KV cache and attention over 4096 positions, final norm, head) for 1 and 4
-sequences. ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same step's tokens.
+sequences. ``online`` times the online mode from fp32 and bfloat16 masters;
+``kernels`` the step's kernels one by one and the plain (ungated) gate|up
+contraction; ``small_configs`` the single-layer and small-FFN workloads;
+``peaks_measured`` the HBM read rate and int8 MFMA rate this GPU reaches with the
+library's probes. ``cpu_baseline`` times the CPU oracle on a bounded sample of
+the same step's tokens, on one thread and on the usable host cores.
 """
 from __future__ import annotations
 
@@ -933,8 +937,8 @@ def cpu_baseline(w_gate, w_up, w_down, x, seconds):
     this process may use (up to 16; one thread per contiguous block of tokens,
     each running the oracle on its block: tokens are independent, the per-token
     arithmetic is the same, so is every result). TOPS scale with the sample.
-    Also times the oracle on the other workloads (single layer, FFN block,
-    one decode projection, one decoder layer at one token)."""
+    Also times the oracle, on one thread, on the single layer and on one decode
+    projection of each shape."""
     import threading
 
     import oracle
