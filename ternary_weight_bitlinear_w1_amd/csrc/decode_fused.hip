@@ -37,18 +37,24 @@ namespace {
 constexpr uint32_t kFieldMask = 0x03030303u;
 constexpr int kFusedMaxK = 8192;
 
-// NV: float4 of one input row per thread (K <= 1024 NV). A row has at most
-// 2 NV lines of 128 bytes, so each of the KS waves of a row loads LPW lines.
-template <int MODE, int EPI, int MT, int KS, int NV>
-__global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
-  constexpr int RG = 4 / KS;  // row groups of 8 rows
-  constexpr int R = 8 * RG;   // weight rows per workgroup
-  constexpr int LPW = 2 * NV / KS;
+#ifndef BL_FUSED_TH
+#define BL_FUSED_TH 256
+#endif
+
+// TH threads per workgroup; NV: float4 of one input row per thread
+// (K <= 4 TH NV). A row has at most TH NV / 128 lines of 128 bytes, so each of
+// the KS waves of a row loads LPW lines.
+template <int MODE, int EPI, int MT, int KS, int NV, int TH>
+__global__ __launch_bounds__(TH) void gemv_fused_kernel(FusedDecode a) {
+  constexpr int NW = TH / 64;
+  constexpr int RG = NW / KS;  // row groups of 8 rows
+  constexpr int R = 8 * RG;    // weight rows per workgroup
+  constexpr int LPW = (TH * NV / 128 + KS - 1) / KS;
   __shared__ __attribute__((aligned(16))) int8_t sc[MT * kFusedMaxK];
   __shared__ int red[KS][RG][8][MT];
-  __shared__ float red_f[4];
-  __shared__ double red_d[4];
-  __shared__ int red_i[4];
+  __shared__ float red_f[NW];
+  __shared__ double red_d[NW];
+  __shared__ int red_i[NW];
   __shared__ float ybuf[EPI == FUSED_EPI_RELU2 || EPI == FUSED_EPI_ROPE ? MT * R : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
   // quantization of the first token waits for its own row only and runs while
   // the weights are in flight.
   RowStage<NV> st;
-  row_load<MODE, NV>(a.src, 0, st);
+  row_load<MODE, NV, false, TH>(a.src, 0, st);
   __builtin_amdgcn_sched_barrier(0);
   // every lane issues LPW loads; pieces past its range reload the first piece
   // of the matrix and are not used
@@ -109,16 +115,17 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
 
   // the codes of every token of the step, into LDS
   RowQuant q[MT];
-  q[0] = row_finish<MODE, NV>(a.src, 0, a.eps, st, reinterpret_cast<int *>(sc), red_f, red_d, red_i);
+  q[0] = row_finish<MODE, NV, false, TH>(a.src, 0, a.eps, st, reinterpret_cast<int *>(sc), red_f, red_d, red_i);
 #pragma unroll
   for (int t = 1; t < MT; ++t) {
     q[t].deq = 0.0f;
     q[t].rowsum = 0;
     if (t < a.m)
-      q[t] = quant_row<MODE, NV>(a.src, t, a.eps, reinterpret_cast<int *>(sc + t * kFusedMaxK), red_f, red_d, red_i);
+      q[t] = quant_row<MODE, NV, false, TH>(a.src, t, a.eps, reinterpret_cast<int *>(sc + t * kFusedMaxK), red_f,
+                                            red_d, red_i);
   }
   if (blockIdx.x == 0 && a.codes_out) {
-    for (int i = threadIdx.x; i < a.m * (K >> 4); i += 256) {
+    for (int i = threadIdx.x; i < a.m * (K >> 4); i += TH) {
       const int t = i / (K >> 4), c = i - t * (K >> 4);
       *reinterpret_cast<v4i *>(a.codes_out + (int64_t)t * K + 16 * c) =
           *reinterpret_cast<const v4i *>(sc + t * kFusedMaxK + 16 * c);
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(FusedDecode a) {
     constexpr int half = R / 2;
     __syncthreads();
     const int inter = N / 2;
-    for (int i = threadIdx.x; i < MT * half; i += 256) {
+    for (int i = threadIdx.x; i < MT * half; i += TH) {
       const int t = i / half, j = i - t * half;
       if (t < a.m) {
         const float gt = ybuf[t * R + j], up = ybuf[t * R + half + j];
@@ -240,9 +247,10 @@ hipError_t launch_mt(const FusedDecode &a, hipStream_t stream) {
   const int min_wgs = MT == 1 ? 128 : 256;
   const int ks = per32 >= min_wgs ? 1 : (2 * per32 >= min_wgs ? 2 : 4);
   const int R = 32 / ks;
+  constexpr int TH = BL_FUSED_TH, F = TH / 256;  // F: waves per row group per wave of the 256-thread form
   const int lines = ((a.src.k >> 2) + 127) >> 7;
-  const int nv = a.src.k <= 4096 ? 4 : 8;
-  if ((lines + ks - 1) / ks > 2 * nv / ks) return hipErrorInvalidValue;
+  const int nv = a.src.k <= 4096 / F ? 4 / F : 8 / F;
+  if (lines > TH * nv / 128) return hipErrorInvalidValue;
   int grid;
   if (EPI == FUSED_EPI_ROPE) {
     // whole heads of hd rows, hd a multiple of R; every row in a workgroup
@@ -254,15 +262,16 @@ hipError_t launch_mt(const FusedDecode &a, hipStream_t stream) {
   } else {
     grid = (a.n + R - 1) / R;
   }
-  const dim3 g((unsigned)grid), b(256);
-  if (nv == 4) {
-    if (ks == 1) gemv_fused_kernel<MODE, EPI, MT, 1, 4><<<g, b, 0, stream>>>(a);
-    else if (ks == 2) gemv_fused_kernel<MODE, EPI, MT, 2, 4><<<g, b, 0, stream>>>(a);
-    else gemv_fused_kernel<MODE, EPI, MT, 4, 4><<<g, b, 0, stream>>>(a);
+  // R rows per workgroup as R / 8 row groups, each split over F ks waves
+  const dim3 g((unsigned)grid), b(TH);
+  if (nv == 4 / F) {
+    if (ks == 1) gemv_fused_kernel<MODE, EPI, MT, F, 4 / F, TH><<<g, b, 0, stream>>>(a);
+    else if (ks == 2) gemv_fused_kernel<MODE, EPI, MT, 2 * F, 4 / F, TH><<<g, b, 0, stream>>>(a);
+    else gemv_fused_kernel<MODE, EPI, MT, 4 * F, 4 / F, TH><<<g, b, 0, stream>>>(a);
   } else {
-    if (ks == 1) gemv_fused_kernel<MODE, EPI, MT, 1, 8><<<g, b, 0, stream>>>(a);
-    else if (ks == 2) gemv_fused_kernel<MODE, EPI, MT, 2, 8><<<g, b, 0, stream>>>(a);
-    else gemv_fused_kernel<MODE, EPI, MT, 4, 8><<<g, b, 0, stream>>>(a);
+    if (ks == 1) gemv_fused_kernel<MODE, EPI, MT, F, 8 / F, TH><<<g, b, 0, stream>>>(a);
+    else if (ks == 2) gemv_fused_kernel<MODE, EPI, MT, 2 * F, 8 / F, TH><<<g, b, 0, stream>>>(a);
+    else gemv_fused_kernel<MODE, EPI, MT, 4 * F, 8 / F, TH><<<g, b, 0, stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -44,6 +44,9 @@ constexpr uint32_t kFieldMask = 0x03030303u;
 #ifndef BL_GEMV_RT1_MAX_M
 #define BL_GEMV_RT1_MAX_M 4
 #endif
+#ifndef BL_GEMV_FEW_WG_NW16
+#define BL_GEMV_FEW_WG_NW16 1
+#endif
 #ifndef BL_GEMV_CODES_FIRST
 #define BL_GEMV_CODES_FIRST 1
 #endif
@@ -398,6 +401,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict
                                                         float *__restrict__ Y, int32_t *__restrict__ acc_out) {
   const Epilogue ep = resolve_gamma(ep_in);
   constexpr int RG = 4 / KS;  // row groups of 8 rows per workgroup
+  constexpr int NT = 256;
   __shared__ __attribute__((aligned(16))) int8_t sc[MT * kDot4MaxK];
   __shared__ int red[KS][RG][8][MT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -414,12 +418,12 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict
   // weights stream, and each weight piece is used as soon as it arrives: the
   // barrier below waits for LDS traffic only. Every lane issues the same
   // number of loads (out-of-range pieces reload a valid address, unused).
-  constexpr int kCodeLoads = (MT * kDot4MaxK / 16 + 255) / 256;
+  constexpr int kCodeLoads = (MT * kDot4MaxK / 16 + NT - 1) / NT;
   const int n_pieces = MT * (K >> 4);
   v4i cw[kCodeLoads];
 #pragma unroll
   for (int j = 0; j < kCodeLoads; ++j) {
-    const int i = threadIdx.x + 256 * j;
+    const int i = threadIdx.x + NT * j;
     const int t = i / (K >> 4), c = i - t * (K >> 4);
     cw[j] = *reinterpret_cast<const v4i *>(i < n_pieces ? A + (int64_t)t * K + 16 * c : A);
   }
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(const int8_t *__restrict
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kCodeLoads; ++j) {
-    const int i = threadIdx.x + 256 * j;
+    const int i = threadIdx.x + NT * j;
     if (i < n_pieces) {
       const int t = i / (K >> 4), c = i - t * (K >> 4);
       *reinterpret_cast<v4i *>(sc + t * kDot4MaxK + 16 * c) = cw[j];
@@ -553,7 +557,7 @@ hipError_t launch_cfg(const int8_t *codes, const uint8_t *packed, const float *d
 #define BL_DECODE_LAUNCH(MC_)                                                                 \
   gemv_decode_kernel<RT, NW, SPW, ROPE, MC_><<<dim3((unsigned)blocks), dim3(NW * 64), 0, stream>>>( \
       codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, rope)
-  if constexpr (BL_GEMV_LDS_CODES && NW * 16 * SPW * 256 <= 128 * 1024) {
+  if constexpr (BL_GEMV_LDS_CODES && NW * 16 * SPW * 256 + NW * RT * 1024 <= 160 * 1024) {
     if (m <= 4)
       BL_DECODE_LAUNCH(4);
     else if (m <= 8)
@@ -576,6 +580,15 @@ hipError_t launch_rt(const int8_t *codes, const uint8_t *packed, const float *de
     return launch_cfg<RT, BL_GEMV_MIN_WAVES, (4 * BL_GEMV_MIN_WAVES + BL_GEMV_MIN_WAVES - 1) / BL_GEMV_MIN_WAVES>(
         codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, stream);
   }
+#if BL_GEMV_FEW_WG_NW16
+  // fewer row tiles than CUs: sixteen waves of at most two supersteps each,
+  // so each CU keeps more loads in flight (measured on MI355X, down 2560 rows
+  // at 4 tokens: 3.86 us against 4.12 with eight waves of four)
+  if constexpr (RT == 1) {
+    if (n / 16 < 256 && S > 4 * BL_GEMV_MIN_WAVES && S <= 2 * 16)
+      return launch_cfg<RT, 16, 2>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, stream);
+  }
+#endif
   if (S <= 4 * 8) return launch_cfg<RT, 8, 4>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, stream);
   if (S <= 4 * 16) return launch_cfg<RT, 16, 4>(codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, stream);
   const int blocks = (n + 16 * RT - 1) / (16 * RT);
@@ -623,7 +636,12 @@ hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const 
 #endif
     }
   }
-  if (m > BL_GEMV_RT1_MAX_M)
+  // two row tiles per workgroup above BL_GEMV_RT1_MAX_M tokens halve the code
+  // bytes each weight byte needs, where that still leaves a workgroup per CU
+  // (measured on MI355X at 8 and 16 tokens: gate|up 13824 rows 5.9 / 6.4 us
+  // against 6.6 / 8.0 with one tile and 5.9 / 6.9 with four; down 2560 rows
+  // 4.9 / 5.0 us with one tile against 6.2 / 6.2 with two)
+  if (m > BL_GEMV_RT1_MAX_M && n / 32 >= 256)
     return launch_rt<2>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream);
   return launch_rt<1>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream);
 }
