@@ -19,10 +19,13 @@
 //   operand; MFMA t of the superstep uses dword t. MFMA operand convention
 //   (checked on gfx950): lane l supplies row l % 16 of A and column l % 16 of
 //   B, both for k-block l / 16; output lane l, register r holds row
-//   4 (l / 16) + r, column l % 16. Here A rows are tokens (rows >= m are zero)
-//   and B columns are output rows. The NW partial tiles are added in LDS
+//   4 (l / 16) + r, column l % 16. Here A rows are tokens (rows >= m repeat
+//   row m - 1 and give outputs that are not stored) and B columns are output
+//   rows. The NW partial tiles are added in LDS
 //   (exact integer sums), then the field offset is removed
 //   (acc = sum q u - sum q) and the rescale is fused.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bl {
@@ -35,14 +38,17 @@ constexpr uint32_t kFieldMask = 0x03030303u;
 #ifndef BL_GEMV_MIN_WAVES
 #define BL_GEMV_MIN_WAVES 4
 #endif
-#ifndef BL_GEMV_DOT4_MAX_M
-#define BL_GEMV_DOT4_MAX_M 2
+#ifndef BL_GEMV_DOT4_MAX_M  // measured at 2 tokens: down 3.65 us with MFMA, 4.21 with v_dot4
+#define BL_GEMV_DOT4_MAX_M 1
 #endif
 #ifndef BL_GEMV_MIN_WGS
 #define BL_GEMV_MIN_WGS 512
 #endif
 #ifndef BL_GEMV_RT1_MAX_M
 #define BL_GEMV_RT1_MAX_M 4
+#endif
+#ifndef BL_GEMV_MC_5_8
+#define BL_GEMV_MC_5_8 8
 #endif
 #ifndef BL_GEMV_FEW_WG_NW16
 #define BL_GEMV_FEW_WG_NW16 1
@@ -76,7 +82,7 @@ __device__ __forceinline__ v4i unpack16(uint32_t p) {
 // consecutive e, so it rotates each pair itself, with the cosine and sine read
 // from the step's rows of the rotary table (rope_gather_kernel) while the weights load, and writes the
 // keys to the bfloat16 cache; workgroups of the value heads append the values.
-template <int RT, int NW, int SPW, bool ROPE = false, int MC = 0>
+template <int RT, int NW, int SPW, bool ROPE = false, int MC = 0, bool K64 = false>
 __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__restrict__ A,
                                                               const uint8_t *__restrict__ B,
                                                               const float *__restrict__ deq,
@@ -84,6 +90,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
                                                               Epilogue ep_in, float *__restrict__ Y,
                                                               int32_t *__restrict__ acc_out, DecodeRope rope) {
   static_assert(!ROPE || RT == 2, "rotated pairs take the two row tiles");
+  static_assert(SPW >= 1 && SPW <= 4, "at most four supersteps per wave");
   const Epilogue ep = resolve_gamma(ep_in);
   __shared__ int red[NW][RT][64][4];
   __shared__ __attribute__((aligned(16))) int8_t scodes[MC > 0 ? NW : 1][MC > 0 ? MC * SPW * 256 : 16];
@@ -103,109 +110,27 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
   const int S = (G + 15) >> 4;
   const int s_lo = S * wave / NW, cnt = S * (wave + 1) / NW - s_lo;
   const int row = lane & 15, kb = lane >> 4;
-  const bool has_a = row < M;
   const int64_t ldb = K >> 2;
+  const int ta = row < M ? row : M - 1;  // token row of this lane's operand loads
 
-  // row data of this thread's epilogue elements, fetched with the weights
+  // Every load below is unconditional, with rows and pieces clamped into
+  // range: a token row past M, a weight row past N or a piece past the row's
+  // end loads in-range data that only meets zero weights or feeds outputs that
+  // are never stored. Loads guarded by conditions made the compiler merge the
+  // guarded values through register copies, each preceded by a wait for every
+  // load in flight, which serialized the code loads (one L2 round trip each).
+
+  // row data of this thread's epilogue elements, fetched first
   constexpr int kEpi = (RT * 256 + NW * 64 - 1) / (NW * 64);
   int e_rs[kEpi];
   float e_dq[kEpi];
 #pragma unroll
   for (int j = 0; j < kEpi; ++j) {
     const int e = threadIdx.x + j * NW * 64;
-    const int m = 4 * ((e >> 6) & 3) + (e & 3);
-    e_rs[j] = 0;
-    e_dq[j] = 0.0f;
-    if (e < RT * 256 && m < M) {
-      e_rs[j] = rowsum[m];
-      e_dq[j] = deq[m];
-    }
-  }
-
-  v4i b[SPW][RT];
-  v4i a[SPW][4];
-  auto load_weights = [&]() {
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      const int g0 = (s_lo + i) * 16 + 4 * kb;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int n = row_of(rt, row);
-        b[i][rt] = v4i{0, 0, 0, 0};
-        if (i < cnt && n < N) {
-          const uint8_t *p = B + (int64_t)n * ldb + 4 * (int64_t)g0;
-          if (g0 + 4 <= G) {
-            const v4i_u t = *reinterpret_cast<const v4i_u *>(p);
-            b[i][rt] = v4i{t[0], t[1], t[2], t[3]};
-          } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (g0 + t < G) b[i][rt][t] = reinterpret_cast<const int *>(p)[t];
-          }
-        }
-      }
-    }
-  };
-  auto load_codes = [&]() {
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      const int g0 = (s_lo + i) * 16 + 4 * kb;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a[i][t] = v4i{0, 0, 0, 0};
-        if (i < cnt && has_a && g0 + t < G)
-          a[i][t] = *reinterpret_cast<const v4i *>(A + (int64_t)row * K + 16 * (g0 + t));
-      }
-    }
-  };
-  if constexpr (MC > 0) {
-    // The wave's code slice goes through LDS: slot (i, t) of its area holds the
-    // 256 codes of token t in its superstep i, its 16-byte piece c at piece
-    // c ^ t, so that the 16 lanes reading one piece of 16 tokens hit 16
-    // distinct bank groups. Every code load is a full
-    // 64-lane load of 16 bytes (lane l covers slot 4 j + l / 16, piece l % 16),
-    // so a few loads carry what per-lane operand loads would take 4 cnt partly
-    // masked loads for. Slots past the token count, the wave's supersteps or
-    // the row's end load some in-range codes; those meet only zero weights or
-    // feed output rows that are never stored.
-    v4i cs[MC * SPW / 4];
-#pragma unroll
-    for (int j = 0; j < MC * SPW / 4; ++j) {
-      const int slot = 4 * j + (lane >> 4);
-      const int i = slot / MC, t = slot - i * MC;
-      if (4 * j < MC * cnt) {  // wave-uniform: slots of the wave's supersteps only
-        int off = (s_lo + i) * 256 + 16 * (lane & 15);
-        off = off < K - 16 ? off : K - 16;
-        cs[j] = *reinterpret_cast<const v4i *>(A + (int64_t)(t < M ? t : M - 1) * K + off);
-      }
-    }
-    load_weights();
-#pragma unroll
-    for (int j = 0; j < MC * SPW / 4; ++j)
-      if (4 * j < MC * cnt) {
-        const int t = (4 * j + (lane >> 4)) % MC;
-        *reinterpret_cast<v4i *>(scodes[wave] + 1024 * j + 256 * (lane >> 4) + 16 * ((lane & 15) ^ t)) = cs[j];
-      }
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own stores are in LDS
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < SPW; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        a[i][t] = row < MC ? *reinterpret_cast<const v4i *>(scodes[wave] + (i * MC + row) * 256 +
-                                                            16 * ((4 * kb + t) ^ row))
-                           : v4i{0, 0, 0, 0};
-  } else {
-#if BL_GEMV_CODES_FIRST
-    // the codes (a few KB, from L2) first: a wave's loads return in issue order,
-    // so they are in registers by the time the first weights arrive
-    load_codes();
-    load_weights();
-#else
-    load_weights();
-    load_codes();
-#endif
+    int m = 4 * ((e >> 6) & 3) + (e & 3);
+    m = m < M ? m : M - 1;
+    e_rs[j] = rowsum[m];
+    e_dq[j] = deq[m];
   }
   // ROPE form: the cosine and sine of each of this thread's pairs (epilogue entries in
   // tile 0: token m, pair e = 16 rj + l % 16)
@@ -216,25 +141,131 @@ __global__ __launch_bounds__(NW * 64) void gemv_decode_kernel(const int8_t *__re
     rsn[j] = 0.0f;
     if constexpr (ROPE) {
       const int e = threadIdx.x + j * NW * 64;
-      const int l = (e >> 2) & 63, m = 4 * (l >> 4) + (e & 3);
-      if (rotated && e < 256 && m < M) {
-        const int pe = 16 * rj + (l & 15);
-        const float2 cs = rope.cs[m * (rope.hd / 2) + pe];
-        rc[j] = cs.x;
-        rsn[j] = cs.y;
-      }
+      const int l = (e >> 2) & 63;
+      int m = 4 * (l >> 4) + (e & 3);
+      m = m < M ? m : M - 1;
+      const float2 cs = rope.cs[m * (rope.hd / 2) + 16 * rj + (l & 15)];
+      rc[j] = cs.x;
+      rsn[j] = cs.y;
     }
+  }
+
+  // four independent accumulators per row tile (one per 64-k block of a
+  // superstep), so the MFMAs do not wait on one another's results
+  v4i acc4[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc4[rt][t] = v4i{0, 0, 0, 0};
+  // The loads and MFMAs of a wave with C supersteps, straight-line code. With
+  // K % 64 == 0 (K64) a 16-byte weight piece lies wholly inside or wholly past
+  // the row: pieces past it load the row's last piece, and the codes they meet
+  // are zero.
+  auto contract = [&](auto cc) {
+    constexpr int C = decltype(cc)::value;
+    v4i b[C][RT];
+    v4i a[C][4];
+    auto load_weights = [&]() {
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const int g0 = (s_lo + i) * 16 + 4 * kb;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int n = row_of(rt, row);
+          if constexpr (K64) {
+            const int gc = g0 < G ? g0 : G - 4;
+            const v4i_u t = *reinterpret_cast<const v4i_u *>(B + (int64_t)(n < N ? n : N - 1) * ldb + 4 * (int64_t)gc);
+            b[i][rt] = v4i{t[0], t[1], t[2], t[3]};
+            continue;
+          }
+          const uint8_t *p = B + (int64_t)(n < N ? n : N - 1) * ldb + 4 * (int64_t)g0;
+          if (g0 + 4 <= G) {
+            const v4i_u t = *reinterpret_cast<const v4i_u *>(p);
+            b[i][rt] = v4i{t[0], t[1], t[2], t[3]};
+          } else {  // the row's last, partial superstep
+            b[i][rt] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (g0 + t < G) b[i][rt][t] = reinterpret_cast<const int *>(p)[t];
+          }
+        }
+      }
+    };
+    if constexpr (MC > 0) {
+      // The wave's code slice goes through LDS: slot (i, t) of its area holds the
+      // 256 codes of token t in its superstep i, its 16-byte piece c at piece
+      // c ^ t, so that the 16 lanes reading one piece of 16 tokens hit 16
+      // distinct bank groups. Every code load is a full 64-lane load of 16
+      // bytes (lane l covers slot 4 j + l / 16, piece l % 16), so a few loads
+      // carry what per-lane operand loads would take 4 C partly masked loads for.
+      v4i cs[MC * C / 4];
+#pragma unroll
+      for (int j = 0; j < MC * C / 4; ++j) {
+        const int slot = 4 * j + (lane >> 4);
+        const int i = slot / MC, t = slot - i * MC;
+        int off = (s_lo + i) * 256 + 16 * (lane & 15);
+        off = off < K - 16 ? off : K - 16;
+        cs[j] = *reinterpret_cast<const v4i *>(A + (int64_t)(t < M ? t : M - 1) * K + off);
+      }
+      load_weights();
+#pragma unroll
+      for (int j = 0; j < MC * C / 4; ++j) {
+        const int slot = 4 * j + (lane >> 4);
+        const int t = slot % MC;
+        v4i v = cs[j];
+        if constexpr (K64) {  // codes past the row's end are zero
+          const bool in = (s_lo + slot / MC) * 256 + 16 * (lane & 15) < K;
+          v = in ? v : v4i{0, 0, 0, 0};
+        }
+        *reinterpret_cast<v4i *>(scodes[wave] + 1024 * j + 256 * (lane >> 4) + 16 * ((lane & 15) ^ t)) = v;
+      }
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own stores are in LDS
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < C; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          a[i][t] = row < MC ? *reinterpret_cast<const v4i *>(scodes[wave] + (i * MC + row) * 256 +
+                                                              16 * ((4 * kb + t) ^ row))
+                             : v4i{0, 0, 0, 0};
+    } else {
+      // the codes (a few KB, from L2) first: a wave's loads return in issue
+      // order, so they are in registers by the time the first weights arrive
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const int g0 = (s_lo + i) * 16 + 4 * kb;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          a[i][t] = *reinterpret_cast<const v4i *>(A + (int64_t)ta * K + 16 * (g0 + t < G ? g0 + t : G - 1));
+      }
+      load_weights();
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v4i ai = a[i][t];
+        if constexpr (K64 && MC == 0) {  // codes past the row's end are zero
+          const int g = (s_lo + i) * 16 + 4 * kb + t;
+          ai = g < G ? ai : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc4[rt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ai, unpack16((uint32_t)b[i][rt][t]), acc4[rt][t], 0, 0, 0);
+      }
+  };
+  // cnt <= SPW (wave-uniform)
+  switch (cnt) {
+    case 1: contract(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (SPW >= 2) contract(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (SPW >= 3) contract(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (SPW >= 4) contract(std::integral_constant<int, 4>{}); break;
+    default: break;
   }
   v4i acc[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc[rt] = v4i{0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < SPW; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i][t], unpack16((uint32_t)b[i][rt][t]), acc[rt], 0, 0, 0);
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = (acc4[rt][0] + acc4[rt][1]) + (acc4[rt][2] + acc4[rt][3]);
 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -382,7 +413,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_loop_kernel(const int8_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Few-token kernel (m <= 4, K % 64 == 0, K <= kDot4MaxK): dot-product form.
+// One-token kernel (K % 64 == 0, K <= kDot4MaxK; written for up to four tokens,
+// but from two tokens on the MFMA kernel is faster): dot-product form.
 //
 // Lane l of a wave reads 16 bytes (64 weights) of row l / 8 at piece l % 8 of
 // each 128-byte line, so every wave-wide load moves 8 full lines. The token
@@ -545,23 +577,30 @@ hipError_t launch_dot4_mt(const int8_t *codes, const uint8_t *packed, const floa
 #undef BL_DOT4
 }
 
-// (codes through LDS: 4 token rows for m <= 4, 16 for 9 <= m <= 16, where the
-// wave areas fit: NW x MC x SPW x 256 bytes; measured on MI355X, 5 to 8 tokens
-// run faster with per-lane operand loads, and an 8-row area made the compiler
-// take over 256 registers)
+// (codes through LDS: 4 token rows for m <= 4, 8 for 5 <= m <= 8, 16 for
+// 9 <= m <= 16, where the wave areas fit: NW x MC x SPW x 256 bytes; measured
+// on MI355X at 8 tokens, gate|up 5.05 us and down 4.16 us against 5.94 and 5.25
+// with per-lane operand loads)
 template <int RT, int NW, int SPW, bool ROPE = false>
 hipError_t launch_cfg(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
                       int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream,
                       const DecodeRope &rope = DecodeRope{}) {
   const int blocks = (n + 16 * RT - 1) / (16 * RT);
-#define BL_DECODE_LAUNCH(MC_)                                                                 \
-  gemv_decode_kernel<RT, NW, SPW, ROPE, MC_><<<dim3((unsigned)blocks), dim3(NW * 64), 0, stream>>>( \
-      codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, rope)
+#define BL_DECODE_LAUNCH(MC_)                                                                          \
+  do {                                                                                                       \
+    if (k % 64 == 0)                                                                                         \
+      gemv_decode_kernel<RT, NW, SPW, ROPE, MC_, true><<<dim3((unsigned)blocks), dim3(NW * 64), 0, stream>>>( \
+          codes, packed, deq, rowsum, m, n, k, ep, y, acc_out, rope);                                        \
+    else                                                                                                     \
+      gemv_decode_kernel<RT, NW, SPW, ROPE, MC_, false><<<dim3((unsigned)blocks), dim3(NW * 64), 0,          \
+                                                          stream>>>(codes, packed, deq, rowsum, m, n, k, ep, y, \
+                                                                    acc_out, rope);                           \
+  } while (0)
   if constexpr (BL_GEMV_LDS_CODES && NW * 16 * SPW * 256 + NW * RT * 1024 <= 160 * 1024) {
     if (m <= 4)
       BL_DECODE_LAUNCH(4);
     else if (m <= 8)
-      BL_DECODE_LAUNCH(0);
+      BL_DECODE_LAUNCH(BL_GEMV_MC_5_8);
     else
       BL_DECODE_LAUNCH(16);
   } else {

@@ -167,9 +167,9 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           # shapes the pipelined kernel takes (N % 128 == 0, K % 128 == 0): every tile
           # variant, K-chunk counts 1, 2, 3, 5, 9 and M not a multiple of the tile
           (130, 512, 256), (65, 384, 384), (40, 768, 640), (333, 1280, 1152), (20, 256, 128), (257, 2560, 2560),
-          # few-token shapes of the dot-product decode kernel (m <= 2, K % 64 == 0) and of the MFMA
-          # decode kernel (3 and 4 tokens): rows not a multiple of 8, K from one partial line to
-          # 8192, every split of K over waves
+          # few-token shapes of the dot-product decode kernel (one token, K % 64 == 0) and of the
+          # MFMA decode kernel (2 to 4 tokens): rows not a multiple of 8, K from one partial line
+          # to 8192, every split of K over waves
           (1, 77, 64), (2, 200, 320), (3, 1000, 576), (4, 40, 8192), (1, 9000, 1024), (4, 5000, 448),
           # 5..16 tokens over at least 8192 rows: two row tiles per workgroup, ragged rows and K
           (12, 8200, 320), (6, 8224, 2576),
