@@ -192,6 +192,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     qv[hh][0] = a.x; qv[hh][1] = a.y; qv[hh][2] = a.z; qv[hh][3] = a.w;
     qv[hh][4] = b.x; qv[hh][5] = b.y; qv[hh][6] = b.z; qv[hh][7] = b.w;
   }
+  // keep every load above the arithmetic: left to itself the compiler sinks the
+  // value loads below the scores, a second memory round trip after the first
+  __builtin_amdgcn_sched_barrier(0);
   const float scale = (float)(1.0 / sqrt((double)HD));
   // ---- scores, and this lane's max over its positions
   float sc[PW][G], mx[G];
