@@ -29,6 +29,8 @@
 // in flight.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace bl {
@@ -174,9 +176,9 @@ __device__ __forceinline__ int part_col(const Src &s, int f, int p) {
 }
 
 // A row whose projection operand is given as split-K partial sums. The plain
-// operands (residual summand, gain) are issued first; then the partial sums
-// plane by plane, two planes at a time for every slot of the thread, so a row
-// takes about S / 2 memory round trips rather than S per slot. Integer sums are
+// operands (residual summand, gain) are issued first; then the partial sums of
+// every plane for every slot of the thread, so a row takes one memory round
+// trip (beyond eight planes: two planes per round trip). Integer sums are
 // exact, so the order of the planes does not matter.
 template <int MODE, int NV, int TH>
 __device__ __forceinline__ void row_load_part(const Src &s, int64_t r, RowStage<NV> &st) {
@@ -199,27 +201,62 @@ __device__ __forceinline__ void row_load_part(const Src &s, int64_t r, RowStage<
   const int32_t *base = s.part + r * s.ld;
   const int S = s.part_splits;
   v4i t[NV][NP];
+  // Up to kPartStraight planes: every plane's loads issued before the first
+  // sum, in straight-line code per plane count (a loop over a run-time count
+  // waits for each round trip in turn). More planes: two per round trip.
+  auto planes = [&](auto sc) {
+    constexpr int SP = decltype(sc)::value;
+    v4i u[SP][NV][NP];
 #pragma unroll
-  for (int j = 0; j < NV; ++j)
+    for (int sp = 0; sp < SP; ++sp)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) t[j][p] = *reinterpret_cast<const v4i *>(base + col[j][p]);
-  for (int sp = 1; sp < S; sp += 2) {
-    // past the last plane the second load repeats plane sp and is not added
-    const bool two = sp + 1 < S;
-    const int64_t o0 = sp * s.part_plane, o1 = (two ? sp + 1 : sp) * s.part_plane;
-    v4i u0[NV][NP], u1[NV][NP];
+      for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          u[sp][j][p] = *reinterpret_cast<const v4i *>(base + sp * s.part_plane + col[j][p]);
 #pragma unroll
     for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        u0[j][p] = *reinterpret_cast<const v4i *>(base + o0 + col[j][p]);
-        u1[j][p] = *reinterpret_cast<const v4i *>(base + o1 + col[j][p]);
+        v4i a = u[0][j][p];
+#pragma unroll
+        for (int sp = 1; sp < SP; ++sp) a += u[sp][j][p];
+        t[j][p] = a;
       }
-    const v4i zero = {0, 0, 0, 0};
+  };
+  switch (S) {
+    case 1: planes(std::integral_constant<int, 1>{}); break;
+    case 2: planes(std::integral_constant<int, 2>{}); break;
+    case 3: planes(std::integral_constant<int, 3>{}); break;
+    case 4: planes(std::integral_constant<int, 4>{}); break;
+    case 5: planes(std::integral_constant<int, 5>{}); break;
+    case 6: planes(std::integral_constant<int, 6>{}); break;
+    case 7: planes(std::integral_constant<int, 7>{}); break;
+    case 8: planes(std::integral_constant<int, 8>{}); break;
+    default: {
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+      for (int j = 0; j < NV; ++j)
 #pragma unroll
-      for (int p = 0; p < NP; ++p) t[j][p] += u0[j][p] + (two ? u1[j][p] : zero);
+        for (int p = 0; p < NP; ++p) t[j][p] = *reinterpret_cast<const v4i *>(base + col[j][p]);
+      for (int sp = 1; sp < S; sp += 2) {
+        // past the last plane the second load repeats plane sp and is not added
+        const bool two = sp + 1 < S;
+        const int64_t o0 = sp * s.part_plane, o1 = (two ? sp + 1 : sp) * s.part_plane;
+        v4i u0[NV][NP], u1[NV][NP];
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            u0[j][p] = *reinterpret_cast<const v4i *>(base + o0 + col[j][p]);
+            u1[j][p] = *reinterpret_cast<const v4i *>(base + o1 + col[j][p]);
+          }
+        const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) t[j][p] += u0[j][p] + (two ? u1[j][p] : zero);
+      }
+    }
   }
   const int rs = s.part_rowsum[r];
   const float dq = s.part_deq[r];
