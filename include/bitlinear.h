@@ -23,6 +23,9 @@
  *  - Arguments are checked on the host before anything is enqueued; a failed
  *    check returns a status and enqueues nothing. bitlinear_last_error() then
  *    gives a one-line reason (per thread).
+ *  - A call over m == 0 tokens is a no-op that returns BITLINEAR_OK after the
+ *    shape and argument checks; its per-token buffers (activations, codes,
+ *    scales, outputs, workspace) may then be NULL.
  *  - Inputs must be finite; NaN and Inf are outside the contract.
  *  - The library is stateless between calls and reentrant on distinct buffers.
  */
@@ -111,8 +114,8 @@ typedef enum {
  *   deq        [m] fp32.
  *   code_rowsum NULL or [m] int32: sum_k codes[m][k].
  * Rounding is half to even; an all-zero token gives codes 0 and deq 0.
- * Errors: NULL x/codes/deq -> ERR_NULL; m < 0, k <= 0, k % 16 != 0 -> ERR_SHAPE;
- * bad mode -> ERR_ARG. m == 0 is a no-op. */
+ * Errors: NULL x/codes/deq (m > 0) -> ERR_NULL; m < 0, k <= 0, k % 16 != 0 ->
+ * ERR_SHAPE; bad mode -> ERR_ARG. m == 0 is a no-op. */
 bitlinear_status bitlinear_quantize_acts(const float *x, int64_t m, int64_t k, int32_t mode,
                                          const float *norm_gain, float eps, int8_t *codes, float *deq,
                                          int32_t *code_rowsum, void *stream);

@@ -201,7 +201,7 @@ bitlinear_status bitlinear_validate_packed(const uint8_t *w_packed, int64_t n, i
 bitlinear_status bitlinear_quantize_acts(const float *x, int64_t m, int64_t k, int32_t mode, const float *norm_gain,
                                          float eps, int8_t *codes, float *deq, int32_t *code_rowsum, void *stream) {
   g_err.clear();
-  if (!x || !codes || !deq) return fail(BITLINEAR_ERR_NULL, "x, codes and deq are required");
+  if (m != 0 && (!x || !codes || !deq)) return fail(BITLINEAR_ERR_NULL, "x, codes and deq are required");
   if (m < 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || k > kMaxDim)
     return fail(BITLINEAR_ERR_SHAPE, "m = %lld, k = %lld: need m >= 0, k > 0, k %% 16 == 0", (long long)m,
                 (long long)k);
@@ -378,8 +378,8 @@ bitlinear_status bitlinear_forward_relu2_glu(const float *x, const int8_t *codes
                                              const uint8_t *w_packed, int64_t inter, const float *gamma, float *y,
                                              int32_t path, void *workspace, size_t workspace_bytes, void *stream) {
   g_err.clear();
-  if (!w_packed || !y || !gamma) return fail(BITLINEAR_ERR_NULL, "w_packed, gamma and y are required");
-  if (!x && (!codes_in || !deq_in)) return fail(BITLINEAR_ERR_NULL, "give x, or codes_in and deq_in");
+  if (!w_packed || !gamma || (m != 0 && !y)) return fail(BITLINEAR_ERR_NULL, "w_packed, gamma and y are required");
+  if (m != 0 && !x && (!codes_in || !deq_in)) return fail(BITLINEAR_ERR_NULL, "give x, or codes_in and deq_in");
   if (m < 0 || inter <= 0 || inter % 4 != 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || 2 * inter > kMaxDim ||
       k > kMaxDim)
     return fail(BITLINEAR_ERR_SHAPE, "m = %lld, inter = %lld, k = %lld: need m >= 0, inter > 0, inter %% 4 == 0, "
@@ -1084,7 +1084,7 @@ bitlinear_status bitlinear_block_forward(const bitlinear_block *blk, const float
                                          void *stream) {
   g_err.clear();
   BL_TRY(check_block(blk));
-  if (!x || !y) return fail(BITLINEAR_ERR_NULL, "x and y are required");
+  if (m != 0 && (!x || !y)) return fail(BITLINEAR_ERR_NULL, "x and y are required");
   if (m < 0 || m > kMaxDim) return fail(BITLINEAR_ERR_SHAPE, "m = %lld", (long long)m);
   if (!aligned16(x) || !aligned16(y)) return fail(BITLINEAR_ERR_ALIGN, "x and y must be 16-byte aligned");
   const size_t need = bitlinear_block_workspace_bytes(blk, m);

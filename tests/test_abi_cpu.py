@@ -65,6 +65,7 @@ def test_forward_validation():
     assert _fw(ws=None) == bl.ERR_WORKSPACE
     assert _fw(wsb=16) == bl.ERR_WORKSPACE
     assert _fw(m=0) == bl.OK  # empty input is a no-op
+    assert _fw(m=0, x=None, y=None, ws=None) == bl.OK
     assert b"seg_end" in bl.lib().bitlinear_last_error() or True
 
 
@@ -105,6 +106,7 @@ def test_forward_relu2_glu_validation():
     assert _glu(y=MIS) == bl.ERR_ALIGN
     assert _glu(ws=None) == bl.ERR_WORKSPACE
     assert _glu(m=0) == bl.OK
+    assert _glu(m=0, x=None, y=None, ws=None) == bl.OK
 
 
 def test_forward_relu2_glu_workspace_sizes():
@@ -263,6 +265,8 @@ def test_quantize_acts_validation():
     assert q(MIS, 4, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_ALIGN
     assert q(A, 4, 64, 1, MIS, ctypes.c_float(1e-5), A, A, None, None) == bl.ERR_ALIGN
     assert q(A, 0, 64, 0, None, ctypes.c_float(1e-5), A, A, None, None) == bl.OK
+    # m == 0: the per-token buffers may be NULL (an empty tensor's data pointer)
+    assert q(None, 0, 64, 0, None, ctypes.c_float(1e-5), None, None, None, None) == bl.OK
 
 
 def test_quantize_weights_validation():
@@ -303,6 +307,8 @@ def test_block_validation():
     blk, keep = _block()
     assert bl.lib().bitlinear_block_workspace_bytes(ctypes.byref(blk), 4) > 0
     assert f(ctypes.byref(blk), A, 0, A, None, None, 0, None) == bl.OK  # m == 0
+    assert f(ctypes.byref(blk), None, 0, None, None, None, 0, None) == bl.OK
+    assert f(ctypes.byref(blk), None, 4, A, None, None, 0, None) == bl.ERR_NULL
     assert f(ctypes.byref(blk), A, 4, A, None, None, 0, None) == bl.ERR_WORKSPACE
     assert f(ctypes.byref(blk), None, 4, A, None, A, 1 << 30, None) == bl.ERR_NULL
     assert f(ctypes.byref(blk), MIS, 4, A, None, A, 1 << 30, None) == bl.ERR_ALIGN

@@ -173,6 +173,9 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           (1, 77, 64), (2, 200, 320), (3, 1000, 576), (4, 40, 8192), (1, 9000, 1024), (4, 5000, 448),
           # 5..16 tokens over at least 8192 rows: two row tiles per workgroup, ragged rows and K
           (12, 8200, 320), (6, 8224, 2576),
+          # long rows: one token past the dot-product kernel's 8192 (sixteen waves of four supersteps,
+          # per-lane code loads), and past 16 waves x 4 supersteps (the looping kernel)
+          (1, 70, 8256), (3, 100, 16400),
           # few output tiles, where K is split into ranges (16, 8, 4 here) whose int32 partial sums a
           # second kernel adds, and neighbours that are not split
           (9, 512, 4096), (5, 256, 2048), (48, 1024, 3072), (37, 512, 1024), (100, 384, 768),
@@ -419,3 +422,39 @@ def test_forward_codes_past_32bit_offsets():
     acc_o = oracle.contract(q, mat.codes)
     assert_equal(a_gpu, acc_o, "acc")
     assert_equal(y_gpu, oracle.rescale(acc_o, d, [mat.gamma], [n]), "y")
+
+
+# ------------------------------------------------------------------------------ empty token batches
+def test_empty_token_batches():
+    """m = 0 is a no-op on every per-token entry point: each returns success with
+    an empty output, and the decode, prefill and automatic paths agree on it."""
+    note("empty token batches")
+    k, n, inter = 256, 96, 128
+    mat = Matrix(n, k, seed(8, 0, 1))
+    packed = gpu(oracle.pack(mat.codes))
+    g = [mat.gamma_f]
+    x0 = torch.empty((0, k), dtype=torch.float32, device=DEV)
+    for mode in (bl.ACT_ABSMAX, bl.ACT_RMSNORM):
+        codes, deq, rowsum = bl.quantize_acts(x0, mode)
+        assert tuple(codes.shape) == (0, k) and deq.numel() == 0 and rowsum.numel() == 0
+    codes, deq, rowsum = bl.quantize_acts(torch.empty((0, 2 * k), device=DEV), bl.ACT_RELU2_RMSNORM)
+    assert tuple(codes.shape) == (0, k)
+    for path in (bl.PATH_AUTO, bl.PATH_PREFILL, bl.PATH_DECODE):
+        y, acc = bl.forward(packed, k, g, x=x0, want_acc=True, path=path)
+        assert tuple(y.shape) == (0, n) and tuple(acc.shape) == (0, n)
+        y = bl.forward(packed, k, g, codes=torch.empty((0, k), dtype=torch.int8, device=DEV),
+                       deq=torch.empty(0, device=DEV), path=path)
+        assert tuple(y.shape) == (0, n)
+    gu = Matrix(2 * inter, k, seed(8, 0, 2))
+    y = bl.forward_relu2_glu(gpu(oracle.pack(gu.codes)), k, [gu.gamma_f, gu.gamma_f], x=x0)
+    assert tuple(y.shape) == (0, inter)
+    head = torch.zeros((64, k), dtype=torch.uint16, device=DEV)
+    assert tuple(bl.lm_head(x0, head).shape) == (0, 64)
+    assert tuple(bl.embed(torch.empty(0, dtype=torch.int64, device=DEV), head).shape) == (0, k)
+    pos = torch.empty(0, dtype=torch.int64, device=DEV)
+    bl.rope(torch.empty((0, 256), device=DEV), pos, 2, 128, bl.rope_table(5e5, 128, 16, DEV))
+    kc = torch.zeros((1, 1, 16, 128), dtype=torch.uint16, device=DEV)
+    vc = torch.zeros_like(kc)
+    o = bl.attention_decode(torch.empty((0, 256), device=DEV), kc, vc, pos, pos, 2)
+    assert tuple(o.shape) == (0, 256)
+    assert not kc.view(torch.int16).any() and not vc.view(torch.int16).any()
