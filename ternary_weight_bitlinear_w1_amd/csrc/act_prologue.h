@@ -143,13 +143,25 @@ __device__ __forceinline__ float4 gain_of(const RawIn &v, float4 p) {
 }
 
 // round(v pre s) half to even. With s = fl(127 / fl(a pre)) and |v| <= a, the
-// product stays below 127.5 in magnitude (two roundings of relative size
-// 2^-24), so the code lies in [-127, 127] without a clamp; a NaN product
-// converts to 0. pre is 1 except on rows whose max is below 2^-64.
-__device__ __forceinline__ int code_of(float v, float pre, float s) {
-  return (int)__builtin_rintf(__fmul_rn(__fmul_rn(v, pre), s));
+// product y stays within 127.5 in magnitude (two roundings of relative size
+// 2^-24), so the code lies in [-127, 127] without a clamp. pre is 1 except on
+// rows whose max is below 2^-64.
+//
+// The rounding is one fp32 add: for |y| < 2^22, y + 1.5 * 2^23 lies in
+// [2^23, 2^24), where the spacing of floats is 1, so the round-to-nearest-even
+// add rounds y to the nearest integer, ties to even, and the result's bit
+// pattern is 0x4B400000 + round(y) (two's complement, borrowing from the upper
+// bits when round(y) < 0). Its low byte is therefore the int8 code, and a sum
+// of such patterns modulo 2^32, less count * 0x4B400000, is the sum of the
+// codes. (Non-finite inputs are outside the contract.)
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr uint32_t kRoundBits = 0x4B400000u;
+__device__ __forceinline__ uint32_t code_bits(float y) { return __float_as_uint(__fadd_rn(y, kRoundMagic)); }
+// four code patterns -> the word of their low bytes (first code lowest)
+__device__ __forceinline__ int pack_codes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return (int)(lo | (hi << 16));
 }
-__device__ __forceinline__ int code_of(float v, float s) { return (int)__builtin_rintf(__fmul_rn(v, s)); }
 
 struct RowQuant {
   float deq;   // dequantization factor of the row's codes
@@ -351,11 +363,16 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
     // keeps 127 / a finite and changes no code the unscaled steps reach
     const float pre = a < 0x1p-64f ? 0x1p64f : 1.0f;
     const float sc = 127.0f / __fmul_rn(a, pre);
+    uint32_t rb = 0;  // sum of code patterns (mod 2^32)
+    int nq = 0;       // codes in rb
     auto emit = [&](int f, float4 v) {
-      const int q0 = code_of(v.x, pre, sc), q1 = code_of(v.y, pre, sc);
-      const int q2 = code_of(v.z, pre, sc), q3 = code_of(v.w, pre, sc);
-      rs += q0 + q1 + q2 + q3;
-      words[f] = (q0 & 0xff) | ((q1 & 0xff) << 8) | ((q2 & 0xff) << 16) | ((int)((unsigned)(q3 & 0xff) << 24));
+      const uint32_t b0 = code_bits(__fmul_rn(__fmul_rn(v.x, pre), sc));
+      const uint32_t b1 = code_bits(__fmul_rn(__fmul_rn(v.y, pre), sc));
+      const uint32_t b2 = code_bits(__fmul_rn(__fmul_rn(v.z, pre), sc));
+      const uint32_t b3 = code_bits(__fmul_rn(__fmul_rn(v.w, pre), sc));
+      rb += b0 + b1 + b2 + b3;
+      nq += 4;
+      words[f] = pack_codes(b0, b1, b2, b3);
     };
     if constexpr (NV > 0) {
       if (pre == 1.0f) {  // (v 1 = v exactly: one multiply per element)
@@ -364,10 +381,11 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
           const int f = tid + j * TH;
           if (f < nf) {
             const float4 v = cache[j];
-            const int q0 = code_of(v.x, sc), q1 = code_of(v.y, sc), q2 = code_of(v.z, sc), q3 = code_of(v.w, sc);
-            rs += q0 + q1 + q2 + q3;
-            words[f] =
-                (q0 & 0xff) | ((q1 & 0xff) << 8) | ((q2 & 0xff) << 16) | ((int)((unsigned)(q3 & 0xff) << 24));
+            const uint32_t b0 = code_bits(__fmul_rn(v.x, sc)), b1 = code_bits(__fmul_rn(v.y, sc));
+            const uint32_t b2 = code_bits(__fmul_rn(v.z, sc)), b3 = code_bits(__fmul_rn(v.w, sc));
+            rb += b0 + b1 + b2 + b3;
+            nq += 4;
+            words[f] = pack_codes(b0, b1, b2, b3);
           }
         }
       } else {
@@ -383,6 +401,7 @@ __device__ __forceinline__ RowQuant row_finish(const Src &s, int64_t r, float ep
         emit(f, gain_of<MODE>(raw, pre_of<MODE>(s, r, f, raw, false)));
       }
     }
+    rs = (int)(rb - (uint32_t)nq * kRoundBits);
   }
   rs = wave_sum(rs);
   if (lane == 0) red_i[wave] = rs;
