@@ -53,9 +53,6 @@ constexpr uint32_t kFieldMask = 0x03030303u;
 #ifndef BL_GEMV_FEW_WG_NW16
 #define BL_GEMV_FEW_WG_NW16 1
 #endif
-#ifndef BL_GEMV_CODES_FIRST
-#define BL_GEMV_CODES_FIRST 1
-#endif
 #ifndef BL_GEMV_LDS_CODES
 #define BL_GEMV_LDS_CODES 1
 #endif
