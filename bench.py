@@ -10,7 +10,9 @@ on the GPU through the C ABI:
     ffn_sub_norm folded into the quantization of [4096][6912]
     down contraction 6912 -> 2560 + rescale
 Weights are packed once before timing (the packed-checkpoint mode). ``value``
-is int8 TOPS of the whole step: 2 M N K of both contractions / step time.
+is int8 TOPS of the whole step: 2 M N K of both contractions / step time, the
+step time being the time of exactly K steps between two events after the
+untimed settling run and the W warmup steps.
 ``roofline`` is the gated gate|up contraction kernel against dense int8 MFMA peak,
 its mean duration over back-to-back launches between two HIP events on the
 stream it runs on; its ``traffic`` comes from the
@@ -54,6 +56,7 @@ ROPE_POSITIONS = 4096
 BASE_SEED = 1234
 RING_BYTES = 600 * 2 ** 20  # > 2 x the 256 MB last-level cache
 TOKEN_STEP_BATCHES = (1, 4)  # sequences per whole-model decode step
+SETTLE_S = 0.2  # untimed run of the prefill step before its warmup steps
 
 
 def parse():
@@ -172,23 +175,44 @@ def main():
         log("calibration kernel: 268435456 bytes read, 268435456 bytes written")
 
     # ---------------------------------------------------------------- prefill step
-    log(f"prefill: warmup {args.warmup}, steps {args.steps}")
-    for _ in range(args.warmup):
+    def step():
         for _, f in ops:
             f()
+
+    # the GPU leaves its idle clocks: the step runs untimed for at least
+    # SETTLE_S seconds before the warmup steps (weight packing alone is too
+    # short a load for that)
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        n_settle += 20
+    log(f"prefill: {n_settle} untimed settling steps, then warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    # the timed region: exactly K steps between two events, nothing else
+    t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    t_a.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = t_a.elapsed_time(t_b) / args.steps
+    # each operation's share, from a second pass with an event between operations
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
     for s in range(args.steps):
         ev[s][0].record(stream)
         for j, (_, f) in enumerate(ops):
             f()
             ev[s][j + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_op = {name: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(args.steps)]))
               for j, (name, _) in enumerate(ops)}
-    step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)]))
     ops_gu = 2.0 * M * (2 * I) * H
     ops_d = 2.0 * M * H * I
     tops = (ops_gu + ops_d) / (step_ms * 1e-3) / 1e12
