@@ -475,6 +475,14 @@ bitlinear_status bitlinear_probe_read(const void *src, int64_t bytes, int64_t gr
  * ERR_SHAPE. */
 bitlinear_status bitlinear_probe_mfma(int32_t iters, int64_t workgroups, int32_t *sink, void *stream);
 
+/* bitlinear_probe_mfma_varied — as bitlinear_probe_mfma, but the operands vary
+ * from one MFMA to the next (four pseudo-random operand sets per lane: A bytes
+ * in {0, 1, 2} like the unpacked ternary codes, B bytes any int8 like the
+ * activation codes). The matrix cores then draw about the power they draw in
+ * the GEMMs, and the clock the GPU holds under that power sets the int8 rate a
+ * contraction over such data can reach. Same arguments and errors. */
+bitlinear_status bitlinear_probe_mfma_varied(int32_t iters, int64_t workgroups, int32_t *sink, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Misc.
  * ------------------------------------------------------------------------- */

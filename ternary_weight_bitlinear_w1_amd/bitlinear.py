@@ -103,6 +103,7 @@ def lib():
             "bitlinear_block_workspace_bytes": (_sz, [ctypes.POINTER(Block), _i64]),
             "bitlinear_probe_read": (_i32, [_p, _i64, _i64, _p, _p]),
             "bitlinear_probe_mfma": (_i32, [_i32, _i64, _p, _p]),
+            "bitlinear_probe_mfma_varied": (_i32, [_i32, _i64, _p, _p]),
             "bitlinear_status_str": (ctypes.c_char_p, [_i32]),
             "bitlinear_last_error": (ctypes.c_char_p, []),
             "bitlinear_abi_version": (_i32, []),
@@ -349,9 +350,12 @@ def probe_read(src: torch.Tensor, nbytes: Optional[int] = None, grid: int = 0,
     _check("bitlinear_probe_read", lib().bitlinear_probe_read(_ptr(src), nb, grid, _ptr(s), _stream(src.device)))
 
 
-def probe_mfma(iters: int, workgroups: int, sink: torch.Tensor) -> None:
-    """Measurement probe: workgroups x 4 waves x iters x 8 int8 MFMA 32x32x32."""
-    _check("bitlinear_probe_mfma", lib().bitlinear_probe_mfma(iters, workgroups, _ptr(sink), _stream(sink.device)))
+def probe_mfma(iters: int, workgroups: int, sink: torch.Tensor, varied: bool = False) -> None:
+    """Measurement probe: workgroups x 4 waves x iters x 8 int8 MFMA 32x32x32,
+    on fixed operands or (varied) on operands that change from one MFMA to the
+    next with the value ranges of the GEMMs' operands."""
+    name = "bitlinear_probe_mfma_varied" if varied else "bitlinear_probe_mfma"
+    _check(name, getattr(lib(), name)(iters, workgroups, _ptr(sink), _stream(sink.device)))
 
 
 def base3_row_bytes(k: int) -> int:

@@ -148,13 +148,21 @@ bitlinear_status bitlinear_probe_read(const void *src, int64_t bytes, int64_t gr
   return launched(bl::launch_probe_read(src, bytes, sink, grid, as_stream(stream)), "probe read");
 }
 
-bitlinear_status bitlinear_probe_mfma(int32_t iters, int64_t workgroups, int32_t *sink, void *stream) {
+static bitlinear_status probe_mfma(int32_t iters, int64_t workgroups, bool varied, int32_t *sink, void *stream) {
   g_err.clear();
   if (!sink) return fail(BITLINEAR_ERR_NULL, "sink is required");
   if (iters <= 0 || workgroups <= 0 || workgroups > 65536)
     return fail(BITLINEAR_ERR_SHAPE, "iters > 0 and 0 < workgroups <= 65536");
   BL_TRY(check_device());
-  return launched(bl::launch_probe_mfma(iters, workgroups, sink, as_stream(stream)), "probe mfma");
+  return launched(bl::launch_probe_mfma(iters, workgroups, varied, sink, as_stream(stream)), "probe mfma");
+}
+
+bitlinear_status bitlinear_probe_mfma(int32_t iters, int64_t workgroups, int32_t *sink, void *stream) {
+  return probe_mfma(iters, workgroups, false, sink, stream);
+}
+
+bitlinear_status bitlinear_probe_mfma_varied(int32_t iters, int64_t workgroups, int32_t *sink, void *stream) {
+  return probe_mfma(iters, workgroups, true, sink, stream);
 }
 
 int32_t bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }

@@ -288,7 +288,7 @@ hipError_t launch_embed(const int64_t *ids, int64_t m, const uint16_t *table, in
 // one thread per 8 loads) and independent int8 MFMA chains (256-thread
 // workgroups, iters x 8 v_mfma_i32_32x32x32_i8 per wave).
 hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, int64_t grid, hipStream_t stream);
-hipError_t launch_probe_mfma(int iters, int64_t workgroups, int32_t *sink, hipStream_t stream);
+hipError_t launch_probe_mfma(int iters, int64_t workgroups, bool varied, int32_t *sink, hipStream_t stream);
 
 // RoPE, the bfloat16 KV cache and causal attention (attention.hip).
 bool attention_supported(int n_heads, int n_kv, int hd);

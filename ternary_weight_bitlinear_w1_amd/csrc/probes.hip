@@ -10,7 +10,14 @@
 // last-level cache, the HBM read rate.
 //
 // probe_mfma_kernel: independent chains of v_mfma_i32_32x32x32_i8 per wave,
-// no memory traffic: the int8 matrix-core issue rate.
+// no memory traffic: the int8 matrix-core issue rate. With fixed operands
+// (every MFMA of a lane multiplies the same small values) it shows the issue
+// rate at the clock such light work allows; with varied operands (VARIED:
+// four operand sets per lane, consecutive MFMAs of a wave taking different
+// ones, A values in {0, 1, 2} like the unpacked ternary codes and B any int8
+// like the activation codes) the matrix cores switch as in the GEMMs, draw
+// more power, and the clock the GPU then holds sets the rate a contraction
+// over such data can reach.
 #include "common.h"
 
 namespace bl {
@@ -38,16 +45,44 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const v4i *__
   if (f == key) sink[0] = f;
 }
 
+// xorshift32 (Marsaglia, "Xorshift RNGs", 2003): operand bytes for the
+// varied-operand probe
+__device__ __forceinline__ uint32_t xorshift32(uint32_t &h) {
+  h ^= h << 13;
+  h ^= h >> 17;
+  h ^= h << 5;
+  return h;
+}
+
+template <bool VARIED>
 __global__ __launch_bounds__(256, 2) void probe_mfma_kernel(int iters, int32_t key, int32_t *__restrict__ sink) {
   v16i acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[c][q] = 0;
-  const v4i a = v4i{(int)threadIdx.x, 1, 2, 3}, b = v4i{3, 2, 1, (int)blockIdx.x};
-  for (int it = 0; it < iters; ++it)
+  if constexpr (VARIED) {
+    v4i a[4], b[4];
+    uint32_t h = threadIdx.x * 0x9E3779B9u + blockIdx.x * 0x85EBCA6Bu + 0x2545F491u;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t u = xorshift32(h) & 0x03030303u;
+        u -= (u & (u >> 1)) & 0x01010101u;  // byte value 3 -> 2
+        a[i][q] = (int)u;
+        b[i][q] = (int)xorshift32(h);
+      }
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c & 3], b[(c + 1 + (c >> 2)) & 3], acc[c], 0, 0, 0);
+  } else {
+    const v4i a = v4i{(int)threadIdx.x, 1, 2, 3}, b = v4i{3, 2, 1, (int)blockIdx.x};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+  }
   int s = 0;
 #pragma unroll
   for (int c = 0; c < 8; ++c)
@@ -68,8 +103,11 @@ hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, int
   return hipGetLastError();
 }
 
-hipError_t launch_probe_mfma(int iters, int64_t workgroups, int32_t *sink, hipStream_t stream) {
-  probe_mfma_kernel<<<dim3((unsigned)workgroups), dim3(256), 0, stream>>>(iters, 0x7f4a7c15, sink);
+hipError_t launch_probe_mfma(int iters, int64_t workgroups, bool varied, int32_t *sink, hipStream_t stream) {
+  if (varied)
+    probe_mfma_kernel<true><<<dim3((unsigned)workgroups), dim3(256), 0, stream>>>(iters, 0x7f4a7c15, sink);
+  else
+    probe_mfma_kernel<false><<<dim3((unsigned)workgroups), dim3(256), 0, stream>>>(iters, 0x7f4a7c15, sink);
   return hipGetLastError();
 }
 
