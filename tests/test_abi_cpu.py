@@ -364,3 +364,16 @@ def test_library_refuses_to_load_when_missing(tmp_path, monkeypatch):
     monkeypatch.setattr(bl, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         bl.lib()
+
+
+def test_probe_validation():
+    L = bl.lib()
+    for probe in (L.bitlinear_probe_mfma, L.bitlinear_probe_mfma_varied):
+        assert probe(10, 4, None, None) == bl.ERR_NULL
+        assert probe(0, 4, A, None) == bl.ERR_SHAPE
+        assert probe(10, 0, A, None) == bl.ERR_SHAPE
+        assert probe(10, 65537, A, None) == bl.ERR_SHAPE
+    assert L.bitlinear_probe_read(A, 0, 0, A, None) == bl.OK  # nothing to read: a no-op
+    assert L.bitlinear_probe_read(None, 64, 0, A, None) == bl.ERR_NULL
+    assert L.bitlinear_probe_read(A, 24, 0, A, None) == bl.ERR_SHAPE
+    assert L.bitlinear_probe_read(MIS, 64, 0, A, None) == bl.ERR_ALIGN
