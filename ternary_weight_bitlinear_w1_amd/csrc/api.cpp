@@ -170,7 +170,7 @@ int32_t bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
 // ---------------------------------------------------------------- weights
 size_t bitlinear_quantize_weights_workspace_bytes(int64_t n, int64_t k) {
   if (n < 0 || k <= 0) return 0;
-  return align256(bl::absmean_partials(n * k) * sizeof(double));
+  return align256(bl::absmean_partials(k, &n, 1) * sizeof(double));
 }
 
 bitlinear_status bitlinear_quantize_weights(const float *w, int64_t n, int64_t k, const double *gamma_in,
@@ -190,9 +190,9 @@ bitlinear_status bitlinear_quantize_weights(const float *w, int64_t n, int64_t k
   if (gamma_in) {
     BL_TRY(launched(bl::launch_copy_gamma(gamma_in, gamma_out, s), "copy gamma"));
   } else {
-    BL_TRY(launched(bl::launch_absmean(w, n * k, static_cast<double *>(workspace), gamma_out, s), "absmean"));
+    BL_TRY(launched(bl::launch_absmean(w, k, &n, 1, static_cast<double *>(workspace), gamma_out, s), "absmean"));
   }
-  return launched(bl::launch_ternarize_pack(w, n, k, gamma_out, w_packed, s), "ternarize");
+  return launched(bl::launch_ternarize_pack(w, k, &n, 1, gamma_out, w_packed, s), "ternarize");
 }
 
 bitlinear_status bitlinear_validate_packed(const uint8_t *w_packed, int64_t n, int64_t k, int64_t *n_bad,
@@ -310,13 +310,7 @@ bitlinear_status bitlinear_forward(const float *x, const int8_t *codes_in, const
 size_t bitlinear_forward_online_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t quantize_inside,
                                                 const int64_t *seg_end, int32_t n_seg) {
   if (m < 0 || n < 0 || k < 0 || !seg_end || n_seg < 1 || n_seg > BITLINEAR_MAX_SEGMENTS) return 0;
-  size_t partials = 1;
-  int64_t lo = 0;
-  for (int s = 0; s < n_seg; ++s) {
-    const size_t p = bl::absmean_partials((seg_end[s] - lo) * k);
-    if (p > partials) partials = p;
-    lo = seg_end[s];
-  }
+  const size_t partials = bl::absmean_partials(k, seg_end, n_seg);  // every segment's, side by side
   return bitlinear_forward_workspace_bytes(m, n, k, quantize_inside) + align256((size_t)(n * (k / 4))) +
          align256(sizeof(double) * BITLINEAR_MAX_SEGMENTS) + align256(partials * sizeof(double));
 }
@@ -344,19 +338,15 @@ bitlinear_status bitlinear_forward_online(const float *x, const int8_t *codes_in
   double *gam = gamma_out ? gamma_out : reinterpret_cast<double *>(ws);
   ws += align256(sizeof(double) * BITLINEAR_MAX_SEGMENTS);
   double *partials = reinterpret_cast<double *>(ws);
-  int64_t lo = 0;
-  for (int j = 0; j < n_seg; ++j) {
-    const int64_t rows = seg_end[j] - lo;
-    if (master_dtype == BITLINEAR_MASTER_BF16) {
-      const uint16_t *w = static_cast<const uint16_t *>(w_master) + lo * k;
-      BL_TRY(launched(bl::launch_absmean_bf16(w, rows * k, partials, gam + j, s), "absmean"));
-      BL_TRY(launched(bl::launch_ternarize_pack_bf16(w, rows, k, gam + j, packed + lo * (k / 4), s), "ternarize"));
-    } else {
-      const float *w = static_cast<const float *>(w_master) + lo * k;
-      BL_TRY(launched(bl::launch_absmean(w, rows * k, partials, gam + j, s), "absmean"));
-      BL_TRY(launched(bl::launch_ternarize_pack(w, rows, k, gam + j, packed + lo * (k / 4), s), "ternarize"));
-    }
-    lo = seg_end[j];
+  // every segment in one launch per pass: partial sums, gammas, ternary codes
+  if (master_dtype == BITLINEAR_MASTER_BF16) {
+    const uint16_t *w = static_cast<const uint16_t *>(w_master);
+    BL_TRY(launched(bl::launch_absmean_bf16(w, k, seg_end, n_seg, partials, gam, s), "absmean"));
+    BL_TRY(launched(bl::launch_ternarize_pack_bf16(w, k, seg_end, n_seg, gam, packed, s), "ternarize"));
+  } else {
+    const float *w = static_cast<const float *>(w_master);
+    BL_TRY(launched(bl::launch_absmean(w, k, seg_end, n_seg, partials, gam, s), "absmean"));
+    BL_TRY(launched(bl::launch_ternarize_pack(w, k, seg_end, n_seg, gam, packed, s), "ternarize"));
   }
   if (m == 0) return BITLINEAR_OK;
   ep.gamma_dev = gam;

@@ -153,16 +153,21 @@ hipError_t launch_add(const float *a, const float *b, float *out, int64_t count,
 // y[m][inter] = fl32(fl32(max(g, 0)^2) * u), gu = [m][g | u], inter % 4 == 0
 hipError_t launch_relu2_glu(const float *gu, int64_t m, int64_t inter, float *y, hipStream_t stream);
 
-size_t absmean_partials(int64_t count);
-hipError_t launch_absmean(const float *w, int64_t count, double *partials, double *gamma_out,
-                          hipStream_t stream);
-hipError_t launch_ternarize_pack(const float *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
-                                 hipStream_t stream);
+// Absmean ternarization of a master matrix [n][k] whose rows form n_seg
+// consecutive segments (row_end[j] exclusive, ascending, row_end[n_seg - 1] =
+// n, 1 <= n_seg <= BITLINEAR_MAX_SEGMENTS), one gamma per segment: one launch
+// reduces every segment's partial sums, one forms the gammas, one ternarizes
+// and packs the whole matrix. partials holds absmean_partials() doubles.
+size_t absmean_partials(int64_t k, const int64_t *row_end, int n_seg);
+hipError_t launch_absmean(const float *w, int64_t k, const int64_t *row_end, int n_seg, double *partials,
+                          double *gamma_out, hipStream_t stream);
+hipError_t launch_ternarize_pack(const float *w, int64_t k, const int64_t *row_end, int n_seg, const double *gamma,
+                                 uint8_t *packed, hipStream_t stream);
 // the same two passes over bfloat16 masters (bit patterns, widened exactly)
-hipError_t launch_absmean_bf16(const uint16_t *w, int64_t count, double *partials, double *gamma_out,
-                               hipStream_t stream);
-hipError_t launch_ternarize_pack_bf16(const uint16_t *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
-                                      hipStream_t stream);
+hipError_t launch_absmean_bf16(const uint16_t *w, int64_t k, const int64_t *row_end, int n_seg, double *partials,
+                               double *gamma_out, hipStream_t stream);
+hipError_t launch_ternarize_pack_bf16(const uint16_t *w, int64_t k, const int64_t *row_end, int n_seg,
+                                      const double *gamma, uint8_t *packed, hipStream_t stream);
 hipError_t launch_copy_gamma(const double *src, double *dst, hipStream_t stream);
 hipError_t launch_validate_packed(const uint8_t *packed, int64_t n, int64_t k, int64_t *n_bad,
                                   hipStream_t stream);

@@ -50,60 +50,87 @@ struct Master<uint16_t> {
   }
 };
 
-// partials[b] = sum |w| over elements [b * per, min((b+1) * per, count)), per % 8 == 0
+// The segments of one launch: segment j is rows [row_end[j - 1], row_end[j])
+// (elements [lo_j, hi_j) = rows times k), cut into partial slices of per[j]
+// elements (a multiple of 16) numbered from part_lo[j]. A segment's slices
+// depend only on its own element count, so its partial sums and gamma are the
+// same whether it is reduced alone or beside other segments.
+struct SegSpan {
+  int n;
+  int64_t k;
+  int64_t row_end[BITLINEAR_MAX_SEGMENTS];
+  int64_t per[BITLINEAR_MAX_SEGMENTS];
+  int part_lo[BITLINEAR_MAX_SEGMENTS + 1];
+  __device__ int64_t elem_lo(int j) const { return (j ? row_end[j - 1] : 0) * k; }
+  __device__ int64_t elem_hi(int j) const { return row_end[j] * k; }
+};
+
+// partials[b] = sum |w| over the elements of slice b of its segment
 template <typename T>
-__global__ __launch_bounds__(kThreads) void absmean_partial_kernel(const T *__restrict__ w, int64_t count,
-                                                                   int64_t per, double *__restrict__ partials) {
+__global__ __launch_bounds__(kThreads) void absmean_partial_kernel(const T *__restrict__ w, SegSpan sp,
+                                                                   double *__restrict__ partials) {
   constexpr int E = Master<T>::E;
   __shared__ double red[kThreads / 64];
-  const int64_t lo = blockIdx.x * per;
-  const int64_t hi = lo + per < count ? lo + per : count;
+  const int b = blockIdx.x;
+  int j = 0;
+  while (j + 1 < sp.n && b >= sp.part_lo[j + 1]) ++j;
+  const int64_t lo = sp.elem_lo(j) + (int64_t)(b - sp.part_lo[j]) * sp.per[j];
+  const int64_t hi = lo + sp.per[j] < sp.elem_hi(j) ? lo + sp.per[j] : sp.elem_hi(j);
   // thread t adds elements t, t + 256, ... (in 16-byte units) of the slice in
   // order; kUnroll loads are issued before their sums
   double s = 0.0;
   for (int64_t i0 = lo + E * (int64_t)threadIdx.x; i0 < hi; i0 += E * kThreads * kUnroll) {
     v4i v[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t i = i0 + E * (int64_t)kThreads * j;
-      v[j] = i < hi ? *reinterpret_cast<const v4i *>(w + i) : v4i{0, 0, 0, 0};
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + E * (int64_t)kThreads * u;
+      v[u] = i < hi ? *reinterpret_cast<const v4i *>(w + i) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j)
+    for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-      for (int e = 0; e < E; ++e) s += fabs((double)Master<T>::at(v[j], e));
+      for (int e = 0; e < E; ++e) s += fabs((double)Master<T>::at(v[u], e));
   }
   s = block_sum(s, red);
-  if (threadIdx.x == 0) partials[blockIdx.x] = s;
+  if (threadIdx.x == 0) partials[b] = s;
 }
 
-__global__ __launch_bounds__(kThreads) void absmean_final_kernel(const double *__restrict__ partials, int np,
-                                                                 int64_t count, double *__restrict__ gamma) {
+// gamma[j] = (sum of segment j's partials, in slice order) / its element count
+// (0 for an empty segment); one workgroup per segment
+__global__ __launch_bounds__(kThreads) void absmean_final_kernel(const double *__restrict__ partials, SegSpan sp,
+                                                                 double *__restrict__ gamma) {
   __shared__ double red[kThreads / 64];
+  const int j = blockIdx.x;
+  const int p0 = sp.part_lo[j], np = sp.part_lo[j + 1] - p0;
+  const int64_t count = sp.elem_hi(j) - sp.elem_lo(j);
   double s = 0.0;
-  for (int i = threadIdx.x; i < np; i += kThreads) s += partials[i];
+  for (int i = threadIdx.x; i < np; i += kThreads) s += partials[p0 + i];
   s = block_sum(s, red);
-  if (threadIdx.x == 0) gamma[0] = count > 0 ? s / (double)count : 0.0;
+  if (threadIdx.x == 0) gamma[j] = count > 0 ? s / (double)count : 0.0;
 }
 
-// one thread per packed 32-bit word (16 codes)
+// one thread per packed 32-bit word (16 codes); word i lies in segment j when
+// it precedes the segment's last row's end (row_end[j] k / 16 words)
 template <typename T>
 __global__ __launch_bounds__(kThreads) void ternarize_pack_kernel(const T *__restrict__ w, int64_t words,
-                                                                  const double *__restrict__ gamma,
+                                                                  SegSpan sp, const double *__restrict__ gamma,
                                                                   uint32_t *__restrict__ packed) {
   constexpr int E = Master<T>::E;
-  const double half = 0.5 * gamma[0];
+  const int64_t wpr = sp.k / 16;
   for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < words; i += (int64_t)gridDim.x * kThreads) {
+    int j = 0;
+    while (j + 1 < sp.n && i >= sp.row_end[j] * wpr) ++j;
+    const double half = 0.5 * gamma[j];
     const v4i *src = reinterpret_cast<const v4i *>(w + 16 * i);
     v4i raw[16 / E];
 #pragma unroll
-    for (int j = 0; j < 16 / E; ++j) raw[j] = src[j];
+    for (int u = 0; u < 16 / E; ++u) raw[u] = src[u];
     uint32_t word = 0;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const float v = Master<T>::at(raw[t / E], t % E);
-      const uint32_t u = fabs((double)v) > half ? (v > 0.0f ? 2u : 0u) : 1u;
-      word |= u << (8 * (t & 3) + 2 * (t >> 2));
+      const uint32_t c = fabs((double)v) > half ? (v > 0.0f ? 2u : 0u) : 1u;
+      word |= c << (8 * (t & 3) + 2 * (t >> 2));
     }
     packed[i] = word;
   }
@@ -149,55 +176,69 @@ unsigned grid_for(int64_t items) {
   return (unsigned)b;
 }
 
+SegSpan make_span(int64_t k, const int64_t *row_end, int n_seg) {
+  SegSpan sp{};
+  sp.n = n_seg;
+  sp.k = k;
+  sp.part_lo[0] = 0;
+  int64_t lo = 0;
+  for (int j = 0; j < n_seg; ++j) {
+    const int64_t count = (row_end[j] - lo) * k;
+    sp.row_end[j] = row_end[j];
+    sp.per[j] = partial_span(count);
+    sp.part_lo[j + 1] = sp.part_lo[j] + (int)((count + sp.per[j] - 1) / sp.per[j]);
+    lo = row_end[j];
+  }
+  return sp;
+}
+
 }  // namespace
 
-size_t absmean_partials(int64_t count) {
-  if (count <= 0) return 1;
-  const int64_t per = partial_span(count);
-  return (size_t)((count + per - 1) / per);
+size_t absmean_partials(int64_t k, const int64_t *row_end, int n_seg) {
+  const int np = make_span(k, row_end, n_seg).part_lo[n_seg];
+  return np > 0 ? (size_t)np : 1;
 }
 
 template <typename T>
-hipError_t absmean_impl(const T *w, int64_t count, double *partials, double *gamma_out, hipStream_t stream) {
-  if (count <= 0) {
-    zero_i64_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<int64_t *>(gamma_out));  // 0.0 is all-zero bits
-    return hipGetLastError();
-  }
-  const int64_t per = partial_span(count);
-  const int np = (int)((count + per - 1) / per);
-  absmean_partial_kernel<T><<<dim3(np), dim3(kThreads), 0, stream>>>(w, count, per, partials);
-  absmean_final_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(partials, np, count, gamma_out);
+hipError_t absmean_impl(const T *w, int64_t k, const int64_t *row_end, int n_seg, double *partials,
+                        double *gamma_out, hipStream_t stream) {
+  const SegSpan sp = make_span(k, row_end, n_seg);
+  if (sp.part_lo[n_seg] > 0)
+    absmean_partial_kernel<T><<<dim3((unsigned)sp.part_lo[n_seg]), dim3(kThreads), 0, stream>>>(w, sp, partials);
+  absmean_final_kernel<<<dim3((unsigned)n_seg), dim3(kThreads), 0, stream>>>(partials, sp, gamma_out);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t ternarize_impl(const T *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
-                          hipStream_t stream) {
-  const int64_t words = n * (k / 16);
+hipError_t ternarize_impl(const T *w, int64_t k, const int64_t *row_end, int n_seg, const double *gamma,
+                          uint8_t *packed, hipStream_t stream) {
+  const int64_t words = row_end[n_seg - 1] * (k / 16);
   if (words == 0) return hipSuccess;
   ternarize_pack_kernel<T><<<dim3(grid_for(words)), dim3(kThreads), 0, stream>>>(
-      w, words, gamma, reinterpret_cast<uint32_t *>(packed));
+      w, words, make_span(k, row_end, n_seg), gamma, reinterpret_cast<uint32_t *>(packed));
   return hipGetLastError();
 }
 
-hipError_t launch_absmean(const float *w, int64_t count, double *partials, double *gamma_out, hipStream_t stream) {
-  return absmean_impl(w, count, partials, gamma_out, stream);
+hipError_t launch_absmean(const float *w, int64_t k, const int64_t *row_end, int n_seg, double *partials,
+                          double *gamma_out, hipStream_t stream) {
+  return absmean_impl(w, k, row_end, n_seg, partials, gamma_out, stream);
 }
 
-hipError_t launch_absmean_bf16(const uint16_t *w, int64_t count, double *partials, double *gamma_out,
-                               hipStream_t stream) {
-  return absmean_impl(w, count, partials, gamma_out, stream);
+hipError_t launch_absmean_bf16(const uint16_t *w, int64_t k, const int64_t *row_end, int n_seg, double *partials,
+                               double *gamma_out, hipStream_t stream) {
+  return absmean_impl(w, k, row_end, n_seg, partials, gamma_out, stream);
 }
 
-hipError_t launch_ternarize_pack(const float *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
-                                 hipStream_t stream) {
-  return ternarize_impl(w, n, k, gamma, packed, stream);
+hipError_t launch_ternarize_pack(const float *w, int64_t k, const int64_t *row_end, int n_seg, const double *gamma,
+                                 uint8_t *packed, hipStream_t stream) {
+  return ternarize_impl(w, k, row_end, n_seg, gamma, packed, stream);
 }
 
-hipError_t launch_ternarize_pack_bf16(const uint16_t *w, int64_t n, int64_t k, const double *gamma, uint8_t *packed,
-                                      hipStream_t stream) {
-  return ternarize_impl(w, n, k, gamma, packed, stream);
+hipError_t launch_ternarize_pack_bf16(const uint16_t *w, int64_t k, const int64_t *row_end, int n_seg,
+                                      const double *gamma, uint8_t *packed, hipStream_t stream) {
+  return ternarize_impl(w, k, row_end, n_seg, gamma, packed, stream);
 }
+
 
 hipError_t launch_copy_gamma(const double *src, double *dst, hipStream_t stream) {
   copy_gamma_kernel<<<1, 64, 0, stream>>>(src, dst);
