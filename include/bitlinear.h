@@ -186,7 +186,11 @@ typedef enum {
  * checkpoints": the online mode; "The projections quantize their inputs and
  * weights"): per segment, gamma = mean|W| (fp64), codes = sign(W) [|W| >
  * gamma / 2], packed into the workspace, then bitlinear_forward with the
- * segments' gammas rounded to fp32.
+ * segments' gammas rounded to fp32. For one token (m == 1, path AUTO or
+ * DECODE, k <= 8192 and each row within 32 128-byte lines per wave: k <= 8192
+ * for bfloat16 masters, k <= 4096 for fp32 ones) the contraction forms the
+ * codes from the masters as it reads them and no packed copy is written; the
+ * result is the same.
  *   w_master   [n][k] master weights in master_dtype (bitlinear_master_dtype),
  *              16-byte aligned; segment j is rows [seg_end[j-1], seg_end[j])
  *              and gets its own gamma. bfloat16 masters are read as their

@@ -338,6 +338,45 @@ bitlinear_status bitlinear_forward_online(const float *x, const int8_t *codes_in
   double *gam = gamma_out ? gamma_out : reinterpret_cast<double *>(ws);
   ws += align256(sizeof(double) * BITLINEAR_MAX_SEGMENTS);
   double *partials = reinterpret_cast<double *>(ws);
+  const bool bf16 = master_dtype == BITLINEAR_MASTER_BF16;
+  const bool decode = path == BITLINEAR_PATH_DECODE || path == BITLINEAR_PATH_AUTO;
+  if (m == 1 && decode && bl::online_dot_supported(n, k, bf16)) {
+    // one token: the gammas, then the codes formed from the masters inside the
+    // contraction (no packed copy written)
+    if (bf16)
+      BL_TRY(launched(bl::launch_absmean_bf16(static_cast<const uint16_t *>(w_master), k, seg_end, n_seg, partials,
+                                              gam, s),
+                      "absmean"));
+    else
+      BL_TRY(launched(bl::launch_absmean(static_cast<const float *>(w_master), k, seg_end, n_seg, partials, gam, s),
+                      "absmean"));
+    // the token's codes, deq and row sum: given, or quantized into the
+    // forward's workspace (row sums first, as the packed forward lays it out)
+    int32_t *rowsum = reinterpret_cast<int32_t *>(ws_fwd);
+    const int8_t *codes = codes_in;
+    const float *deq = deq_in;
+    if (x) {
+      int8_t *c = reinterpret_cast<int8_t *>(ws_fwd + align256(sizeof(int32_t)));
+      float *d = reinterpret_cast<float *>(ws_fwd + align256(sizeof(int32_t)) + align256((size_t)k));
+      BL_TRY(launched(bl::launch_quant_acts(BITLINEAR_ACT_ABSMAX, x, nullptr, k, 1, k, nullptr, 0.0f, 0, 1, 1,
+                                            nullptr, c, d, rowsum, s),
+                      "quantize_acts"));
+      codes = c;
+      deq = d;
+    } else if (rowsum_in) {
+      rowsum = const_cast<int32_t *>(rowsum_in);
+    } else {
+      BL_TRY(launched(bl::launch_code_rowsum(codes, 1, k, rowsum, s), "code row sums"));
+    }
+    ep.gamma_dev = gam;
+    if (bf16)
+      return launched(bl::launch_online_dot_bf16(codes, deq, rowsum, static_cast<const uint16_t *>(w_master), n, k, ep,
+                                                 y, acc_out, s),
+                      "online contraction");
+    return launched(bl::launch_online_dot(codes, deq, rowsum, static_cast<const float *>(w_master), n, k, ep, y,
+                                          acc_out, s),
+                    "online contraction");
+  }
   // every segment in one launch per pass: partial sums, gammas, ternary codes
   if (master_dtype == BITLINEAR_MASTER_BF16) {
     const uint16_t *w = static_cast<const uint16_t *>(w_master);

@@ -168,6 +168,16 @@ hipError_t launch_absmean_bf16(const uint16_t *w, int64_t k, const int64_t *row_
                                double *gamma_out, hipStream_t stream);
 hipError_t launch_ternarize_pack_bf16(const uint16_t *w, int64_t k, const int64_t *row_end, int n_seg,
                                       const double *gamma, uint8_t *packed, hipStream_t stream);
+// One token (m = 1) of the online mode straight from the masters: the codes,
+// deq and row sum of the token, the masters [n][k], and ep with gamma_dev set
+// to the segments' gammas (as launch_absmean writes them). Equal bit for bit
+// to ternarize + the packed forward. Supported where online_dot_supported().
+bool online_dot_supported(int64_t n, int64_t k, bool bf16);
+hipError_t launch_online_dot(const int8_t *codes, const float *deq, const int32_t *rowsum, const float *w, int64_t n,
+                             int64_t k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream);
+hipError_t launch_online_dot_bf16(const int8_t *codes, const float *deq, const int32_t *rowsum, const uint16_t *w,
+                                  int64_t n, int64_t k, const Epilogue &ep, float *y, int32_t *acc_out,
+                                  hipStream_t stream);
 hipError_t launch_copy_gamma(const double *src, double *dst, hipStream_t stream);
 hipError_t launch_validate_packed(const uint8_t *packed, int64_t n, int64_t k, int64_t *n_bad,
                                   hipStream_t stream);

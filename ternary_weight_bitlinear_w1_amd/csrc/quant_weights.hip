@@ -136,6 +136,193 @@ __global__ __launch_bounds__(kThreads) void ternarize_pack_kernel(const T *__res
   }
 }
 
+// ---------------------------------------------------------------------------
+// One-token online contraction: y[n] = rescale(sum_k q_k u(w[n][k]) - sum_k q_k,
+// deq, fl32(gamma_j)), u = c + 1 the field of the ternary code that the
+// ternarize pass would store for w[n][k] under gamma_j of row n's segment, so
+// the result is that of ternarize + the packed forward, bit for bit, without
+// writing and re-reading the packed codes. The masters are read straight from
+// HBM once more (the mean|W| pass read them first).
+//
+// The code test |w| > gamma / 2 is taken in fp32 against h = gamma / 2 rounded
+// down to fp32: for an fp32 |w|, |w| > gamma / 2 exactly when |w| > h (no fp32
+// lies strictly between h and gamma / 2), so it agrees with the fp64 test of
+// the ternarize pass; a NaN compares false in both.
+//
+// Shape as the packed one-token kernel: lane l reads the 16-byte piece l % 8 of
+// each 128-byte line of row l / 8 (E weights: 8 bfloat16 or 4 fp32), 8 rows per
+// wave, KS waves splitting a row's lines, the token's codes in LDS; four
+// fields at a time go into one v_dot4_i32_i8 against the matching code dword.
+constexpr int kOnlineMaxK = 8192;
+constexpr int kOnlineMaxLines = 32;  // 128-byte lines per wave
+
+__device__ __forceinline__ void lds_only_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); loads in flight keep flowing
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+typedef short short2 __attribute__((ext_vector_type(2)));
+
+// The fields u = c + 1 (bytes, element e in byte e) of four bfloat16 weights,
+// elements 0, 1 in da (low half first) and 2, 3 in db. For a bfloat16 w and an
+// fp32 h >= 0, |w| > h exactly when w's 15 magnitude bits exceed h's top 15
+// (floats of one sign order as their bits, and w's low 16 bits are zero), so
+// h16 - |w|16 is negative exactly where the code is nonzero; the code's sign
+// is w's sign bit. With G and S the 0/1 bytes of those two tests,
+// u = 1 + G - 2 (G & S), which never borrows across bytes.
+__device__ __forceinline__ uint32_t bf16_fields4(uint32_t da, uint32_t db, short2 hh) {
+  const short2 ta = hh - __builtin_bit_cast(short2, da & 0x7fff7fffu);
+  const short2 tb = hh - __builtin_bit_cast(short2, db & 0x7fff7fffu);
+  constexpr uint32_t kHighBytes = 0x07050301u;  // byte 1 and 3 of each source, da first
+  const uint32_t g = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, tb), __builtin_bit_cast(uint32_t, ta),
+                                           kHighBytes) & 0x80808080u;
+  const uint32_t s = __builtin_amdgcn_perm(db, da, kHighBytes) & 0x80808080u;
+  return 0x01010101u + (g >> 7) - ((g & s) >> 6);
+}
+
+template <typename T, int KS, int LPW>
+__global__ __launch_bounds__(256) void online_dot_kernel(const int8_t *__restrict__ codes, const float *__restrict__ deq,
+                                                         const int32_t *__restrict__ rowsum, const T *__restrict__ w,
+                                                         int N, int K, Epilogue ep_in, float *__restrict__ Y,
+                                                         int32_t *__restrict__ acc_out) {
+  constexpr int E = Master<T>::E;
+  constexpr int RG = 4 / KS;  // row groups of 8 rows per workgroup
+  constexpr int kCodeLoads = kOnlineMaxK / 16 / kThreads;
+  __shared__ __attribute__((aligned(16))) int8_t sc[kOnlineMaxK];
+  __shared__ int red[KS][RG][8];
+  const Epilogue ep = resolve_gamma(ep_in);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % KS, rg = wave / KS;
+  const int n = blockIdx.x * 8 * RG + rg * 8 + (lane >> 3);
+  const int p = lane & 7;
+  const int rowb = K * (int)sizeof(T);  // bytes per master row (a multiple of 32)
+  const int L = (rowb + 127) >> 7;      // 128-byte lines per row, the last may be partial
+  const int l_lo = L * ks / KS, l_hi = L * (ks + 1) / KS;
+  const int nc = n < N ? n : N - 1;
+
+  // loads in issue order: the token's codes (L2), then the masters (HBM); a
+  // piece past the row's end reloads the lane's first piece, unused
+  v4i cw[kCodeLoads];
+#pragma unroll
+  for (int j = 0; j < kCodeLoads; ++j) {
+    const int i = threadIdx.x + kThreads * j;
+    cw[j] = *reinterpret_cast<const v4i *>(codes + (16 * i < K ? 16 * i : 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const char *row = reinterpret_cast<const char *>(w) + (int64_t)nc * rowb;
+  v4i wv[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int off = 128 * (l_lo + i) + 16 * p;
+    const bool use = l_lo + i < l_hi && off < rowb;
+    wv[i] = *reinterpret_cast<const v4i *>(row + (use ? off : 16 * p < rowb ? 16 * p : 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < kCodeLoads; ++j) {
+    const int i = threadIdx.x + kThreads * j;
+    if (16 * i < K) *reinterpret_cast<v4i *>(sc + 16 * i) = cw[j];
+  }
+  lds_only_barrier();
+
+  // row n's segment and its threshold
+  int seg = 0;
+#pragma unroll
+  for (int q = 1; q < BITLINEAR_MAX_SEGMENTS; ++q)
+    if (q < ep.n_seg && nc >= ep.seg_end[q - 1]) seg = q;
+  const float h = __double2float_rd(0.5 * ep_in.gamma_dev[seg]);
+  // bfloat16 masters: |w| > h on the 15 magnitude bits against h's top 15
+  // (a NaN threshold, from NaN masters, lets nothing pass, as in fp)
+  const uint32_t h16 = h != h ? 0x7fffu : (__float_as_uint(h) >> 16) & 0x7fffu;
+  const short2 hh = {(short)h16, (short)h16};
+
+  // Branch-free: a piece past the row's end (or the wave's lines) meets code
+  // words of zero and adds nothing.
+  int acc = 0;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int off = 128 * (l_lo + i) + 16 * p;
+    const bool use = l_lo + i < l_hi && off < rowb;
+    const int k0 = use ? off / (int)sizeof(T) : 0;  // first weight of this piece
+    int cv[E / 4];
+    if constexpr (E == 8) {
+      const int2 c2 = *reinterpret_cast<const int2 *>(sc + k0);
+      cv[0] = c2.x;
+      cv[1] = c2.y;
+    } else {
+      cv[0] = *reinterpret_cast<const int *>(sc + k0);
+    }
+#pragma unroll
+    for (int g = 0; g < E / 4; ++g) {
+      uint32_t u;
+      if constexpr (E == 8) {
+        u = bf16_fields4((uint32_t)wv[i][2 * g], (uint32_t)wv[i][2 * g + 1], hh);
+      } else {
+        u = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = Master<T>::at(wv[i], 4 * g + e);
+          const uint32_t f = fabsf(v) > h ? (v > 0.0f ? 2u : 0u) : 1u;
+          u |= f << (8 * e);
+        }
+      }
+      acc = __builtin_amdgcn_sdot4((int)u, use ? cv[g] : 0, acc, false);
+    }
+  }
+  acc = lanes8_sum(acc);  // the 8 lanes of a row
+  if (p == 0) red[ks][rg][lane >> 3] = acc;
+  __syncthreads();
+  if (ks == 0 && p == 0 && n < N) {
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) sum += red[q][rg][lane >> 3];
+    const int a = sum - rowsum[0];
+    if (acc_out) acc_out[n] = a;
+    Y[n] = rescale(a, deq[0], epi_gamma(ep, n));
+  }
+}
+
+template <typename T, int KS>
+hipError_t launch_online_dot_ks(const int8_t *codes, const float *deq, const int32_t *rowsum, const T *w, int n, int k,
+                                const Epilogue &ep, float *y, int32_t *acc_out, int lpw, hipStream_t stream) {
+  const dim3 grid((unsigned)((n + 32 / KS - 1) / (32 / KS))), block(kThreads);
+#define BL_ONLINE(LPW_)                                                                                    \
+  online_dot_kernel<T, KS, LPW_><<<grid, block, 0, stream>>>(codes, deq, rowsum, w, n, k, ep, y, acc_out); \
+  return hipGetLastError()
+  if (lpw <= 8) { BL_ONLINE(8); }
+  if (lpw <= 16) { BL_ONLINE(16); }
+  if (lpw <= 20) { BL_ONLINE(20); }
+  if (lpw <= 24) { BL_ONLINE(24); }
+  BL_ONLINE(32);
+#undef BL_ONLINE
+}
+
+// K split over the fewest waves (1, 2 or 4) that give at least 512
+// workgroups and at most kOnlineMaxLines lines per wave; 0 if none does
+int online_dot_splits(int64_t n, int64_t k, int esize) {
+  if (n <= 0 || k <= 0 || k > kOnlineMaxK || k % 16 != 0) return 0;
+  const int64_t lines = (k * esize + 127) / 128;
+  for (int ks = 1; ks <= 4; ks *= 2) {
+    const int64_t wgs = (n + 32 / ks - 1) / (32 / ks);
+    if ((wgs >= 512 || ks == 4) && (lines + ks - 1) / ks <= kOnlineMaxLines) return ks;
+  }
+  return 0;
+}
+
+template <typename T>
+hipError_t launch_online_dot_impl(const int8_t *codes, const float *deq, const int32_t *rowsum, const T *w, int64_t n,
+                                  int64_t k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
+  const int ks = online_dot_splits(n, k, (int)sizeof(T));
+  if (ks == 0 || !ep.gamma_dev) return hipErrorInvalidValue;
+  const int lines = (int)((k * (int64_t)sizeof(T) + 127) / 128);
+  const int lpw = (lines + ks - 1) / ks;
+  if (ks == 1) return launch_online_dot_ks<T, 1>(codes, deq, rowsum, w, (int)n, (int)k, ep, y, acc_out, lpw, stream);
+  if (ks == 2) return launch_online_dot_ks<T, 2>(codes, deq, rowsum, w, (int)n, (int)k, ep, y, acc_out, lpw, stream);
+  return launch_online_dot_ks<T, 4>(codes, deq, rowsum, w, (int)n, (int)k, ep, y, acc_out, lpw, stream);
+}
+
 __global__ void copy_gamma_kernel(const double *__restrict__ src, double *__restrict__ dst) {
   if (threadIdx.x == 0 && blockIdx.x == 0) dst[0] = src[0];
 }
@@ -252,6 +439,19 @@ hipError_t launch_validate_packed(const uint8_t *packed, int64_t n, int64_t k, i
     validate_kernel<<<dim3(grid_for(words)), dim3(kThreads), 0, stream>>>(reinterpret_cast<const uint32_t *>(packed),
                                                                           words, n_bad);
   return hipGetLastError();
+}
+
+bool online_dot_supported(int64_t n, int64_t k, bool bf16) { return online_dot_splits(n, k, bf16 ? 2 : 4) > 0; }
+
+hipError_t launch_online_dot(const int8_t *codes, const float *deq, const int32_t *rowsum, const float *w, int64_t n,
+                             int64_t k, const Epilogue &ep, float *y, int32_t *acc_out, hipStream_t stream) {
+  return launch_online_dot_impl(codes, deq, rowsum, w, n, k, ep, y, acc_out, stream);
+}
+
+hipError_t launch_online_dot_bf16(const int8_t *codes, const float *deq, const int32_t *rowsum, const uint16_t *w,
+                                  int64_t n, int64_t k, const Epilogue &ep, float *y, int32_t *acc_out,
+                                  hipStream_t stream) {
+  return launch_online_dot_impl(codes, deq, rowsum, w, n, k, ep, y, acc_out, stream);
 }
 
 }  // namespace bl

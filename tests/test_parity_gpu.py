@@ -302,6 +302,51 @@ def test_forward_online_bf16(m, seg, k):
     assert_equal(host(y32), host(y), "bf16 masters == their fp32 widening")
 
 
+# one token: the contraction that forms the codes from the masters as it reads
+# them (fp32 up to k = 4096, bfloat16 up to 8192), with a partial last line
+# (k = 2576) and segments of ragged length; fp32 at k = 6912 takes the packed
+# path instead
+ONLINE_ONE = [("f32", [512], 256), ("f32", [100, 257], 2576), ("bf16", [6912, 13824], 2560),
+              ("bf16", [300, 301, 700], 6912), ("bf16", [37], 8192), ("f32", [64, 200], 6912)]
+
+
+@pytest.mark.parametrize("dt,seg,k", ONLINE_ONE)
+def test_forward_online_one_token(dt, seg, k):
+    """One token in the online mode: y and acc bit-exact against the oracle run
+    with the GPU's gammas, the gammas within 1e-6 of the oracle's, and y, acc and
+    gammas equal to the packed path (path PREFILL, which ternarizes into the
+    workspace first), also when the token's codes are given."""
+    note(f"forward online one token {dt} seg={seg} k={k}")
+    n = seg[-1]
+    lo = [0] + seg[:-1]
+    w = np.concatenate([synth.weights(seed(11, n + j, k), hi - a, k, 0.02 + 0.01 * j)
+                        for j, (a, hi) in enumerate(zip(lo, seg))])
+    if dt == "bf16":
+        bits = oracle.round_bf16(w)
+        wide, wt = oracle.bf16_to_f32(bits), gpu(bits)
+    else:
+        wide, wt = w, gpu(w)
+    x = synth.activations(seed(11, 1, k), 1, k, 1)
+    y, acc, gamma = bl.forward_online(wt, seg, x=gpu(x), want_acc=True)
+    g = host(gamma)
+    for j, (a, hi) in enumerate(zip(lo, seg)):
+        go = oracle.absmean(wide[a:hi])
+        assert abs(g[j] - go) <= GAMMA_TOL * go, (j, g[j], go)
+    codes = np.concatenate([oracle.ternarize(wide[a:hi], float(g[j])) for j, (a, hi) in enumerate(zip(lo, seg))])
+    ref = oracle.forward(x, codes, [float(v) for v in g], seg)
+    assert_equal(host(acc), ref["acc"], "online one-token acc")
+    assert_equal(host(y), ref["y"], "online one-token y")
+    y_p, acc_p, g_p = bl.forward_online(wt, seg, x=gpu(x), want_acc=True, path=bl.PATH_PREFILL)
+    assert_equal(host(g_p), g, "gammas of the packed path")
+    assert_equal(host(acc_p), host(acc), "acc of the packed path")
+    assert_equal(host(y_p), host(y), "y of the packed path")
+    c, d, r = bl.quantize_acts(gpu(x))
+    y_c, g_c = bl.forward_online(wt, seg, codes=c, deq=d, rowsum=r)
+    assert_equal(host(y_c), host(y), "codes given")
+    y_c2, _ = bl.forward_online(wt, seg, codes=c, deq=d)
+    assert_equal(host(y_c2), host(y), "codes given, row sum formed")
+
+
 def test_forward_codes_in_path():
     note("forward with pre-quantized codes")
     m, k, n = 37, 512, 300
