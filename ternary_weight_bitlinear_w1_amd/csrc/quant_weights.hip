@@ -103,8 +103,22 @@ __global__ __launch_bounds__(kThreads) void absmean_final_kernel(const double *_
   const int j = blockIdx.x;
   const int p0 = sp.part_lo[j], np = sp.part_lo[j + 1] - p0;
   const int64_t count = sp.elem_hi(j) - sp.elem_lo(j);
+  // thread t adds partials t, t + 256, ... in order; all its loads (clamped
+  // into range, at most kMaxPartials / 256) are issued before the first sum,
+  // and the ones past the end add 0
+  constexpr int kLoads = kMaxPartials / kThreads;
   double s = 0.0;
-  for (int i = threadIdx.x; i < np; i += kThreads) s += partials[p0 + i];
+  if (np > 0) {
+    double v[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int i = threadIdx.x + kThreads * u;
+      v[u] = partials[p0 + (i < np ? i : np - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u)
+      if ((int)threadIdx.x + kThreads * u < np) s += v[u];
+  }
   s = block_sum(s, red);
   if (threadIdx.x == 0) gamma[j] = count > 0 ? s / (double)count : 0.0;
 }
