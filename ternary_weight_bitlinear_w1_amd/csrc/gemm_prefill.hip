@@ -26,6 +26,8 @@
 // load and its four A blocks one 64-byte LDS row segment.
 // Output: lane l, accumulator q holds row 8 (q / 4) + 4 (l / 32) + q % 4,
 // column l % 32 of the 32 x 32 tile.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bl {
@@ -674,8 +676,33 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const int32_t *__res
   const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (4 * i4 >= plane) return;
   const int m = (int)(4 * i4 / N), n = (int)(4 * i4 - (int64_t)m * N);
-  v4i t = *reinterpret_cast<const v4i *>(part + 4 * i4);
-  for (int s = 1; s < S; ++s) t += *reinterpret_cast<const v4i *>(part + s * plane + 4 * i4);
+  // every plane's load issued before the first add (straight-line code per
+  // plane count: a loop over a run-time count waits for each load in turn)
+  const int32_t *p0 = part + 4 * i4;
+  v4i t;
+  auto planes = [&](auto sc) {
+    constexpr int SP = decltype(sc)::value;
+    v4i u[SP];
+#pragma unroll
+    for (int j = 0; j < SP; ++j) u[j] = *reinterpret_cast<const v4i *>(p0 + j * plane);
+    t = u[0];
+#pragma unroll
+    for (int j = 1; j < SP; ++j) t += u[j];
+  };
+  switch (S) {
+    case 1: planes(std::integral_constant<int, 1>{}); break;
+    case 2: planes(std::integral_constant<int, 2>{}); break;
+    case 3: planes(std::integral_constant<int, 3>{}); break;
+    case 4: planes(std::integral_constant<int, 4>{}); break;
+    case 5: planes(std::integral_constant<int, 5>{}); break;
+    case 6: planes(std::integral_constant<int, 6>{}); break;
+    case 7: planes(std::integral_constant<int, 7>{}); break;
+    case 8: planes(std::integral_constant<int, 8>{}); break;
+    case 9: planes(std::integral_constant<int, 9>{}); break;
+    default:
+      t = *reinterpret_cast<const v4i *>(p0);
+      for (int j = 1; j < S; ++j) t += *reinterpret_cast<const v4i *>(p0 + j * plane);
+  }
   const int rs = rowsum[m];
   const float dq = deq[m];
   t -= v4i{rs, rs, rs, rs};
