@@ -26,6 +26,7 @@
 // load and its four A blocks one 64-byte LDS row segment.
 // Output: lane l, accumulator q holds row 8 (q / 4) + 4 (l / 32) + q % 4,
 // column l % 32 of the 32 x 32 tile.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -633,16 +634,18 @@ hipError_t launch_generic(const int8_t *codes, const uint8_t *packed, const floa
   return hipGetLastError();
 }
 
+// CUs of the current device, asked once per device (threads that race on the
+// first call store the same value)
 int cu_count() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int WM, int WN, int TM, int TN, int P, bool GLU = false>
