@@ -347,6 +347,39 @@ def test_forward_online_one_token(dt, seg, k):
     assert_equal(host(y_c2), host(y), "codes given, row sum formed")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("special", [np.inf, np.nan])
+def test_forward_online_one_token_special_masters(dt, special):
+    """A segment whose masters hold an infinity or a NaN: its gamma is inf or NaN,
+    no weight passes the threshold test (as in the oracle's fp64 test), and its
+    outputs are NaN; the other segment is untouched (bit-exact against the
+    oracle), and the one-token path equals the packed path."""
+    note(f"forward online one token, {dt} masters with {special}")
+    k, seg = 512, [64, 136]
+    w = np.concatenate([synth.weights(seed(12, 1, k), 64, k, 0.02), synth.weights(seed(12, 2, k), 72, k, 0.03)])
+    w[100, 7] = special
+    if dt == "bf16":
+        bits = oracle.round_bf16(w)
+        wide, wt = oracle.bf16_to_f32(bits), gpu(bits)
+    else:
+        wide, wt = w, gpu(w)
+    x = synth.activations(seed(12, 1, k), 1, k, 1)
+    y, acc, gamma = bl.forward_online(wt, seg, x=gpu(x), want_acc=True)
+    g = host(gamma)
+    assert abs(g[0] - oracle.absmean(wide[:64])) <= GAMMA_TOL * g[0]
+    assert (np.isinf(g[1]) if special == np.inf else np.isnan(g[1])), g[1]
+    codes0 = oracle.ternarize(wide[:64], float(g[0]))
+    ref = oracle.forward(x, codes0, [float(g[0])], [64])
+    assert_equal(host(acc)[:, :64], ref["acc"], "finite segment acc")
+    assert_equal(host(y)[:, :64], ref["y"], "finite segment y")
+    assert_equal(host(acc)[:, 64:], np.zeros((1, 72), np.int32), "no weight passes the test")
+    assert np.isnan(host(y)[:, 64:]).all()
+    y_p, acc_p, g_p = bl.forward_online(wt, seg, x=gpu(x), want_acc=True, path=bl.PATH_PREFILL)
+    assert_equal(host(acc_p), host(acc), "acc of the packed path")
+    assert_equal(host(y_p)[:, :64], host(y)[:, :64], "y of the packed path")
+    assert np.isnan(host(y_p)[:, 64:]).all()
+
+
 def test_forward_codes_in_path():
     note("forward with pre-quantized codes")
     m, k, n = 37, 512, 300
