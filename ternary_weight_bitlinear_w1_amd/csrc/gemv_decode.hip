@@ -677,14 +677,15 @@ hipError_t launch_gemv_decode(const int8_t *codes, const uint8_t *packed, const 
   // (measured on MI355X at 8 and 16 tokens: gate|up 13824 rows 5.9 / 6.4 us
   // against 6.6 / 8.0 with one tile and 5.9 / 6.9 with four; down 2560 rows
   // 4.9 / 5.0 us with one tile against 6.2 / 6.2 with two)
-  // 9 to 16 tokens on a tall matrix whose rows hold at most 16 supersteps of
+  // 5 to 16 tokens on a tall matrix whose rows hold at most 16 supersteps of
   // 256 k: four row tiles per workgroup, one wave per superstep (measured on
   // MI355X, gate|up 13824 x 2560 at 16 tokens: 5.19 us with ten waves of one
   // superstep, against 5.61 with two row tiles of four waves, 5.80 with two of
   // eight waves, 5.82 with four tiles of eight waves and 5.37-5.40 with four
-  // tiles of sixteen waves)
+  // tiles of sixteen waves; at 8 tokens 4.89 against 5.03 us; at 2 and 4
+  // tokens no faster than one tile of four waves)
   const int S = ((int)(k >> 4) + 15) >> 4;
-  if (m > 8 && n / 64 >= 200 && S <= 16) {
+  if (m > 4 && n / 64 >= 200 && S <= 16) {
     if (S <= 4) return launch_cfg<4, 4, 1>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream);
     if (S <= 6) return launch_cfg<4, 6, 1>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream);
     if (S <= 8) return launch_cfg<4, 8, 1>(codes, packed, deq, rowsum, (int)m, (int)n, (int)k, ep, y, acc_out, stream);

@@ -173,10 +173,10 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           (1, 77, 64), (2, 200, 320), (3, 1000, 576), (4, 40, 8192), (1, 9000, 1024), (4, 5000, 448),
           # 5..16 tokens over at least 8192 rows: two row tiles per workgroup, ragged rows and K
           (12, 8200, 320), (6, 8224, 2576),
-          # 9..16 tokens over at least 12800 rows and at most 16 supersteps of 256 k: four row tiles
+          # 5..16 tokens over at least 12800 rows and at most 16 supersteps of 256 k: four row tiles
           # per workgroup, one wave per superstep (4 to 16 waves, some without a superstep), ragged
           (16, 13824, 2560), (9, 12864, 4096), (12, 12848, 1040), (13, 12800, 1536), (10, 12816, 208),
-          (16, 12816, 2832),
+          (16, 12816, 2832), (5, 12864, 2560), (8, 12816, 1040),
           # long rows: one token past the dot-product kernel's 8192 (sixteen waves of four supersteps,
           # per-lane code loads), and past 16 waves x 4 supersteps (the looping kernel)
           (1, 70, 8256), (3, 100, 16400),
