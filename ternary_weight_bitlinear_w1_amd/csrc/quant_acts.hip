@@ -1,6 +1,6 @@
 // Per-token int8 quantization of fp32 activations, with the fused prologues
 // of a BitNet b1.58 block (gfx950): one workgroup per token row, 256 threads,
-// or 1024 for 17 to 128 rows (each thread then walks a quarter as many
+// or 512 for 17 to 128 rows (each thread then walks a quarter as many
 // elements); the arithmetic is quant_row (act_prologue.h).
 // HBM-bound: 4 (or 8 for gate|up, 8 for the residual pair) bytes read and
 // 1 byte written per element.
@@ -45,13 +45,15 @@ hipError_t launch_threads(const Src &s, int64_t m, int8_t *codes, float *deq, in
   return hipGetLastError();
 }
 
-// 17 to 128 rows (too few to fill the CUs) take 1024-thread workgroups:
-// measured on the 30-layer stack at 64 tokens, 1.650-1.658 ms against
-// 1.673 ms; at 3 and 4 tokens the wide form was 1-2% slower.
+// 17 to 128 rows (too few to fill the CUs) take 512-thread workgroups:
+// measured on the 30-layer stack at 64 tokens, 1.510-1.518 ms against 1.528
+// with 320 threads, 1.515-1.518 with 448 or 640 and 1.550-1.556 with 1024
+// (and, in an earlier form of the step, 1.673 ms with 256); at 3 and 4 tokens
+// a wide form was 1-2% slower than 256 threads.
 template <int MODE, bool PART = false>
 hipError_t launch_mode(const Src &s, int64_t m, int8_t *codes, float *deq, int32_t *rowsum, float eps,
                        hipStream_t stream) {
-  if (m > 16 && m <= 128) return launch_threads<MODE, PART, 1024>(s, m, codes, deq, rowsum, eps, stream);
+  if (m > 16 && m <= 128) return launch_threads<MODE, PART, 512>(s, m, codes, deq, rowsum, eps, stream);
   return launch_threads<MODE, PART, kThreads>(s, m, codes, deq, rowsum, eps, stream);
 }
 
