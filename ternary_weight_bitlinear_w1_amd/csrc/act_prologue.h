@@ -39,14 +39,6 @@ constexpr int kQuantThreads = 256;
 
 typedef ActSrc Src;
 
-// Workgroup barrier that orders LDS traffic only: outstanding global loads
-// keep flowing across it.
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
 
 // The raw operands of elements 4f .. 4f+3 of one row, as loaded.
 struct RawIn {

@@ -86,6 +86,15 @@ __device__ __forceinline__ double dpp(double v) {  // the two 32-bit halves
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
+// Workgroup barrier that orders LDS traffic only: outstanding global loads
+// keep flowing across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T lanes8_sum(T v) {  // lanes 8 g .. 8 g + 7
   v += dpp<kDppXor1>(v);

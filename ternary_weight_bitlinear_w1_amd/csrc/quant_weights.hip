@@ -170,13 +170,6 @@ __global__ __launch_bounds__(kThreads) void ternarize_pack_kernel(const T *__res
 constexpr int kOnlineMaxK = 8192;
 constexpr int kOnlineMaxLines = 32;  // 128-byte lines per wave
 
-__device__ __forceinline__ void lds_only_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); loads in flight keep flowing
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 typedef short short2 __attribute__((ext_vector_type(2)));
 
 // The fields u = c + 1 (bytes, element e in byte e) of four bfloat16 weights,
@@ -239,7 +232,7 @@ __global__ __launch_bounds__(256) void online_dot_kernel(const int8_t *__restric
     const int i = threadIdx.x + kThreads * j;
     if (16 * i < K) *reinterpret_cast<v4i *>(sc + 16 * i) = cw[j];
   }
-  lds_only_barrier();
+  lds_barrier();
 
   // row n's segment and its threshold
   int seg = 0;
