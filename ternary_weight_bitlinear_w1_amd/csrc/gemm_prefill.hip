@@ -308,8 +308,18 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds_base)
 // and stores its exact int32 sum of q * u over that range to
 // part[s][m][n]; the row sums, rescale and sum over s are left to the
 // consumer (integer sums: the total is the same in any order).
-template <int WM, int WN, int TM, int TN, int P, bool GLU>
-__global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_kernel(const int8_t *__restrict__ A,
+//
+// K groups (KG > 1, for few-token shapes with at most one work item per CU):
+// the workgroup holds KG groups of WM x WN waves, each with a ring of its own;
+// group g takes chunks g, g + KG, g + 2 KG, ... of the work item, so each wave
+// walks 1 / KG of the chunk chain and two or more waves share each SIMD. At
+// the end the groups' exact int32 sums are added in group 0 through LDS and
+// group 0 runs the epilogue. Every group steps through the same number of
+// chunks, so all waves meet at every barrier. KG > 1 needs one work item per
+// workgroup (the host launches one workgroup per item), since a group's ring
+// serves as the area its sums are handed over in.
+template <int WM, int WN, int TM, int TN, int P, bool GLU, int KG = 1>
+__global__ __launch_bounds__(KG *WM *WN * 64, wgs_per_cu(KG *WM *WN)) void gemm_prefill_kernel(const int8_t *__restrict__ A,
                                                                       const uint8_t *__restrict__ B,
                                                                       const float *__restrict__ deq,
                                                                       const int32_t *__restrict__ rowsum, int M,
@@ -340,14 +350,17 @@ __global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_
   // the epilogue transposes through the stage just consumed, or through an
   // area of its own when the waves' 4 KB blocks do not fit in one stage
   constexpr bool kOwnScratch = NW * 32 * 32 * 4 > kStage;
-  __shared__ __attribute__((aligned(1024))) int8_t ring[P * kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t ring[KG * P * kStage];
   __shared__ __attribute__((aligned(1024))) float own_scratch[kOwnScratch ? NW * 32 * 32 : 1];
   __shared__ __attribute__((aligned(256))) int s_dummy[64];
   __shared__ __attribute__((aligned(256))) float s_deq[2][BM];
   __shared__ __attribute__((aligned(256))) int s_rs[2][BM];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int kg = KG == 1 ? 0 : (int)(threadIdx.x >> 6) / NW;  // K group
+  const int wave = KG == 1 ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 6) % NW;  // wave in the group
   const int wm = wave / WN, wn = wave % WN;
+  int8_t *const my_ring = ring + kg * (P * kStage);  // this K group's stages
   const int half = lane >> 5, l32 = lane & 31;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;  // GLU: (N / 2) / (BN / 2)
@@ -358,7 +371,8 @@ __global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_
   const int my_tiles = (T - b + G - 1) / G;
   const int64_t ldb = K >> 2;
   const int nk = (K >> 7) / S;  // chunks per work item
-  const int total = my_tiles * nk;
+  const int nkg = nk / KG;      // of them, this K group's
+  const int total = my_tiles * nkg;
   const bool two_stores = acc_out != nullptr;
 
   // work item i of this workgroup -> (m0, n0, split): XCD-contiguous ranges,
@@ -388,7 +402,7 @@ __global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_
       const int r = 8 * (wave * LA + j) + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int row = min(is_m0 + r, M - 1);
-      a_off[j] = (uint32_t)row * (uint32_t)K + 16u * c + 128u * (uint32_t)(is_s * nk);
+      a_off[j] = (uint32_t)row * (uint32_t)K + 16u * c + 128u * (uint32_t)(is_s * nk + kg);
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
@@ -396,23 +410,23 @@ __global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_
       const int r = 32 * jj + (lane >> 1);
       const int h = (lane & 1) ^ ((r >> 3) & 1);
       const int wrow = GLU ? ((r >> 5) & 1) * I + is_n0 + 32 * (r >> 6) + (r & 31) : is_n0 + r;
-      b_off[j] = (uint32_t)wrow * (uint32_t)ldb + 16u * h + 32u * (uint32_t)(is_s * nk);
+      b_off[j] = (uint32_t)wrow * (uint32_t)ldb + 16u * h + 32u * (uint32_t)(is_s * nk + kg);
     }
   };
   set_src();
   auto issue_chunk = [&](int8_t *st) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st) + wave * 1024 * LA);
 #pragma unroll
-    for (int j = 0; j < LA; ++j) copy16_to_lds(A + a_off[j] + 128 * is_kc, base + j * 1024);
+    for (int j = 0; j < LA; ++j) copy16_to_lds(A + a_off[j] + 128 * KG * is_kc, base + j * 1024);
     const uint32_t bbase = __builtin_amdgcn_readfirstlane(lds_addr(st + kAStage) + wave * 1024);
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
       if (LBT % NW == 0 || j * NW + wave < LBT)  // wave-uniform
-        copy16_to_lds(B + b_off[j] + 32 * is_kc, bbase + j * NW * 1024);
+        copy16_to_lds(B + b_off[j] + 32 * KG * is_kc, bbase + j * NW * 1024);
       else
         copy4_to_lds(B + 4 * lane, __builtin_amdgcn_readfirstlane(lds_addr(s_dummy)));
     }
-    if (++is_kc == nk) {
+    if (++is_kc == nkg) {
       is_kc = 0;
       if (++is_i < my_tiles) {
         coords(is_i, is_m0, is_n0, is_s);
@@ -590,17 +604,20 @@ __global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_
     asm volatile("" ::: "memory");
   };
 
-  issue_rows(0);
+  // the row data of a tile is group 0's: only its epilogue reads it (in the
+  // other groups every wait then covers one operation fewer, which waits for
+  // no less)
+  if (kg == 0) issue_rows(0);
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (j < total) issue_chunk(ring + j * kStage);
+    if (j < total) issue_chunk(my_ring + j * kStage);
   int stage = 0;  // ring slot of chunk c
   int c = 0;
   for (; c_i < my_tiles;) {
-    for (int kc = 0; kc < nk; ++kc, ++c) {
+    for (int kc = 0; kc < nkg; ++kc, ++c) {
       // wait for this wave's loads of chunk c: everything but the operations
       // issued after them (see the note above the kernel)
-      if (c + D - 1 >= total || nk <= D)
+      if (c + D - 1 >= total || nkg <= D)
         wait_vm<0>();
       else if (c_i > 0 && kc < D)
         two_stores ? wait_vm<0>() : wait_vm<kWaitAfterTile>();
@@ -608,17 +625,52 @@ __global__ __launch_bounds__(WM *WN * 64, wgs_per_cu(WM *WN)) void gemm_prefill_
         wait_vm<kWaitSteady>();
       meet();
       const int prev = stage == 0 ? P - 1 : stage - 1;  // the slot computed in the last step
-      if (c + D < total) issue_chunk(ring + prev * kStage);
-      compute(ring + stage * kStage);
+      if (c + D < total) issue_chunk(my_ring + prev * kStage);
+      compute(my_ring + stage * kStage);
       stage = stage == P - 1 ? 0 : stage + 1;
     }
-    if (c_i + 1 < my_tiles) issue_rows(c_i + 1);
-    if (nk <= D) {
+    if (kg == 0 && c_i + 1 < my_tiles) issue_rows(c_i + 1);
+    if (nkg <= D) {
       // with so few chunks the row data may still be in flight
       wait_vm<0>();
       meet();
     }
-    epilogue(ring + (stage == 0 ? P - 1 : stage - 1) * kStage);
+    if constexpr (KG > 1) {
+      // Hand the sums to group 0. Every wave is past its last chunk and, with
+      // one work item per workgroup, no chunk is in flight: each group's ring
+      // is free. Lane l's accumulator q of tile t goes to int (t 16 + q) 64 + l
+      // of its wave's block (one wave's stores cover 64 consecutive ints).
+      constexpr int kAccInts = TN * TM * 16 * 64;
+      static_assert(NW * kAccInts * 4 <= P * kStage, "a group's sums fit in its ring");
+      wait_vm<0>();
+      meet();
+      if (kg != 0) {
+        int *dst = reinterpret_cast<int *>(my_ring) + wave * kAccInts;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) dst[((tn * TM + tm) * 16 + q) * 64 + lane] = acc[tn][tm][q];
+      }
+      meet();
+      if (kg == 0) {
+#pragma unroll
+        for (int g = 1; g < KG; ++g) {
+          const int *src = reinterpret_cast<const int *>(ring + g * (P * kStage)) + wave * kAccInts;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+              for (int q = 0; q < 16; ++q) acc[tn][tm][q] += src[((tn * TM + tm) * 16 + q) * 64 + lane];
+        }
+      }
+    }
+    if (kg == 0)
+      epilogue(my_ring + (stage == 0 ? P - 1 : stage - 1) * kStage);
+    else if constexpr (!kOwnScratch)
+      meet();  // the epilogue's one barrier
     if (++c_i < my_tiles) coords(c_i, c_m0, c_n0, c_s);
   }
 }
@@ -648,19 +700,22 @@ int cu_count() {
   return n;
 }
 
-template <int WM, int WN, int TM, int TN, int P, bool GLU = false>
+template <int WM, int WN, int TM, int TN, int P, bool GLU = false, int KG = 1>
 hipError_t launch_pipelined(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum, int m,
                             int n, int k, const Epilogue &ep, float *y, int32_t *acc_out, int splits, int32_t *part,
                             hipStream_t stream) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * (n / BN) * splits;
+  // K groups: each group takes an equal share of a work item's chunks
+  if (KG > 1 && ((k / 128) / splits) % KG != 0) return hipErrorInvalidValue;
 #if BL_GEMM_PERSIST
-  int64_t grid = wgs_per_cu(WM * WN) * (int64_t)cu_count();
-  if (grid > tiles) grid = tiles;
+  int64_t grid = wgs_per_cu(KG * WM * WN) * (int64_t)cu_count();
+  if (grid > tiles || KG > 1) grid = tiles;  // K groups: one work item per workgroup
 #else
   const int64_t grid = tiles;
 #endif
-  gemm_prefill_kernel<WM, WN, TM, TN, P, GLU><<<dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream>>>(
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  gemm_prefill_kernel<WM, WN, TM, TN, P, GLU, KG><<<dim3((unsigned)grid), dim3(KG * WM * WN * 64), 0, stream>>>(
       codes, packed, deq, rowsum, m, n, k, ep, y, part ? nullptr : acc_out, splits, part);
   return hipGetLastError();
 }
@@ -786,6 +841,16 @@ int gemm_prefill_splits(int64_t m, int64_t n, int64_t k) {
   return best;
 }
 
+// Two K groups for the few-token tile of (m, n, k) split S ways: where every
+// work item gets a CU of its own and its chunk count is even. On MI355X the
+// 30-layer stack at 64 tokens took 1.458 ms per step with up to two groups,
+// 1.490 with none, 1.461 with up to three and 1.492 with up to four (the
+// 64-token gate|up contraction: 10.3 against 12.1 us).
+static bool small_k_groups(int64_t m, int64_t n, int64_t k, int S) {
+  const int64_t items = ((m + 63) / 64) * (n / BL_GEMM_SMALL_BN) * S, nk = (k / 128) / S;
+  return items <= cu_count() && nk % 2 == 0;
+}
+
 bool gemm_glu_supported(int64_t m, int64_t inter, int64_t k) {
   return m > 64 && k % 128 == 0 && inter % (BL_GEMM_BIG_BN / 2) == 0 && inter > 0 && m * k < kPipelinedMaxBytes &&
          2 * inter * (k / 4) < kPipelinedMaxBytes;
@@ -831,7 +896,12 @@ hipError_t launch_gemm_prefill(const int8_t *codes, const uint8_t *packed, const
       e = launch_pipelined<1, 4, 2, 2, 3>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
       break;
     case CFG_SMALL:
-      e = launch_pipelined<BL_GEMM_SMALL_CFG, BL_GEMM_SMALL_STAGES>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, S, part, stream);
+      if (small_k_groups(m, n, k, S))
+        e = launch_pipelined<BL_GEMM_SMALL_CFG, BL_GEMM_SMALL_STAGES, false, 2>(codes, packed, deq, rowsum, M, N, K, ep,
+                                                                                y, acc_out, S, part, stream);
+      else
+        e = launch_pipelined<BL_GEMM_SMALL_CFG, BL_GEMM_SMALL_STAGES>(codes, packed, deq, rowsum, M, N, K, ep, y,
+                                                                      acc_out, S, part, stream);
       break;
     default:
       if (m >= 256) return launch_generic<2, 2, 4, 2>(codes, packed, deq, rowsum, M, N, K, ep, y, acc_out, stream);
