@@ -382,7 +382,9 @@ def bench_small_configs(torch, bl, synth, dev, reps):
     """The two small workloads, each a chain of a few launches: the single layer
     (M=128, K=256 -> N=512, quantization inside bitlinear_forward) and the FFN
     block (M=1024, hidden 512, intermediate 2048, bitlinear_block_forward).
-    Mean time per call over back-to-back calls, and its int8 TOPS."""
+    ``us``: mean GPU time per call, 20 calls captured back to back in one HIP
+    graph and replayed; ``eager_us``: mean time per call of back-to-back calls
+    from Python, which the host's cost per call can pace. Int8 TOPS from ``us``."""
     stream = torch.cuda.current_stream(dev)
     res = {}
     # single layer
@@ -405,8 +407,14 @@ def bench_small_configs(torch, bl, synth, dev, reps):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps * 1e3
 
-    us = timed(lambda: bl.forward(packed, k, gam, x=x, out=y))
-    res["single_layer"] = {"us": round(us, 2), "tops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 3),
+    def graphed(f):
+        return graph_per_launch_us(torch, lambda i, sp: f(), 20)
+
+    f1 = lambda: bl.forward(packed, k, gam, x=x, out=y)  # noqa: E731
+    eager = timed(f1)
+    us = graphed(f1)
+    res["single_layer"] = {"us": round(us, 2), "eager_us": round(eager, 2),
+                           "tops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 3),
                            "launches": 2, "workload": "M=128, K=256 -> N=512, fp32 in and out"}
     # FFN block
     m, hd, it = 1024, 512, 2048
@@ -422,8 +430,11 @@ def bench_small_configs(torch, bl, synth, dev, reps):
     xb = torch.from_numpy(synth.activations(synth.stream_seed(BASE_SEED, 2, 0, 5), m, hd)).to(dev)
     yb = torch.empty_like(xb)
     ws = torch.empty(max(1, bl.block_workspace_bytes(spec, m)), dtype=torch.uint8, device=dev)
-    us = timed(lambda: bl.block_forward(spec, xb, out=yb, workspace=ws))
-    res["ffn_block"] = {"us": round(us, 2), "tops": round(2.0 * m * 3 * it * hd / (us * 1e-6) / 1e12, 2),
+    f2 = lambda: bl.block_forward(spec, xb, out=yb, workspace=ws)  # noqa: E731
+    eager = timed(f2)
+    us = graphed(f2)
+    res["ffn_block"] = {"us": round(us, 2), "eager_us": round(eager, 2),
+                        "tops": round(2.0 * m * 3 * it * hd / (us * 1e-6) / 1e12, 2),
                         "workload": "M=1024, hidden 512, intermediate 2048: quantize, gate|up + ReLU^2, "
                                     "ffn_sub_norm quantize, down"}
     log(f"single layer {res['single_layer']['us']:.1f} us; FFN block {res['ffn_block']['us']:.1f} us "

@@ -801,16 +801,30 @@ bool wide_pays(int64_t m, int64_t n) {
 // stay below 2^31; larger ones go to the generic kernel's 64-bit indexing.
 constexpr int64_t kPipelinedMaxBytes = (int64_t)1 << 31;
 
+// Where 128-row tiles leave at least half of the CUs without one, the 64 x 64
+// tile of the few-token shapes spreads the same work over 4 to 8 times as many
+// workgroups (on MI355X the FFN block at 1024 tokens, hidden 512: its down
+// projection, 16 tiles of 128 x 256, took 21 us).
+bool few_big_tiles(int64_t m, int64_t n, int64_t bm, int64_t bn) {
+  return n % BL_GEMM_SMALL_BN == 0 && 2 * ((m + bm - 1) / bm) * (n / bn) <= cu_count();
+}
+
 int pick_cfg(int64_t m, int64_t n, int64_t k, int64_t *bm, int64_t *bn) {
   *bm = 0;
   *bn = 0;
   if (k % 128 != 0) return CFG_GENERIC;
   if (m * k >= kPipelinedMaxBytes || n * (k / 4) >= kPipelinedMaxBytes) return CFG_GENERIC;
-  if (wide_pays(m, n)) { *bm = 128; *bn = BL_GEMM_WIDE_BN; return CFG_WIDE; }
-  if (n % BL_GEMM_BIG_BN == 0 && m > 64) { *bm = 128; *bn = BL_GEMM_BIG_BN; return CFG_BIG; }
-  if (n % 256 == 0 && m > 64) { *bm = 128; *bn = 256; return CFG_2224; }
-  if (n % 128 == 0 && m > 64) { *bm = 128; *bn = 128; return CFG_2222; }
-  if (m <= 64 && n % BL_GEMM_SMALL_BN == 0) { *bm = 64; *bn = BL_GEMM_SMALL_BN; return CFG_SMALL; }
+  int cfg = CFG_GENERIC;
+  if (wide_pays(m, n)) { *bm = 128; *bn = BL_GEMM_WIDE_BN; cfg = CFG_WIDE; }
+  else if (n % BL_GEMM_BIG_BN == 0 && m > 64) { *bm = 128; *bn = BL_GEMM_BIG_BN; cfg = CFG_BIG; }
+  else if (n % 256 == 0 && m > 64) { *bm = 128; *bn = 256; cfg = CFG_2224; }
+  else if (n % 128 == 0 && m > 64) { *bm = 128; *bn = 128; cfg = CFG_2222; }
+  if (cfg != CFG_GENERIC && !few_big_tiles(m, n, *bm, *bn)) return cfg;
+  if ((m <= 64 || cfg != CFG_GENERIC) && n % BL_GEMM_SMALL_BN == 0) {
+    *bm = 64; *bn = BL_GEMM_SMALL_BN; return CFG_SMALL;
+  }
+  *bm = 0;
+  *bn = 0;
   if (n % 256 == 0) { *bm = 64; *bn = 256; return CFG_1422; }
   return CFG_GENERIC;
 }
@@ -859,6 +873,12 @@ bool gemm_glu_supported(int64_t m, int64_t inter, int64_t k) {
 hipError_t launch_gemm_glu(const int8_t *codes, const uint8_t *packed, const float *deq, const int32_t *rowsum,
                            int64_t m, int64_t inter, int64_t k, const Epilogue &ep, float *y, hipStream_t stream) {
   if (!gemm_glu_supported(m, inter, k) || ep.n_seg != 2) return hipErrorInvalidValue;
+  // few 128 x 256 tiles: 64 x 128 ones (64 features of gate and up, four waves
+  // of 32 x 64), 8 times as many (the FFN block at 1024 tokens, intermediate
+  // 2048: 128 tiles of 128 x 256 took 12 us on MI355X)
+  if (few_big_tiles(m, 2 * inter, 128, BL_GEMM_BIG_BN))
+    return launch_pipelined<2, 2, 1, 2, 4, true>(codes, packed, deq, rowsum, (int)m, (int)(2 * inter), (int)k, ep, y,
+                                                 nullptr, 1, nullptr, stream);
   return launch_pipelined<BL_GEMM_BIG_CFG, 3, true>(codes, packed, deq, rowsum, (int)m, (int)(2 * inter), (int)k, ep,
                                                     y, nullptr, 1, nullptr, stream);
 }

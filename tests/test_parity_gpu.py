@@ -164,9 +164,12 @@ def test_forward_single_layer():
 
 RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 16), (257, 129, 2576),
           (16, 16, 16), (2, 33, 4112), (300, 700, 1040),
-          # shapes the pipelined kernel takes (N % 128 == 0, K % 128 == 0): every tile
-          # variant, K-chunk counts 1, 2, 3, 5, 9 and M not a multiple of the tile
+          # shapes the pipelined kernel takes (N % 128 == 0, K % 128 == 0): K-chunk counts 1, 2, 3,
+          # 5, 9 and M not a multiple of the tile; past 64 tokens, where 128-row tiles would leave
+          # half of the CUs idle, the 64 x 64 tile
           (130, 512, 256), (65, 384, 384), (40, 768, 640), (333, 1280, 1152), (20, 256, 128), (257, 2560, 2560),
+          # enough 128-row tiles: 128 x 256 and 128 x 128
+          (1100, 4096, 384), (2000, 1152, 256),
           # few-token shapes of the dot-product decode kernel (one token, K % 64 == 0) and of the
           # MFMA decode kernel (2 to 4 tokens): rows not a multiple of 8, K from one partial line
           # to 8192, every split of K over waves
@@ -209,8 +212,9 @@ def test_forward_ragged(m, n, k):
 
 
 # ------------------------------------------------------------------------------ gated up-projection
-GLU = [(200, 512, 1024), (130, 384, 256), (65, 256, 2560), (257, 640, 640),  # gating fused in the kernel
-       (1000, 8448, 128),  # 528 tiles for 512 workgroups
+GLU = [(200, 512, 1024), (130, 384, 256), (65, 256, 2560), (257, 640, 640),  # gating fused, 64 x 128 tiles
+       (1000, 8448, 128),  # 528 tiles of 128 x 256 for 512 workgroups
+       (1100, 2048, 256),  # 144 tiles of 128 x 256
        (300, 200, 1040), (40, 256, 512), (5, 512, 512), (1, 96, 320)]          # gate|up through the workspace
 
 
