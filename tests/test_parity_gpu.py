@@ -190,8 +190,9 @@ RAGGED = [(1, 40, 48), (3, 200, 80), (17, 130, 272), (130, 1000, 64), (64, 96, 1
           # ragged rows, few and many supersteps per wave
           (17, 130, 512), (32, 1000, 768), (33, 48, 2560), (64, 2600, 6912), (50, 3000, 1024),
           # at most 64 tokens, one work item per CU and an even chunk count: two K groups per
-          # workgroup (200 tiles unsplit; 24 tiles split in two)
-          (61, 12800, 512), (50, 1536, 1024),
+          # workgroup (200 tiles unsplit; 24 tiles split in two; exactly 256 items, unsplit and
+          # split four ways)
+          (61, 12800, 512), (50, 1536, 1024), (64, 16384, 256), (47, 4096, 2048),
           # the 8-wave 128 x 320 tile (N % 320 == 0 and at least one tile per CU): ragged last row
           # tile; two rounds of tiles with one K chunk each
           (4000, 2560, 256), (4096, 5120, 128),
