@@ -559,7 +559,7 @@ def bench_decode(torch, bl, synth, dev, reps, packed_gu, gam_gu, packed_d, gam_d
                                    "packed_bytes": nbytes, "ring_copies": copies}
             log(f"decode {name} m={m}: {b2b_us:.2f} us/launch back-to-back (graph), {gbs:.0f} GB/s "
                 f"(one launch between events: {us:.2f} us)")
-            if m <= 4:
+            if m in (1, 4, 16):
                 res[f"{name}_m{m}_probe_whole_ring"] = bench_decode_tall(torch, L, bl, ring, k, gam[0], seg[0], codes,
                                                                          deq, rs, y, reps, name, m, sp0, stream)
         # reference: a device copy of the same bytes (one ring copy per launch,

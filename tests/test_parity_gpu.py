@@ -428,7 +428,7 @@ def test_forward_decode_full_size(m, proj):
         assert_equal(host(y_dec), host(y_pre), "decode == prefill")
 
 
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 4, 16])
 @pytest.mark.parametrize("proj", ["gate_up", "down"])
 def test_forward_decode_tall(m, proj):
     """The decode kernels in one launch over many stacked copies of a 2B4T matrix
